@@ -1,0 +1,168 @@
+"""CPU oracle for block-scaled FP8 GEMM (D = C + A.B^T, NT) and its M-grouped forms.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The GPU library never
+imports, links or calls anything here, and nothing here imports the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain C, FP64, one pthread per core);
+this module only compiles it and marshals numpy arrays through ctypes.
+Semantics and citations are in the header of ``oracle.c``:
+
+* DeepGEMM README, "Interfaces / Notes": D = C + A @ B.T for the NT layout,
+  FP32 scale factors, LHS scales stored MN-major.
+* DeepGEMM launch article, section 2: per-block promotion into a
+  higher-precision accumulator.
+* DeepGEMM README, "Grouped GEMM (contiguous layout)" and "(masked layout)".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+KBLOCK = 128
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile ``oracle.c`` (or a given copy of it) into a shared library."""
+    cmd = ["gcc", "-O2", "-Wall", "-shared", "-fPIC", "-pthread", "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _needs_build() -> bool:
+    return (not os.path.exists(_LIB_PATH)
+            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+
+
+def _declare(lib):
+    c = ctypes
+    p = c.c_void_p
+    lib.oracle_e4m3_value.restype = c.c_double
+    lib.oracle_e4m3_value.argtypes = [c.c_uint8]
+    lib.oracle_e4m3_table.restype = None
+    lib.oracle_e4m3_table.argtypes = [p]
+    lib.oracle_bf16_rne.restype = c.c_uint16
+    lib.oracle_bf16_rne.argtypes = [c.c_double]
+    lib.oracle_default_threads.restype = c.c_int
+    lib.oracle_default_threads.argtypes = []
+    lib.oracle_fp8_gemm_nt.restype = c.c_int
+    lib.oracle_fp8_gemm_nt.argtypes = [p, p, p, p, p, c.c_int64, c.c_int, c.c_int,
+                                       p, c.c_int64, p, c.c_int]
+    for name in ("oracle_m_grouped_contiguous", "oracle_m_grouped_masked"):
+        f = getattr(lib, name)
+        f.restype = c.c_int
+        f.argtypes = [p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                      p, c.c_int64, p, p, c.c_int]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it first if missing or stale).
+
+    With ``path`` given, load that file (used for deliberately broken copies
+    in the negative-control tests) without caching it.
+    """
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if _needs_build():
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+class Oracle:
+    """numpy front-end over one loaded copy of the oracle library."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else load()
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_default_threads())
+
+    def e4m3_table(self) -> np.ndarray:
+        out = np.empty(256, dtype=np.float64)
+        self.lib.oracle_e4m3_table(_ptr(out))
+        return out
+
+    def bf16_rne(self, x: np.ndarray) -> np.ndarray:
+        x = np.asarray(x, dtype=np.float64).ravel()
+        return np.array([self.lib.oracle_bf16_rne(float(v)) for v in x], dtype=np.uint16)
+
+    def fp8_gemm_nt(self, A, sfa, B, sfb, C=None, rows=None, threads=0):
+        """D (FP64) of the dense form; A [M,K] u8, sfa [K/128,M], B [N,K] u8, sfb [Nb,Kb]."""
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32); C = _c(C, np.float32)
+        M, K = A.shape
+        N = B.shape[0]
+        r, nr = _rows(rows)
+        out = np.empty(((nr if r is not None else M), N), dtype=np.float64)
+        rc = self.lib.oracle_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C),
+                                         M, N, K, _ptr(r), nr, _ptr(out), threads)
+        if rc != 0:
+            raise ValueError("oracle_fp8_gemm_nt: bad sizes")
+        return out
+
+    def m_grouped_contiguous(self, A, sfa, B, sfb, m_indices, C=None, rows=None, threads=0):
+        """(D FP64 [rows,N], computed u8 [rows]) of the contiguous grouped form."""
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32); C = _c(C, np.float32)
+        mi = _c(m_indices, np.int32)
+        M, K = A.shape
+        G, N = B.shape[0], B.shape[1]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else M
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_m_grouped_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(mi),
+                                                  _ptr(C), M, N, K, G, _ptr(r), nr, _ptr(out),
+                                                  _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_m_grouped_contiguous: bad sizes")
+        return out, comp.astype(bool)
+
+    def m_grouped_masked(self, A, sfa, B, sfb, masked_m, C=None, rows=None, threads=0):
+        """(D FP64 [rows,N], computed u8 [rows]) of the masked grouped form.
+
+        A [G,M_max,K], sfa [G,K/128,M_max], B [G,N,K], sfb [G,Nb,Kb]; rows are flat
+        indices g*M_max + m (None: all rows, output shaped [G*M_max, N]).
+        """
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32); C = _c(C, np.float32)
+        mm = _c(masked_m, np.int32)
+        G, M_max, K = A.shape
+        N = B.shape[1]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else G * M_max
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_m_grouped_masked(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(mm),
+                                              _ptr(C), M_max, N, K, G, _ptr(r), nr, _ptr(out),
+                                              _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_m_grouped_masked: bad sizes")
+        return out, comp.astype(bool)

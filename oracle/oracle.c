@@ -1,0 +1,325 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for block-scaled
+ * FP8 GEMM  D = C + A . B^T  (NT layout) and its two M-grouped forms.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load or call this file.  The GPU
+ * library never includes, links or calls it, and it shares no code, header,
+ * table or constant with the GPU library.
+ *
+ * Sources (the pages this follows):
+ *  - DeepGEMM README (pigsec.cn mirror), "Interfaces / Notes": kernels compute
+ *    D = C + A @ B with the NT input layout, so fp8_gemm_nt is D = C + A @ B.T;
+ *    on the SM90 path the scale factors are FP32 and the LHS scales are stored
+ *    transposed (MN-major).
+ *  - DeepGEMM launch article (2048ai.net), section 2 "FP8": the FP8 tensor-core
+ *    partial products are accumulated a second time in higher precision
+ *    ("promotion"), i.e. each 128-wide K block is reduced on its own and then
+ *    scaled and added into an FP32 accumulator.
+ *  - DeepGEMM README, "Grouped GEMM (contiguous layout)": only M is grouped,
+ *    N and K are shared, each expert segment is aligned to the GEMM M block.
+ *  - DeepGEMM README, "Grouped GEMM (masked layout)": a mask tensor tells the
+ *    kernel which part of each group is valid; only that part is computed.
+ *  - The FP8 format is E4M3.  The pages do not define the encoding; this file
+ *    takes the OCP "E4M3FN" reading (max finite 448, no infinities, NaN only
+ *    at S.1111.111), because the workloads scale blocks by amax/448.
+ *  - Block sizes: A scales per 1x128 (one row, one K block), B scales per
+ *    128x128 (128 rows of B, one K block).
+ *
+ * What is computed, for every output row m that is computed and every n:
+ *     S[m,n,kb] = sum_{k in block kb} e4m3(A[m,k]) * e4m3(B[n,k])      (FP64)
+ *     D[m,n]    = C[m,n] + sum_kb (sfa[kb][m] * sfb[n/128][kb]) * S[m,n,kb]
+ * in FP64, ascending kb, with no rounding to BF16 (D stays FP64).
+ * Every finite E4M3 value is a multiple of 2^-9 and |S| <= 128*448^2 < 2^25,
+ * so S needs at most 43 significant bits and FP64 sums it exactly in any order.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_KBLOCK 128   /* K extent of one scale block (1x128 and 128x128) */
+#define ORACLE_NBLOCK 128   /* N extent of one B scale block (128x128)        */
+
+/* ------------------------------------------------------------------ */
+/* E4M3 (OCP FN) decode, from the bit fields: sign s = bit 7,          */
+/* exponent e = bits 6..3 (bias 7), mantissa m = bits 2..0.            */
+/*   e == 0           : (-1)^s * (m/8) * 2^-6         (subnormal)      */
+/*   e in 1..15       : (-1)^s * (1 + m/8) * 2^(e-7)  (normal)         */
+/*   e == 15 && m == 7: NaN  (the only non-finite pattern; no Inf)     */
+/* ------------------------------------------------------------------ */
+double oracle_e4m3_value(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+void oracle_e4m3_table(double *out256)
+{
+    for (int c = 0; c < 256; ++c)
+        out256[c] = oracle_e4m3_value((uint8_t)c);
+}
+
+/* ------------------------------------------------------------------ */
+/* BF16 (1 sign, 8 exponent bits with bias 127, 7 mantissa bits),     */
+/* round-to-nearest, ties-to-even, straight from a double.  The        */
+/* outputs of all three operations are BF16.                           */
+/* ------------------------------------------------------------------ */
+static double round_half_even(double v) /* v >= 0, v < 2^52 */
+{
+    double fl = floor(v);
+    double d = v - fl;
+    if (d > 0.5)
+        return fl + 1.0;
+    if (d < 0.5)
+        return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+uint16_t oracle_bf16_rne(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7F80;
+    int e;
+    (void)frexp(a, &e);          /* a in [2^(e-1), 2^e) */
+    int E = e - 1;               /* a = 1.f * 2^E */
+    int qexp = (E < -126) ? -133 : E - 7;  /* value of one unit in the last place */
+    double r = ldexp(round_half_even(ldexp(a, -qexp)), qexp);
+    if (r >= 0x1p128)
+        return sign | 0x7F80;    /* rounds past the largest finite BF16 */
+    if (r < 0x1p-126)
+        return sign | (uint16_t)ldexp(r, 133);        /* subnormal */
+    int e2;
+    (void)frexp(r, &e2);
+    int E2 = e2 - 1;
+    uint16_t mant = (uint16_t)(ldexp(r, 7 - E2) - 128.0);
+    return sign | (uint16_t)((E2 + 127) << 7) | mant;
+}
+
+/* ------------------------------------------------------------------ */
+/* One output row: D[n] = C[n] + sum_kb sa(kb) * sfb[n/128][kb] * S    */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const double *dec;      /* 256-entry decode table */
+    const uint8_t *a_row;   /* K codes of this row of A */
+    const float *sa;        /* sfa for this row; the kb-th value is sa[kb * sa_stride] */
+    int64_t sa_stride;
+    const uint8_t *b;       /* B of the selected group, [N][K] codes */
+    const float *sfb;       /* sfb of the selected group, [Nb][Kb] */
+    const float *c_row;     /* NULL or N floats */
+    int N, K;
+    double *out;            /* N doubles */
+} row_job;
+
+static void compute_row(const row_job *j)
+{
+    const int Kb = j->K / ORACLE_KBLOCK;
+    for (int n = 0; n < j->N; ++n) {
+        const uint8_t *b_row = j->b + (int64_t)n * j->K;
+        const float *sb = j->sfb + (int64_t)(n / ORACLE_NBLOCK) * Kb;
+        double acc = 0.0;
+        for (int kb = 0; kb < Kb; ++kb) {
+            double s = 0.0;   /* exact block sum */
+            const uint8_t *ap = j->a_row + kb * ORACLE_KBLOCK;
+            const uint8_t *bp = b_row + kb * ORACLE_KBLOCK;
+            for (int k = 0; k < ORACLE_KBLOCK; ++k)
+                s += j->dec[ap[k]] * j->dec[bp[k]];
+            double scale = (double)j->sa[kb * j->sa_stride] * (double)sb[kb];
+            acc += scale * s;
+        }
+        j->out[n] = acc + (j->c_row ? (double)j->c_row[n] : 0.0);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Row scheduling over threads.                                        */
+/* ------------------------------------------------------------------ */
+enum { KIND_DENSE = 0, KIND_CONTIG = 1, KIND_MASKED = 2 };
+
+typedef struct {
+    int kind;
+    const uint8_t *A; const float *sfa; const uint8_t *B; const float *sfb;
+    const int32_t *group_info;   /* m_indices (contig) or masked_m (masked) */
+    const float *C;
+    int64_t M;                   /* rows of A (dense/contig) or M_max (masked) */
+    int N, K, G;
+    const int64_t *rows; int64_t n_rows;
+    double *out; uint8_t *computed;
+    double dec[256];
+} problem;
+
+typedef struct { const problem *p; int64_t r0, r1; } slice;
+
+static void do_row(const problem *p, int64_t i)
+{
+    const int Kb = p->K / ORACLE_KBLOCK;
+    const int Nb = (p->N + ORACLE_NBLOCK - 1) / ORACLE_NBLOCK;
+    int64_t r = p->rows ? p->rows[i] : i;
+    double *out = p->out + i * (int64_t)p->N;
+    row_job j;
+    j.dec = p->dec; j.N = p->N; j.K = p->K; j.out = out;
+
+    if (p->kind == KIND_DENSE) {
+        j.a_row = p->A + r * p->K;
+        j.sa = p->sfa + r; j.sa_stride = p->M;
+        j.b = p->B; j.sfb = p->sfb;
+        j.c_row = p->C ? p->C + r * p->N : NULL;
+    } else if (p->kind == KIND_CONTIG) {
+        int32_t g = p->group_info[r];
+        if (g < 0 || g >= p->G) {            /* padding row: not computed */
+            for (int n = 0; n < p->N; ++n) out[n] = NAN;
+            if (p->computed) p->computed[i] = 0;
+            return;
+        }
+        j.a_row = p->A + r * p->K;
+        j.sa = p->sfa + r; j.sa_stride = p->M;
+        j.b = p->B + (int64_t)g * p->N * p->K;
+        j.sfb = p->sfb + (int64_t)g * Nb * Kb;
+        j.c_row = p->C ? p->C + r * p->N : NULL;
+    } else {
+        int64_t g = r / p->M, m = r % p->M;
+        int64_t valid = p->group_info[g];
+        if (valid < 0) valid = 0;
+        if (valid > p->M) valid = p->M;
+        if (m >= valid) {                    /* masked row: not computed */
+            for (int n = 0; n < p->N; ++n) out[n] = NAN;
+            if (p->computed) p->computed[i] = 0;
+            return;
+        }
+        j.a_row = p->A + r * p->K;
+        j.sa = p->sfa + g * Kb * p->M + m; j.sa_stride = p->M;
+        j.b = p->B + g * p->N * (int64_t)p->K;
+        j.sfb = p->sfb + g * Nb * (int64_t)Kb;
+        j.c_row = p->C ? p->C + r * p->N : NULL;
+    }
+    compute_row(&j);
+    if (p->computed) p->computed[i] = 1;
+}
+
+static void *worker(void *arg)
+{
+    const slice *s = (const slice *)arg;
+    for (int64_t i = s->r0; i < s->r1; ++i)
+        do_row(s->p, i);
+    return NULL;
+}
+
+int oracle_default_threads(void)
+{
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+        int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    return 1;
+}
+
+static int run(problem *p, int n_threads)
+{
+    if (p->K <= 0 || p->K % ORACLE_KBLOCK != 0 || p->N <= 0 || p->M <= 0 || p->n_rows < 0)
+        return -1;
+    oracle_e4m3_table(p->dec);
+    if (n_threads <= 0) n_threads = oracle_default_threads();
+    if (n_threads > p->n_rows) n_threads = (int)(p->n_rows > 0 ? p->n_rows : 1);
+    if (n_threads > 256) n_threads = 256;
+    pthread_t tid[256];
+    int joined[256];
+    slice sl[256];
+    int64_t per = (p->n_rows + n_threads - 1) / n_threads;
+    for (int t = 0; t < n_threads; ++t) {
+        sl[t].p = p;
+        sl[t].r0 = t * per < p->n_rows ? t * per : p->n_rows;
+        sl[t].r1 = (t + 1) * per < p->n_rows ? (t + 1) * per : p->n_rows;
+        joined[t] = 0;
+        if (sl[t].r0 >= sl[t].r1)
+            continue;
+        if (pthread_create(&tid[t], NULL, worker, &sl[t]) == 0)
+            joined[t] = 1;
+        else
+            worker(&sl[t]);          /* could not start a thread: do it here */
+    }
+    for (int t = 0; t < n_threads; ++t)
+        if (joined[t])
+            pthread_join(tid[t], NULL);
+    return 0;
+}
+
+/*
+ * Dense:  D = C + A . B^T.
+ *   A [M][K] e4m3 codes, sfa [K/128][M], B [N][K] codes, sfb [ceil(N/128)][K/128],
+ *   C NULL or [M][N] fp32.  rows: NULL (all M rows, out is [M][N]) or n_rows row
+ *   indices (out is [n_rows][N]).  Returns 0, or -1 on bad sizes.
+ */
+int oracle_fp8_gemm_nt(const uint8_t *A, const float *sfa, const uint8_t *B, const float *sfb,
+                       const float *C, int64_t M, int N, int K,
+                       const int64_t *rows, int64_t n_rows, double *out, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    p.kind = KIND_DENSE; p.A = A; p.sfa = sfa; p.B = B; p.sfb = sfb; p.C = C;
+    p.M = M; p.N = N; p.K = K; p.G = 1;
+    p.rows = rows; p.n_rows = rows ? n_rows : M; p.out = out;
+    return run(&p, n_threads);
+}
+
+/*
+ * M-grouped contiguous: row m uses expert g = m_indices[m] (B[g], sfb[g]);
+ * rows whose index lies outside [0, G) are padding and are not computed
+ * (out row = NaN, computed[i] = 0).
+ *   A [M][K], sfa [K/128][M], B [G][N][K], sfb [G][ceil(N/128)][K/128],
+ *   m_indices [M] int32, C NULL or [M][N].
+ */
+int oracle_m_grouped_contiguous(const uint8_t *A, const float *sfa, const uint8_t *B,
+                                const float *sfb, const int32_t *m_indices, const float *C,
+                                int64_t M, int N, int K, int G,
+                                const int64_t *rows, int64_t n_rows, double *out,
+                                uint8_t *computed, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    p.kind = KIND_CONTIG; p.A = A; p.sfa = sfa; p.B = B; p.sfb = sfb; p.C = C;
+    p.group_info = m_indices; p.M = M; p.N = N; p.K = K; p.G = G;
+    p.rows = rows; p.n_rows = rows ? n_rows : M; p.out = out; p.computed = computed;
+    if (G <= 0) return -1;
+    return run(&p, n_threads);
+}
+
+/*
+ * M-grouped masked: group g computes rows m < clamp(masked_m[g], 0, M_max);
+ * the other rows are not computed (out row = NaN, computed[i] = 0).
+ *   A [G][M_max][K], sfa [G][K/128][M_max], B [G][N][K], sfb [G][ceil(N/128)][K/128],
+ *   masked_m [G] int32, C NULL or [G][M_max][N].
+ *   rows are flat indices g*M_max + m (NULL: all G*M_max rows).
+ */
+int oracle_m_grouped_masked(const uint8_t *A, const float *sfa, const uint8_t *B,
+                            const float *sfb, const int32_t *masked_m, const float *C,
+                            int64_t M_max, int N, int K, int G,
+                            const int64_t *rows, int64_t n_rows, double *out,
+                            uint8_t *computed, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    p.kind = KIND_MASKED; p.A = A; p.sfa = sfa; p.B = B; p.sfb = sfb; p.C = C;
+    p.group_info = masked_m; p.M = M_max; p.N = N; p.K = K; p.G = G;
+    p.rows = rows; p.n_rows = rows ? n_rows : (int64_t)G * M_max; p.out = out; p.computed = computed;
+    if (G <= 0) return -1;
+    return run(&p, n_threads);
+}

@@ -1,0 +1,212 @@
+"""Seeded synthetic inputs for block-scaled FP8 GEMM, shared by the tests and the bench.
+
+This module draws random numbers and quantises them; it holds none of the
+GEMM's arithmetic and imports neither the GPU library nor the oracle.
+
+Quantisation is the caller's job on the pages (DeepGEMM README, "Interfaces /
+Notes": FP8 casting and transposition are left to the user), so it lives here,
+on the input side:
+
+* A, one scale per 1x128 block (one row, 128 consecutive K), stored MN-major
+  as ``sfa[K/128][M]`` (the README's "transposed" LHS-scale layout);
+* B, one scale per 128x128 block (128 rows of B, 128 consecutive K), stored
+  ``sfb[ceil(N/128)][K/128]``;
+* scale = amax/448 in FP32 (1.0 for an all-zero block), code =
+  E4M3FN(clamp(x/scale, -448, 448)), rounded to nearest-even by torch's cast.
+
+Workload recipe (sizes from the DeepGEMM launch article, section 3 tables):
+values ~N(0,1) from ``torch.Generator('cpu')`` seeded with ``1000 + config``,
+drawn in the order A, B, C, masked_m.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+KBLOCK = 128
+E4M3_MAX = 448.0
+
+
+# ---------------------------------------------------------------- quantisers
+def _cast_e4m3(x: torch.Tensor) -> torch.Tensor:
+    return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quantize_1x128(x: torch.Tensor):
+    """x [..., M, K] fp32 -> (codes u8 [..., M, K], sfa fp32 [..., K/128, M])."""
+    *lead, M, K = x.shape
+    assert K % KBLOCK == 0
+    xb = x.reshape(*lead, M, K // KBLOCK, KBLOCK)
+    amax = xb.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = _cast_e4m3(xb / s.unsqueeze(-1)).reshape(*lead, M, K)
+    return q.contiguous(), s.transpose(-1, -2).contiguous()
+
+
+def quantize_128x128(x: torch.Tensor):
+    """x [..., N, K] fp32 -> (codes u8 [..., N, K], sfb fp32 [..., ceil(N/128), K/128])."""
+    *lead, N, K = x.shape
+    assert K % KBLOCK == 0
+    Nb = (N + KBLOCK - 1) // KBLOCK
+    pad = Nb * KBLOCK - N
+    xp = torch.nn.functional.pad(x, (0, 0, 0, pad)) if pad else x
+    xb = xp.reshape(*lead, Nb, KBLOCK, K // KBLOCK, KBLOCK)
+    amax = xb.abs().amax(dim=(-3, -1))
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = _cast_e4m3(xb / s[..., :, None, :, None]).reshape(*lead, Nb * KBLOCK, K)
+    return q[..., :N, :].contiguous(), s.contiguous()
+
+
+# ---------------------------------------------------------------- problems
+@dataclasses.dataclass
+class Problem:
+    kind: str                       # "dense" | "contiguous" | "masked"
+    A: torch.Tensor                 # u8 codes
+    sfa: torch.Tensor               # fp32
+    B: torch.Tensor                 # u8 codes
+    sfb: torch.Tensor               # fp32
+    C: Optional[torch.Tensor] = None
+    m_indices: Optional[torch.Tensor] = None   # int32 [M] (contiguous)
+    masked_m: Optional[torch.Tensor] = None    # int32 [G] (masked)
+    seed: int = 0
+
+    @property
+    def M(self):
+        return self.A.shape[-2]
+
+    @property
+    def N(self):
+        return self.B.shape[-2]
+
+    @property
+    def K(self):
+        return self.A.shape[-1]
+
+    @property
+    def G(self):
+        return 1 if self.kind == "dense" else self.B.shape[0]
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def make_dense(M, N, K, seed, with_c=False) -> Problem:
+    g = _gen(seed)
+    a = torch.randn(M, K, generator=g, dtype=torch.float32)
+    b = torch.randn(N, K, generator=g, dtype=torch.float32)
+    c = torch.randn(M, N, generator=g, dtype=torch.float32) if with_c else None
+    A, sfa = quantize_1x128(a)
+    del a
+    B, sfb = quantize_128x128(b)
+    del b
+    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed)
+
+
+def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128) -> Problem:
+    """Experts' tokens concatenated along M, each segment padded to ``align`` rows.
+
+    group_rows[g] valid rows for expert g; padding rows get index -1.  With
+    ``pad_rows`` given, that many extra -1 rows are appended.
+    """
+    G = len(group_rows)
+    g = _gen(seed)
+    seg = [((r + align - 1) // align) * align for r in group_rows]
+    M = sum(seg) + (pad_rows or 0)
+    a = torch.randn(M, K, generator=g, dtype=torch.float32)
+    b = torch.randn(G, N, K, generator=g, dtype=torch.float32)
+    c = torch.randn(M, N, generator=g, dtype=torch.float32) if with_c else None
+    idx = torch.full((M,), -1, dtype=torch.int32)
+    off = 0
+    for e, (r, s) in enumerate(zip(group_rows, seg)):
+        idx[off:off + r] = e
+        off += s
+    A, sfa = quantize_1x128(a)
+    del a
+    B, sfb = quantize_128x128(b)
+    del b
+    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed)
+
+
+def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None) -> Problem:
+    g = _gen(seed)
+    a = torch.randn(G, M_max, K, generator=g, dtype=torch.float32)
+    b = torch.randn(G, N, K, generator=g, dtype=torch.float32)
+    c = torch.randn(G, M_max, N, generator=g, dtype=torch.float32) if with_c else None
+    if masked_m is None:
+        mm = torch.randint(0, M_max + 1, (G,), generator=g, dtype=torch.int32)
+    else:
+        mm = torch.as_tensor(masked_m, dtype=torch.int32)
+    A, sfa = quantize_1x128(a)
+    del a
+    B, sfb = quantize_128x128(b)
+    del b
+    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed)
+
+
+# ---------------------------------------------------------------- the five workloads
+# (shapes: DeepGEMM launch article, section 3, dense table and MoE table)
+CONFIGS = {
+    0: dict(kind="dense", M=64, N=2112, K=7168),
+    1: dict(kind="dense", M=128, N=24576, K=1536),
+    "1c": dict(kind="dense", M=128, N=24576, K=1536, with_c=True),
+    2: dict(kind="dense", M=4096, N=7168, K=16384),
+    3: dict(kind="contiguous", G=4, rows_per_group=8192, N=4096, K=7168),
+    4: dict(kind="masked", G=4, M_max=256, N=7168, K=2048),
+}
+
+CONFIG_NAMES = {
+    0: "dense_64x2112x7168",
+    1: "dense_128x24576x1536",
+    "1c": "dense_128x24576x1536_plusC",
+    2: "dense_4096x7168x16384",
+    3: "contiguous_4x8192x4096x7168",
+    4: "masked_4x256x7168x2048",
+}
+
+
+def config_seed(cfg) -> int:
+    return 1000 + (1 if cfg == "1c" else int(cfg))
+
+
+def make_config(cfg) -> Problem:
+    c = CONFIGS[cfg]
+    seed = config_seed(cfg)
+    if c["kind"] == "dense":
+        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False))
+    if c["kind"] == "contiguous":
+        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed)
+    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed)
+
+
+# ---------------------------------------------------------------- structured inputs for pins
+E4M3_ONE = 0x38
+
+
+def integer_codes(shape, gen, max_abs=16):
+    """E4M3 codes of random integers in [-max_abs, max_abs] (all exactly representable)."""
+    v = torch.randint(-max_abs, max_abs + 1, shape, generator=gen).to(torch.float32)
+    return _cast_e4m3(v)
+
+
+def pow2_scales(shape, gen, lo=-3, hi=3):
+    e = torch.randint(lo, hi + 1, shape, generator=gen).to(torch.float32)
+    return torch.pow(2.0, e)
+
+
+def sentinel_like(shape, seed) -> torch.Tensor:
+    """Seeded random 16-bit patterns (viewed as bf16) used to prefill D."""
+    g = _gen(seed)
+    return torch.randint(0, 1 << 16, shape, generator=g, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+
+
+def to_numpy(p: Problem):
+    """numpy views of a problem's tensors (for the oracle)."""
+    f = lambda t: None if t is None else t.numpy()
+    return dict(A=f(p.A), sfa=f(p.sfa), B=f(p.B), sfb=f(p.sfb), C=f(p.C),
+                m_indices=f(p.m_indices), masked_m=f(p.masked_m))

@@ -1,0 +1,276 @@
+"""Pins of the CPU oracle against things other than itself (all CPU-only).
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped K block,
+the FNUZ reading of E4M3, a wrong scale index or layout, a transposed operand,
+a lost sign, an ignored C, a wrong group or mask rule) fails at least one of
+them; ``test_oracle_mutants.py`` plants those slips and checks that they do.
+
+Pins used:
+* library routines: torch's float8_e4m3fn -> float32 decode, torch's
+  float32 -> bfloat16 cast, numpy FP64 matmul of dequantised operands;
+* exact integer arithmetic: int64 matmul of codes x 512;
+* closed forms: all-ones codes, one-hot rows, sign flip, power-of-two scaling;
+* group/mask invariants from the grouped-layout sections of the DeepGEMM README.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from tests import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_decode_table():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+
+
+def dequant_ref(p, dec):
+    """numpy FP64 (A*sfa) @ (B*sfb)^T (+C) for a dense problem; also the |.| bound."""
+    A = dec[p.A.numpy()]
+    B = dec[p.B.numpy()]
+    M, K = A.shape
+    N = B.shape[0]
+    sa = np.repeat(p.sfa.numpy().astype(np.float64).T, 128, axis=1)            # [M, K]
+    sb = np.repeat(np.repeat(p.sfb.numpy().astype(np.float64), 128, axis=0)[:N], 128, axis=1)
+    Ad, Bd = A * sa, B * sb
+    ref = Ad @ Bd.T
+    mag = np.abs(Ad) @ np.abs(Bd).T
+    if p.C is not None:
+        ref = ref + p.C.numpy().astype(np.float64)
+        mag = mag + np.abs(p.C.numpy().astype(np.float64))
+    return ref, mag
+
+
+# ------------------------------------------------------------------ E4M3 decode
+def test_e4m3_table_matches_torch_decode(oracle):
+    t = oracle.e4m3_table()
+    r = torch_decode_table()
+    assert np.array_equal(np.isnan(t), np.isnan(r))
+    ok = ~np.isnan(t)
+    assert np.array_equal(t[ok], r[ok])
+    # signed zero as well
+    assert np.array_equal(np.signbit(t[ok]), np.signbit(r[ok]))
+
+
+def test_e4m3_table_format_facts(oracle):
+    """Facts fixed by the E4M3FN format (see tests/golden/e4m3_points.json)."""
+    t = oracle.e4m3_table()
+    with open(os.path.join(GOLDEN, "e4m3_points.json")) as f:
+        pts = json.load(f)
+    for code, val in pts["points"].items():
+        c = int(code, 16)
+        if val == "nan":
+            assert np.isnan(t[c])
+        else:
+            assert t[c] == float(val), (code, t[c], val)
+    assert int(np.isnan(t).sum()) == 2
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)                     # strictly increasing 0x00..0x7E
+    assert np.all(t[0x80:0xFF] == -t[0x00:0x7F])        # sign bit is a pure sign
+    fin = t[~np.isnan(t)]
+    assert np.all(fin * 512 == np.round(fin * 512))     # every value is a multiple of 2^-9
+    assert np.max(np.abs(fin)) == 448.0                 # amax/448 scaling hits the top code
+
+
+# ------------------------------------------------------------------ BF16 rounding
+def test_bf16_rne_matches_torch_cast(oracle):
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(4000, generator=g) * torch.pow(2.0, torch.randint(-30, 30, (4000,), generator=g).float())
+    special = torch.tensor([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 1.0078125 + 2 ** -9, 3.3895313892515355e38,
+                            3.4028234663852886e38, 1e-38, 9.183549615799121e-41, 1.1754943508222875e-38,
+                            -2.5, 65504.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], dtype=torch.float32)
+    x = torch.cat([x, special])
+    want = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne(x.numpy().astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ dense: brute force
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 127, 128, 129])
+@pytest.mark.parametrize("N", [1, 3, 128, 129])
+@pytest.mark.parametrize("K", [128, 384])
+def test_dense_vs_numpy_dequant_matmul(oracle, M, N, K):
+    p = gen.make_dense(M, N, K, seed=M * 1000 + N * 10 + K, with_c=(M + N) % 2 == 1)
+    d = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(),
+                           None if p.C is None else p.C.numpy())
+    ref, mag = dequant_ref(p, torch_decode_table())
+    assert np.all(np.abs(d - ref) <= 1e-13 * mag + 1e-300)
+
+
+def test_dense_integer_data_exact_vs_int64(oracle):
+    """Integer-valued codes, power-of-two scales: D is exact; compare to int64 matmul."""
+    g = torch.Generator().manual_seed(11)
+    M, N, K = 37, 300, 512
+    A = gen.integer_codes((M, K), g)
+    B = gen.integer_codes((N, K), g)
+    sfa = gen.pow2_scales((K // 128, M), g)
+    sfb = gen.pow2_scales(((N + 127) // 128, K // 128), g)
+    d = oracle.fp8_gemm_nt(A.numpy(), sfa.numpy(), B.numpy(), sfb.numpy())
+    dec = torch_decode_table()
+    Ai = np.rint(dec[A.numpy()] * 512).astype(np.int64)
+    Bi = np.rint(dec[B.numpy()] * 512).astype(np.int64)
+    exact = np.zeros((M, N), dtype=np.float64)
+    for kb in range(K // 128):
+        S = Ai[:, kb * 128:(kb + 1) * 128] @ Bi[:, kb * 128:(kb + 1) * 128].T   # exact int64
+        sa = sfa.numpy()[kb][:, None].astype(np.float64)
+        sb = sfb.numpy()[np.arange(N) // 128, kb][None, :].astype(np.float64)
+        exact += S.astype(np.float64) / 2.0 ** 18 * sa * sb
+    assert np.array_equal(d, exact)
+
+
+# ------------------------------------------------------------------ dense: closed forms
+def test_all_ones_closed_form(oracle):
+    g = torch.Generator().manual_seed(3)
+    M, N, K = 19, 260, 640
+    A = torch.full((M, K), gen.E4M3_ONE, dtype=torch.uint8)
+    B = torch.full((N, K), gen.E4M3_ONE, dtype=torch.uint8)
+    sfa = torch.rand(K // 128, M, generator=g) + 0.5
+    sfb = torch.rand((N + 127) // 128, K // 128, generator=g) + 0.5
+    C = torch.randn(M, N, generator=g)
+    d = oracle.fp8_gemm_nt(A.numpy(), sfa.numpy(), B.numpy(), sfb.numpy(), C.numpy())
+    nb = np.arange(N) // 128
+    want = 128.0 * (sfa.numpy().astype(np.float64).T @ sfb.numpy().astype(np.float64)[nb].T) + C.numpy()
+    assert np.allclose(d, want, rtol=1e-14, atol=0)
+    # constant scales: K * sA * sB exactly
+    d2 = oracle.fp8_gemm_nt(A.numpy(), np.full((K // 128, M), 0.25, np.float32), B.numpy(),
+                            np.full(((N + 127) // 128, K // 128), 2.0, np.float32))
+    assert np.all(d2 == K * 0.25 * 2.0)
+
+
+def test_one_hot_rows(oracle):
+    """A[m, pi(m)] = 1: D[m, n] = sfa[pi/128][m] * sfb[n/128][pi/128] * e4m3(B[n, pi])."""
+    g = torch.Generator().manual_seed(5)
+    M, N, K = 40, 200, 768
+    pi = torch.randint(0, K, (M,), generator=g)
+    A = torch.zeros(M, K, dtype=torch.uint8)
+    A[torch.arange(M), pi] = gen.E4M3_ONE
+    p = gen.make_dense(1, N, K, seed=99)
+    sfa = torch.rand(K // 128, M, generator=g) + 0.1
+    d = oracle.fp8_gemm_nt(A.numpy(), sfa.numpy(), p.B.numpy(), p.sfb.numpy())
+    dec = torch_decode_table()
+    pin = pi.numpy()
+    kb = pin // 128
+    want = (sfa.numpy()[kb, np.arange(M)][:, None].astype(np.float64)
+            * p.sfb.numpy()[np.arange(N)[None, :] // 128, kb[:, None]].astype(np.float64)
+            * dec[p.B.numpy()[:, pin].T])
+    assert np.array_equal(d, want)
+
+
+def test_sign_flip_and_pow2_scaling(oracle):
+    p = gen.make_dense(33, 257, 384, seed=21)
+    A = p.A.numpy()
+    base = oracle.fp8_gemm_nt(A, p.sfa.numpy(), p.B.numpy(), p.sfb.numpy())
+    flipped = np.where(A != 0, A ^ 0x80, A).astype(np.uint8)
+    neg = oracle.fp8_gemm_nt(flipped, p.sfa.numpy(), p.B.numpy(), p.sfb.numpy())
+    assert np.array_equal(neg, -base)
+    up = oracle.fp8_gemm_nt(A, p.sfa.numpy() * 8.0, p.B.numpy(), p.sfb.numpy())
+    assert np.array_equal(up, 8.0 * base)
+    # swapping the operands transposes D when both sides carry 128x128 block
+    # scales: D[m,n] = sum_kb SA[m/128][kb] SB[n/128][kb] S[m,n,kb] is symmetric
+    g = torch.Generator().manual_seed(23)
+    Ma, Nb_, K = 256, 384, 512
+    A2 = gen.integer_codes((Ma, K), g, max_abs=448)
+    B2 = gen.integer_codes((Nb_, K), g, max_abs=448)
+    SA = (torch.rand(Ma // 128, K // 128, generator=g) + 0.1).numpy()
+    SB = (torch.rand(Nb_ // 128, K // 128, generator=g) + 0.1).numpy()
+    sfa_a = np.ascontiguousarray(np.repeat(SA, 128, axis=0).T)          # [Kb, Ma]
+    sfa_b = np.ascontiguousarray(np.repeat(SB, 128, axis=0).T)          # [Kb, Nb_]
+    d_ab = oracle.fp8_gemm_nt(A2.numpy(), sfa_a, B2.numpy(), SB)
+    d_ba = oracle.fp8_gemm_nt(B2.numpy(), sfa_b, A2.numpy(), SA)
+    assert np.array_equal(d_ab, d_ba.T)
+
+
+def test_rows_subset_equals_full(oracle):
+    p = gen.make_dense(70, 150, 256, seed=31, with_c=True)
+    full = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(), p.C.numpy())
+    rows = np.array([69, 0, 13, 13, 64])
+    sub = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(), p.C.numpy(), rows=rows)
+    assert np.array_equal(sub, full[rows])
+    one = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(), p.C.numpy(), threads=1)
+    assert np.array_equal(one, full)
+
+
+def test_c_is_added(oracle):
+    p = gen.make_dense(9, 140, 256, seed=41, with_c=True)
+    with_c = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(), p.C.numpy())
+    without = oracle.fp8_gemm_nt(p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy())
+    assert np.allclose(with_c - without, p.C.numpy().astype(np.float64), rtol=0, atol=1e-9)
+
+
+def test_bad_sizes_rejected(oracle):
+    A = np.zeros((4, 100), np.uint8)
+    with pytest.raises(ValueError):
+        oracle.fp8_gemm_nt(A, np.ones((1, 4), np.float32), np.zeros((4, 100), np.uint8), np.ones((1, 1), np.float32))
+
+
+# ------------------------------------------------------------------ contiguous grouped
+def test_contiguous_segments_equal_dense(oracle):
+    p = gen.make_contiguous([128, 0, 256, 100], N=200, K=256, seed=51, with_c=True, pad_rows=128)
+    npd = gen.to_numpy(p)
+    d, comp = oracle.m_grouped_contiguous(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["m_indices"], npd["C"])
+    idx = npd["m_indices"]
+    assert np.array_equal(comp, (idx >= 0) & (idx < 4))
+    assert np.all(np.isnan(d[~comp]))
+    for g in range(4):
+        rows = np.nonzero(idx == g)[0]
+        if rows.size == 0:
+            continue
+        dd = oracle.fp8_gemm_nt(npd["A"], npd["sfa"], npd["B"][g], npd["sfb"][g], npd["C"], rows=rows)
+        assert np.array_equal(d[rows], dd)
+
+
+def test_contiguous_group_independence_and_permutation(oracle):
+    p = gen.make_contiguous([128, 128, 128], N=130, K=256, seed=52)
+    npd = gen.to_numpy(p)
+    d, _ = oracle.m_grouped_contiguous(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["m_indices"])
+    B2 = npd["B"].copy()
+    B2[1] = np.where(B2[1] != 0, B2[1] ^ 0x80, B2[1])
+    d2, _ = oracle.m_grouped_contiguous(npd["A"], npd["sfa"], B2, npd["sfb"], npd["m_indices"])
+    idx = npd["m_indices"]
+    assert np.array_equal(d2[idx != 1], d[idx != 1])
+    assert np.array_equal(d2[idx == 1], -d[idx == 1])
+    # relabel the groups: rows follow their expert's weights
+    perm = np.array([2, 0, 1])
+    idx_p = perm[idx].astype(np.int32)
+    Bp = np.empty_like(npd["B"]); sfbp = np.empty_like(npd["sfb"])
+    Bp[perm] = npd["B"]; sfbp[perm] = npd["sfb"]
+    d3, _ = oracle.m_grouped_contiguous(npd["A"], npd["sfa"], Bp, sfbp, idx_p)
+    assert np.array_equal(d3, d)
+    # G = 1 with all rows valid is the dense form
+    d4, _ = oracle.m_grouped_contiguous(npd["A"], npd["sfa"], npd["B"][:1], npd["sfb"][:1],
+                                        np.zeros_like(idx))
+    assert np.array_equal(d4, oracle.fp8_gemm_nt(npd["A"], npd["sfa"], npd["B"][0], npd["sfb"][0]))
+
+
+# ------------------------------------------------------------------ masked grouped
+def test_masked_rows_and_groups(oracle):
+    G, M_max, N, K = 4, 70, 150, 256
+    p = gen.make_masked(G, M_max, N, K, seed=61, with_c=True, masked_m=[0, 70, 33, 200])
+    npd = gen.to_numpy(p)
+    d, comp = oracle.m_grouped_masked(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["masked_m"], npd["C"])
+    valid = np.array([0, 70, 33, 70])
+    want_comp = (np.arange(M_max)[None, :] < valid[:, None]).ravel()
+    assert np.array_equal(comp, want_comp)
+    assert np.all(np.isnan(d[~comp]))
+    for g in range(G):
+        if valid[g] == 0:
+            continue
+        dd = oracle.fp8_gemm_nt(npd["A"][g], npd["sfa"][g], npd["B"][g], npd["sfb"][g], npd["C"][g])
+        assert np.array_equal(d.reshape(G, M_max, N)[g, :valid[g]], dd[:valid[g]])
+
+
+def test_masked_negative_and_subset(oracle):
+    G, M_max, N, K = 2, 16, 40, 128
+    p = gen.make_masked(G, M_max, N, K, seed=62, masked_m=[-5, 16])
+    npd = gen.to_numpy(p)
+    d, comp = oracle.m_grouped_masked(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["masked_m"])
+    assert not comp[:M_max].any() and comp[M_max:].all()
+    rows = np.array([31, 16, 3])
+    ds, cs = oracle.m_grouped_masked(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["masked_m"], rows=rows)
+    assert np.array_equal(cs, comp[rows])
+    assert np.array_equal(ds[cs], d[rows][cs])

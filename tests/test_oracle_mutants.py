@@ -1,0 +1,77 @@
+"""Negative controls for the oracle's pins: plant one plausible mistake at a
+time in a copy of ``oracle/oracle.c`` (on the CPU), rebuild, and check that at
+least one pin in ``test_oracle.py`` rejects the broken copy."""
+import os
+import shutil
+
+import pytest
+
+import oracle as oracle_pkg
+from oracle import Oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
+
+# (name, original text, replacement): each must occur exactly once in oracle.c
+MUTANTS = [
+    ("drop_last_k_block", "for (int kb = 0; kb < Kb; ++kb) {", "for (int kb = 0; kb < Kb - 1; ++kb) {"),
+    ("fnuz_bias", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("lost_sign", "return s ? -mag : mag;", "return mag;"),
+    ("sfb_ignores_kb", "double scale = (double)j->sa[kb * j->sa_stride] * (double)sb[kb];",
+     "double scale = (double)j->sa[kb * j->sa_stride] * (double)sb[0];"),
+    ("sfb_block_64", "const float *sb = j->sfb + (int64_t)(n / ORACLE_NBLOCK) * Kb;",
+     "const float *sb = j->sfb + (int64_t)(n / 64 < (j->N + 127) / 128 ? n / 64 : 0) * Kb;"),
+    ("sfa_k_major", "        j.sa = p->sfa + r; j.sa_stride = p->M;\n        j.b = p->B; j.sfb = p->sfb;",
+     "        j.sa = p->sfa + r * (p->K / 128); j.sa_stride = 1;\n        j.b = p->B; j.sfb = p->sfb;"),
+    ("c_ignored", "j->out[n] = acc + (j->c_row ? (double)j->c_row[n] : 0.0);", "j->out[n] = acc;"),
+    ("b_transposed", "s += j->dec[ap[k]] * j->dec[bp[k]];",
+     "s += j->dec[ap[k]] * j->dec[j->b[(int64_t)(kb * ORACLE_KBLOCK + k) * j->N + n]];"),
+    ("contig_group0", "        j.b = p->B + (int64_t)g * p->N * p->K;\n        j.sfb = p->sfb + (int64_t)g * Nb * Kb;",
+     "        j.b = p->B;\n        j.sfb = p->sfb;"),
+    ("masked_off_by_one", "if (m >= valid) {", "if (m > valid) {"),
+    ("bf16_ties_up", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    ("scale_squared", "acc += scale * s;", "acc += scale * scale * s;"),
+]
+
+
+def _pin_calls(o):
+    calls = []
+    calls.append(lambda: pins.test_e4m3_table_matches_torch_decode(o))
+    calls.append(lambda: pins.test_e4m3_table_format_facts(o))
+    calls.append(lambda: pins.test_bf16_rne_matches_torch_cast(o))
+    for M, N, K in [(3, 129, 384), (129, 3, 128), (5, 128, 384)]:
+        calls.append(lambda M=M, N=N, K=K: pins.test_dense_vs_numpy_dequant_matmul(o, M, N, K))
+    for f in (pins.test_dense_integer_data_exact_vs_int64, pins.test_all_ones_closed_form,
+              pins.test_one_hot_rows, pins.test_sign_flip_and_pow2_scaling,
+              pins.test_rows_subset_equals_full, pins.test_c_is_added,
+              pins.test_contiguous_segments_equal_dense,
+              pins.test_contiguous_group_independence_and_permutation,
+              pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset):
+        calls.append(lambda f=f: f(o))
+    return calls
+
+
+def test_unmodified_copy_passes_every_pin(tmp_path):
+    src = tmp_path / "oracle.c"
+    shutil.copy(SRC, src)
+    lib = oracle_pkg.build(str(src), str(tmp_path / "liboracle_copy.so"))
+    o = Oracle(oracle_pkg.load(lib))
+    for call in _pin_calls(o):
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle_pkg.build(str(src), str(tmp_path / f"liboracle_{name}.so"))
+    o = Oracle(oracle_pkg.load(lib))
+    caught = []
+    for call in _pin_calls(o):
+        try:
+            call()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(call)
+    assert caught, f"no pin caught the planted mistake '{name}'"
