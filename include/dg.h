@@ -1,0 +1,145 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) block-scaled FP8 GEMM library (libdg.so).
+ *
+ * Operation (DeepGEMM README, "Interfaces / Notes"): the kernels follow the
+ * naming D = C + A @ B with the NT input layout, so the `_nt` calls compute
+ *
+ *     D = C + A . B^T
+ *
+ * with A and B in FP8 E4M3 (OCP "FN" encoding: max 448, no infinities),
+ * FP32 accumulation, and BF16 D.  Fine-grained scaling (same section, and
+ * the DeepGEMM launch article, section 2 "FP8"): one FP32 scale per 1x128
+ * block of A (one row, 128 consecutive K) and one per 128x128 block of B.
+ * Every 128-wide K block is reduced on the matrix cores, then multiplied by
+ * its two scales and added into an FP32 accumulator ("promotion").
+ * Quantisation and any transposition are the caller's job (same section).
+ *
+ * Notation: Kb = K/128, Nb = ceil(N/128).  All tensors are row-major and
+ * densely packed.
+ *
+ *   A    uint8 (E4M3 codes) [rows][K]
+ *   sfa  float [Kb][rows]             MN-major ("transposed") LHS scales, as the
+ *                                     README's notes require for the LHS
+ *   B    uint8 (E4M3 codes) [N][K]    (the "T" of NT: row n of B is column n of B^T)
+ *   sfb  float [Nb][Kb]               rows n in [128 i, 128 i + 128) use sfb[i][kb]
+ *   C    float [rows][N] or NULL      added before the single BF16 rounding
+ *   D    bf16  [rows][N]              written with round-to-nearest-even
+ *
+ * Ownership and execution:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never frees or keeps it.  A, B, C and D must be 16-byte aligned; the
+ *     scale and index arrays 4-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  They never synchronise the host and never read device data
+ *     (group indices, masks) on the host.
+ *   - The library owns its compiled-kernel cache and a per-stream device
+ *     workspace (split-K partials and arrival counters), created on first use
+ *     (or by dg_init) and kept until process exit.  The first call for a new
+ *     shape compiles a kernel (hipRTC) and may allocate; later calls with the
+ *     same shape neither compile nor allocate.
+ *   - Work queued on different streams must not share output buffers.
+ *
+ * Errors: every call validates its arguments on the host before touching the
+ * GPU and returns a dg_status; dg_last_error() gives a message for the last
+ * non-OK status of the calling thread.  No exception crosses the ABI.
+ * Data-dependent cases are defined behaviour, not errors: masked_m values are
+ * clamped to [0, M_max]; m_indices values outside [0, num_groups) mark rows
+ * that are not computed (their D rows are left as they were).
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = -1,   /* NULL pointer, non-positive size, bad group count */
+    DG_ERR_UNSUPPORTED = -2,   /* K not a multiple of 128, sizes beyond 32-bit offsets */
+    DG_ERR_ALIGNMENT = -3,     /* pointer not 16-byte aligned, contiguous M not aligned */
+    DG_ERR_JIT = -4,           /* hipRTC compile or code-object load failed */
+    DG_ERR_HIP = -5            /* a HIP runtime call failed (no device, launch error) */
+} dg_status;
+
+/*
+ * Dense:  D[M][N] = C + A[M][K] . B[N][K]^T.
+ * DeepGEMM README, "Normal dense GEMM (non-grouped)" (fp8_gemm_nt), and
+ * "Interfaces / Notes" for the layouts above.  C may be NULL.
+ */
+dg_status dg_fp8_gemm_nt(const void *A, const float *sfa, const void *B, const float *sfb,
+                         const float *C, void *D, int M, int N, int K, void *stream);
+
+/*
+ * M-grouped, contiguous layout (MoE prefill / training forward).
+ * DeepGEMM README, "Grouped GEMM (contiguous layout)": only M is grouped, N
+ * and K are shared; the experts' tokens are concatenated along M and every
+ * expert's segment starts on a multiple of
+ * dg_get_mk_alignment_for_contiguous_layout() rows.
+ *   A [M][K], sfa [Kb][M], B [G][N][K], sfb [G][Nb][Kb], C NULL or [M][N], D [M][N],
+ *   m_indices int32 [M] (device): expert of each row; a value outside [0, G)
+ *   marks a padding row, which is not computed and whose D row is untouched.
+ * M must be a multiple of the alignment.  All valid rows of one aligned
+ * block must name the same expert (rows naming another are left untouched).
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void *A, const float *sfa, const void *B,
+                                              const float *sfb, const int32_t *m_indices,
+                                              const float *C, void *D, int M, int N, int K,
+                                              int num_groups, void *stream);
+
+/*
+ * M-grouped, masked layout (MoE decode, graph-friendly).
+ * DeepGEMM README, "Grouped GEMM (masked layout)": the host does not know how
+ * many rows each expert received; a device mask tells the kernel which part
+ * to compute.
+ *   A [G][M_max][K], sfa [G][Kb][M_max], B [G][N][K], sfb [G][Nb][Kb],
+ *   C NULL or [G][M_max][N], D [G][M_max][N],
+ *   masked_m int32 [G] (device): group g computes rows m < clamp(masked_m[g], 0, M_max);
+ *   D rows at or beyond that are never written.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void *A, const float *sfa, const void *B,
+                                          const float *sfb, const int32_t *masked_m,
+                                          const float *C, void *D, int M_max, int N, int K,
+                                          int num_groups, void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
+const char *dg_last_error(void);
+
+/*
+ * Row alignment every expert segment of the contiguous layout must start on
+ * (DeepGEMM README, utility functions: get_mk_alignment_for_contiguous_layout).
+ * Always 128 here.
+ */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/*
+ * Upper bound on the compute units the kernels spread over (README utility
+ * functions: set_num_sms / get_num_sms).  n <= 0 or above the device's count
+ * restores the device's count.  Affects tile heuristics of later calls only.
+ */
+dg_status dg_set_num_cus(int n);
+int dg_get_num_cus(void);
+
+/*
+ * Optional eager set-up on the current device: device query, cache directory,
+ * default-stream workspace.  Never needed, but lets a caller keep first-call
+ * allocation out of a timed or captured region.
+ */
+dg_status dg_init(void);
+
+/*
+ * Compile (or load from the cache) the kernel that a later call with these
+ * arguments would use, without launching anything.  kind: 0 dense,
+ * 1 contiguous, 2 masked; has_c: 0/1; rows = M (dense/contiguous) or M_max.
+ * Needs no GPU: the code object is built for gfx950 and stored in the cache
+ * directory (DG_CACHE_DIR, else <library dir>/jit_cache).
+ */
+dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

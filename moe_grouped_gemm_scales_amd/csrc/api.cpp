@@ -1,0 +1,272 @@
+// The C ABI of libdg.so: argument checks, tile selection, JIT lookup,
+// workspace management and the kernel launch.  The operations and their
+// layouts are specified in include/dg.h.
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "dg_internal.h"
+
+namespace dg {
+
+namespace {
+
+thread_local std::string t_last_error;
+
+// Mirror of the kernel's Params (same order, same types, same padding).
+struct LaunchParams {
+    const void* A;
+    const float* sfa;
+    const void* B;
+    const float* sfb;
+    const float* C;
+    void* D;
+    const int32_t* grp;
+    float* ws;
+    uint32_t* counters;
+    int M;
+    int num_tiles;
+};
+
+struct Workspace {
+    float* partials = nullptr;
+    size_t partial_bytes = 0;
+    uint32_t* counters = nullptr;
+    size_t counter_bytes = 0;
+};
+
+struct DeviceState {
+    int num_cus = 0;
+    std::map<hipStream_t, Workspace> ws;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+int g_num_cus_limit = 0;   // 0: use the device's count
+
+dg_status hip_fail(hipError_t e, const char* what) {
+    return set_error(DG_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+dg_status device_state(DeviceState** out, int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    auto& st = g_dev[dev];
+    if (st.num_cus == 0) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+        st.num_cus = n;
+    }
+    *out = &st;
+    *dev_out = dev;
+    return DG_OK;
+}
+
+int effective_cus(const DeviceState& st) {
+    if (g_num_cus_limit > 0 && g_num_cus_limit < st.num_cus) return g_num_cus_limit;
+    return st.num_cus;
+}
+
+// Grow (never shrink) the stream's workspace.  New arrival counters start at
+// zero; kernels leave them at zero again when they finish.
+dg_status ensure_workspace(DeviceState& st, hipStream_t stream, size_t partial_bytes, size_t counter_bytes,
+                           Workspace** out) {
+    Workspace& w = st.ws[stream];
+    if (w.partial_bytes < partial_bytes) {
+        if (w.partials) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(w.partials);
+            w.partials = nullptr;
+            w.partial_bytes = 0;
+        }
+        size_t bytes = std::max<size_t>(partial_bytes, size_t(8) << 20);
+        hipError_t e = hipMalloc((void**)&w.partials, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K workspace)");
+        w.partial_bytes = bytes;
+    }
+    if (w.counter_bytes < counter_bytes) {
+        if (w.counters) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(w.counters);
+            w.counters = nullptr;
+            w.counter_bytes = 0;
+        }
+        size_t bytes = std::max<size_t>(counter_bytes, size_t(64) << 10);
+        hipError_t e = hipMalloc((void**)&w.counters, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K counters)");
+        e = hipMemset(w.counters, 0, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMemset(split-K counters)");
+        w.counter_bytes = bytes;
+    }
+    *out = &w;
+    return DG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dg_status check_common(const void* A, const float* sfa, const void* B, const float* sfb, const float* C,
+                       const void* D, int rows, int N, int K) {
+    if (!A || !sfa || !B || !sfb || !D) return set_error(DG_ERR_INVALID_ARG, "A, sfa, B, sfb and D must be non-NULL");
+    if (rows < 0 || N <= 0 || K <= 0)
+        return set_error(DG_ERR_INVALID_ARG, "sizes must be positive (M may be 0)");
+    if (K % 128 != 0) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128 (the scale block)");
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
+        return set_error(DG_ERR_ALIGNMENT, "A, B, C and D must be 16-byte aligned");
+    if (!aligned(sfa, 4) || !aligned(sfb, 4)) return set_error(DG_ERR_ALIGNMENT, "scales must be 4-byte aligned");
+    // per-tile buffer offsets are 32-bit: one scale plane of A and one 256-row slab must fit
+    if ((uint64_t)(K / 128) * (uint64_t)rows * 4u >= (1ull << 32) || (uint64_t)K * 256u >= (1ull << 32))
+        return set_error(DG_ERR_UNSUPPORTED, "sizes exceed 32-bit buffer offsets");
+    return DG_OK;
+}
+
+dg_status launch(const Problem& p, const void* A, const float* sfa, const void* B, const float* sfb,
+                 const int32_t* grp, const float* C, void* D, void* stream_ptr) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* st = nullptr;
+    int dev = 0;
+    dg_status s = device_state(&st, &dev);
+    if (s != DG_OK) return s;
+    const int cus = effective_cus(*st);
+    KernelConfig cfg = select_config(p, cus);
+    void* fptr = nullptr;
+    s = get_function(cfg, &fptr);
+    if (s != DG_OK) return s;
+    hipFunction_t f = static_cast<hipFunction_t>(fptr);
+
+    const int64_t items = num_work_items(cfg, p.rows);
+    if (items <= 0) return DG_OK;
+    if (items > INT_MAX) return set_error(DG_ERR_UNSUPPORTED, "too many tiles");
+    int occ = 1;
+    if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, cfg.threads(), 0) != hipSuccess || occ < 1)
+        occ = 1;
+    const int grid = (int)std::min<int64_t>(items, (int64_t)cus * occ);
+
+    LaunchParams lp{};
+    lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
+    lp.M = p.rows;
+    lp.num_tiles = (int)items;
+    if (cfg.splitk > 1) {
+        const int64_t mn = items / cfg.splitk;
+        Workspace* w = nullptr;
+        s = ensure_workspace(*st, stream, (size_t)items * cfg.bm * cfg.bn * sizeof(float),
+                             (size_t)mn * sizeof(uint32_t), &w);
+        if (s != DG_OK) return s;
+        lp.ws = w->partials;
+        lp.counters = w->counters;
+    }
+    if (env_flag("DG_PRINT_CONFIGS"))
+        std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), grid,
+                     cfg.threads(), (long long)items, cfg.lds_bytes());
+    void* args[] = {&lp};
+    hipError_t e = hipModuleLaunchKernel(f, grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+    return DG_OK;
+}
+
+}  // namespace
+
+dg_status set_error(dg_status s, const std::string& msg) {
+    t_last_error = msg;
+    if (env_flag("DG_DEBUG")) std::fprintf(stderr, "[dg] error %d: %s\n", (int)s, msg.c_str());
+    return s;
+}
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+const char* dg_last_error(void) { return t_last_error.c_str(); }
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+dg_status dg_set_num_cus(int n) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_num_cus_limit = n > 0 ? n : 0;
+    return DG_OK;
+}
+
+int dg_get_num_cus(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* st = nullptr;
+    int dev = 0;
+    if (device_state(&st, &dev) != DG_OK) return g_num_cus_limit > 0 ? g_num_cus_limit : 0;
+    return effective_cus(*st);
+}
+
+dg_status dg_init(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* st = nullptr;
+    int dev = 0;
+    dg_status s = device_state(&st, &dev);
+    if (s != DG_OK) return s;
+    Workspace* w = nullptr;
+    return ensure_workspace(*st, nullptr, 0, 0, &w);
+}
+
+dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus) {
+    if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
+        return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
+    if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
+    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
+    KernelConfig cfg = select_config(p, num_cus > 0 ? num_cus : 256);
+    std::vector<char> code;
+    return compile_code(cfg, &code);
+}
+
+dg_status dg_fp8_gemm_nt(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
+                         int M, int N, int K, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (M == 0) return DG_OK;
+    Problem p{kDense, M, N, K, 1, C ? 1 : 0};
+    return launch(p, A, sfa, B, sfb, nullptr, C, D, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const float* sfa, const void* B, const float* sfb,
+                                              const int32_t* m_indices, const float* C, void* D, int M, int N, int K,
+                                              int num_groups, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (!m_indices) return set_error(DG_ERR_INVALID_ARG, "m_indices must be non-NULL");
+    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+    if (!aligned(m_indices, 4)) return set_error(DG_ERR_ALIGNMENT, "m_indices must be 4-byte aligned");
+    if (M % dg_get_mk_alignment_for_contiguous_layout() != 0)
+        return set_error(DG_ERR_ALIGNMENT, "contiguous M must be a multiple of the M alignment (128)");
+    if (M == 0) return DG_OK;
+    Problem p{kContiguous, M, N, K, num_groups, C ? 1 : 0};
+    return launch(p, A, sfa, B, sfb, m_indices, C, D, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const float* sfa, const void* B, const float* sfb,
+                                          const int32_t* masked_m, const float* C, void* D, int M_max, int N, int K,
+                                          int num_groups, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M_max, N, K);
+    if (s != DG_OK) return s;
+    if (!masked_m) return set_error(DG_ERR_INVALID_ARG, "masked_m must be non-NULL");
+    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+    if (!aligned(masked_m, 4)) return set_error(DG_ERR_ALIGNMENT, "masked_m must be 4-byte aligned");
+    if (M_max == 0) return DG_OK;
+    Problem p{kMasked, M_max, N, K, num_groups, C ? 1 : 0};
+    return launch(p, A, sfa, B, sfb, masked_m, C, D, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal declarations of libdg.so (host side).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "dg.h"
+
+namespace dg {
+
+enum Kind : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// One compiled specialisation of the kernel.  Everything here becomes a -D
+// macro of the hipRTC compile; N and K are compile-time constants (the
+// DeepGEMM launch article, section 4.2, bakes the matrix sizes into each JIT
+// kernel), M stays a run-time argument so a changing token count reuses code.
+struct KernelConfig {
+    int kind = kDense;
+    int bm = 128, bn = 128;    // workgroup tile (rows of A, rows of B)
+    int wm = 2, wn = 2;        // waves along m and n
+    int stages = 2;            // LDS ring depth
+    int splitk = 1;            // K splits (dense only)
+    int has_c = 0;
+    int n = 0, k = 0, g = 1;
+
+    int threads() const { return 64 * wm * wn; }
+    int stage_bytes() const { return bm * 128 + bn * 128 + ((bm + 63) / 64) * 256; }
+    int lds_bytes() const { return stages * stage_bytes(); }
+    std::string key() const;
+};
+
+struct Problem {
+    int kind;
+    int rows;      // M (dense, contiguous) or M_max (masked)
+    int n, k, g;
+    int has_c;
+};
+
+// Tile heuristics (heuristics.cpp).
+KernelConfig select_config(const Problem& p, int num_cus);
+// Output tiles times splits, i.e. the launch's work items; for masked the
+// worst case (every row of every group valid).
+int64_t num_work_items(const KernelConfig& c, int rows);
+
+// JIT (jit.cpp).  compile_code() needs no GPU; get_function() loads on the
+// current device.
+dg_status compile_code(const KernelConfig& c, std::vector<char>* code);
+dg_status get_function(const KernelConfig& c, void** function /* hipFunction_t */);
+std::string cache_dir();
+
+// Errors (api.cpp).
+dg_status set_error(dg_status s, const std::string& msg);
+bool env_flag(const char* name);
+
+}  // namespace dg

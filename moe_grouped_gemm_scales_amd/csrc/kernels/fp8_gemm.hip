@@ -1,0 +1,496 @@
+// Block-scaled FP8 GEMM for gfx950 (CDNA4):  D = C + A . B^T  (NT layout).
+//
+// Device code only.  The host library embeds this file as text and compiles
+// it at run time with hipRTC, once per shape/tile key, with the key's values
+// passed as -D macros (DeepGEMM launch article, section 4.2: matrix sizes and
+// tile/pipeline parameters are compile-time constants of a JIT-built kernel).
+//
+// What it computes (DeepGEMM README, "Interfaces / Notes"; launch article,
+// section 2 "FP8" on promotion):
+//   A  [rows][K]  E4M3 codes, one FP32 scale per 1x128 block, sfa[K/128][rows]
+//   B  [N][K]     E4M3 codes, one FP32 scale per 128x128 block, sfb[ceil(N/128)][K/128]
+//   D[m][n] = bf16( C[m][n] + sum_kb sfa[kb][m] * sfb[n/128][kb] * P_kb[m][n] )
+// where P_kb is the exact-product, FP32-summed 128-wide block dot product from
+// one v_mfma_f32_16x16x128_f8f6f4, promoted into FP32 VGPR accumulators.
+//
+// Forms (DG_KIND):
+//   0 dense
+//   1 M-grouped contiguous (README "Grouped GEMM (contiguous layout)"): rows of
+//     all experts concatenated; grp = m_indices[rows]; a row block takes its
+//     expert from its first row, rows whose index differs are left untouched.
+//   2 M-grouped masked (README "Grouped GEMM (masked layout)"): A/D are
+//     [G][M_max][.]; grp = masked_m[G]; rows >= clamp(masked_m[g]) untouched.
+//
+// Layout of the work (MI355X-specific, not from the pages):
+//   * MFMA orientation is swapped: the MFMA "row" operand is a 16-row slice of
+//     B and the "column" operand a 16-row slice of A, so a lane owns one m and
+//     four consecutive n.  Promotion then needs one scale product per
+//     (m, 128-wide n block) and the BF16 store is 8 contiguous bytes.
+//   * Operand tiles go global -> LDS by buffer_load ... lds (no VGPR staging)
+//     into a STAGES-deep ring; each 128-byte row is stored with its 16-byte
+//     chunks XOR-swizzled by ((row >> 1) & 7) so that the 16 rows read by one
+//     quarter-wave land in 16 distinct bank groups.
+//   * A persistent grid walks tiles; split-K partials (dense only) are summed
+//     in a fixed order by the last-arriving workgroup of a tile.
+
+typedef unsigned char u8;
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef unsigned long long u64;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef u16 v4u16 __attribute__((ext_vector_type(4)));
+
+#ifndef DG_KIND
+#define DG_KIND 0
+#define DG_BM 128
+#define DG_BN 128
+#define DG_WM 2
+#define DG_WN 2
+#define DG_STAGES 2
+#define DG_SPLITK 1
+#define DG_HAS_C 0
+#define DG_N 256
+#define DG_K 256
+#define DG_G 1
+#endif
+
+namespace dg {
+
+constexpr int kKind = DG_KIND;
+constexpr int BM = DG_BM, BN = DG_BN, WM = DG_WM, WN = DG_WN;
+constexpr int NWAVES = WM * WN;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int WAVE_M = BM / WM, WAVE_N = BN / WN;
+constexpr int TM = WAVE_M / 16, TN = WAVE_N / 16;
+constexpr int STAGES = DG_STAGES;
+constexpr int SPLITK = DG_SPLITK;
+constexpr bool HAS_C = DG_HAS_C != 0;
+constexpr int N = DG_N, K = DG_K, G = DG_G;
+constexpr int KBLK = 128;
+constexpr int KBLKS = K / KBLK;
+constexpr int NBLKS = (N + KBLK - 1) / KBLK;
+constexpr int NUM_NT = (N + BN - 1) / BN;     // n tiles
+// a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
+// WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N)
+constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0;
+
+static_assert(K % KBLK == 0, "K must be a multiple of 128");
+static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles must be 16-aligned");
+static_assert(BM % 8 == 0 && BN % 8 == 0, "tiles are loaded 8 rows per instruction");
+static_assert(KBLKS % SPLITK == 0, "split-K must divide the K blocks");
+static_assert(STAGES >= 2, "at least double buffering");
+
+// LDS ring: per stage [A tile BM x 128 B][B tile BN x 128 B][sfa BM floats, padded]
+constexpr int NA_INS = BM / 8;                 // 1 KB DMA instructions for A
+constexpr int NB_INS = BN / 8;                 // ... for B
+constexpr int NS_INS = (BM + 63) / 64;         // 256 B DMA instructions for sfa
+constexpr int A_OFF = 0;
+constexpr int B_OFF = BM * 128;
+constexpr int S_OFF = B_OFF + BN * 128;
+constexpr int STAGE_BYTES = S_OFF + NS_INS * 256;
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+
+// Every wave issues the same number of DMA instructions per stage, so one
+// vmcnt immediate fits all waves: instruction i of a category goes to wave
+// i % NWAVES, and a wave whose share runs out repeats the category's last
+// instruction (identical bytes to identical LDS addresses, so harmless).
+constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
+constexpr int IB = (NB_INS + NWAVES - 1) / NWAVES;
+constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
+constexpr int INS_PER_WAVE = IA + IB + IS;
+static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
+
+struct Params {
+    const u8* A;
+    const float* sfa;
+    const u8* B;
+    const float* sfb;
+    const float* C;
+    u16* D;
+    const int* grp;        // m_indices (contiguous) or masked_m (masked); unused for dense
+    float* ws;             // split-K partials
+    u32* counters;         // split-K arrival counters, zero between calls
+    int M;                 // rows of A (dense, contiguous) or M_max (masked)
+    int num_tiles;         // total work items for this launch
+};
+
+// ------------------------------------------------------------ small helpers
+__device__ __forceinline__ v4i make_rsrc(const void* base, u32 num_bytes) {
+    u64 p = (u64)base;
+    v4i r;
+    r.x = (int)(u32)p;
+    r.y = (int)((u32)(p >> 32) & 0xffffu);   // stride 0
+    r.z = (int)num_bytes;
+    r.w = 0x00020000;                        // raw buffer, dword data format
+    r.x = __builtin_amdgcn_readfirstlane(r.x);
+    r.y = __builtin_amdgcn_readfirstlane(r.y);
+    r.z = __builtin_amdgcn_readfirstlane(r.z);
+    r.w = __builtin_amdgcn_readfirstlane(r.w);
+    return r;
+}
+
+// One lane-linear LDS DMA: lane l writes its 16 (or 4) bytes to lds + 16*l (or 4*l).
+// Issued through inline asm so that the compiler does not answer every later
+// LDS read with a blanket wait for all outstanding DMA; the ring's own
+// vmcnt waits below give the exact ordering instead.
+__device__ __forceinline__ void dma16(v4i rsrc, u32 voff, u32 soff, u32 lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(v4i rsrc, u32 voff, u32 soff, u32 lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+template <int CNT>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(CNT >= 0 && CNT <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(CNT) : "memory");
+}
+// Wait until at most PENDING whole stages of this wave's DMA remain in flight.
+template <int PENDING>
+__device__ __forceinline__ void wait_stages() { wait_vmcnt<PENDING * INS_PER_WAVE>(); }
+
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+    u32 u = __builtin_bit_cast(u32, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                          // nearest-even
+    return (u16)(u >> 16);
+}
+
+__device__ __forceinline__ u32 lds_addr(const void* p) {
+    return (u32)(u64)(const __attribute__((address_space(3))) void*)p;
+}
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const float lds_f32;
+typedef __attribute__((address_space(3))) const u8 lds_u8;
+// Fragment read: two 16-byte chunks at lane-specific bases plus a constant
+// offset, written as pointer arithmetic so the offset folds into ds_read_b128.
+__device__ __forceinline__ v8i lds_read_frag(lds_u8* lo, lds_u8* hi, int off) {
+    const v4i a = *(lds_v4i*)(lo + off);
+    const v4i b = *(lds_v4i*)(hi + off);
+    return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+__device__ __forceinline__ float lds_read_f32(lds_u8* base, int off) { return *(lds_f32*)(base + off); }
+
+// ------------------------------------------------------------ tile decode
+struct Tile {
+    int m0;          // first row of the tile within its A/D (per-group for masked)
+    int n0;          // first column
+    int g;           // group (B/sfb select; A/sfa/C/D too for masked)
+    int rows;        // valid rows in [m0, m0 + BM) for loads (>= 1)
+    int row_limit;   // rows m0 + r with r < row_limit may be stored (masked / dense tail)
+    int kb0, kb1;    // K-block range
+    int split;       // split index
+    int mn;          // output tile index (for split-K bookkeeping)
+    bool skip;
+};
+
+__device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
+    Tile tl;
+    tl.skip = false;
+    tl.split = 0;
+    tl.kb0 = 0;
+    tl.kb1 = KBLKS;
+    if constexpr (kKind == 2) {
+        // Masked: enumerate only the active row blocks, group by group.
+        const int nmt_max = (p.M + BM - 1) / BM;
+        int g = 0, base = 0;
+        int mb = 0, nt = 0, valid = 0;
+        tl.skip = true;
+        for (; g < G; ++g) {
+            int v = p.grp[g];
+            v = v < 0 ? 0 : (v > p.M ? p.M : v);
+            int nmt = (v + BM - 1) / BM;
+            if (nmt > nmt_max) nmt = nmt_max;
+            int cnt = nmt * NUM_NT;
+            if (t < base + cnt) {
+                int local = t - base;
+                mb = local % nmt;                 // row blocks fastest: they share B
+                nt = local / nmt;
+                valid = v;
+                tl.skip = false;
+                break;
+            }
+            base += cnt;
+        }
+        tl.g = g;
+        tl.m0 = mb * BM;
+        tl.n0 = nt * BN;
+        tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
+        tl.row_limit = valid - tl.m0;
+        tl.mn = 0;
+    } else {
+        const int num_mt = (p.M + BM - 1) / BM;
+        int mn = t / SPLITK;
+        tl.split = t % SPLITK;
+        tl.mn = mn;
+        // Grouped order: walk 8 m-tiles per column sweep so that concurrently
+        // resident workgroups share A and B tiles in L2.
+        constexpr int GROUP_M = 8;
+        int width = GROUP_M * NUM_NT;
+        int grp_id = mn / width;
+        int first_m = grp_id * GROUP_M;
+        int gsize = num_mt - first_m < GROUP_M ? num_mt - first_m : GROUP_M;
+        int mt = first_m + (mn % width) % gsize;
+        int nt = (mn % width) / gsize;
+        tl.m0 = mt * BM;
+        tl.n0 = nt * BN;
+        tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
+        tl.row_limit = tl.rows;
+        tl.kb0 = tl.split * (KBLKS / SPLITK);
+        tl.kb1 = tl.kb0 + KBLKS / SPLITK;
+        if constexpr (kKind == 1) {
+            int g = p.grp[tl.m0];
+            tl.g = g;
+            tl.skip = (g < 0 || g >= G);
+        } else {
+            tl.g = 0;
+        }
+    }
+    return tl;
+}
+
+// ------------------------------------------------------------ the kernel
+extern "C" __global__ void __launch_bounds__(NTHREADS, 1)
+dg_fp8_gemm_nt_kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM;          // wave position along m
+    const int wn = wave / WM;          // wave position along n
+    const int l16 = lane & 15;
+    const int q = lane >> 4;
+    const u32 smem_base = lds_addr(smem);
+    // Every fragment row this lane reads is l16 plus a multiple of 16, so the
+    // swizzle term (row >> 1) & 7 is the same for all of them.
+    const int sw = (l16 >> 1) & 7;
+    const u32 chunk_lo = (u32)(((2 * q) ^ sw) << 4);
+    const u32 chunk_hi = (u32)(((2 * q + 1) ^ sw) << 4);
+    const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * 128u;
+    const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * 128u;
+
+#pragma unroll 1
+    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
+        const Tile tl = decode_tile(p, t);
+        if (tl.skip) continue;
+
+        // ---- per-tile buffer resources (bases advanced to the tile's rows)
+        const u8* a_base;
+        const float* sfa_base;
+        int a_rows_total;        // rows of this A (for sfa stride)
+        if constexpr (kKind == 2) {
+            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
+            sfa_base = p.sfa + (u64)tl.g * KBLKS * p.M;
+        } else {
+            a_base = p.A + (u64)tl.m0 * K;
+            sfa_base = p.sfa;
+        }
+        a_rows_total = p.M;
+        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
+        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
+        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * a_rows_total * 4u);
+
+        // ---- per-lane DMA offsets for this wave's instructions (fixed over K)
+        u32 voff[INS_PER_WAVE];
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            const int i = min(wave + j * NWAVES, NA_INS - 1);
+            const int r = i * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const int rr = r < tl.rows ? r : tl.rows - 1;
+            voff[j] = (u32)rr * K + c * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int i = min(wave + j * NWAVES, NB_INS - 1);
+            const int r = i * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const int rr = r < n_rows ? r : n_rows - 1;
+            voff[IA + j] = (u32)rr * K + c * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < IS; ++j) {
+            const int i = min(wave + j * NWAVES, NS_INS - 1);
+            const int m = tl.m0 + i * 64 + lane;
+            const int mm = m < a_rows_total ? m : a_rows_total - 1;
+            voff[IA + IB + j] = (u32)mm * 4u;
+        }
+
+        auto issue_stage = [&](int kb, int stage) {
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+            const u32 soff_ab = __builtin_amdgcn_readfirstlane((u32)kb * KBLK);
+            const u32 soff_s = __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u);
+#pragma unroll
+            for (int j = 0; j < IA; ++j) {
+                const int i = min(wave + j * NWAVES, NA_INS - 1);
+                dma16(rs_a, voff[j], soff_ab, st + A_OFF + i * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < IB; ++j) {
+                const int i = min(wave + j * NWAVES, NB_INS - 1);
+                dma16(rs_b, voff[IA + j], soff_ab, st + B_OFF + i * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < IS; ++j) {
+                const int i = min(wave + j * NWAVES, NS_INS - 1);
+                dma4(rs_s, voff[IA + IB + j], soff_s, st + S_OFF + i * 256);
+            }
+        };
+
+        // ---- accumulators
+        v4f acc[TM][TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        // earlier tile's stores and LDS reads are finished before the ring is refilled
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        const int nkb = tl.kb1 - tl.kb0;
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nkb) issue_stage(tl.kb0 + s, s);
+
+        // row offsets of this lane's fragments inside a stage
+        const int a_row0 = wm * WAVE_M + l16;   // + a*16
+        const int b_row0 = wn * WAVE_N + l16;   // + b*16
+        const int wave_n0 = tl.n0 + wn * WAVE_N;
+
+#pragma unroll 1
+        for (int it = 0; it < nkb; ++it) {
+            const int kb = tl.kb0 + it;
+            const int stage = it % STAGES;
+            // stage `it` has landed (for this wave) once at most the later stages are pending
+            if (it + STAGES - 1 <= nkb) wait_stages<STAGES - 2>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (it + STAGES - 1 < nkb) issue_stage(kb + STAGES - 1, (it + STAGES - 1) % STAGES);
+
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+            // scales: sfa for this lane's TM rows (LDS), sfb per 128-wide n block (scalar loads)
+            float sa[TM];
+            lds_u8* const stp = (lds_u8*)st;
+            lds_u8* const sa_p = stp + a_row0 * 4;
+#pragma unroll
+            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+            const float* sfb_g = p.sfb + (u64)tl.g * NBLKS * KBLKS + kb;
+            float sab[TM];          // sa * sb when the wave's n range lies in one 128 block
+            float sb[TN];
+            if constexpr (SB_UNIFORM) {
+                const float sb0 = sfb_g[(u64)(wave_n0 / KBLK) * KBLKS];
+#pragma unroll
+                for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb0;
+            } else {
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    int nblk = (wave_n0 + b * 16) / KBLK;
+                    nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+                    sb[b] = sfb_g[(u64)nblk * KBLKS];
+                }
+            }
+
+            // A fragments (MFMA column operand): logical K chunks 2q, 2q+1 of row a_row0 + 16a
+            v8i fa[TM];
+            lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
+            lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
+            lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
+            lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
+#pragma unroll
+            for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * 128);
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const v8i fb = lds_read_frag(b_lo, b_hi, B_OFF + b * 16 * 128);
+#pragma unroll
+                for (int a = 0; a < TM; ++a) {
+                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                    // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                    v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                    float s;
+                    if constexpr (SB_UNIFORM) s = sab[a];
+                    else s = sa[a] * sb[b];
+                    acc[a][b] += pr * s;
+                }
+            }
+        }
+
+        // ---- split-K: publish the partial, the last arrival sums all in split order
+        if constexpr (SPLITK > 1) {
+            float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    *(v4f*)(ws + ((u64)tl.split * BM * BN) + ((a * TN + b) * NTHREADS + tid) * 4) = acc[a][b];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (tid == 0) {
+                u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                s_flag = (old == (u32)(SPLITK - 1));
+                if (old == (u32)(SPLITK - 1))
+                    __hip_atomic_store(&p.counters[tl.mn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!s_flag) continue;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    v4f sum = {0.f, 0.f, 0.f, 0.f};
+                    for (int s = 0; s < SPLITK; ++s) {
+                        v4f part = (s == tl.split)
+                                       ? acc[a][b]
+                                       : *(const v4f*)(ws + ((u64)s * BM * BN) + ((a * TN + b) * NTHREADS + tid) * 4);
+                        sum += part;
+                    }
+                    acc[a][b] = sum;
+                }
+        }
+
+        // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
+        u64 row_base;      // element offset of row 0 of this tile in C/D
+        if constexpr (kKind == 2) row_base = ((u64)tl.g * p.M + tl.m0) * N;
+        else row_base = (u64)tl.m0 * N;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int r = a_row0 + a * 16;          // row inside the tile
+            bool row_ok = r < tl.row_limit;
+            if constexpr (kKind == 1) row_ok = row_ok && (p.grp[tl.m0 + r] == tl.g);
+            if (!row_ok) continue;
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const int n = tl.n0 + wn * WAVE_N + b * 16 + 4 * q;
+                if (n >= N) continue;
+                const u64 off = row_base + (u64)r * N + n;
+                v4f v = acc[a][b];
+                if constexpr (N % 4 == 0) {
+                    if constexpr (HAS_C) v += *(const v4f*)(p.C + off);
+                    v4u16 o = {f32_to_bf16(v.x), f32_to_bf16(v.y), f32_to_bf16(v.z), f32_to_bf16(v.w)};
+                    *(v4u16*)(p.D + off) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (n + e < N) {
+                            float x = v[e];
+                            if constexpr (HAS_C) x += p.C[off + e];
+                            p.D[off + e] = f32_to_bf16(x);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace dg

@@ -1,0 +1,190 @@
+"""Python binding of libdg.so: argument marshalling only.
+
+Every function here checks the torch tensors' dtypes, shapes, devices and
+contiguity, then calls the C entry point of the same name with raw device
+pointers and the current HIP stream.  All arithmetic runs in the library's
+HIP kernels; there is no other code path.  If libdg.so is missing the import
+fails loudly (build it with ``python -m moe_grouped_gemm_scales_amd.build``).
+
+Layouts (DeepGEMM README, "Interfaces / Notes"): D = C + A @ B.T with A
+[M, K] and B [N, K] in FP8 E4M3 (torch.float8_e4m3fn or raw uint8 codes),
+sfa float32 [K/128, M] (MN-major LHS scales), sfb float32 [ceil(N/128), K/128],
+optional float32 C [M, N], bfloat16 D [M, N].  Grouped forms add a leading
+group dimension as documented in include/dg.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK = 0
+STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_UNSUPPORTED",
+                -3: "DG_ERR_ALIGNMENT", -4: "DG_ERR_JIT", -5: "DG_ERR_HIP"}
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m moe_grouped_gemm_scales_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    for f in (lib.dg_fp8_gemm_nt, lib.dg_m_grouped_fp8_gemm_nt_contiguous, lib.dg_m_grouped_fp8_gemm_nt_masked):
+        f.restype = i32
+    lib.dg_last_error.restype = ctypes.c_char_p
+    lib.dg_last_error.argtypes = []
+    lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
+    lib.dg_set_num_cus.argtypes = [i32]
+    lib.dg_set_num_cus.restype = i32
+    lib.dg_get_num_cus.restype = i32
+    lib.dg_init.restype = i32
+    lib.dg_precompile.argtypes = [i32] * 7
+    lib.dg_precompile.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != DG_OK:
+        raise DGError(status, lib.dg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _fp8(t: torch.Tensor, name: str):
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} must be float8_e4m3fn or uint8 E4M3 codes, got {t.dtype}")
+    _dev(t, name)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _f32(t: torch.Tensor, name: str, shape):
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _dev(t, name)
+
+
+def _out(d: torch.Tensor, shape):
+    if d.dtype != torch.bfloat16:
+        raise TypeError(f"D must be bfloat16, got {d.dtype}")
+    if tuple(d.shape) != tuple(shape):
+        raise ValueError(f"D must have shape {tuple(shape)}, got {tuple(d.shape)}")
+    _dev(d, "D")
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def dg_fp8_gemm_nt(A, sfa, B, sfb, C, D, stream=None):
+    """D = C + A @ B.T (C may be None).  A [M,K], sfa [K/128,M], B [N,K], sfb [ceil(N/128),K/128]."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share K")
+    _f32(sfa, "sfa", (_cdiv(K, 128), M))
+    _f32(sfb, "sfb", (_cdiv(N, 128), _cdiv(K, 128)))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    """Contiguous M-grouped: row m uses B[m_indices[m]]; rows with an index outside [0,G) are untouched."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    if B.shape[2] != K:
+        raise ValueError("A and B must share K")
+    _f32(sfa, "sfa", (_cdiv(K, 128), M))
+    _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
+                                                   _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream=None):
+    """Masked M-grouped: group g computes rows m < clamp(masked_m[g], 0, M_max); other rows untouched."""
+    _fp8(A, "A"); _fp8(B, "B")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != G or B.shape[2] != K:
+        raise ValueError("B must be [G, N, K]")
+    _f32(sfa, "sfa", (G, _cdiv(K, 128), M_max))
+    _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
+    if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be int32 [G]")
+    _dev(masked_m, "masked_m")
+    if C is not None:
+        _f32(C, "C", (G, M_max, N))
+    _out(D, (G, M_max, N))
+    _check(lib.dg_m_grouped_fp8_gemm_nt_masked(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m),
+                                               _ptr(C), _ptr(D), M_max, N, K, G, _stream(stream)))
+    return D
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return int(lib.dg_get_mk_alignment_for_contiguous_layout())
+
+
+def set_num_cus(n: int) -> None:
+    _check(lib.dg_set_num_cus(int(n)))
+
+
+def get_num_cus() -> int:
+    return int(lib.dg_get_num_cus())
+
+
+def init() -> None:
+    _check(lib.dg_init())
+
+
+def precompile(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,
+               num_cus: int = 0) -> None:
+    _check(lib.dg_precompile(kind, rows, N, K, num_groups, int(has_c), num_cus))
+
+
+# names without the C prefix, as on the pages
+fp8_gemm_nt = dg_fp8_gemm_nt
+m_grouped_fp8_gemm_nt_contiguous = dg_m_grouped_fp8_gemm_nt_contiguous
+m_grouped_fp8_gemm_nt_masked = dg_m_grouped_fp8_gemm_nt_masked

@@ -1,0 +1,82 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/dg.h
+declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_scales_amd as pkg
+from moe_grouped_gemm_scales_amd import dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+FAKE = 0x100000   # a 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "dg_fp8_gemm_nt" in names and "dg_m_grouped_fp8_gemm_nt_masked" in names
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dg.h but not exported"
+
+
+def test_alignment_query():
+    assert pkg.get_mk_alignment_for_contiguous_layout() == 128
+
+
+def _dense(A=FAKE, sfa=FAKE, B=FAKE, sfb=FAKE, C=None, D=FAKE, M=64, N=64, K=128):
+    v = ctypes.c_void_p
+    return dg.lib.dg_fp8_gemm_nt(v(A), v(sfa), v(B), v(sfb), v(C), v(D), M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=0), -1), (dict(sfa=0), -1), (dict(B=0), -1), (dict(sfb=0), -1), (dict(D=0), -1),
+    (dict(M=-1), -1), (dict(N=0), -1), (dict(K=0), -1),
+    (dict(K=100), -2), (dict(K=7168 + 64), -2),
+    (dict(A=FAKE + 8), -3), (dict(D=FAKE + 2), -3), (dict(C=FAKE + 4), -3), (dict(sfa=FAKE + 2), -3),
+])
+def test_dense_validation(kw, status):
+    assert _dense(**kw) == status
+    assert dg.lib.dg_last_error().decode()
+
+
+def test_empty_m_is_a_no_op():
+    assert _dense(M=0) == 0
+
+
+def test_grouped_validation():
+    v = ctypes.c_void_p
+    f = dg.lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), 128, 64, 128, 2, None) == -1
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 100, 64, 128, 2, None) == -3
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 128, 64, 128, 0, None) == -1
+    g = dg.lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert g(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), 64, 64, 128, 2, None) == -1
+    assert g(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE + 2), None, v(FAKE), 64, 64, 128, 2, None) == -3
+    assert g(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 0, 64, 128, 2, None) == 0
+
+
+def test_no_device_is_a_hip_error():
+    """Valid arguments on a host without a GPU: the first HIP call fails cleanly."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _dense() == -5
+
+
+def test_binding_marshalling_errors():
+    import torch
+    A = torch.zeros(4, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        pkg.dg_fp8_gemm_nt(A, torch.zeros(1, 4), A, torch.zeros(1, 1), None, torch.zeros(4, 4, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        pkg.dg_fp8_gemm_nt(A.float(), torch.zeros(1, 4), A, torch.zeros(1, 1), None, None)

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bar: every computed element within |D - ref| <= 2^-7 |ref| + 1e-3 rms(ref)
+(tests/check.py); bitwise equality where the exact result is representable
+(integer data with power-of-two scales, one-hot rows); rows the method does
+not compute keep the sentinel bits they were prefilled with.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests import check, gen
+from tests.gpu_util import flat_rows, oracle_rows, run, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _compare(p, D, sent, ref, comp, rows=None, what=""):
+    Df = flat_rows(D)
+    Sf = flat_rows(sent)
+    idx = np.arange(Df.shape[0]) if rows is None else rows
+    got = check.bf16_to_f64(Df[torch.as_tensor(idx)])
+    if comp.any():
+        check.assert_close(got[comp], ref[comp], what)
+    if (~comp).any():
+        untouched = idx[~comp]
+        assert np.array_equal(check.bf16_bits(Df[torch.as_tensor(untouched)]),
+                              check.bf16_bits(Sf[torch.as_tensor(untouched)])), f"{what}: a skipped row was written"
+
+
+# ------------------------------------------------------------------ dense, small and ragged
+DENSE_SHAPES = [
+    (1, 16, 128, False),
+    (5, 129, 384, True),
+    (16, 64, 256, False),
+    (64, 2112, 1024, False),
+    (100, 300, 512, True),
+    (128, 256, 1536, False),
+    (257, 515, 640, True),
+    (300, 1000, 2048, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,with_c", DENSE_SHAPES)
+def test_dense_small(oracle, M, N, K, with_c):
+    p = gen.make_dense(M, N, K, seed=M * 7 + N + K, with_c=with_c)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"dense {M}x{N}x{K}")
+
+
+def test_dense_integer_data_bitwise(oracle):
+    g = torch.Generator().manual_seed(77)
+    M, N, K = 96, 400, 1024
+    A = gen.integer_codes((M, K), g, max_abs=8)
+    B = gen.integer_codes((N, K), g, max_abs=8)
+    sfa = gen.pow2_scales((K // 128, M), g, -2, 2)
+    sfb = gen.pow2_scales(((N + 127) // 128, K // 128), g, -2, 2)
+    p = gen.Problem("dense", A, sfa, B, sfb)
+    D, _ = run(p)
+    ref, _ = oracle_rows(oracle, p)
+    # every partial sum is an integer multiple of 2^-9 below 2^24 ulps: exact in FP32
+    want = oracle.bf16_rne(ref).reshape(M, N)
+    assert np.array_equal(check.bf16_bits(D), want)
+
+
+def test_dense_one_hot_maps_lanes(oracle):
+    """A[m, pi(m)] = 1 picks one column of B per row: checks row/column/lane mapping bitwise."""
+    g = torch.Generator().manual_seed(5)
+    M, N, K = 80, 272, 768
+    pi = torch.randint(0, K, (M,), generator=g)
+    A = torch.zeros(M, K, dtype=torch.uint8)
+    A[torch.arange(M), pi] = gen.E4M3_ONE
+    q = gen.make_dense(1, N, K, seed=99)
+    sfa = gen.pow2_scales((K // 128, M), g)
+    p = gen.Problem("dense", A, sfa, q.B, q.sfb)
+    D, _ = run(p)
+    ref, _ = oracle_rows(oracle, p)
+    assert np.array_equal(check.bf16_bits(D), oracle.bf16_rne(ref).reshape(M, N))
+
+
+def test_dense_repeatable_and_stream(oracle):
+    p = gen.make_dense(64, 2112, 7168, seed=1000)
+    dev = to_dev(p)
+    D1, _ = run(p, dev=dev)
+    D2, _ = run(p, dev=dev, sentinel_seed=1)
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        D3, _ = run(p, dev=dev, sentinel_seed=2)
+    assert torch.equal(D1.view(torch.int16), D3.view(torch.int16))
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+@pytest.mark.parametrize("cfg", [0, 1, "1c", 2])
+def test_workload_dense(oracle, cfg):
+    p = gen.make_config(cfg)
+    D, sent = run(p)
+    rows = np.arange(p.M) if p.M <= 128 else sample_rows(p.M, 48, seed=3)
+    ref, comp = oracle_rows(oracle, p, rows=rows)
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[cfg])
+    # every row of a dense result is written: no sentinel survives in sampled-out rows either
+    assert not torch.equal(D.view(torch.int16)[-1], sent.view(torch.int16)[-1])
+
+
+def test_workload_contiguous(oracle):
+    p = gen.make_config(3)
+    D, sent = run(p)
+    rows = sample_rows(p.M, 48, seed=4, block=128)
+    ref, comp = oracle_rows(oracle, p, rows=rows)
+    assert comp.all()
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[3])
+
+
+def test_workload_masked(oracle):
+    p = gen.make_config(4)
+    D, sent = run(p)
+    G, M_max = p.A.shape[0], p.A.shape[1]
+    mm = p.masked_m.numpy().clip(0, M_max)
+    rows = np.arange(G * M_max)          # all rows: cheap enough at K = 2048
+    ref, comp = oracle_rows(oracle, p, rows=rows)
+    assert comp.sum() == mm.sum()
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[4])
+
+
+# ------------------------------------------------------------------ contiguous, edge cases
+@pytest.mark.parametrize("group_rows,N,K,pad,with_c", [
+    ([128, 0, 256, 100], 200, 256, 128, True),
+    ([1, 127, 128, 129], 129, 384, 0, False),
+    ([512], 512, 1024, 0, False),
+    ([0, 0, 300], 96, 128, 256, True),
+])
+def test_contiguous_edges(oracle, group_rows, N, K, pad, with_c):
+    p = gen.make_contiguous(group_rows, N, K, seed=sum(group_rows) + N, with_c=with_c, pad_rows=pad)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"contiguous {group_rows}")
+
+
+def test_contiguous_groups_independent(oracle):
+    p = gen.make_contiguous([256, 128, 128], 300, 512, seed=8)
+    dev = to_dev(p)
+    D1, _ = run(p, dev=dev)
+    B2 = dev["B"].clone()
+    B2[1] = torch.where(B2[1] != 0, B2[1] ^ 0x80, B2[1])
+    dev2 = dict(dev, B=B2)
+    D2, _ = run(p, dev=dev2)
+    idx = p.m_indices
+    assert torch.equal(D1.view(torch.int16)[idx != 1], D2.view(torch.int16)[idx != 1])
+    # flipping the sign of every code of B[1] negates its rows exactly (RNE is sign-symmetric)
+    assert torch.equal(D1.view(torch.int16)[idx == 1] ^ torch.tensor(-32768, dtype=torch.int16),
+                       D2.view(torch.int16)[idx == 1]) or torch.equal(
+        (-D1.float())[idx == 1], D2.float()[idx == 1])
+
+
+# ------------------------------------------------------------------ masked, edge cases
+@pytest.mark.parametrize("masked_m", [[0, 0, 0], [96, 96, 96], [-3, 200, 17], [1, 95, 48]])
+def test_masked_edges(oracle, masked_m):
+    p = gen.make_masked(3, 96, 333, 512, seed=len(masked_m) + sum(masked_m), with_c=True, masked_m=masked_m)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"masked {masked_m}")
+
+
+def test_masked_full_equals_dense(oracle):
+    p = gen.make_masked(2, 128, 256, 384, seed=9, masked_m=[128, 128])
+    D, _ = run(p)
+    for g in range(2):
+        q = gen.Problem("dense", p.A[g], p.sfa[g], p.B[g], p.sfb[g])
+        Dg, _ = run(q)
+        assert torch.equal(D[g].view(torch.int16), Dg.view(torch.int16))
+
+
+# ------------------------------------------------------------------ tile configurations
+FORCED = [
+    "16,16,1,1,2,1",
+    "32,64,1,2,3,2",
+    "64,96,2,2,4,1",
+    "64,112,1,1,2,4",
+    "128,128,2,2,2,1",
+    "128,256,2,4,2,1",
+    "256,224,4,2,2,1",
+    "256,256,4,2,2,1",
+]
+
+
+@pytest.mark.parametrize("forced", FORCED)
+def test_forced_tile_configs(oracle, monkeypatch, forced):
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    p = gen.make_dense(300, 520, 1024, seed=11, with_c=True)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"forced {forced}")
