@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 GEMM hot path on one MI355X.
+
+One step = one library call (the whole hot path: dispatch, staging, FP8 MFMA,
+promotion, BF16 epilogue) on one batch of seeded synthetic input that is
+already resident in HBM.  The default workload is the dense 128 x 24576 x 1536
+GEMM (a shape of the DeepGEMM launch article's section 3 table); --workload
+picks another of the five, --all runs every one of them and prints one line
+per shape on stderr.
+
+Metric (as the pages quote it): TFLOPS = 2 M N K / t and HBM GB/s =
+(|A| + |B| + |D| [+ |C|] + scales) / t with 1-byte A/B and 2-byte D, t the
+kernel time; the roofline fraction is the bound resource's share of the
+MI355X peak (8 TB/s HBM, 5.0 PFLOP/s dense FP8).
+
+HBM honesty: inputs are rotated over enough copies that the working set of a
+cycle exceeds 512 MB, twice the 256 MB Infinity Cache, so every step reads its
+operands from HBM, not from the cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS + HBM GB/s per shape (FP8 block-scaled GEMM), % of roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
+# The pages' H800 numbers for the same shapes (DeepGEMM launch article,
+# section 3 dense table): other hardware, context only.
+PAGES_TFLOPS = {0: 206.0, 1: 535.0, 2: 1358.0}
+KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_scales_amd", "csrc", "kernels", "fp8_gemm.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(p) -> tuple[float, float, int]:
+    """(FLOPs, bytes, computed rows) of one call, by the pages' convention."""
+    K, N = p.K, p.N
+    Kb, Nb = K // 128, (N + 127) // 128
+    if p.kind == "dense":
+        rows, groups_used = p.M, 1
+    elif p.kind == "contiguous":
+        idx = p.m_indices
+        rows = int(((idx >= 0) & (idx < p.G)).sum())
+        groups_used = int(idx[(idx >= 0) & (idx < p.G)].unique().numel())
+    else:
+        mm = p.masked_m.clamp(0, p.A.shape[1])
+        rows = int(mm.sum())
+        groups_used = int((mm > 0).sum())
+    flops = 2.0 * rows * N * K
+    nbytes = rows * K + groups_used * N * K + rows * N * 2
+    if p.C is not None:
+        nbytes += rows * N * 4
+    nbytes += rows * Kb * 4 + groups_used * Nb * Kb * 4
+    return flops, float(nbytes), rows
+
+
+def kind_id(kind: str) -> int:
+    return {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+
+
+def bench_workload(cfg, steps: int, warmup: int, graph: bool):
+    import torch
+
+    import moe_grouped_gemm_scales_amd as dg
+    from tests import gen
+    from tests.gpu_util import out_shape, to_dev
+
+    p = gen.make_config(cfg)
+    flops, nbytes, rows = algorithmic(p)
+    ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
+    ws += math.prod(out_shape(p)) * 2
+    copies = max(1, min(64, math.ceil(512e6 / ws)))
+    devs = [to_dev(p) for _ in range(copies)]
+    outs = [torch.empty(out_shape(p), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def call(i):
+        d, D = devs[i % copies], outs[i % copies]
+        if p.kind == "dense":
+            dg.dg_fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
+        elif p.kind == "contiguous":
+            dg.dg_m_grouped_fp8_gemm_nt_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["m_indices"], d["C"], D)
+        else:
+            dg.dg_m_grouped_fp8_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"], D)
+
+    rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
+    kernel = dg.describe_config(kind_id(p.kind), rows_arg, p.N, p.K, p.G, p.C is not None)
+    t_jit = time.perf_counter()
+    call(0)                                    # JIT compile / cache load, never timed
+    torch.cuda.synchronize()
+    t_jit = time.perf_counter() - t_jit
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    g = None
+    if graph:
+        # one captured launch per copy; replays walk the copies in order
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(copies):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph:
+        reps = math.ceil(steps / copies)
+        starts[0].record(stream)
+        for _ in range(reps):
+            g.replay()
+        ends[0].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        n_launch = reps * copies
+        kernel_ms = starts[0].elapsed_time(ends[0]) / n_launch
+        ms_per_step = wall * 1e3 / n_launch
+    else:
+        for i in range(steps):
+            starts[i].record(stream)
+            call(i)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+        kernel_ms = sum(per) / len(per)
+        ms_per_step = wall * 1e3 / steps
+    t_kernel = kernel_ms * 1e-3
+    ai = flops / nbytes
+    bound = "mfma" if ai >= RIDGE else "hbm"
+    tflops = flops / t_kernel / 1e12
+    gbs = nbytes / t_kernel / 1e9
+    frac = (tflops / PEAK_FP8_TFLOPS) if bound == "mfma" else (gbs / PEAK_HBM_GBS)
+    return dict(problem=p, flops=flops, bytes=nbytes, rows=rows, kernel=kernel, copies=copies,
+                kernel_ms=kernel_ms, ms_per_step=ms_per_step, wall_s=wall, tflops=tflops, gbs=gbs,
+                bound=bound, frac=frac, jit_s=t_jit, step_tflops=flops / (ms_per_step * 1e-3) / 1e12)
+
+
+def cpu_baseline(cfg, budget_s: float = 20.0):
+    """The oracle, as it stands, on this host's cores: the full workload when it
+    fits the budget, else a row sample scaled to the whole."""
+    import numpy as np
+
+    from oracle import Oracle
+    from tests import gen
+    from tests.gpu_util import oracle_rows
+
+    o = Oracle()
+    p = gen.make_config(cfg)
+    flops_total, _, rows_total = algorithmic(p)
+    total_rows = p.A.shape[0] * p.A.shape[1] if p.kind == "masked" else p.M
+    # probe with a few rows to size the sample
+    probe = np.arange(min(8, total_rows))
+    t = time.perf_counter()
+    oracle_rows(o, p, rows=probe)
+    per_row = (time.perf_counter() - t) / len(probe)
+    n = int(min(total_rows, max(len(probe), budget_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, total_rows - 1, n).astype(np.int64)
+    t = time.perf_counter()
+    _, comp = oracle_rows(o, p, rows=rows)
+    dt = time.perf_counter() - t
+    computed = int(comp.sum())
+    flops = 2.0 * computed * p.N * p.K
+    desc = ("full problem" if n == total_rows else f"{n} of {total_rows} rows, evenly spaced") + \
+        f", {dt:.1f} s, FP64 exact block sums"
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOPS", cores=o.threads(), kind="oracle",
+                sample=desc)
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="1", help="0, 1, 1c, 2, 3 or 4 (default 1)")
+    ap.add_argument("--all", action="store_true", help="also run every workload, one stderr line each")
+    ap.add_argument("--graph", action="store_true", help="replay the steps from a captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also write the per-shape results as JSON here")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    from tests import gen
+
+    cfg = args.workload if args.workload == "1c" else int(args.workload)
+    per_shape = []
+    if args.all:
+        for c in [0, 1, "1c", 2, 3, 4]:
+            steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
+            r = bench_workload(c, steps, min(args.warmup, steps), args.graph)
+            line = dict(workload=gen.CONFIG_NAMES[c], kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
+                        tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
+                        roofline_frac=round(r["frac"], 4), step_us=round(r["ms_per_step"] * 1e3, 3),
+                        rows=r["rows"], copies=r["copies"])
+            per_shape.append(line)
+            print(json.dumps(line), file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+
+    r = bench_workload(cfg, args.steps, args.warmup, args.graph)
+    p = r["problem"]
+    name = gen.CONFIG_NAMES[cfg]
+    roof = dict(bound=r["bound"],
+                achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
+                peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
+                unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
+                frac=round(r["frac"], 4),
+                traffic=traffic_for(name))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    value = r["step_tflops"]
+    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / pages, 4) if pages else None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": name, "kind": p.kind, "M": p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
+                   "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],
+                   "graph": bool(args.graph)},
+        "kernel_us": round(r["kernel_ms"] * 1e3, 3),
+        "kernel_tflops": round(r["tflops"], 3),
+        "hbm_gbs": round(r["gbs"], 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(dict(main=out, per_shape=per_shape), f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

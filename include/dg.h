@@ -138,6 +138,15 @@ dg_status dg_init(void);
  */
 dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus);
 
+/*
+ * Name of the kernel configuration (tile, waves, LDS stages, split-K, sizes)
+ * that a call with these arguments selects on the current device (or for
+ * `num_cus` compute units when num_cus > 0), written NUL-terminated into
+ * buf[0..len).  Informational; nothing is compiled or launched.
+ */
+dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus,
+                             char *buf, int len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 
 #include <hip/hip_runtime.h>
 
@@ -42,9 +43,20 @@ struct Workspace {
     size_t counter_bytes = 0;
 };
 
+// Everything a call needs besides the pointers, computed once per shape.
+struct Plan {
+    KernelConfig cfg;
+    hipFunction_t fn = nullptr;
+    int grid = 0;
+    int64_t items = 0;
+};
+
+using PlanKey = std::tuple<int, int, int, int, int, int, int, std::string>;
+
 struct DeviceState {
     int num_cus = 0;
     std::map<hipStream_t, Workspace> ws;
+    std::map<PlanKey, Plan> plans;
 };
 
 std::mutex g_mu;
@@ -139,19 +151,31 @@ dg_status launch(const Problem& p, const void* A, const float* sfa, const void* 
     dg_status s = device_state(&st, &dev);
     if (s != DG_OK) return s;
     const int cus = effective_cus(*st);
-    KernelConfig cfg = select_config(p, cus);
-    void* fptr = nullptr;
-    s = get_function(cfg, &fptr);
-    if (s != DG_OK) return s;
-    hipFunction_t f = static_cast<hipFunction_t>(fptr);
-
-    const int64_t items = num_work_items(cfg, p.rows);
+    const char* forced = std::getenv("DG_FORCE_CONFIG");
+    PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, cus, forced ? forced : ""};
+    auto it = st->plans.find(key);
+    if (it == st->plans.end()) {
+        Plan plan;
+        plan.cfg = select_config(p, cus);
+        void* fptr = nullptr;
+        s = get_function(plan.cfg, &fptr);
+        if (s != DG_OK) return s;
+        plan.fn = static_cast<hipFunction_t>(fptr);
+        plan.items = num_work_items(plan.cfg, p.rows);
+        if (plan.items > INT_MAX) return set_error(DG_ERR_UNSUPPORTED, "too many tiles");
+        int occ = 1;
+        if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, plan.fn, plan.cfg.threads(), 0) != hipSuccess ||
+            occ < 1)
+            occ = 1;
+        plan.grid = (int)std::min<int64_t>(plan.items, (int64_t)cus * occ);
+        it = st->plans.emplace(key, plan).first;
+    }
+    const Plan& plan = it->second;
+    const KernelConfig& cfg = plan.cfg;
+    hipFunction_t f = plan.fn;
+    const int64_t items = plan.items;
+    const int grid = plan.grid;
     if (items <= 0) return DG_OK;
-    if (items > INT_MAX) return set_error(DG_ERR_UNSUPPORTED, "too many tiles");
-    int occ = 1;
-    if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, cfg.threads(), 0) != hipSuccess || occ < 1)
-        occ = 1;
-    const int grid = (int)std::min<int64_t>(items, (int64_t)cus * occ);
 
     LaunchParams lp{};
     lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
@@ -230,6 +254,26 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
     KernelConfig cfg = select_config(p, num_cus > 0 ? num_cus : 256);
     std::vector<char> code;
     return compile_code(cfg, &code);
+}
+
+dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus, char* buf,
+                             int len) {
+    if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
+        return set_error(DG_ERR_INVALID_ARG, "dg_describe_config: bad arguments");
+    if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
+    int cus = num_cus;
+    if (cus <= 0) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        DeviceState* st = nullptr;
+        int dev = 0;
+        dg_status s = device_state(&st, &dev);
+        if (s != DG_OK) return s;
+        cus = effective_cus(*st);
+    }
+    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
+    const std::string key = select_config(p, cus).key();
+    std::snprintf(buf, (size_t)len, "%s", key.c_str());
+    return DG_OK;
 }
 
 dg_status dg_fp8_gemm_nt(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,

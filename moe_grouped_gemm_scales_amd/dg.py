@@ -53,6 +53,8 @@ def _load():
     lib.dg_init.restype = i32
     lib.dg_precompile.argtypes = [i32] * 7
     lib.dg_precompile.restype = i32
+    lib.dg_describe_config.argtypes = [i32] * 7 + [ctypes.c_char_p, i32]
+    lib.dg_describe_config.restype = i32
     return lib
 
 
@@ -182,6 +184,14 @@ def init() -> None:
 def precompile(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,
                num_cus: int = 0) -> None:
     _check(lib.dg_precompile(kind, rows, N, K, num_groups, int(has_c), num_cus))
+
+
+def describe_config(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,
+                    num_cus: int = 0) -> str:
+    """Key of the kernel configuration a call with these sizes selects."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.dg_describe_config(kind, rows, N, K, num_groups, int(has_c), num_cus, buf, len(buf)))
+    return buf.value.decode()
 
 
 # names without the C prefix, as on the pages
