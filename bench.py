@@ -78,7 +78,7 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool):
     from tests import gen
     from tests.gpu_util import out_shape, to_dev
 
-    p = gen.make_config(cfg)
+    p = gen.make_workload(cfg)
     flops, nbytes, rows = algorithmic(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
     ws += math.prod(out_shape(p)) * 2
@@ -97,49 +97,45 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool):
 
     rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
     kernel = dg.describe_config(kind_id(p.kind), rows_arg, p.N, p.K, p.G, p.C is not None)
-    t_jit = time.perf_counter()
-    call(0)                                    # JIT compile / cache load, never timed
-    torch.cuda.synchronize()
-    t_jit = time.perf_counter() - t_jit
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    g = None
-    if graph:
-        # one captured launch per copy; replays walk the copies in order
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(copies):
-                call(i)
-        g.replay()
+    # everything runs on one non-default stream (HIP graphs cannot capture the null stream)
+    stream = torch.cuda.Stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t_jit = time.perf_counter()
+        call(0)                                    # JIT compile / cache load, never timed
         torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graph:
-        reps = math.ceil(steps / copies)
-        starts[0].record(stream)
-        for _ in range(reps):
-            g.replay()
-        ends[0].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        n_launch = reps * copies
-        kernel_ms = starts[0].elapsed_time(ends[0]) / n_launch
-        ms_per_step = wall * 1e3 / n_launch
-    else:
-        for i in range(steps):
-            starts[i].record(stream)
+        t_jit = time.perf_counter() - t_jit
+        for i in range(warmup):
             call(i)
-            ends[i].record(stream)
+        torch.cuda.synchronize()
+        g = None
+        if graph:
+            # all K steps captured into one graph (one kernel node per step, walking
+            # the input copies in order); one untimed replay uploads it
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    call(i)
+            g.replay()
+            torch.cuda.synchronize()
+        n_launch = steps
+        # Timed region: the K launches back to back on this stream, one HIP event
+        # pair around all of them (per-launch event pairs would add the dispatch
+        # cost of every event to every kernel).
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        if graph:
+            g.replay()
+        else:
+            for i in range(steps):
+                call(i)
+        end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-        kernel_ms = sum(per) / len(per)
-        ms_per_step = wall * 1e3 / steps
+    kernel_ms = start.elapsed_time(end) / n_launch
+    ms_per_step = wall * 1e3 / n_launch
     t_kernel = kernel_ms * 1e-3
     ai = flops / nbytes
     bound = "mfma" if ai >= RIDGE else "hbm"
@@ -161,7 +157,7 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
     from tests.gpu_util import oracle_rows
 
     o = Oracle()
-    p = gen.make_config(cfg)
+    p = gen.make_workload(cfg)
     flops_total, _, rows_total = algorithmic(p)
     total_rows = p.A.shape[0] * p.A.shape[1] if p.kind == "masked" else p.M
     # probe with a few rows to size the sample
@@ -171,13 +167,17 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
     per_row = (time.perf_counter() - t) / len(probe)
     n = int(min(total_rows, max(len(probe), budget_s / max(per_row, 1e-9))))
     rows = np.linspace(0, total_rows - 1, n).astype(np.int64)
-    t = time.perf_counter()
-    _, comp = oracle_rows(o, p, rows=rows)
-    dt = time.perf_counter() - t
-    computed = int(comp.sum())
+    # repeat the sample until about half the budget has been spent (at least once)
+    reps, dt, computed = 0, 0.0, 0
+    while reps == 0 or dt < 0.5 * budget_s:
+        t = time.perf_counter()
+        _, comp = oracle_rows(o, p, rows=rows)
+        dt += time.perf_counter() - t
+        computed += int(comp.sum())
+        reps += 1
     flops = 2.0 * computed * p.N * p.K
     desc = ("full problem" if n == total_rows else f"{n} of {total_rows} rows, evenly spaced") + \
-        f", {dt:.1f} s, FP64 exact block sums"
+        f" x {reps}, {dt:.1f} s, FP64 exact block sums"
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOPS", cores=o.threads(), kind="oracle",
                 sample=desc)
 
@@ -205,10 +205,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="1", help="0, 1, 1c, 2, 3 or 4 (default 1)")
     ap.add_argument("--all", action="store_true", help="also run every workload, one stderr line each")
-    ap.add_argument("--graph", action="store_true", help="replay the steps from a captured HIP graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a captured HIP graph")
+    ap.add_argument("--copy-kernel", action="store_true",
+                    help="only run a plain 256 MiB device copy (calibrates rocprofv3 byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also write the per-shape results as JSON here")
     args = ap.parse_args()
+
+    if args.copy_kernel:
+        import torch
+        x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel_bytes_read": 256 << 20, "copy_kernel_bytes_written": 256 << 20,
+                          "launches": 3}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -226,8 +241,8 @@ def main():
     if args.all:
         for c in [0, 1, "1c", 2, 3, 4]:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
-            r = bench_workload(c, steps, min(args.warmup, steps), args.graph)
-            line = dict(workload=gen.CONFIG_NAMES[c], kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
+            r = bench_workload(c, steps, min(args.warmup, steps), not args.eager)
+            line = dict(workload=gen.WORKLOAD_NAMES[c], kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
                         roofline_frac=round(r["frac"], 4), step_us=round(r["ms_per_step"] * 1e3, 3),
                         rows=r["rows"], copies=r["copies"])
@@ -236,9 +251,9 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    r = bench_workload(cfg, args.steps, args.warmup, args.graph)
+    r = bench_workload(cfg, args.steps, args.warmup, not args.eager)
     p = r["problem"]
-    name = gen.CONFIG_NAMES[cfg]
+    name = gen.WORKLOAD_NAMES[cfg]
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
@@ -263,7 +278,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "kind": p.kind, "M": p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
                    "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],
-                   "graph": bool(args.graph)},
+                   "hip_graph": bool(not args.eager)},
         "kernel_us": round(r["kernel_ms"] * 1e3, 3),
         "kernel_tflops": round(r["tflops"], 3),
         "hbm_gbs": round(r["gbs"], 1),

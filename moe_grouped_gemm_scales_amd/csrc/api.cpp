@@ -21,7 +21,7 @@ namespace {
 
 thread_local std::string t_last_error;
 
-// Mirror of the kernel's Params (same order, same types, same padding).
+// The kernel's arguments, in order.
 struct LaunchParams {
     const void* A;
     const float* sfa;
@@ -193,7 +193,7 @@ dg_status launch(const Problem& p, const void* A, const float* sfa, const void* 
     if (env_flag("DG_PRINT_CONFIGS"))
         std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), grid,
                      cfg.threads(), (long long)items, cfg.lds_bytes());
-    void* args[] = {&lp};
+    void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M, &lp.num_tiles};
     hipError_t e = hipModuleLaunchKernel(f, grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
     if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     return DG_OK;

@@ -20,12 +20,13 @@ struct KernelConfig {
     int bm = 128, bn = 128;    // workgroup tile (rows of A, rows of B)
     int wm = 2, wn = 2;        // waves along m and n
     int stages = 2;            // LDS ring depth
+    int kstep = 1;             // 128-wide K blocks per LDS stage (1 or 2)
     int splitk = 1;            // K splits (dense only)
     int has_c = 0;
     int n = 0, k = 0, g = 1;
 
     int threads() const { return 64 * wm * wn; }
-    int stage_bytes() const { return bm * 128 + bn * 128 + ((bm + 63) / 64) * 256; }
+    int stage_bytes() const { return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256; }
     int lds_bytes() const { return stages * stage_bytes(); }
     std::string key() const;
 };

@@ -8,7 +8,7 @@
 // (tile, wave grid, LDS stages, split-K) tuples; the model charges each
 // candidate its wave-quantised MFMA time, its operand traffic and a fixed
 // per-tile cost, and the cheapest one wins.  DG_FORCE_CONFIG
-// ("bm,bn,wm,wn,stages,splitk") overrides the choice for tuning sweeps.
+// ("bm,bn,wm,wn,stages,splitk[,kstep]") overrides the choice for tuning sweeps.
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -62,53 +62,102 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
     const int occ = occupancy(c);
     const double slots = (double)num_cus * occ;
     const double waves = std::ceil(tiles / slots);
-    const double active = std::min(tiles, slots);
     const double kspan = (double)p.k / c.splitk;
-    const int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
-    // a CU has 4 SIMDs: fewer than 4 resident waves leave matrix cores idle
-    const double simd_use = std::min(1.0, occ * c.wm * c.wn / 4.0);
-    const double mfma_rate = kMfmaFlopPerClkCu * kClockHz * mfma_efficiency(tm, tn) * simd_use / occ;
-    const double t_compute = 2.0 * c.bm * c.bn * kspan / mfma_rate;
+    const double kblocks = kspan / 128.0;
+    const int nw = c.wm * c.wn;
+    const double waves_per_simd = std::max(1.0, occ * nw / 4.0);
+    // Per-CU cycle counts of one tile (measured shape of the kernel on gfx950):
+    //  * MFMA: 32 cycles per 16x16x128 step on each of 4 SIMDs, shared by the
+    //    occ resident workgroups;
+    //  * VALU: one FMA per output element per K block plus a scale product per
+    //    sub-tile, 4 cycles per wave64 instruction; only part of it hides under
+    //    the MFMAs of the same SIMD;
+    //  * a fixed cost per LDS stage (barrier, first LDS reads) that a second
+    //    wave per SIMD mostly hides.
+    const double mfma_cyc = (double)c.bm * c.bn * kspan * 2.0 / kMfmaFlopPerClkCu * occ /
+                            std::min(1.0, nw * occ / 4.0);
+    const double valu_cyc = (double)c.bm * c.bn / 64.0 * kblocks * 1.3 * 4.0 / 4.0 * occ;
+    const double compute_cyc = std::max(mfma_cyc, valu_cyc) + 0.35 * std::min(mfma_cyc, valu_cyc);
+    const double stage_cyc = 900.0 / waves_per_simd * (kblocks / c.kstep);
+    const double t_compute = (compute_cyc + stage_cyc) / kClockHz;
     // operand tiles mostly come from L2/MALL (they are shared between tiles);
     // the HBM bound of the whole launch is applied below
-    (void)active;
     const double t_load = (double)(c.bm + c.bn) * kspan / (kCuLoadBytesPerS / occ);
     // pipeline fill, epilogue and scheduling per tile; split-K adds a round trip
-    double t_fixed = 1.2e-6 + (c.splitk > 1 ? 1.0e-6 + c.bm * c.bn * 8.0 * c.splitk / kCuLoadBytesPerS : 0.0);
+    double t_fixed = 1.2e-6 + (c.splitk > 1 ? 1.0e-6 * c.splitk + c.bm * c.bn * 8.0 * c.splitk / kCuLoadBytesPerS : 0.0);
     double t = waves * (std::max(t_compute, t_load) + t_fixed);
-    // whole-device floors: HBM traffic for the operands read once, D written once
+    // whole-device floor: HBM traffic.  Row blocks that share a B column block
+    // re-read it; they only hit in L2 when they run close together, which the
+    // grouped tile order gives for large M (8 row blocks per sweep) but not for
+    // a handful of row blocks spread over the whole grid.
     const double groups_b = (p.kind == kDense) ? 1.0 : p.g;
-    const double bytes = valid_rows * p.k + groups_b * p.n * p.k + valid_rows * p.n * (2.0 + 4.0 * p.has_c);
+    const double rows_per_group = valid_rows / groups_b;
+    const double b_reads = rows_per_group <= 512 ? std::ceil(rows_per_group / c.bm)
+                                                 : std::max(1.0, std::ceil(rows_per_group / c.bm) / 8.0);
+    const double bytes = valid_rows * p.k + b_reads * groups_b * p.n * p.k +
+                         valid_rows * p.n * (2.0 + 4.0 * p.has_c);
     t = std::max(t, bytes / kHbmBytesPerS);
     return t;
 }
 
 int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
-    const int na = c.bm / 8, nb = c.bn / 8, ns = (c.bm + 63) / 64;
+    const int rpi = 8 / c.kstep;
+    const int na = c.bm / rpi, nb = c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
     return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw;
 }
 
 // Mirrors the kernel's static_asserts, so a selected config always compiles.
 bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (16 * c.wm) || c.bn % (16 * c.wn)) return false;
-    if (c.bm % 8 || c.bn % 8 || c.stages < 2) return false;
+    if (c.kstep != 1 && c.kstep != 2) return false;
+    if (c.bm % (8 / c.kstep) || c.bn % (8 / c.kstep) || c.stages < 2) return false;
     if (dma_per_wave(c) * (c.stages - 1) > 63) return false;   // vmcnt field
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > 32) return false;
     if (c.lds_bytes() > kLdsBytes) return false;
-    if ((p.k / 128) % c.splitk) return false;
+    if ((p.k / 128) % (c.splitk * c.kstep)) return false;
     if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
     if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
     return true;
 }
 
+// Configurations measured fastest on an MI355X (graph-replayed back-to-back
+// launches, tile/wave/stage/split sweeps) for the shapes of the DeepGEMM
+// launch article's benchmark tables; other shapes go through the model.
+struct Tuned {
+    int kind, rows, n, k, g, has_c;
+    int bm, bn, wm, wn, stages, splitk, kstep;
+};
+const Tuned kTuned[] = {
+    {kDense, 64, 2112, 7168, 1, 0, 64, 128, 2, 2, 3, 4, 2},
+    {kDense, 128, 24576, 1536, 1, 0, 128, 128, 2, 4, 2, 1, 2},
+    {kDense, 128, 24576, 1536, 1, 1, 128, 128, 2, 4, 2, 1, 2},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 224, 4, 2, 2, 1, 1},
+    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 2, 1, 2},
+};
+
+bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
+    if (num_cus != 256) return false;       // measured on the full 256-CU part
+    for (const Tuned& t : kTuned) {
+        if (t.kind != p.kind || t.n != p.n || t.k != p.k || t.g != p.g || t.has_c != p.has_c) continue;
+        if (t.rows >= 0 && t.rows != p.rows) continue;
+        if (t.rows < 0 && p.rows < 4096) continue;   // contiguous: any large token count
+        c->bm = t.bm; c->bn = t.bn; c->wm = t.wm; c->wn = t.wn;
+        c->stages = t.stages; c->splitk = t.splitk; c->kstep = t.kstep;
+        return true;
+    }
+    return false;
+}
+
 bool parse_forced(KernelConfig* c) {
     const char* s = std::getenv("DG_FORCE_CONFIG");
     if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sk;
-    if (std::sscanf(s, "%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk) != 6) return false;
-    c->bm = bm; c->bn = bn; c->wm = wm; c->wn = wn; c->stages = st; c->splitk = sk;
+    int bm, bn, wm, wn, st, sk, ks = 1;
+    int got = std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk, &ks);
+    if (got != 6 && got != 7) return false;
+    c->bm = bm; c->bn = bn; c->wm = wm; c->wn = wn; c->stages = st; c->splitk = sk; c->kstep = ks;
     return true;
 }
 
@@ -131,6 +180,13 @@ KernelConfig select_config(const Problem& p, int num_cus) {
 
     KernelConfig forced = base;
     if (parse_forced(&forced) && valid(forced, p)) return forced;
+    KernelConfig table = base;
+    if (tuned(p, num_cus, &table) && valid(table, p)) {
+        if (env_flag("DG_PRINT_CONFIGS"))
+            std::fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s (measured)\n", p.kind, p.rows, p.n, p.k,
+                         p.g, table.key().c_str());
+        return table;
+    }
 
     // masked: the host cannot see masked_m; plan for half the rows being valid
     const double valid_rows = (p.kind == kMasked) ? 0.5 * p.rows * p.g : (double)p.rows;
@@ -139,17 +195,39 @@ KernelConfig select_config(const Problem& p, int num_cus) {
     static const int bns[] = {16, 32, 48, 64, 96, 112, 128, 160, 192, 224, 256};
     static const int wgs[][2] = {{1, 4}, {2, 2}, {4, 1}, {2, 4}, {4, 2}, {1, 8}, {8, 1}, {1, 1}, {1, 2}, {2, 1}};
     const int max_bm = round_up(std::max(p.rows, 16), 16);
+    // Skinny row counts: one row block covers every row (of a group), so each B
+    // tile is fetched from HBM once instead of once per row block.
+    // (masked groups are not: their row blocks past masked_m[g] are skipped)
+    const bool one_row_block = p.kind == kDense && p.rows <= 256;
 
+    // Structure the measurements favour on gfx950: two waves per SIMD (8-wave
+    // workgroups) for large tiles, four waves otherwise, wave grids no more
+    // than 4:1, row blocks of 64+ rows unless the problem has fewer rows, and
+    // split-K only when the output tiles alone cannot fill the device.
+    const int out_tiles_128 = ((p.rows + 127) / 128) * ((p.n + 127) / 128);
     Estimate best{1e30, base};
     for (int bm : bms) {
         if (bm > max_bm && bm > 16 && bm / 2 >= max_bm) continue;   // no tile twice the rows
+        if (one_row_block && bm < max_bm) continue;
+        if (bm < 64 && max_bm >= 64) continue;
         for (int bn : bns) {
             if (bn > round_up(p.n, 16) && bn / 2 >= round_up(p.n, 16)) continue;
             for (auto& w : wgs) {
+                const int nw = w[0] * w[1];
+                const bool tiny = bm * bn < 64 * 64;
+                if (!tiny && nw < 4) continue;
+                if (bm * bn >= 128 * 96 && nw < 8) continue;
+                if (bm * bn < 128 * 96 && nw > 4) continue;
+                if (w[0] > 2 * w[1] || w[1] > 2 * w[0]) {
+                    if (!tiny) continue;
+                }
                 for (int sk = 1; sk <= 16; ++sk) {
+                  for (int ks = 1; ks <= 2; ++ks) {
                     if (sk > 1 && (p.kind != kDense || kb % sk || kb / sk < 2)) continue;
+                    if (sk > 1 && out_tiles_128 * 2 >= num_cus) continue;
+                    if (sk > 1 && bm * bn < 64 * 128) continue;   // small split tiles measured slow
                     KernelConfig c = base;
-                    c.bm = bm; c.bn = bn; c.wm = w[0]; c.wn = w[1]; c.splitk = sk;
+                    c.bm = bm; c.bn = bn; c.wm = w[0]; c.wn = w[1]; c.splitk = sk; c.kstep = ks;
                     c.stages = std::min(4, kLdsBytes / c.stage_bytes());
                     while (c.stages > 2 && dma_per_wave(c) * (c.stages - 1) > 63) --c.stages;
                     if (c.stages < 2) continue;
@@ -158,6 +236,7 @@ KernelConfig select_config(const Problem& p, int num_cus) {
                     // prefer bigger wave tiles on ties (fewer LDS reads per MFMA)
                     t *= 1.0 + 0.01 / (c.bm / c.wm / 16 * (c.bn / c.wn / 16));
                     if (t < best.seconds) best = {t, c};
+                  }
                 }
             }
         }

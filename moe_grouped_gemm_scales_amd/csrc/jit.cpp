@@ -58,6 +58,7 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     def("DG_WM", c.wm);
     def("DG_WN", c.wn);
     def("DG_STAGES", c.stages);
+    def("DG_KSTEP", c.kstep);
     def("DG_SPLITK", c.splitk);
     def("DG_HAS_C", c.has_c);
     def("DG_N", c.n);
@@ -172,7 +173,8 @@ dg_status compile_locked(const KernelConfig& c, std::vector<char>* code) {
 
 std::string KernelConfig::key() const {
     std::ostringstream s;
-    s << "k" << kind << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "_sk" << splitk
+    s << "k" << kind << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
+      << "_sk" << splitk
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
     return s.str();
 }

@@ -28,8 +28,8 @@
 //     (m, 128-wide n block) and the BF16 store is 8 contiguous bytes.
 //   * Operand tiles go global -> LDS by buffer_load ... lds (no VGPR staging)
 //     into a STAGES-deep ring; each 128-byte row is stored with its 16-byte
-//     chunks XOR-swizzled by ((row >> 1) & 7) so that the 16 rows read by one
-//     quarter-wave land in 16 distinct bank groups.
+//     chunks XOR-swizzled by (row & 7), which makes the fragment reads
+//     bank-conflict free (measured with SQ_LDS_BANK_CONFLICT).
 //   * A persistent grid walks tiles; split-K partials (dense only) are summed
 //     in a fixed order by the last-arriving workgroup of a tile.
 
@@ -49,6 +49,7 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 #define DG_WM 2
 #define DG_WN 2
 #define DG_STAGES 2
+#define DG_KSTEP 1
 #define DG_SPLITK 1
 #define DG_HAS_C 0
 #define DG_N 256
@@ -65,6 +66,7 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WAVE_M = BM / WM, WAVE_N = BN / WN;
 constexpr int TM = WAVE_M / 16, TN = WAVE_N / 16;
 constexpr int STAGES = DG_STAGES;
+constexpr int KSTEP = DG_KSTEP;             // 128-wide K blocks per LDS stage
 constexpr int SPLITK = DG_SPLITK;
 constexpr bool HAS_C = DG_HAS_C != 0;
 constexpr int N = DG_N, K = DG_K, G = DG_G;
@@ -78,19 +80,27 @@ constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0;
 
 static_assert(K % KBLK == 0, "K must be a multiple of 128");
 static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles must be 16-aligned");
-static_assert(BM % 8 == 0 && BN % 8 == 0, "tiles are loaded 8 rows per instruction");
-static_assert(KBLKS % SPLITK == 0, "split-K must divide the K blocks");
+static_assert(KSTEP == 1 || KSTEP == 2, "one or two K blocks per stage");
+static_assert(KBLKS % (SPLITK * KSTEP) == 0, "split-K and stage depth must divide the K blocks");
 static_assert(STAGES >= 2, "at least double buffering");
 
-// LDS ring: per stage [A tile BM x 128 B][B tile BN x 128 B][sfa BM floats, padded]
-constexpr int NA_INS = BM / 8;                 // 1 KB DMA instructions for A
-constexpr int NB_INS = BN / 8;                 // ... for B
-constexpr int NS_INS = (BM + 63) / 64;         // 256 B DMA instructions for sfa
+// LDS ring: per stage [A tile BM x ROWB][B tile BN x ROWB][sfa, BM floats per K block, padded].
+// A stage holds KSTEP consecutive K blocks, so each tile row is ROWB contiguous
+// bytes of its global row: with K = 1536 (a 1.5 KB row pitch) HBM streams B
+// far better in 256-byte than in 128-byte pieces.
+constexpr int ROWB = 128 * KSTEP;               // bytes of one tile row in a stage
+constexpr int RPI = 1024 / ROWB;                // tile rows per 1 KB DMA instruction
+constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
+constexpr int NB_INS = BN / RPI;                // ... for B
+constexpr int NS_PER_KB = (BM + 63) / 64;       // 256 B DMA instructions for one K block of sfa
+constexpr int NS_INS = NS_PER_KB * KSTEP;
 constexpr int A_OFF = 0;
-constexpr int B_OFF = BM * 128;
-constexpr int S_OFF = B_OFF + BN * 128;
-constexpr int STAGE_BYTES = S_OFF + NS_INS * 256;
+constexpr int B_OFF = BM * ROWB;
+constexpr int S_OFF = B_OFF + BN * ROWB;
+constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
+constexpr int STAGE_BYTES = S_OFF + KSTEP * S_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 
 // Every wave issues the same number of DMA instructions per stage, so one
@@ -254,8 +264,14 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
 }
 
 // ------------------------------------------------------------ the kernel
+// Arguments are separate __restrict__ pointers (not one struct) so that the
+// compiler may read the uniform ones (sfb, group info) with scalar loads.
 extern "C" __global__ void __launch_bounds__(NTHREADS, 1)
-dg_fp8_gemm_nt_kernel(Params p) {
+dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
+                      const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
+                      const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
+                      int num_tiles) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
     __shared__ int s_flag;
 
@@ -268,12 +284,16 @@ dg_fp8_gemm_nt_kernel(Params p) {
     const int q = lane >> 4;
     const u32 smem_base = lds_addr(smem);
     // Every fragment row this lane reads is l16 plus a multiple of 16, so the
-    // swizzle term (row >> 1) & 7 is the same for all of them.
-    const int sw = (l16 >> 1) & 7;
-    const u32 chunk_lo = (u32)(((2 * q) ^ sw) << 4);
-    const u32 chunk_hi = (u32)(((2 * q + 1) ^ sw) << 4);
-    const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * 128u;
-    const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * 128u;
+    // swizzle term row & 7 is the same for all of them.  Lane group q takes the
+    // 16-byte K chunks q and q + 4 of its row (the K order inside one MFMA only
+    // has to agree between the two operands, and it does: both use this map);
+    // with chunks XOR-swizzled by row & 7 these reads are free of LDS bank
+    // conflicts on gfx950, where chunks 2q, 2q + 1 were not.
+    const int sw = l16 & 7;
+    const u32 chunk_lo = (u32)((q ^ sw) << 4);
+    const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
+    const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * ROWB;
+    const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * ROWB;
 
 #pragma unroll 1
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
@@ -298,51 +318,50 @@ dg_fp8_gemm_nt_kernel(Params p) {
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
         const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * a_rows_total * 4u);
 
-        // ---- per-lane DMA offsets for this wave's instructions (fixed over K)
+        // ---- per-lane DMA offsets for this wave's instructions (fixed over K).
+        // Lane l of an instruction writes LDS bytes [16 l, 16 l + 16) of its 1 KB:
+        // tile row RPI*i + l / (ROWB/16), K block h of the stage, physical chunk
+        // p = l % 8, which holds logical chunk p ^ (row & 7).
         u32 voff[INS_PER_WAVE];
+        auto row_voff = [&](int i, int rows_valid) {
+            const int r = i * RPI + lane / (ROWB / 16);
+            const int h = (lane % (ROWB / 16)) / 8;
+            const int c = (lane & 7) ^ (r & 7);
+            const int rr = r < rows_valid ? r : rows_valid - 1;
+            return (u32)rr * K + h * 128 + c * 16;
+        };
 #pragma unroll
-        for (int j = 0; j < IA; ++j) {
-            const int i = min(wave + j * NWAVES, NA_INS - 1);
-            const int r = i * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((r >> 1) & 7);
-            const int rr = r < tl.rows ? r : tl.rows - 1;
-            voff[j] = (u32)rr * K + c * 16;
-        }
+        for (int j = 0; j < IA; ++j) voff[j] = row_voff(min(wave + j * NWAVES, NA_INS - 1), tl.rows);
 #pragma unroll
-        for (int j = 0; j < IB; ++j) {
-            const int i = min(wave + j * NWAVES, NB_INS - 1);
-            const int r = i * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((r >> 1) & 7);
-            const int rr = r < n_rows ? r : n_rows - 1;
-            voff[IA + j] = (u32)rr * K + c * 16;
-        }
+        for (int j = 0; j < IB; ++j) voff[IA + j] = row_voff(min(wave + j * NWAVES, NB_INS - 1), n_rows);
 #pragma unroll
         for (int j = 0; j < IS; ++j) {
             const int i = min(wave + j * NWAVES, NS_INS - 1);
-            const int m = tl.m0 + i * 64 + lane;
+            const int h = i / NS_PER_KB;
+            const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
-            voff[IA + IB + j] = (u32)mm * 4u;
+            voff[IA + IB + j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
         }
 
-        auto issue_stage = [&](int kb, int stage) {
+        // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
+        // (kb: first K block of the stage)
+        auto issue_one = [&](int j, int kb, int stage) {
             const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
-            const u32 soff_ab = __builtin_amdgcn_readfirstlane((u32)kb * KBLK);
-            const u32 soff_s = __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u);
-#pragma unroll
-            for (int j = 0; j < IA; ++j) {
+            if (j < IA) {
                 const int i = min(wave + j * NWAVES, NA_INS - 1);
-                dma16(rs_a, voff[j], soff_ab, st + A_OFF + i * 1024);
+                dma16(rs_a, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
+            } else if (j < IA + IB) {
+                const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
+                dma16(rs_b, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+            } else {
+                const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
+                dma4(rs_s, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u),
+                     st + S_OFF + i * 256);
             }
+        };
+        auto issue_stage = [&](int kb, int stage) {
 #pragma unroll
-            for (int j = 0; j < IB; ++j) {
-                const int i = min(wave + j * NWAVES, NB_INS - 1);
-                dma16(rs_b, voff[IA + j], soff_ab, st + B_OFF + i * 1024);
-            }
-#pragma unroll
-            for (int j = 0; j < IS; ++j) {
-                const int i = min(wave + j * NWAVES, NS_INS - 1);
-                dma4(rs_s, voff[IA + IB + j], soff_s, st + S_OFF + i * 256);
-            }
+            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage);
         };
 
         // ---- accumulators
@@ -351,77 +370,131 @@ dg_fp8_gemm_nt_kernel(Params p) {
         for (int a = 0; a < TM; ++a)
 #pragma unroll
             for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        // MFMA results of the last n sub-tile of the previous K block and their
+        // scales: promoted while the next K block's first MFMAs run.
+        v4f p_carry[TM];
+        float s_carry[TM];
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            p_carry[a] = v4f{0.f, 0.f, 0.f, 0.f};
+            s_carry[a] = 0.f;
+        }
 
         // earlier tile's stores and LDS reads are finished before the ring is refilled
         wait_vmcnt<0>();
         __syncthreads();
 
-        const int nkb = tl.kb1 - tl.kb0;
+        const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nkb) issue_stage(tl.kb0 + s, s);
+            if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
 
         // row offsets of this lane's fragments inside a stage
         const int a_row0 = wm * WAVE_M + l16;   // + a*16
-        const int b_row0 = wn * WAVE_N + l16;   // + b*16
         const int wave_n0 = tl.n0 + wn * WAVE_N;
+        // sfb of this group, row-block index of each n sub-tile (uniform per wave)
+        const float* sfb_g = p.sfb + (u64)tl.g * NBLKS * KBLKS;
+        int sb_row[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            int nblk = (wave_n0 + b * 16) / KBLK;
+            sb_row[b] = __builtin_amdgcn_readfirstlane((nblk < NBLKS ? nblk : NBLKS - 1) * KBLKS);
+        }
 
 #pragma unroll 1
-        for (int it = 0; it < nkb; ++it) {
-            const int kb = tl.kb0 + it;
+        for (int it = 0; it < nst; ++it) {
             const int stage = it % STAGES;
             // stage `it` has landed (for this wave) once at most the later stages are pending
-            if (it + STAGES - 1 <= nkb) wait_stages<STAGES - 2>();
+            if (it + STAGES - 1 <= nst) wait_stages<STAGES - 2>();
             else wait_vmcnt<0>();
             __syncthreads();
-            if (it + STAGES - 1 < nkb) issue_stage(kb + STAGES - 1, (it + STAGES - 1) % STAGES);
-
-            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
-            // scales: sfa for this lane's TM rows (LDS), sfb per 128-wide n block (scalar loads)
-            float sa[TM];
-            lds_u8* const stp = (lds_u8*)st;
-            lds_u8* const sa_p = stp + a_row0 * 4;
-#pragma unroll
-            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
-            const float* sfb_g = p.sfb + (u64)tl.g * NBLKS * KBLKS + kb;
-            float sab[TM];          // sa * sb when the wave's n range lies in one 128 block
-            float sb[TN];
-            if constexpr (SB_UNIFORM) {
-                const float sb0 = sfb_g[(u64)(wave_n0 / KBLK) * KBLKS];
-#pragma unroll
-                for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb0;
-            } else {
-#pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    int nblk = (wave_n0 + b * 16) / KBLK;
-                    nblk = nblk < NBLKS ? nblk : NBLKS - 1;
-                    sb[b] = sfb_g[(u64)nblk * KBLKS];
-                }
+            // Refill the slot every wave finished reading last iteration.  With two
+            // slots the refill is needed by the next iteration, so it goes out
+            // at once; with three or more it is spread over this iteration's
+            // MFMA steps, so no wave stalls on a burst of vector-memory issue.
+            const bool refill = it + STAGES - 1 < nst;
+            const int kb_fill = tl.kb0 + (it + STAGES - 1) * KSTEP, slot_fill = (it + STAGES - 1) % STAGES;
+            if constexpr (STAGES == 2) {
+                if (refill) issue_stage(kb_fill, slot_fill);
             }
 
-            // A fragments (MFMA column operand): logical K chunks 2q, 2q+1 of row a_row0 + 16a
-            v8i fa[TM];
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+#pragma unroll
+            for (int h = 0; h < KSTEP; ++h) {
+            const int kb = tl.kb0 + it * KSTEP + h;
+            // scale of B: scalar loads
+            float sb[TN];
+            if constexpr (SB_UNIFORM) {
+                sb[0] = sfb_g[sb_row[0] + kb];
+            } else {
+#pragma unroll
+                for (int b = 0; b < TN; ++b) sb[b] = sfb_g[sb_row[b] + kb];
+            }
+            lds_u8* const stp = (lds_u8*)(st + h * 128);
+            lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
             lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
             lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
             lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
             lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
+
+            float sa[TM];
 #pragma unroll
-            for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * 128);
+            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+            v8i fa[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
+            v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
+
+            float sab[TM];           // sa * sb for the uniform case
+            if constexpr (SB_UNIFORM) {
+#pragma unroll
+                for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+            }
+
+            // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
+            // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
+            // last sub-tile of the previous K block).
+            v4f pr[TM];
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
-                const v8i fb = lds_read_frag(b_lo, b_hi, B_OFF + b * 16 * 128);
+                if constexpr (STAGES > 2) {
+                    if (refill && h == 0) {
+#pragma unroll
+                        for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
+                            issue_one(j, kb_fill, slot_fill);
+                    }
+                }
+                v8i fb_next;
+                if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
+                v4f prev[TM];
+#pragma unroll
+                for (int a = 0; a < TM; ++a) prev[a] = pr[a];
 #pragma unroll
                 for (int a = 0; a < TM; ++a) {
                     const v4f zero = {0.f, 0.f, 0.f, 0.f};
                     // P[n][m] over this 128-wide K block: exact products, FP32 sums
-                    v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
-                    float s;
-                    if constexpr (SB_UNIFORM) s = sab[a];
-                    else s = sa[a] * sb[b];
-                    acc[a][b] += pr * s;
+                    pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                    if (b == 0) {
+                        acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                    } else {
+                        float sc;
+                        if constexpr (SB_UNIFORM) sc = sab[a];
+                        else sc = sa[a] * sb[b - 1];
+                        acc[a][b - 1] += prev[a] * sc;
+                    }
                 }
+                if (b + 1 < TN) fb = fb_next;
             }
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                p_carry[a] = pr[a];
+                if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
+                else s_carry[a] = sa[a] * sb[TN - 1];
+            }
+            }   // K blocks of the stage
         }
+#pragma unroll
+        for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
 
         // ---- split-K: publish the partial, the last arrival sums all in split order
         if constexpr (SPLITK > 1) {

@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdg.so")
+# DG_LIBRARY: load another build of the same C ABI instead of the in-tree one
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdg.so")
 
 DG_OK = 0
 STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_UNSUPPORTED",

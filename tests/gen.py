@@ -151,7 +151,7 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None) -> Problem:
 
 # ---------------------------------------------------------------- the five workloads
 # (shapes: DeepGEMM launch article, section 3, dense table and MoE table)
-CONFIGS = {
+WORKLOADS = {
     0: dict(kind="dense", M=64, N=2112, K=7168),
     1: dict(kind="dense", M=128, N=24576, K=1536),
     "1c": dict(kind="dense", M=128, N=24576, K=1536, with_c=True),
@@ -160,7 +160,7 @@ CONFIGS = {
     4: dict(kind="masked", G=4, M_max=256, N=7168, K=2048),
 }
 
-CONFIG_NAMES = {
+WORKLOAD_NAMES = {
     0: "dense_64x2112x7168",
     1: "dense_128x24576x1536",
     "1c": "dense_128x24576x1536_plusC",
@@ -170,13 +170,13 @@ CONFIG_NAMES = {
 }
 
 
-def config_seed(cfg) -> int:
+def workload_seed(cfg) -> int:
     return 1000 + (1 if cfg == "1c" else int(cfg))
 
 
-def make_config(cfg) -> Problem:
-    c = CONFIGS[cfg]
-    seed = config_seed(cfg)
+def make_workload(cfg) -> Problem:
+    c = WORKLOADS[cfg]
+    seed = workload_seed(cfg)
     if c["kind"] == "dense":
         return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False))
     if c["kind"] == "contiguous":

@@ -101,33 +101,33 @@ def test_dense_repeatable_and_stream(oracle):
 # ------------------------------------------------------------------ the five workloads at full size
 @pytest.mark.parametrize("cfg", [0, 1, "1c", 2])
 def test_workload_dense(oracle, cfg):
-    p = gen.make_config(cfg)
+    p = gen.make_workload(cfg)
     D, sent = run(p)
     rows = np.arange(p.M) if p.M <= 128 else sample_rows(p.M, 48, seed=3)
     ref, comp = oracle_rows(oracle, p, rows=rows)
-    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[cfg])
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[cfg])
     # every row of a dense result is written: no sentinel survives in sampled-out rows either
     assert not torch.equal(D.view(torch.int16)[-1], sent.view(torch.int16)[-1])
 
 
 def test_workload_contiguous(oracle):
-    p = gen.make_config(3)
+    p = gen.make_workload(3)
     D, sent = run(p)
     rows = sample_rows(p.M, 48, seed=4, block=128)
     ref, comp = oracle_rows(oracle, p, rows=rows)
     assert comp.all()
-    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[3])
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[3])
 
 
 def test_workload_masked(oracle):
-    p = gen.make_config(4)
+    p = gen.make_workload(4)
     D, sent = run(p)
     G, M_max = p.A.shape[0], p.A.shape[1]
     mm = p.masked_m.numpy().clip(0, M_max)
     rows = np.arange(G * M_max)          # all rows: cheap enough at K = 2048
     ref, comp = oracle_rows(oracle, p, rows=rows)
     assert comp.sum() == mm.sum()
-    _compare(p, D, sent, ref, comp, rows=rows, what=gen.CONFIG_NAMES[4])
+    _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[4])
 
 
 # ------------------------------------------------------------------ contiguous, edge cases
@@ -188,6 +188,9 @@ FORCED = [
     "128,256,2,4,2,1",
     "256,224,4,2,2,1",
     "256,256,4,2,2,1",
+    "128,96,2,2,2,1,2",
+    "64,64,2,2,3,2,2",
+    "32,128,1,4,2,4,2",
 ]
 
 
@@ -198,3 +201,35 @@ def test_forced_tile_configs(oracle, monkeypatch, forced):
     D, sent = run(p)
     ref, comp = oracle_rows(oracle, p)
     _compare(p, D, sent, ref, comp, what=f"forced {forced}")
+
+
+# ------------------------------------------------------------------ HIP graph capture
+def test_graph_replays_match_eager(oracle):
+    """Calls captured into a HIP graph (split-K dense, masked) give the eager bits
+    on every replay, with eager work and synchronisations between replays."""
+    import moe_grouped_gemm_scales_amd as dg
+    pd = gen.make_dense(64, 2112, 7168, seed=1000)          # selects split-K
+    pm = gen.make_workload(4)
+    dd, dm = to_dev(pd), to_dev(pm)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        De = torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda")
+        Me = gen.sentinel_like((4, 256, 7168), 3).to("cuda")
+        dg.dg_fp8_gemm_nt(dd["A"], dd["sfa"], dd["B"], dd["sfb"], None, De)
+        dg.dg_m_grouped_fp8_gemm_nt_masked(dm["A"], dm["sfa"], dm["B"], dm["sfb"], dm["masked_m"], None, Me)
+        torch.cuda.synchronize()
+        Dg = torch.empty_like(De)
+        Mg = gen.sentinel_like((4, 256, 7168), 3).to("cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            dg.dg_fp8_gemm_nt(dd["A"], dd["sfa"], dd["B"], dd["sfb"], None, Dg)
+            dg.dg_m_grouped_fp8_gemm_nt_masked(dm["A"], dm["sfa"], dm["B"], dm["sfb"], dm["masked_m"], None, Mg)
+        for rep in range(3):
+            Dg.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Dg.view(torch.int16), De.view(torch.int16)), f"dense replay {rep}"
+            assert torch.equal(Mg.view(torch.int16), Me.view(torch.int16)), f"masked replay {rep}"
+            # eager work between replays, on the same stream and workspace
+            dg.dg_fp8_gemm_nt(dd["A"], dd["sfa"], dd["B"], dd["sfb"], None, De)
+            torch.cuda.synchronize()
