@@ -26,7 +26,7 @@ struct KernelConfig {
     int n = 0, k = 0, g = 1;
 
     int threads() const { return 64 * wm * wn; }
-    int stage_bytes() const { return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256; }
+    int stage_bytes() const { return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256; }
     int lds_bytes() const { return stages * stage_bytes(); }
     std::string key() const;
 };

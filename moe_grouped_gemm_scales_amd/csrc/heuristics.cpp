@@ -104,7 +104,7 @@ int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
     const int rpi = 8 / c.kstep;
     const int na = c.bm / rpi, nb = c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
-    return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw;
+    return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (c.kstep + nw - 1) / nw;
 }
 
 // Mirrors the kernel's static_asserts, so a selected config always compiles.
@@ -116,6 +116,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > 32) return false;
     if (c.lds_bytes() > kLdsBytes) return false;
+    if (c.bn > 256) return false;
     if ((p.k / 128) % (c.splitk * c.kstep)) return false;
     if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
     if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block

@@ -98,7 +98,12 @@ constexpr int A_OFF = 0;
 constexpr int B_OFF = BM * ROWB;
 constexpr int S_OFF = B_OFF + BN * ROWB;
 constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
-constexpr int STAGE_BYTES = S_OFF + KSTEP * S_BYTES;
+// sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
+// DMA per K block, so the K loop issues no scalar loads
+constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
+constexpr int NT_INS = KSTEP;
+constexpr int STAGE_BYTES = T_OFF + KSTEP * 256;
+static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
@@ -110,7 +115,8 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
 constexpr int IB = (NB_INS + NWAVES - 1) / NWAVES;
 constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
-constexpr int INS_PER_WAVE = IA + IB + IS;
+constexpr int IT = (NT_INS + NWAVES - 1) / NWAVES;
+constexpr int INS_PER_WAVE = IA + IB + IS + IT;
 static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
 
 struct Params {
@@ -317,6 +323,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
         const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * a_rows_total * 4u);
+        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
+        const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
         // ---- per-lane DMA offsets for this wave's instructions (fixed over K).
         // Lane l of an instruction writes LDS bytes [16 l, 16 l + 16) of its 1 KB:
@@ -342,6 +350,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
             voff[IA + IB + j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
         }
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int h = min(wave + j * NWAVES, NT_INS - 1);
+            const int nb = min(nb_t0 + lane, NBLKS - 1);
+            voff[IA + IB + IS + j] = (u32)nb * KBLKS * 4u + (u32)h * 4u;
+        }
 
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
         // (kb: first K block of the stage)
@@ -353,10 +367,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             } else if (j < IA + IB) {
                 const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
                 dma16(rs_b, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
-            } else {
+            } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
                 dma4(rs_s, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u),
                      st + S_OFF + i * 256);
+            } else {
+                const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
+                dma4(rs_t, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * 4u), st + T_OFF + h * 256);
             }
         };
         auto issue_stage = [&](int kb, int stage) {
@@ -392,13 +409,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         // row offsets of this lane's fragments inside a stage
         const int a_row0 = wm * WAVE_M + l16;   // + a*16
         const int wave_n0 = tl.n0 + wn * WAVE_N;
-        // sfb of this group, row-block index of each n sub-tile (uniform per wave)
-        const float* sfb_g = p.sfb + (u64)tl.g * NBLKS * KBLKS;
-        int sb_row[TN];
+        // LDS byte offset of each n sub-tile's sfb inside a K block's sfb slice
+        int sb_off[TN];
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
             int nblk = (wave_n0 + b * 16) / KBLK;
-            sb_row[b] = __builtin_amdgcn_readfirstlane((nblk < NBLKS ? nblk : NBLKS - 1) * KBLKS);
+            nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+            sb_off[b] = __builtin_amdgcn_readfirstlane((nblk - nb_t0) * 4);
         }
 
 #pragma unroll 1
@@ -422,13 +439,14 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
             for (int h = 0; h < KSTEP; ++h) {
             const int kb = tl.kb0 + it * KSTEP + h;
-            // scale of B: scalar loads
+            // scale of B from the stage (same address in every lane: a broadcast read)
+            lds_u8* const sb_p = (lds_u8*)(st + T_OFF + h * 256);
             float sb[TN];
             if constexpr (SB_UNIFORM) {
-                sb[0] = sfb_g[sb_row[0] + kb];
+                sb[0] = lds_read_f32(sb_p, sb_off[0]);
             } else {
 #pragma unroll
-                for (int b = 0; b < TN; ++b) sb[b] = sfb_g[sb_row[b] + kb];
+                for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
             }
             lds_u8* const stp = (lds_u8*)(st + h * 128);
             lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
