@@ -22,12 +22,20 @@ struct KernelConfig {
     int stages = 2;            // LDS ring depth
     int kstep = 1;             // 128-wide K blocks per LDS stage (1 or 2)
     int splitk = 1;            // K splits (dense only)
+    int variant = 0;           // 0: A and B through LDS; 1: B straight into VGPRs, A through an LDS
+                               // ring; 2: B straight into VGPRs, A of the K range resident in LDS
     int has_c = 0;
     int n = 0, k = 0, g = 1;
 
     int threads() const { return 64 * wm * wn; }
-    int stage_bytes() const { return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256; }
-    int lds_bytes() const { return stages * stage_bytes(); }
+    int stage_bytes() const {
+        if (variant == 1) return bm * 128 + (bm + 63) / 64 * 256 + 256;
+        return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
+    }
+    int lds_bytes() const {
+        if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
+        return stages * stage_bytes();
+    }
     std::string key() const;
 };
 

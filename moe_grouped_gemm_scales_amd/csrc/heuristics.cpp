@@ -8,7 +8,7 @@
 // (tile, wave grid, LDS stages, split-K) tuples; the model charges each
 // candidate its wave-quantised MFMA time, its operand traffic and a fixed
 // per-tile cost, and the cheapest one wins.  DG_FORCE_CONFIG
-// ("bm,bn,wm,wn,stages,splitk[,kstep]") overrides the choice for tuning sweeps.
+// ("bm,bn,wm,wn,stages,splitk[,kstep[,variant]]") overrides the choice for tuning sweeps.
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -107,19 +107,40 @@ int dma_per_wave(const KernelConfig& c) {
     return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (c.kstep + nw - 1) / nw;
 }
 
+// Vector-memory instructions per wave per K block of variant 1 (A/sfa DMA
+// share, one sfb DMA, two 16-byte B loads per 16-row sub-tile).
+int unit_per_wave_v1(const KernelConfig& c) {
+    const int nw = c.wm * c.wn;
+    return (c.bm / 8 + nw - 1) / nw + ((c.bm + 63) / 64 + nw - 1) / nw + 1 + 2 * (c.bn / c.wn / 16);
+}
+
 // Mirrors the kernel's static_asserts, so a selected config always compiles.
 bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (16 * c.wm) || c.bn % (16 * c.wn)) return false;
+    if (c.variant < 0 || c.variant > 2) return false;
+    int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
+    if (c.lds_bytes() > kLdsBytes) return false;
+    if (c.bn > 256) return false;
+    if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
+    if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
+    if (c.variant != 0) {
+        // waves along n only, one K block at a time, the whole K range of a
+        // work item unrolled, B registers of stages - 1 blocks in flight
+        if (c.wm != 1 || c.kstep != 1 || c.stages < 2) return false;
+        if ((p.k / 128) % c.splitk || p.k / 128 / c.splitk > 64) return false;
+        const int ub = 2 * (c.bn / c.wn / 16);
+        const int nkb = p.k / 128 / c.splitk, pre = std::min(c.stages - 1, nkb);
+        if (c.variant == 1 && unit_per_wave_v1(c) * (c.stages - 2) > 63) return false;
+        if (c.variant == 2 && (ub * (c.stages - 2) > 63 || ub * pre > 63)) return false;
+        if (tm < 1 || tn < 1 || tm > 16 || tn > 4 || tm * tn > 32) return false;
+        if (c.bm % 8) return false;
+        return true;
+    }
     if (c.kstep != 1 && c.kstep != 2) return false;
     if (c.bm % (8 / c.kstep) || c.bn % (8 / c.kstep) || c.stages < 2) return false;
     if (dma_per_wave(c) * (c.stages - 1) > 63) return false;   // vmcnt field
-    int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > 32) return false;
-    if (c.lds_bytes() > kLdsBytes) return false;
-    if (c.bn > 256) return false;
     if ((p.k / 128) % (c.splitk * c.kstep)) return false;
-    if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
-    if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
     return true;
 }
 
@@ -134,7 +155,7 @@ const Tuned kTuned[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 128, 2, 2, 3, 4, 2},
     {kDense, 128, 24576, 1536, 1, 0, 128, 128, 2, 4, 2, 1, 2},
     {kDense, 128, 24576, 1536, 1, 1, 128, 128, 2, 4, 2, 1, 2},
-    {kDense, 4096, 7168, 16384, 1, 0, 256, 224, 4, 2, 2, 1, 1},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1},
     {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 2, 1, 2},
 };
@@ -155,10 +176,11 @@ bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
 bool parse_forced(KernelConfig* c) {
     const char* s = std::getenv("DG_FORCE_CONFIG");
     if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sk, ks = 1;
-    int got = std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk, &ks);
-    if (got != 6 && got != 7) return false;
+    int bm, bn, wm, wn, st, sk, ks = 1, var = 0;
+    int got = std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk, &ks, &var);
+    if (got < 6) return false;
     c->bm = bm; c->bn = bn; c->wm = wm; c->wn = wn; c->stages = st; c->splitk = sk; c->kstep = ks;
+    c->variant = var;
     return true;
 }
 

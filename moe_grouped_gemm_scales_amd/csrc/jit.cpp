@@ -64,6 +64,7 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     def("DG_N", c.n);
     def("DG_K", c.k);
     def("DG_G", c.g);
+    def("DG_VARIANT", c.variant);
     return o;
 }
 
@@ -173,7 +174,7 @@ dg_status compile_locked(const KernelConfig& c, std::vector<char>* code) {
 
 std::string KernelConfig::key() const {
     std::ostringstream s;
-    s << "k" << kind << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
+    s << "k" << kind << (variant ? "v" + std::to_string(variant) : std::string()) << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
       << "_sk" << splitk
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
     return s.str();

@@ -56,6 +56,9 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 #define DG_K 256
 #define DG_G 1
 #endif
+#ifndef DG_VARIANT
+#define DG_VARIANT 0
+#endif
 
 namespace dg {
 
@@ -84,40 +87,13 @@ static_assert(KSTEP == 1 || KSTEP == 2, "one or two K blocks per stage");
 static_assert(KBLKS % (SPLITK * KSTEP) == 0, "split-K and stage depth must divide the K blocks");
 static_assert(STAGES >= 2, "at least double buffering");
 
-// LDS ring: per stage [A tile BM x ROWB][B tile BN x ROWB][sfa, BM floats per K block, padded].
-// A stage holds KSTEP consecutive K blocks, so each tile row is ROWB contiguous
-// bytes of its global row: with K = 1536 (a 1.5 KB row pitch) HBM streams B
-// far better in 256-byte than in 128-byte pieces.
-constexpr int ROWB = 128 * KSTEP;               // bytes of one tile row in a stage
-constexpr int RPI = 1024 / ROWB;                // tile rows per 1 KB DMA instruction
-constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
-constexpr int NB_INS = BN / RPI;                // ... for B
-constexpr int NS_PER_KB = (BM + 63) / 64;       // 256 B DMA instructions for one K block of sfa
-constexpr int NS_INS = NS_PER_KB * KSTEP;
-constexpr int A_OFF = 0;
-constexpr int B_OFF = BM * ROWB;
-constexpr int S_OFF = B_OFF + BN * ROWB;
-constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
-// sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
-// DMA per K block, so the K loop issues no scalar loads
-constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
-constexpr int NT_INS = KSTEP;
-constexpr int STAGE_BYTES = T_OFF + KSTEP * 256;
-static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
-
-// Every wave issues the same number of DMA instructions per stage, so one
-// vmcnt immediate fits all waves: instruction i of a category goes to wave
-// i % NWAVES, and a wave whose share runs out repeats the category's last
-// instruction (identical bytes to identical LDS addresses, so harmless).
-constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
-constexpr int IB = (NB_INS + NWAVES - 1) / NWAVES;
-constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
-constexpr int IT = (NT_INS + NWAVES - 1) / NWAVES;
-constexpr int INS_PER_WAVE = IA + IB + IS + IT;
-static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
+// Register budget: 256 per lane, as for two waves per SIMD, whatever the wave
+// count.  The kernel declares a maximum workgroup size of at least 512 lanes
+// (it is launched with NTHREADS; LDS keeps one workgroup per CU): with a
+// 256-lane maximum the compiler plans for one wave per SIMD, writes MFMA
+// results to AGPRs and copies every one back with v_accvgpr_read before the
+// promotion FMA, doubling the VALU work per MFMA.
+constexpr int MAX_THREADS_DECL = NTHREADS < 512 ? 512 : NTHREADS;
 
 struct Params {
     const u8* A;
@@ -165,9 +141,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(CNT >= 0 && CNT <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(CNT) : "memory");
 }
-// Wait until at most PENDING whole stages of this wave's DMA remain in flight.
-template <int PENDING>
-__device__ __forceinline__ void wait_stages() { wait_vmcnt<PENDING * INS_PER_WAVE>(); }
 
 __device__ __forceinline__ u16 f32_to_bf16(float f) {
     u32 u = __builtin_bit_cast(u32, f);
@@ -240,6 +213,18 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         tl.mn = 0;
     } else {
         const int num_mt = (p.M + BM - 1) / BM;
+        // Workgroups go to the 8 XCDs (each with its own L2) round-robin by
+        // index.  Within every full round of the persistent grid, give XCD x
+        // the contiguous logical range [x, x + 1) * grid / 8, so tiles that are
+        // neighbours in the order below (and share A or B) share an L2.
+        const int grid = gridDim.x;
+        if (grid % 8 == 0) {
+            const int r0 = t - t % grid;                  // first tile of this round
+            if (r0 + grid <= p.num_tiles) {
+                const int b = t - r0;
+                t = r0 + (b % 8) * (grid / 8) + b / 8;
+            }
+        }
         int mn = t / SPLITK;
         tl.split = t % SPLITK;
         tl.mn = mn;
@@ -269,10 +254,128 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
     return tl;
 }
 
+
+// ------------------------------------------------------------ end of a work item
+// Split-K bookkeeping and the epilogue, shared by both kernel variants.  acc
+// holds TM_ x TN_ blocks of 16 x 16: lane (l16, q) owns row row0 + 16 a and
+// the four columns col0 + 16 b + [0, 4) of each (row0, col0 relative to the
+// tile).  Returns after storing, or early when another split finishes the tile.
+template <int TM_, int TN_>
+__device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f (&acc)[TM_][TN_], int row0,
+                                            int col0, int tid, int* s_flag) {
+    // ---- split-K: publish the partial, the last arrival sums all in split order
+    if constexpr (SPLITK > 1) {
+        float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
+#pragma unroll
+        for (int a = 0; a < TM_; ++a)
+#pragma unroll
+            for (int b = 0; b < TN_; ++b)
+                *(v4f*)(ws + ((u64)tl.split * BM * BN) + ((a * TN_ + b) * NTHREADS + tid) * 4) = acc[a][b];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) {
+            u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            *s_flag = (old == (u32)(SPLITK - 1));
+            if (old == (u32)(SPLITK - 1))
+                __hip_atomic_store(&p.counters[tl.mn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!*s_flag) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int a = 0; a < TM_; ++a)
+#pragma unroll
+            for (int b = 0; b < TN_; ++b) {
+                v4f sum = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < SPLITK; ++s) {
+                    v4f part = (s == tl.split)
+                                   ? acc[a][b]
+                                   : *(const v4f*)(ws + ((u64)s * BM * BN) + ((a * TN_ + b) * NTHREADS + tid) * 4);
+                    sum += part;
+                }
+                acc[a][b] = sum;
+            }
+    }
+
+    // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
+    u64 row_base;      // element offset of row 0 of this tile in C/D
+    if constexpr (kKind == 2) row_base = ((u64)tl.g * p.M + tl.m0) * N;
+    else row_base = (u64)tl.m0 * N;
+#pragma unroll
+    for (int a = 0; a < TM_; ++a) {
+        const int r = row0 + a * 16;            // row inside the tile
+        bool row_ok = r < tl.row_limit;
+        if constexpr (kKind == 1) row_ok = row_ok && (p.grp[tl.m0 + r] == tl.g);
+        if (!row_ok) continue;
+#pragma unroll
+        for (int b = 0; b < TN_; ++b) {
+            const int n = tl.n0 + col0 + b * 16;
+            if (n >= N) continue;
+            const u64 off = row_base + (u64)r * N + n;
+            v4f v = acc[a][b];
+            if constexpr (N % 4 == 0) {
+                if constexpr (HAS_C) v += *(const v4f*)(p.C + off);
+                v4u16 o = {f32_to_bf16(v.x), f32_to_bf16(v.y), f32_to_bf16(v.z), f32_to_bf16(v.w)};
+                *(v4u16*)(p.D + off) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (n + e < N) {
+                        float x = v[e];
+                        if constexpr (HAS_C) x += p.C[off + e];
+                        p.D[off + e] = f32_to_bf16(x);
+                    }
+                }
+            }
+        }
+    }
+}
+
+#if DG_VARIANT == 0
+// ============================================================ variant 0: both operands through LDS
+// LDS ring: per stage [A tile BM x ROWB][B tile BN x ROWB][sfa, BM floats per K block, padded].
+// A stage holds KSTEP consecutive K blocks, so each tile row is ROWB contiguous
+// bytes of its global row: with K = 1536 (a 1.5 KB row pitch) HBM streams B
+// far better in 256-byte than in 128-byte pieces.
+constexpr int ROWB = 128 * KSTEP;               // bytes of one tile row in a stage
+constexpr int RPI = 1024 / ROWB;                // tile rows per 1 KB DMA instruction
+constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
+constexpr int NB_INS = BN / RPI;                // ... for B
+constexpr int NS_PER_KB = (BM + 63) / 64;       // 256 B DMA instructions for one K block of sfa
+constexpr int NS_INS = NS_PER_KB * KSTEP;
+constexpr int A_OFF = 0;
+constexpr int B_OFF = BM * ROWB;
+constexpr int S_OFF = B_OFF + BN * ROWB;
+constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
+// sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
+// DMA per K block, so the K loop issues no scalar loads
+constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
+constexpr int NT_INS = KSTEP;
+constexpr int STAGE_BYTES = T_OFF + KSTEP * 256;
+static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+
+// Every wave issues the same number of DMA instructions per stage, so one
+// vmcnt immediate fits all waves: instruction i of a category goes to wave
+// i % NWAVES, and a wave whose share runs out repeats the category's last
+// instruction (identical bytes to identical LDS addresses, so harmless).
+constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
+constexpr int IB = (NB_INS + NWAVES - 1) / NWAVES;
+constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
+constexpr int IT = (NT_INS + NWAVES - 1) / NWAVES;
+constexpr int INS_PER_WAVE = IA + IB + IS + IT;
+static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
+
+// Wait until at most PENDING whole stages of this wave's DMA remain in flight.
+template <int PENDING>
+__device__ __forceinline__ void wait_stages() { wait_vmcnt<PENDING * INS_PER_WAVE>(); }
+
 // ------------------------------------------------------------ the kernel
 // Arguments are separate __restrict__ pointers (not one struct) so that the
 // compiler may read the uniform ones (sfb, group info) with scalar loads.
-extern "C" __global__ void __launch_bounds__(NTHREADS, 1)
+extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THREADS_DECL)))
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
@@ -514,74 +617,331 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
         for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
 
-        // ---- split-K: publish the partial, the last arrival sums all in split order
-        if constexpr (SPLITK > 1) {
-            float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    *(v4f*)(ws + ((u64)tl.split * BM * BN) + ((a * TN + b) * NTHREADS + tid) * 4) = acc[a][b];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
-            if (tid == 0) {
-                u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                s_flag = (old == (u32)(SPLITK - 1));
-                if (old == (u32)(SPLITK - 1))
-                    __hip_atomic_store(&p.counters[tl.mn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            if (!s_flag) continue;
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    v4f sum = {0.f, 0.f, 0.f, 0.f};
-                    for (int s = 0; s < SPLITK; ++s) {
-                        v4f part = (s == tl.split)
-                                       ? acc[a][b]
-                                       : *(const v4f*)(ws + ((u64)s * BM * BN) + ((a * TN + b) * NTHREADS + tid) * 4);
-                        sum += part;
-                    }
-                    acc[a][b] = sum;
-                }
-        }
-
-        // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
-        u64 row_base;      // element offset of row 0 of this tile in C/D
-        if constexpr (kKind == 2) row_base = ((u64)tl.g * p.M + tl.m0) * N;
-        else row_base = (u64)tl.m0 * N;
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            const int r = a_row0 + a * 16;          // row inside the tile
-            bool row_ok = r < tl.row_limit;
-            if constexpr (kKind == 1) row_ok = row_ok && (p.grp[tl.m0 + r] == tl.g);
-            if (!row_ok) continue;
-#pragma unroll
-            for (int b = 0; b < TN; ++b) {
-                const int n = tl.n0 + wn * WAVE_N + b * 16 + 4 * q;
-                if (n >= N) continue;
-                const u64 off = row_base + (u64)r * N + n;
-                v4f v = acc[a][b];
-                if constexpr (N % 4 == 0) {
-                    if constexpr (HAS_C) v += *(const v4f*)(p.C + off);
-                    v4u16 o = {f32_to_bf16(v.x), f32_to_bf16(v.y), f32_to_bf16(v.z), f32_to_bf16(v.w)};
-                    *(v4u16*)(p.D + off) = o;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (n + e < N) {
-                            float x = v[e];
-                            if constexpr (HAS_C) x += p.C[off + e];
-                            p.D[off + e] = f32_to_bf16(x);
-                        }
-                    }
-                }
-            }
-        }
+        finish_tile<TM, TN>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag);
     }
 }
+
+#else
+// ============================================================ variants 1 and 2: B straight into VGPRs
+// For few rows (every row of a problem or group in one or two row blocks):
+// each wave owns WAVE_N rows of B and loads them from global memory straight
+// into VGPRs, DEPTH K blocks ahead of their use.  A wave's B rows are one
+// contiguous stretch of memory that it requests within a short window, so HBM
+// streams it well, and the bytes in flight per CU are bounded by the register
+// file rather than by LDS.  The K range of a work item is unrolled completely,
+// so every wait count is a compile-time constant.
+//   variant 1: the A tile (read by every wave), its scales and the B scales
+//              pass through an LDS ring, one K block per slot, one barrier per
+//              K block;
+//   variant 2: the A tile of the whole K range is loaded into LDS once per
+//              work item (it must fit), so the K loop has no barrier at all
+//              and the waves run independently.
+constexpr bool ARES = DG_VARIANT == 2;
+static_assert(WM == 1, "variants 1 and 2 spread their waves along n only");
+static_assert(KSTEP == 1, "variants 1 and 2 stage one K block at a time");
+constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
+static_assert(NKB <= 64, "the whole K range of a work item is unrolled");
+constexpr int DEPTH = STAGES - 1;                 // K blocks of B requested ahead of use
+constexpr int NREG = ARES ? NKB : STAGES;         // K blocks held in LDS (variant 1: ring slots)
+constexpr int NA_INS = BM / 8;                    // 1 KB DMA instructions for one K block of A
+constexpr int NS_INS = (BM + 63) / 64;            // 256 B DMA instructions for its sfa
+// LDS: [sfb][sfa: NREG x NS_INS x 256 B][A: NREG x BM rows x 128 B], where sfb
+// is, in variant 1, one row of 64 floats per slot (one per 128-row block of B
+// from the tile's first on) and, in variant 2, three rows of 64 floats (the
+// tile's 128-row blocks j = 0..2 over the item's K blocks).  The scales come
+// first so that their offsets fit a ds_read immediate.
+constexpr int T_OFF = 0;
+constexpr int S_OFF = T_OFF + (ARES ? 3 : NREG) * 256;
+constexpr int A_OFF = S_OFF + NREG * NS_INS * 256;
+constexpr int LDS_BYTES = A_OFF + NREG * BM * 128;
+// A fragment reads address LDS from a few per-tile base registers 32 KB apart,
+// so that every offset fits the 16-bit ds_read immediate
+constexpr int A_BANK = 32768;
+constexpr int NBANK = (LDS_BYTES + A_BANK - 1) / A_BANK;
+static_assert(BM % 8 == 0, "A is loaded 8 rows per DMA instruction");
+static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS exceeds 160 KB");
+// Vector-memory instructions per wave.  Every wave issues the same count
+// (repeating its category's last instruction where its share runs out), so
+// one vmcnt immediate fits all waves.
+constexpr int UB = 2 * TN;                        // B: two 16-byte loads per lane per 16-row sub-tile
+// variant 1, per K block: share of the A and sfa DMA, one sfb DMA, the B loads
+constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
+constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
+constexpr int UNIT = ARES ? UB : IA + IS + 1 + UB;
+// variant 2, once per work item: the same A and sfa shares for every K block, and sfb
+constexpr int IT_ALL = (3 + NWAVES - 1) / NWAVES;
+constexpr int PRE_UNITS = DEPTH < NKB ? DEPTH : NKB;
+static_assert(UNIT * (DEPTH - 1) <= 63 && (!ARES || UNIT * PRE_UNITS <= 63), "vmcnt range");
+#ifndef DG_FA_AHEAD
+#define DG_FA_AHEAD 4
+#endif
+constexpr int FA_AHEAD = DG_FA_AHEAD < TM ? DG_FA_AHEAD : TM;   // A fragments read ahead of use
+
+// 16 bytes per lane from global memory into VGPRs.  Inline asm, like the DMA,
+// so that the compiler leaves the wait to the kernel's own vmcnt accounting;
+// the destination is only read after that wait and tie() below.
+template <int OFF>
+__device__ __forceinline__ v4i load16(v4i rsrc, u32 voff, u32 soff) {
+    v4i r;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
+                 : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF) : "memory");
+    return r;
+}
+// After the wait: a register the loads wrote is redefined here, so no use of it
+// can be scheduled before the wait.
+__device__ __forceinline__ void tie(v4i& x) { asm volatile("" : "+v"(x)); }
+
+template <int... Is> struct iseq {};
+template <int Nn, int... Is> struct make_iseq { using type = typename make_iseq<Nn - 1, Nn - 1, Is...>::type; };
+template <int... Is> struct make_iseq<0, Is...> { using type = iseq<Is...>; };
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, iseq<Is...>) { (f.template operator()<Is>(), ...); }
+template <int Nn, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl(f, typename make_iseq<Nn>::type{}); }
+
+extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THREADS_DECL)))
+dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
+                      const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
+                      const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
+                      int num_tiles) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+    __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int q = lane >> 4;
+    const u32 smem_base = lds_addr(smem);
+    // A fragments: the swizzled chunk pair {q, q ^ 4} of row l16 (+16 a), as in variant 0
+    const int sw = l16 & 7;
+    const u32 chunk_lo = (u32)((q ^ sw) << 4);
+    const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
+    const u32 a_frag_off = (u32)l16 * 128u;
+    const int wave_n = wave * WAVE_N;             // first column of this wave inside the tile
+
+#pragma unroll 1
+    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
+        const Tile tl = decode_tile(p, t);
+        if (tl.skip) continue;
+
+        const u8* a_base;
+        const float* sfa_base;
+        if constexpr (kKind == 2) {
+            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
+            sfa_base = p.sfa + (u64)tl.g * KBLKS * p.M;
+        } else {
+            a_base = p.A + (u64)tl.m0 * K;
+            sfa_base = p.sfa;
+        }
+        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
+        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
+        const int nb_t0 = tl.n0 / KBLK;
+        // B: sub-tile b, row l16 (clamped to the valid rows), logical chunks q and q + 4
+        u32 bvoff[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int r = wave_n + b * 16 + l16;
+            bvoff[b] = (u32)(r < n_rows ? r : n_rows - 1) * K + q * 16;
+        }
+        auto issue_b = [&](int kb, v4i (&dst)[TN][2]) __attribute__((always_inline)) {
+            const u32 ka = __builtin_amdgcn_readfirstlane((u32)kb * KBLK);
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                dst[b][0] = load16<0>(rs_b, bvoff[b], ka);
+                dst[b][1] = load16<64>(rs_b, bvoff[b], ka);
+            }
+        };
+        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * p.M * 4u);
+        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
+        // A DMA: lane l of instruction i (8 tile rows) writes LDS bytes [16 l, 16 l + 16)
+        // of its 1 KB = tile row 8 i + l / 8, physical chunk l % 8, which holds
+        // logical chunk (l % 8) ^ (row & 7).
+        // (the same offsets serve every K block: only the scalar offset moves)
+        u32 voff_a[IA], voff_s[IS];
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            const int i = min(wave + j * NWAVES, NA_INS - 1);
+            const int r = i * 8 + lane / 8;
+            const int c = (lane & 7) ^ (r & 7);
+            const int rr = r < tl.rows ? r : tl.rows - 1;
+            voff_a[j] = (u32)rr * K + c * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < IS; ++j) {
+            const int i = min(wave + j * NWAVES, NS_INS - 1);
+            const int m = tl.m0 + i * 64 + lane;
+            voff_s[j] = (u32)(m < p.M ? m : p.M - 1) * 4u;
+        }
+        // this wave's share of one K block of A and sfa, into LDS region ri
+        auto issue_a = [&](int kb, int ri) __attribute__((always_inline)) {
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base);
+            const u32 ka = __builtin_amdgcn_readfirstlane((u32)kb * KBLK);
+#pragma unroll
+            for (int j = 0; j < IA; ++j) {
+                const int i = min(wave + j * NWAVES, NA_INS - 1);
+                dma16(rs_a, voff_a[j], ka, st + A_OFF + ri * (BM * 128) + i * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < IS; ++j) {
+                const int i = min(wave + j * NWAVES, NS_INS - 1);
+                dma4(rs_s, voff_s[j], __builtin_amdgcn_readfirstlane((u32)kb * p.M * 4u),
+                     st + S_OFF + (ri * NS_INS + i) * 256);
+            }
+        };
+        // variant 1: one K block of A, sfa and sfb into ring slot `slot`
+        auto issue_ring = [&](int kb, int slot) __attribute__((always_inline)) {
+            issue_a(kb, slot);
+            dma4(rs_t, (u32)min(nb_t0 + lane, NBLKS - 1) * KBLKS * 4u, __builtin_amdgcn_readfirstlane((u32)kb * 4u),
+                 __builtin_amdgcn_readfirstlane(smem_base) + T_OFF + slot * 256);
+        };
+        // LDS read pointers, fixed per tile; every K block adds a compile-time
+        // offset (which the compiler folds into the ds_read immediates instead
+        // of keeping one address register per K block alive).  sb_p[b]: the
+        // sub-tile's sfb, variant 1 inside a slot's sfb row (one float per
+        // 128-row block), variant 2 the row of its block.
+        lds_u8* const lds = (lds_u8*)smem_base;
+        lds_u8* sb_p[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            int nblk = (tl.n0 + wave_n + b * 16) / KBLK;
+            nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+            sb_p[b] = lds + T_OFF + (nblk - nb_t0) * (ARES ? 256 : 4);
+        }
+        lds_u8* const sa_p0 = lds + S_OFF + l16 * 4;
+        lds_u8* a_lo_bank[NBANK];
+        lds_u8* a_hi_bank[NBANK];
+#pragma unroll
+        for (int k = 0; k < NBANK; ++k) {
+            a_lo_bank[k] = lds + k * A_BANK + a_frag_off + chunk_lo;
+            a_hi_bank[k] = lds + k * A_BANK + a_frag_off + chunk_hi;
+            // opaque, so the compiler keeps these registers instead of re-deriving
+            // one address register per K block from the first
+            asm volatile("" : "+v"(a_lo_bank[k]), "+v"(a_hi_bank[k]));
+        }
+
+        v4f acc[TM][TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        // the last product of a K block and its scale, promoted under the next block's first MFMA
+        v4f p_carry = {0.f, 0.f, 0.f, 0.f};
+        float s_carry = 0.f;
+        v4i breg[NKB][TN][2];
+
+        // earlier tile's stores and LDS reads are finished before LDS is refilled
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        if constexpr (ARES) {
+            // the whole K range of A, sfa and sfb, then the first DEPTH K blocks of B
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base);
+            static_for<NKB>([&]<int KB>() __attribute__((always_inline)) { issue_a(tl.kb0 + KB, KB); });
+#pragma unroll
+            for (int j = 0; j < IT_ALL; ++j) {
+                const int jb = min(wave + j * NWAVES, 2);
+                const int nb = min(nb_t0 + jb, NBLKS - 1);
+                const int kb = min(tl.kb0 + lane, KBLKS - 1);
+                dma4(rs_t, (u32)(nb * KBLKS + kb) * 4u, 0u, st + T_OFF + jb * 256);
+            }
+            static_for<PRE_UNITS>([&]<int J>() __attribute__((always_inline)) { issue_b(tl.kb0 + J, breg[J]); });
+            // this wave's A share has landed once only the B loads may be pending
+            wait_vmcnt<PRE_UNITS * UB>();
+            __syncthreads();
+        } else {
+            static_for<PRE_UNITS>([&]<int J>() __attribute__((always_inline)) {
+                issue_ring(tl.kb0 + J, J % NREG);
+                issue_b(tl.kb0 + J, breg[J]);
+            });
+        }
+
+        static_for<NKB>([&]<int IT>() __attribute__((always_inline)) {
+            // this wave's loads of K block IT have landed once only the later
+            // requested blocks (up to IT + DEPTH - 1) may still be in flight
+            constexpr int last = IT + DEPTH - 1 < NKB - 1 ? IT + DEPTH - 1 : NKB - 1;
+            wait_vmcnt<(last - IT) * UNIT>();
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                tie(breg[IT][b][0]);
+                tie(breg[IT][b][1]);
+            }
+            // byte offsets of this K block's A, sfa and sfb from the per-tile pointers
+            constexpr int ri = ARES ? IT : IT % NREG;          // LDS region of this K block
+            constexpr int a_off = A_OFF + ri * (BM * 128);
+            constexpr int sa_off = ri * (NS_INS * 256);
+            constexpr int sb_off = ARES ? IT * 4 : ri * 256;
+            if constexpr (ARES) {
+                if constexpr (IT + DEPTH < NKB) issue_b(tl.kb0 + IT + DEPTH, breg[IT + DEPTH]);
+            } else {
+                // every wave's share of A has landed, and every wave is done with slot IT - 1
+                __syncthreads();
+                if constexpr (IT + DEPTH < NKB) {
+                    issue_ring(tl.kb0 + IT + DEPTH, (IT + DEPTH) % NREG);
+                    issue_b(tl.kb0 + IT + DEPTH, breg[IT + DEPTH]);
+                }
+            }
+
+            float sb[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p[b], sb_off);
+            float sa[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p0, sa_off + a * 64);
+            lds_u8* const a_lo = a_lo_bank[a_off / A_BANK] + a_off % A_BANK;
+            lds_u8* const a_hi = a_hi_bank[a_off / A_BANK] + a_off % A_BANK;
+            v8i fb[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const v4i x = breg[IT][b][0], y = breg[IT][b][1];
+                fb[b] = v8i{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            }
+            // A fragments are read FA_AHEAD sub-tiles ahead of their MFMA, so the
+            // LDS latency hides behind the MFMAs in between.  Software pipeline
+            // over the (a, b) sub-tiles: each MFMA runs while the FMAs promote
+            // the previous sub-tile's product.
+            v8i fa[TM];
+#pragma unroll
+            for (int a = 0; a < FA_AHEAD; ++a) fa[a] = lds_read_frag(a_lo, a_hi, a * 16 * 128);
+            v4f prev = p_carry;
+            float sprev = s_carry;
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                if (a + FA_AHEAD < TM) fa[a + FA_AHEAD] = lds_read_frag(a_lo, a_hi, (a + FA_AHEAD) * 16 * 128);
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                    // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[b], fa[a], zero, 0, 0, 0, 0, 0, 0);
+                    if (a == 0 && b == 0) acc[TM - 1][TN - 1] += prev * sprev;
+                    else if (b == 0) acc[a - 1][TN - 1] += prev * sprev;
+                    else acc[a][b - 1] += prev * sprev;
+                    prev = pr;
+                    sprev = sa[a] * sb[b];
+                }
+                // keep the read-ahead: the scheduler would otherwise sink each
+                // fragment read down to its MFMA
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            p_carry = prev;
+            s_carry = sprev;
+            // Pin the accumulators at the end of every block: with the K range
+            // unrolled, the compiler would otherwise sink all promotion FMAs into
+            // the epilogue (their only use) and keep every product alive until then.
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b) asm volatile("" : "+v"(acc[a][b]));
+        });
+        acc[TM - 1][TN - 1] += p_carry * s_carry;
+
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+    }
+}
+#endif
 
 }  // namespace dg

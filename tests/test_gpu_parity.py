@@ -191,6 +191,18 @@ FORCED = [
     "128,96,2,2,2,1,2",
     "64,64,2,2,3,2,2",
     "32,128,1,4,2,4,2",
+    # variant 1: B straight into VGPRs (fields 7-8: kstep 1, variant 1)
+    "128,128,1,8,9,1,1,1",
+    "128,128,1,4,4,1,1,1",
+    "64,96,1,2,4,2,1,1",
+    "256,64,1,4,3,1,1,1",
+    "32,64,1,1,3,4,1,1",
+    "16,48,1,1,2,8,1,1",
+    # variant 2: B straight into VGPRs, A of the K range resident in LDS
+    "64,128,1,4,4,1,1,2",
+    "64,192,1,4,4,2,1,2",
+    "128,64,1,4,4,1,1,2",
+    "32,48,1,1,3,4,1,2",
 ]
 
 
@@ -233,3 +245,17 @@ def test_graph_replays_match_eager(oracle):
             # eager work between replays, on the same stream and workspace
             dg.dg_fp8_gemm_nt(dd["A"], dd["sfa"], dd["B"], dd["sfb"], None, De)
             torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ variants 1 and 2 on the grouped forms
+@pytest.mark.parametrize("forced", ["128,128,1,8,5,1,1,1", "64,64,1,4,3,1,1,1", "64,128,1,4,4,1,1,2"])
+def test_bdirect_grouped(oracle, monkeypatch, forced):
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    pm = gen.make_masked(3, 200, 333, 512, seed=21, with_c=True, masked_m=[200, 0, 77])
+    D, sent = run(pm)
+    ref, comp = oracle_rows(oracle, pm)
+    _compare(pm, D, sent, ref, comp, what=f"masked {forced}")
+    pc = gen.make_contiguous([128, 0, 256, 100], 200, 384, seed=22, with_c=True, pad_rows=128)
+    D, sent = run(pc)
+    ref, comp = oracle_rows(oracle, pc)
+    _compare(pc, D, sent, ref, comp, what=f"contiguous {forced}")
