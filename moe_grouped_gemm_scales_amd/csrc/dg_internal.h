@@ -1,6 +1,7 @@
 // Internal declarations of libdg.so (host side).
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -23,17 +24,23 @@ struct KernelConfig {
     int kstep = 1;             // 128-wide K blocks per LDS stage (1 or 2)
     int splitk = 1;            // K splits (dense only)
     int variant = 0;           // 0: A and B through LDS; 1: B straight into VGPRs, A through an LDS
-                               // ring; 2: B straight into VGPRs, A of the K range resident in LDS
+                               // ring; 2: B straight into VGPRs, A of the K range resident in LDS;
+                               // 3: as 1, with an extra producer wave for A and no K-loop barrier
     int has_c = 0;
     int n = 0, k = 0, g = 1;
 
-    int threads() const { return 64 * wm * wn; }
+    int threads() const { return 64 * (wm * wn + (variant == 3 ? 1 : 0)); }   // variant 3: + producer wave
     int stage_bytes() const {
         if (variant == 1) return bm * 128 + (bm + 63) / 64 * 256 + 256;
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
     int lds_bytes() const {
         if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
+        if (variant == 3) {   // as many ring slots as fit (at most 16), see the kernel
+            const int slot = bm * 128 + (bm + 63) / 64 * 256;
+            const int slots = std::min(16, (160 * 1024 - 1024 - 768) / slot);
+            return 768 + slots * slot;
+        }
         return stages * stage_bytes();
     }
     std::string key() const;

@@ -117,7 +117,7 @@ int unit_per_wave_v1(const KernelConfig& c) {
 // Mirrors the kernel's static_asserts, so a selected config always compiles.
 bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (16 * c.wm) || c.bn % (16 * c.wn)) return false;
-    if (c.variant < 0 || c.variant > 2) return false;
+    if (c.variant < 0 || c.variant > 3) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
     if (c.bn > 256) return false;
@@ -132,6 +132,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
         const int nkb = p.k / 128 / c.splitk, pre = std::min(c.stages - 1, nkb);
         if (c.variant == 1 && unit_per_wave_v1(c) * (c.stages - 2) > 63) return false;
         if (c.variant == 2 && (ub * (c.stages - 2) > 63 || ub * pre > 63)) return false;
+        if (c.variant == 3 && (ub * pre > 63 || c.splitk != 1 || c.bm * 128 + 256 > 78 * 1024)) return false;
         if (tm < 1 || tn < 1 || tm > 16 || tn > 4 || tm * tn > 32) return false;
         if (c.bm % 8) return false;
         return true;
@@ -149,15 +150,15 @@ bool valid(const KernelConfig& c, const Problem& p) {
 // launch article's benchmark tables; other shapes go through the model.
 struct Tuned {
     int kind, rows, n, k, g, has_c;
-    int bm, bn, wm, wn, stages, splitk, kstep;
+    int bm, bn, wm, wn, stages, splitk, kstep, variant;
 };
 const Tuned kTuned[] = {
-    {kDense, 64, 2112, 7168, 1, 0, 64, 128, 2, 2, 3, 4, 2},
-    {kDense, 128, 24576, 1536, 1, 0, 128, 128, 2, 4, 2, 1, 2},
-    {kDense, 128, 24576, 1536, 1, 1, 128, 128, 2, 4, 2, 1, 2},
-    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1},
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1},
-    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 2, 1, 2},
+    {kDense, 64, 2112, 7168, 1, 0, 64, 128, 2, 2, 3, 4, 2, 0},
+    {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3},
+    {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 2, 1, 2, 0},
 };
 
 bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
@@ -167,7 +168,7 @@ bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
         if (t.rows >= 0 && t.rows != p.rows) continue;
         if (t.rows < 0 && p.rows < 4096) continue;   // contiguous: any large token count
         c->bm = t.bm; c->bn = t.bn; c->wm = t.wm; c->wn = t.wn;
-        c->stages = t.stages; c->splitk = t.splitk; c->kstep = t.kstep;
+        c->stages = t.stages; c->splitk = t.splitk; c->kstep = t.kstep; c->variant = t.variant;
         return true;
     }
     return false;

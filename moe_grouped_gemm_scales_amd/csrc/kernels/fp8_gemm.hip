@@ -331,6 +331,28 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
     }
 }
 
+// 16 bytes per lane from global memory into VGPRs.  Inline asm, like the DMA,
+// so that the compiler leaves the wait to the kernel's own vmcnt accounting;
+// the destination is only read after that wait and tie() below.
+template <int OFF>
+__device__ __forceinline__ v4i load16(v4i rsrc, u32 voff, u32 soff) {
+    v4i r;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
+                 : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF) : "memory");
+    return r;
+}
+// After the wait: a register the loads wrote is redefined here, so no use of it
+// can be scheduled before the wait.
+__device__ __forceinline__ void tie(v4i& x) { asm volatile("" : "+v"(x)); }
+
+template <int... Is> struct iseq {};
+template <int Nn, int... Is> struct make_iseq { using type = typename make_iseq<Nn - 1, Nn - 1, Is...>::type; };
+template <int... Is> struct make_iseq<0, Is...> { using type = iseq<Is...>; };
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, iseq<Is...>) { (f.template operator()<Is>(), ...); }
+template <int Nn, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl(f, typename make_iseq<Nn>::type{}); }
+
 #if DG_VARIANT == 0
 // ============================================================ variant 0: both operands through LDS
 // LDS ring: per stage [A tile BM x ROWB][B tile BN x ROWB][sfa, BM floats per K block, padded].
@@ -381,6 +403,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
                       int num_tiles) {
     const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+    // Every argument in one round trip of scalar loads: otherwise the loop bound
+    // is fetched first and the pointers only after it arrives (~0.5 us each).
+    asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
+                 "s"(num_tiles), "s"(gridDim.x));
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
     __shared__ int s_flag;
 
@@ -621,7 +647,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
     }
 }
 
-#else
+#elif DG_VARIANT == 1 || DG_VARIANT == 2
 // ============================================================ variants 1 and 2: B straight into VGPRs
 // For few rows (every row of a problem or group in one or two row blocks):
 // each wave owns WAVE_N rows of B and loads them from global memory straight
@@ -678,27 +704,6 @@ static_assert(UNIT * (DEPTH - 1) <= 63 && (!ARES || UNIT * PRE_UNITS <= 63), "vm
 #endif
 constexpr int FA_AHEAD = DG_FA_AHEAD < TM ? DG_FA_AHEAD : TM;   // A fragments read ahead of use
 
-// 16 bytes per lane from global memory into VGPRs.  Inline asm, like the DMA,
-// so that the compiler leaves the wait to the kernel's own vmcnt accounting;
-// the destination is only read after that wait and tie() below.
-template <int OFF>
-__device__ __forceinline__ v4i load16(v4i rsrc, u32 voff, u32 soff) {
-    v4i r;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
-                 : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF) : "memory");
-    return r;
-}
-// After the wait: a register the loads wrote is redefined here, so no use of it
-// can be scheduled before the wait.
-__device__ __forceinline__ void tie(v4i& x) { asm volatile("" : "+v"(x)); }
-
-template <int... Is> struct iseq {};
-template <int Nn, int... Is> struct make_iseq { using type = typename make_iseq<Nn - 1, Nn - 1, Is...>::type; };
-template <int... Is> struct make_iseq<0, Is...> { using type = iseq<Is...>; };
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F& f, iseq<Is...>) { (f.template operator()<Is>(), ...); }
-template <int Nn, typename F>
-__device__ __forceinline__ void static_for(F&& f) { static_for_impl(f, typename make_iseq<Nn>::type{}); }
 
 extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THREADS_DECL)))
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
@@ -706,6 +711,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
                       int num_tiles) {
     const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+    // Every argument in one round trip of scalar loads: otherwise the loop bound
+    // is fetched first and the pointers only after it arrives (~0.5 us each).
+    asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
+                 "s"(num_tiles), "s"(gridDim.x));
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
     __shared__ int s_flag;
 
@@ -932,6 +941,286 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             // Pin the accumulators at the end of every block: with the K range
             // unrolled, the compiler would otherwise sink all promotion FMAs into
             // the epilogue (their only use) and keep every product alive until then.
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b) asm volatile("" : "+v"(acc[a][b]));
+        });
+        acc[TM - 1][TN - 1] += p_carry * s_carry;
+
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+    }
+}
+#elif DG_VARIANT == 3
+// ============================================================ variant 3: a producer wave for A
+// For few rows, like variant 1, but without any workgroup barrier in the K
+// loop.  One extra wave (the last) only loads A and its scales into an LDS
+// ring and publishes each K block with an LDS flag; the NWAVES other waves
+// each stream their own rows of B straight into VGPRs (DEPTH K blocks ahead),
+// wait on the flag of the K block they need rather than on the slowest wave,
+// and count themselves off each slot when done with it.  The producer
+// refills a slot only once every consumer has counted off, and publishes a
+// block LAG blocks after issuing it (LAG < SLOTS, so the slot it waits for
+// always holds a published block: no wait can be circular).  Every wait on a
+// flag is also bounded, so a fault in this protocol would cost correctness,
+// which the tests check, and never hang the device.
+static_assert(WM == 1, "variant 3 spreads its consumer waves along n only");
+static_assert(KSTEP == 1, "variant 3 stages one K block per slot");
+static_assert(SPLITK == 1, "variant 3 computes whole K ranges");
+constexpr int NKB = KBLKS;
+static_assert(NKB <= 64, "the whole K range of a work item is unrolled");
+constexpr int DEPTH = STAGES - 1;                 // K blocks of B requested ahead of use
+constexpr int UB = 2 * TN;                        // B loads per lane per K block
+constexpr int PRE_UNITS = DEPTH < NKB ? DEPTH : NKB;
+static_assert(DEPTH >= 1 && UB * PRE_UNITS <= 63, "vmcnt range");
+constexpr int NA_INS = BM / 8;                    // 1 KB DMA instructions for one K block of A
+constexpr int NS_INS = (BM + 63) / 64;            // 256 B DMA instructions for its sfa
+static_assert(BM % 8 == 0, "A is loaded 8 rows per DMA instruction");
+static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
+// LDS: [sfb: rows j = 0..2 (the tile's 128-row blocks of B) x 64 K blocks]
+//      [sfa: SLOTS x NS_INS x 256 B][A: SLOTS x BM rows x 128 B]
+constexpr int T_OFF = 0;
+constexpr int S_OFF = 3 * 256;
+constexpr int SLOT_A = BM * 128;
+constexpr int SLOT_S = NS_INS * 256;
+constexpr int SLOTS_FIT = (160 * 1024 - 1024 - S_OFF) / (SLOT_A + SLOT_S);
+constexpr int SLOTS = SLOTS_FIT < 16 ? SLOTS_FIT : 16;
+constexpr int A_OFF = S_OFF + SLOTS * SLOT_S;
+constexpr int LDS_BYTES = A_OFF + SLOTS * SLOT_A;
+constexpr int PU = NA_INS + NS_INS;               // producer DMA instructions per K block
+constexpr int LAG = (SLOTS - 1) < (63 / PU) ? (SLOTS - 1) : (63 / PU);
+static_assert(SLOTS >= 2 && LAG >= 1, "ring too small");
+constexpr int V3_THREADS = NTHREADS + 64;
+constexpr int V3_MAX_DECL = V3_THREADS < 512 ? 512 : V3_THREADS;
+constexpr int SPIN_LIMIT = 1 << 20;               // about 30 ms of s_sleep 1 before giving up
+constexpr int A_BANK = 32768;
+constexpr int NBANK = (LDS_BYTES + A_BANK - 1) / A_BANK;
+#ifndef DG_FA_AHEAD
+#define DG_FA_AHEAD 4
+#endif
+constexpr int FA_AHEAD = DG_FA_AHEAD < TM ? DG_FA_AHEAD : TM;
+
+// Bounded wait until *flag >= target (an LDS word written by another wave).
+__device__ __forceinline__ void wait_flag(u32* flag, u32 target) {
+    for (int i = 0; i < SPIN_LIMIT; ++i) {
+        const u32 v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");   // later LDS reads stay after the wait
+}
+
+extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, V3_MAX_DECL)))
+dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
+                      const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
+                      const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
+                      int num_tiles) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+    // Every argument in one round trip of scalar loads: otherwise the loop bound
+    // is fetched first and the pointers only after it arrives (~0.5 us each).
+    asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
+                 "s"(num_tiles), "s"(gridDim.x));
+    __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
+    __shared__ u32 ready[SLOTS];     // K block index + 1 held by the slot, once landed
+    __shared__ u32 freed[SLOTS];     // consumer waves done with the slot's current block
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave == NWAVES;
+    const int l16 = lane & 15;
+    const int q = lane >> 4;
+    const u32 smem_base = lds_addr(smem);
+    const int sw = l16 & 7;
+    const u32 chunk_lo = (u32)((q ^ sw) << 4);
+    const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
+    const u32 a_frag_off = (u32)l16 * 128u;
+    const int wave_n = wave * WAVE_N;
+
+#pragma unroll 1
+    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
+        const Tile tl = decode_tile(p, t);
+        if (tl.skip) continue;
+        // every wave is done with the previous tile: reset the ring's flags
+        __syncthreads();
+        if (tid < SLOTS) {
+            ready[tid] = 0u;
+            freed[tid] = 0u;
+        }
+        __syncthreads();
+
+        const u8* a_base;
+        const float* sfa_base;
+        if constexpr (kKind == 2) {
+            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
+            sfa_base = p.sfa + (u64)tl.g * KBLKS * p.M;
+        } else {
+            a_base = p.A + (u64)tl.m0 * K;
+            sfa_base = p.sfa;
+        }
+        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const int nb_t0 = tl.n0 / KBLK;
+
+        if (producer) {
+            const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
+            const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * p.M * 4u);
+            const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base);
+            // sfb of the tile's 128-row blocks over all K blocks (published with block 0)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int nb = min(nb_t0 + j, NBLKS - 1);
+                const int kb = min(tl.kb0 + lane, KBLKS - 1);
+                dma4(rs_t, (u32)(nb * KBLKS + kb) * 4u, 0u, st + T_OFF + j * 256);
+            }
+            // A DMA: lane l of instruction i (8 tile rows) writes LDS bytes [16 l, 16 l + 16)
+            // of its 1 KB = tile row 8 i + l / 8, physical chunk l % 8, which holds
+            // logical chunk (l % 8) ^ (row & 7).
+            u32 voff_a[NA_INS], voff_s[NS_INS];
+#pragma unroll
+            for (int i = 0; i < NA_INS; ++i) {
+                const int r = i * 8 + lane / 8;
+                const int c = (lane & 7) ^ (r & 7);
+                voff_a[i] = (u32)(r < tl.rows ? r : tl.rows - 1) * K + c * 16;
+            }
+#pragma unroll
+            for (int i = 0; i < NS_INS; ++i) {
+                const int m = tl.m0 + i * 64 + lane;
+                voff_s[i] = (u32)(m < p.M ? m : p.M - 1) * 4u;
+            }
+            auto publish = [&](int kb) __attribute__((always_inline)) {
+                if (lane == 0)
+                    __hip_atomic_store(&ready[kb % SLOTS], (u32)(kb + 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            };
+            static_for<NKB>([&]<int KB>() __attribute__((always_inline)) {
+                constexpr int slot = KB % SLOTS;
+                // the slot's previous block (KB - SLOTS) has been read by every consumer
+                if constexpr (KB >= SLOTS) wait_flag(&freed[slot], (u32)(NWAVES * (KB / SLOTS)));
+                const u32 ka = __builtin_amdgcn_readfirstlane((u32)(tl.kb0 + KB) * KBLK);
+#pragma unroll
+                for (int i = 0; i < NA_INS; ++i) dma16(rs_a, voff_a[i], ka, st + A_OFF + slot * SLOT_A + i * 1024);
+#pragma unroll
+                for (int i = 0; i < NS_INS; ++i)
+                    dma4(rs_s, voff_s[i], __builtin_amdgcn_readfirstlane((u32)(tl.kb0 + KB) * p.M * 4u),
+                         st + S_OFF + slot * SLOT_S + i * 256);
+                // block KB - LAG has landed once only the LAG newer blocks may be in flight
+                if constexpr (KB >= LAG) {
+                    wait_vmcnt<LAG * PU>();
+                    publish(KB - LAG);
+                }
+            });
+            static_for<(LAG < NKB ? LAG : NKB)>([&]<int J>() __attribute__((always_inline)) {
+                constexpr int kb = NKB - (LAG < NKB ? LAG : NKB) + J;   // the unpublished tail, oldest first
+                wait_vmcnt<(NKB - 1 - kb) * PU>();
+                publish(kb);
+            });
+            continue;
+        }
+
+        // ---------------------------------------------------------- consumer waves
+        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
+        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
+        u32 bvoff[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int r = wave_n + b * 16 + l16;
+            bvoff[b] = (u32)(r < n_rows ? r : n_rows - 1) * K + q * 16;
+        }
+        auto issue_b = [&](int kb, v4i (&dst)[TN][2]) __attribute__((always_inline)) {
+            const u32 ka = __builtin_amdgcn_readfirstlane((u32)kb * KBLK);
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                dst[b][0] = load16<0>(rs_b, bvoff[b], ka);
+                dst[b][1] = load16<64>(rs_b, bvoff[b], ka);
+            }
+        };
+        lds_u8* const lds = (lds_u8*)smem_base;
+        lds_u8* sb_p[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            int nblk = (tl.n0 + wave_n + b * 16) / KBLK;
+            nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+            sb_p[b] = lds + T_OFF + (nblk - nb_t0) * 256;
+        }
+        lds_u8* const sa_p0 = lds + S_OFF + l16 * 4;
+        lds_u8* a_lo_bank[NBANK];
+        lds_u8* a_hi_bank[NBANK];
+#pragma unroll
+        for (int k = 0; k < NBANK; ++k) {
+            a_lo_bank[k] = lds + k * A_BANK + a_frag_off + chunk_lo;
+            a_hi_bank[k] = lds + k * A_BANK + a_frag_off + chunk_hi;
+            asm volatile("" : "+v"(a_lo_bank[k]), "+v"(a_hi_bank[k]));
+        }
+
+        v4f acc[TM][TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        v4f p_carry = {0.f, 0.f, 0.f, 0.f};
+        float s_carry = 0.f;
+        v4i breg[NKB][TN][2];
+
+        // earlier tile's stores are finished before this wave's load accounting starts
+        wait_vmcnt<0>();
+        static_for<PRE_UNITS>([&]<int J>() __attribute__((always_inline)) { issue_b(tl.kb0 + J, breg[J]); });
+
+        static_for<NKB>([&]<int IT>() __attribute__((always_inline)) {
+            constexpr int last = IT + DEPTH - 1 < NKB - 1 ? IT + DEPTH - 1 : NKB - 1;
+            wait_vmcnt<(last - IT) * UB>();
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                tie(breg[IT][b][0]);
+                tie(breg[IT][b][1]);
+            }
+            constexpr int slot = IT % SLOTS;
+            wait_flag(&ready[slot], (u32)(IT + 1));
+            if constexpr (IT + DEPTH < NKB) issue_b(tl.kb0 + IT + DEPTH, breg[IT + DEPTH]);
+
+            constexpr int a_off = A_OFF + slot * SLOT_A;
+            float sb[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p[b], IT * 4);
+            float sa[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p0, slot * SLOT_S + a * 64);
+            lds_u8* const a_lo = a_lo_bank[a_off / A_BANK] + a_off % A_BANK;
+            lds_u8* const a_hi = a_hi_bank[a_off / A_BANK] + a_off % A_BANK;
+            v8i fb[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const v4i x = breg[IT][b][0], y = breg[IT][b][1];
+                fb[b] = v8i{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            }
+            v8i fa[TM];
+#pragma unroll
+            for (int a = 0; a < FA_AHEAD; ++a) fa[a] = lds_read_frag(a_lo, a_hi, a * 16 * 128);
+            v4f prev = p_carry;
+            float sprev = s_carry;
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                if (a + FA_AHEAD < TM) fa[a + FA_AHEAD] = lds_read_frag(a_lo, a_hi, (a + FA_AHEAD) * 16 * 128);
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                    // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[b], fa[a], zero, 0, 0, 0, 0, 0, 0);
+                    if (a == 0 && b == 0) acc[TM - 1][TN - 1] += prev * sprev;
+                    else if (b == 0) acc[a - 1][TN - 1] += prev * sprev;
+                    else acc[a][b - 1] += prev * sprev;
+                    prev = pr;
+                    sprev = sa[a] * sb[b];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            p_carry = prev;
+            s_carry = sprev;
+            // this wave has read everything of the slot it needs: count off
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) __hip_atomic_fetch_add(&freed[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
             for (int a = 0; a < TM; ++a)
 #pragma unroll

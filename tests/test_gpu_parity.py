@@ -203,6 +203,10 @@ FORCED = [
     "64,192,1,4,4,2,1,2",
     "128,64,1,4,4,1,1,2",
     "32,48,1,1,3,4,1,2",
+    # variant 3: B straight into VGPRs, a producer wave streams A through LDS
+    "128,96,1,6,3,1,1,3",
+    "64,64,1,4,3,1,1,3",
+    "32,48,1,1,2,1,1,3",
 ]
 
 
@@ -248,7 +252,8 @@ def test_graph_replays_match_eager(oracle):
 
 
 # ------------------------------------------------------------------ variants 1 and 2 on the grouped forms
-@pytest.mark.parametrize("forced", ["128,128,1,8,5,1,1,1", "64,64,1,4,3,1,1,1", "64,128,1,4,4,1,1,2"])
+@pytest.mark.parametrize("forced", ["128,128,1,8,5,1,1,1", "64,64,1,4,3,1,1,1", "64,128,1,4,4,1,1,2",
+                                    "64,64,1,4,3,1,1,3"])
 def test_bdirect_grouped(oracle, monkeypatch, forced):
     monkeypatch.setenv("DG_FORCE_CONFIG", forced)
     pm = gen.make_masked(3, 200, 333, 512, seed=21, with_c=True, masked_m=[200, 0, 77])
