@@ -153,7 +153,7 @@ struct Tuned {
     int bm, bn, wm, wn, stages, splitk, kstep, variant;
 };
 const Tuned kTuned[] = {
-    {kDense, 64, 2112, 7168, 1, 0, 64, 128, 2, 2, 3, 4, 2, 0},
+    {kDense, 64, 2112, 7168, 1, 0, 64, 64, 1, 4, 4, 7, 1, 2},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3},
     {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0},

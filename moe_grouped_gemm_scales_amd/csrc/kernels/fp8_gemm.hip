@@ -266,35 +266,68 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
     // ---- split-K: publish the partial, the last arrival sums all in split order
     if constexpr (SPLITK > 1) {
         float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
+        // Partials go out as agent-scope (write-through) stores and come back as
+        // agent-scope loads, so no cache maintenance is needed: an agent-scope
+        // release fence here (a write-back of the whole L2) measured 7-10 us per
+        // work item, longer than the K loop itself.  Once this wave's stores are
+        // acknowledged (vmcnt 0) they are visible at agent scope; the barrier
+        // orders every wave's stores before the arrival count.
+        // (sc1 = agent scope on the 16-byte buffer stores and loads below)
+        constexpr int CPOL_AGENT = 16;
+        const __amdgpu_buffer_rsrc_t rs_ws =
+            __builtin_amdgcn_make_buffer_rsrc(ws, 0, SPLITK * BM * BN * 4, 0x00020000);
 #pragma unroll
         for (int a = 0; a < TM_; ++a)
 #pragma unroll
             for (int b = 0; b < TN_; ++b)
-                *(v4f*)(ws + ((u64)tl.split * BM * BN) + ((a * TN_ + b) * NTHREADS + tid) * 4) = acc[a][b];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(v4i, acc[a][b]), rs_ws,
+                    (tl.split * BM * BN + ((a * TN_ + b) * NTHREADS + tid) * 4) * 4, 0, CPOL_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-            u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             *s_flag = (old == (u32)(SPLITK - 1));
             if (old == (u32)(SPLITK - 1))
                 __hip_atomic_store(&p.counters[tl.mn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!*s_flag) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        asm volatile("" ::: "memory");
+        // Every partial, this split's own included (it reads back exactly what it
+        // wrote), is loaded unconditionally, CH splits at a time so that their
+        // loads are in flight together without running out of registers; they
+        // are summed in split order, the same order on every run.
+        constexpr int CH0 = 28 / (TM_ * TN_);
+        constexpr int CH = CH0 < 1 ? 1 : (CH0 > SPLITK ? SPLITK : CH0);
+        int wofs = 0;
 #pragma unroll
-        for (int a = 0; a < TM_; ++a)
+        for (int s0 = 0; s0 < SPLITK; s0 += CH) {
+            v4f part[CH][TM_][TN_];
 #pragma unroll
-            for (int b = 0; b < TN_; ++b) {
-                v4f sum = {0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < SPLITK; ++s) {
-                    v4f part = (s == tl.split)
-                                   ? acc[a][b]
-                                   : *(const v4f*)(ws + ((u64)s * BM * BN) + ((a * TN_ + b) * NTHREADS + tid) * 4);
-                    sum += part;
-                }
-                acc[a][b] = sum;
-            }
+            for (int c = 0; c < CH; ++c)
+                if (s0 + c < SPLITK)
+#pragma unroll
+                    for (int a = 0; a < TM_; ++a)
+#pragma unroll
+                        for (int b = 0; b < TN_; ++b)
+                            part[c][a][b] = __builtin_bit_cast(
+                                v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs_ws, (wofs + (s0 + c) * BM * BN + ((a * TN_ + b) * NTHREADS + tid) * 4) * 4,
+                                         0, CPOL_AGENT));
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if (s0 + c < SPLITK)
+#pragma unroll
+                    for (int a = 0; a < TM_; ++a)
+#pragma unroll
+                        for (int b = 0; b < TN_; ++b)
+                            acc[a][b] = (s0 + c == 0) ? part[c][a][b] : acc[a][b] + part[c][a][b];
+            // the next chunk's loads depend on this opaque zero, taken after this
+            // chunk's sums, so the compiler cannot hoist them all (and spill them)
+            // ahead of those sums
+            asm volatile("" : "+s"(wofs) : "v"(acc[0][0]));
+        }
     }
 
     // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
