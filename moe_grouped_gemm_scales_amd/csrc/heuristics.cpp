@@ -158,7 +158,7 @@ const Tuned kTuned[] = {
     {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0},
     {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0},
-    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 2, 1, 2, 0},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3},
 };
 
 bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
