@@ -422,6 +422,13 @@ constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
 constexpr int IT = (NT_INS + NWAVES - 1) / NWAVES;
 constexpr int INS_PER_WAVE = IA + IB + IS + IT;
 static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
+// MFMA steps (n sub-tiles of a stage's first K block) the refill is spread over;
+// 0: all at once.  It must be issued before the last sub-tile, where the wait
+// for the next stage counts it.
+#ifndef DG_SPREAD
+#define DG_SPREAD (STAGES == 2 ? (TN + 1) / 2 : TN)
+#endif
+constexpr int SPREAD = DG_SPREAD < TN - 1 ? DG_SPREAD : TN - 1;
 
 // Wait until at most PENDING whole stages of this wave's DMA remain in flight.
 template <int PENDING>
@@ -488,59 +495,72 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
         const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
-        // ---- per-lane DMA offsets for this wave's instructions (fixed over K).
-        // Lane l of an instruction writes LDS bytes [16 l, 16 l + 16) of its 1 KB:
-        // tile row RPI*i + l / (ROWB/16), K block h of the stage, physical chunk
-        // p = l % 8, which holds logical chunk p ^ (row & 7).
-        u32 voff[INS_PER_WAVE];
-        auto row_voff = [&](int i, int rows_valid) {
+        // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
+        // writes LDS bytes [16 l, 16 l + 16) of its 1 KB: tile row RPI*i + l / (ROWB/16),
+        // K block h of the stage, physical chunk p = l % 8, which holds logical
+        // chunk p ^ (row & 7).  The lane part is kept in one register (two when
+        // RPI = 4, where the swizzle also depends on the parity of i) and the
+        // instruction's row offset i*RPI*K is added at issue.  Rows past the tile
+        // (ragged M or N) give offsets past the buffer's size: the load returns
+        // zeros without touching memory, and those rows are never stored.
+        auto lane_voff = [&](int i) {
             const int r = i * RPI + lane / (ROWB / 16);
             const int h = (lane % (ROWB / 16)) / 8;
             const int c = (lane & 7) ^ (r & 7);
-            const int rr = r < rows_valid ? r : rows_valid - 1;
-            return (u32)rr * K + h * 128 + c * 16;
+            return (u32)(lane / (ROWB / 16)) * K + h * 128 + c * 16;
         };
+        constexpr int NPAR = (RPI % 8) == 0 ? 1 : 8 / RPI;   // distinct (i*RPI) & 7 values
+        static_assert(NPAR == 1 || NPAR == 2, "rows per instruction");
+        u32 voff_rows[NPAR];
 #pragma unroll
-        for (int j = 0; j < IA; ++j) voff[j] = row_voff(min(wave + j * NWAVES, NA_INS - 1), tl.rows);
-#pragma unroll
-        for (int j = 0; j < IB; ++j) voff[IA + j] = row_voff(min(wave + j * NWAVES, NB_INS - 1), n_rows);
+        for (int par = 0; par < NPAR; ++par) voff_rows[par] = lane_voff(par);
+        u32 voff_s[IS];          // A scales: clamped rows (the offset includes the K block's row of sfa)
 #pragma unroll
         for (int j = 0; j < IS; ++j) {
             const int i = min(wave + j * NWAVES, NS_INS - 1);
             const int h = i / NS_PER_KB;
             const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
-            voff[IA + IB + j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
+            voff_s[j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
         }
+        u32 voff_t[IT];
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int h = min(wave + j * NWAVES, NT_INS - 1);
             const int nb = min(nb_t0 + lane, NBLKS - 1);
-            voff[IA + IB + IS + j] = (u32)nb * KBLKS * 4u + (u32)h * 4u;
+            voff_t[j] = (u32)nb * KBLKS * 4u + (u32)h * 4u;
         }
 
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
         // (kb: first K block of the stage)
-        auto issue_one = [&](int j, int kb, int stage) {
+        // live = false: a placeholder load whose buffer size is zero, so it moves
+        // no data (every lane is out of range) but keeps the vmcnt count fixed.
+        auto issue_one = [&](int j, int kb, int stage, bool live = true) {
             const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+            auto lim = [&](v4i r) {
+                r.z = live ? r.z : 0;
+                return r;
+            };
             if (j < IA) {
                 const int i = min(wave + j * NWAVES, NA_INS - 1);
-                dma16(rs_a, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
+                dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                      __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
             } else if (j < IA + IB) {
                 const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
-                dma16(rs_b, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+                dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                      __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
-                dma4(rs_s, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u),
+                dma4(lim(rs_s), voff_s[j - IA - IB], __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u),
                      st + S_OFF + i * 256);
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
-                dma4(rs_t, voff[j], __builtin_amdgcn_readfirstlane((u32)kb * 4u), st + T_OFF + h * 256);
+                dma4(lim(rs_t), voff_t[j - IA - IB - IS], __builtin_amdgcn_readfirstlane((u32)kb * 4u), st + T_OFF + h * 256);
             }
         };
-        auto issue_stage = [&](int kb, int stage) {
+        auto issue_stage = [&](int kb, int stage, bool live = true) {
 #pragma unroll
-            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage);
+            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage, live);
         };
 
         // ---- accumulators
@@ -580,98 +600,244 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             sb_off[b] = __builtin_amdgcn_readfirstlane((nblk - nb_t0) * 4);
         }
 
-#pragma unroll 1
-        for (int it = 0; it < nst; ++it) {
-            const int stage = it % STAGES;
-            // stage `it` has landed (for this wave) once at most the later stages are pending
-            if (it + STAGES - 1 <= nst) wait_stages<STAGES - 2>();
+        if constexpr (KSTEP == 1) {
+            // One K block per stage: the barrier sits in the last n sub-tile, where
+            // the next K block's fragments are fetched while its MFMAs run.
+            // LDS bases of one K block (stage slot, K block h inside the stage)
+            const u32 b_frag = b_frag_off + chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
+            const u32 a_frag = a_frag_off + chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
+            auto kblock_base = [&](int stage, int h) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + h * 128);
+            };
+            auto kblock_scales = [&](int stage, int h) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + h * S_BYTES);
+            };
+            auto kblock_sfb = [&](int stage, int h) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + T_OFF + h * 256);
+            };
+            // Registers of the K block being multiplied: its A fragments, its first
+            // (then current) B fragment and the scales.  They are read from LDS one K
+            // block ahead, during the last n sub-tile of the previous one.
+            v8i fa[TM];
+            v8i fb;
+            float sa[TM];
+            float sb[TN];
+            auto read_scales = [&](int stage, int h) __attribute__((always_inline)) {
+                lds_u8* const sb_p = kblock_sfb(stage, h);
+                if constexpr (SB_UNIFORM) {
+                    sb[0] = lds_read_f32(sb_p, sb_off[0]);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
+                }
+                lds_u8* const sa_p = kblock_scales(stage, h) + a_row0 * 4;
+#pragma unroll
+                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+            };
+
+            // stage 0 in LDS (this wave's DMA, then everyone's), then its registers
+            if (STAGES - 1 <= nst) wait_stages<STAGES - 2>();
             else wait_vmcnt<0>();
             __syncthreads();
-            // Refill the slot every wave finished reading last iteration.  With two
-            // slots the refill is needed by the next iteration, so it goes out
-            // at once; with three or more it is spread over this iteration's
-            // MFMA steps, so no wave stalls on a burst of vector-memory issue.
-            const bool refill = it + STAGES - 1 < nst;
-            const int kb_fill = tl.kb0 + (it + STAGES - 1) * KSTEP, slot_fill = (it + STAGES - 1) % STAGES;
-            if constexpr (STAGES == 2) {
-                if (refill) issue_stage(kb_fill, slot_fill);
+            {
+                lds_u8* const kb0 = kblock_base(0, 0);
+                read_scales(0, 0);
+#pragma unroll
+                for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(kb0 + a_frag, kb0 + a_frag_hi, A_OFF + a * 16 * ROWB);
+                fb = lds_read_frag(kb0 + b_frag, kb0 + b_frag_hi, B_OFF);
             }
 
-            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+#pragma unroll 1
+            for (int it = 0; it < nst; ++it) {
+                const int stage = it % STAGES;
+                // The slot of stage it-1 is free: every wave read all of it into
+                // registers before the barrier in the previous iteration.  Its refill
+                // (the stage STAGES-1 ahead) is spread over the first MFMA steps.  In
+                // the last STAGES-1 iterations the refill is a placeholder that moves
+                // no data, so the loop has no branch and the number of stages in
+                // flight is always the same.
+                const bool live = it + STAGES - 1 < nst;
+                const int kb_fill = tl.kb0 + min(it + STAGES - 1, nst - 1) * KSTEP;
+                const int slot_fill = (it + STAGES - 1) % STAGES;
+                // the K block after the last one of this stage: first of the next stage
+                const int stage_next = (it + 1) % STAGES;
 #pragma unroll
-            for (int h = 0; h < KSTEP; ++h) {
-            const int kb = tl.kb0 + it * KSTEP + h;
-            // scale of B from the stage (same address in every lane: a broadcast read)
-            lds_u8* const sb_p = (lds_u8*)(st + T_OFF + h * 256);
-            float sb[TN];
-            if constexpr (SB_UNIFORM) {
-                sb[0] = lds_read_f32(sb_p, sb_off[0]);
-            } else {
-#pragma unroll
-                for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
-            }
-            lds_u8* const stp = (lds_u8*)(st + h * 128);
-            lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
-            lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
-            lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
-            lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
-            lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
+                for (int h = 0; h < KSTEP; ++h) {
+                lds_u8* const kbp = kblock_base(stage, h);
+                lds_u8* const b_lo = kbp + b_frag;
+                lds_u8* const b_hi = kbp + b_frag_hi;
+                const int h_next = h + 1 < KSTEP ? h + 1 : 0;
+                const int st_next = h + 1 < KSTEP ? stage : stage_next;
+                lds_u8* const kbn = kblock_base(st_next, h_next);
 
-            float sa[TM];
+                float sab[TM];           // sa * sb for the uniform case
+                if constexpr (SB_UNIFORM) {
 #pragma unroll
-            for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
-            v8i fa[TM];
-#pragma unroll
-            for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
-            v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
+                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                }
 
-            float sab[TM];           // sa * sb for the uniform case
-            if constexpr (SB_UNIFORM) {
+                // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
+                // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
+                // last sub-tile of the previous K block).
+                v4f pr[TM];
 #pragma unroll
-                for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
-            }
-
-            // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
-            // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
-            // last sub-tile of the previous K block).
-            v4f pr[TM];
+                for (int b = 0; b < TN; ++b) {
+                    if (h == 0) {
+                        if constexpr (SPREAD == 0) {
+                            if (b == 0) issue_stage(kb_fill, slot_fill, live);
+                        } else if (b < SPREAD) {
 #pragma unroll
-            for (int b = 0; b < TN; ++b) {
-                if constexpr (STAGES > 2) {
-                    if (refill && h == 0) {
+                            for (int j = b * INS_PER_WAVE / SPREAD; j < (b + 1) * INS_PER_WAVE / SPREAD; ++j)
+                                issue_one(j, kb_fill, slot_fill, live);
+                        }
+                    }
+                    const bool last = b + 1 == TN;
+                    v8i fb_next;
+                    if (!last) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
+                    // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
+                    // b itself (carried), taken before the next K block's replace them
+                    float sc_prev[TM], s_last[TM];
 #pragma unroll
-                        for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
-                            issue_one(j, kb_fill, slot_fill);
+                    for (int a = 0; a < TM; ++a) {
+                        if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
+                        else {
+                            sc_prev[a] = b > 0 ? sa[a] * sb[b > 0 ? b - 1 : 0] : 0.f;
+                            s_last[a] = sa[a] * sb[b];
+                        }
+                    }
+                    if (last) {
+                        if (h + 1 == KSTEP) {
+                            // next stage landed (own DMA; the later stages pending), then
+                            // everyone's; all reads of this stage are in registers
+                            wait_stages<STAGES - 2>();
+                            __syncthreads();
+                        }
+                        read_scales(st_next, h_next);
+                    }
+                    v4f prev[TM];
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) {
+                        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                        // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                        pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                        if (b == 0) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                        else acc[a][b - 1] += prev[a] * sc_prev[a];
+                        // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
+                        // (after the tile's last block these reads are unused)
+                        if (last) fa[a] = lds_read_frag(kbn + a_frag, kbn + a_frag_hi, A_OFF + a * 16 * ROWB);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (!last) {
+                        fb = fb_next;
+                    } else {
+                        fb = lds_read_frag(kbn + b_frag, kbn + b_frag_hi, B_OFF);
+#pragma unroll
+                        for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
                     }
                 }
-                v8i fb_next;
-                if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
-                v4f prev[TM];
 #pragma unroll
-                for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+                for (int a = 0; a < TM; ++a) p_carry[a] = pr[a];
+                }   // K blocks of the stage
+            }
+            wait_vmcnt<0>();         // no DMA (placeholders included) outlives the tile
+        } else {
+            // Two K blocks per stage (short K loops): barrier at the top of each
+            // stage, fragments read at the start of each K block.
+#pragma unroll 1
+            for (int it = 0; it < nst; ++it) {
+                const int stage = it % STAGES;
+                // stage `it` has landed (for this wave) once at most the later stages are pending
+                if (it + STAGES - 1 <= nst) wait_stages<STAGES - 2>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                // Refill the slot every wave finished reading last iteration.  With two
+                // slots the refill is needed by the next iteration, so it goes out
+                // at once; with three or more it is spread over this iteration's
+                // MFMA steps, so no wave stalls on a burst of vector-memory issue.
+                const bool refill = it + STAGES - 1 < nst;
+                const int kb_fill = tl.kb0 + (it + STAGES - 1) * KSTEP, slot_fill = (it + STAGES - 1) % STAGES;
+                if constexpr (STAGES == 2) {
+                    if (refill) issue_stage(kb_fill, slot_fill);
+                }
+
+                const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+#pragma unroll
+                for (int h = 0; h < KSTEP; ++h) {
+                const int kb = tl.kb0 + it * KSTEP + h;
+                // scale of B from the stage (same address in every lane: a broadcast read)
+                lds_u8* const sb_p = (lds_u8*)(st + T_OFF + h * 256);
+                float sb[TN];
+                if constexpr (SB_UNIFORM) {
+                    sb[0] = lds_read_f32(sb_p, sb_off[0]);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
+                }
+                lds_u8* const stp = (lds_u8*)(st + h * 128);
+                lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
+                lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
+                lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
+                lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
+                lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
+
+                float sa[TM];
+#pragma unroll
+                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+                v8i fa[TM];
+#pragma unroll
+                for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
+                v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
+
+                float sab[TM];           // sa * sb for the uniform case
+                if constexpr (SB_UNIFORM) {
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                }
+
+                // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
+                // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
+                // last sub-tile of the previous K block).
+                v4f pr[TM];
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    if constexpr (STAGES > 2) {
+                        if (refill && h == 0) {
+#pragma unroll
+                            for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
+                                issue_one(j, kb_fill, slot_fill);
+                        }
+                    }
+                    v8i fb_next;
+                    if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
+                    v4f prev[TM];
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) {
+                        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                        // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                        pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                        if (b == 0) {
+                            acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                        } else {
+                            float sc;
+                            if constexpr (SB_UNIFORM) sc = sab[a];
+                            else sc = sa[a] * sb[b - 1];
+                            acc[a][b - 1] += prev[a] * sc;
+                        }
+                    }
+                    if (b + 1 < TN) fb = fb_next;
+                }
 #pragma unroll
                 for (int a = 0; a < TM; ++a) {
-                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-                    // P[n][m] over this 128-wide K block: exact products, FP32 sums
-                    pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
-                    if (b == 0) {
-                        acc[a][TN - 1] += p_carry[a] * s_carry[a];
-                    } else {
-                        float sc;
-                        if constexpr (SB_UNIFORM) sc = sab[a];
-                        else sc = sa[a] * sb[b - 1];
-                        acc[a][b - 1] += prev[a] * sc;
-                    }
+                    p_carry[a] = pr[a];
+                    if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
+                    else s_carry[a] = sa[a] * sb[TN - 1];
                 }
-                if (b + 1 < TN) fb = fb_next;
+                }   // K blocks of the stage
             }
-#pragma unroll
-            for (int a = 0; a < TM; ++a) {
-                p_carry[a] = pr[a];
-                if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
-                else s_carry[a] = sa[a] * sb[TN - 1];
-            }
-            }   // K blocks of the stage
         }
 #pragma unroll
         for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
