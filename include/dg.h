@@ -130,7 +130,7 @@ int dg_get_num_cus(void);
 dg_status dg_init(void);
 
 /*
- * Compile (or load from the cache) the kernel that a later call with these
+ * Compile (or load from the cache) the kernel(s) that a later call with these
  * arguments would use, without launching anything.  kind: 0 dense,
  * 1 contiguous, 2 masked; has_c: 0/1; rows = M (dense/contiguous) or M_max.
  * Needs no GPU: the code object is built for gfx950 and stored in the cache
@@ -142,7 +142,9 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
  * Name of the kernel configuration (tile, waves, LDS stages, split-K, sizes)
  * that a call with these arguments selects on the current device (or for
  * `num_cus` compute units when num_cus > 0), written NUL-terminated into
- * buf[0..len).  Informational; nothing is compiled or launched.
+ * buf[0..len).  A call that launches two kernels over disjoint column ranges
+ * (two tile widths) gets both names joined by '+'.  Informational; nothing is
+ * compiled or launched.
  */
 dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus,
                              char *buf, int len);

@@ -43,12 +43,17 @@ struct Workspace {
     size_t counter_bytes = 0;
 };
 
-// Everything a call needs besides the pointers, computed once per shape.
-struct Plan {
+// One kernel launch of a call.
+struct Segment {
     KernelConfig cfg;
     hipFunction_t fn = nullptr;
     int grid = 0;
     int64_t items = 0;
+};
+// Everything a call needs besides the pointers, computed once per shape: its
+// launches in order (two when the columns are split between tile widths).
+struct Plan {
+    std::vector<Segment> segs;
 };
 
 using PlanKey = std::tuple<int, int, int, int, int, int, int, std::string>;
@@ -156,46 +161,50 @@ dg_status launch(const Problem& p, const void* A, const float* sfa, const void* 
     auto it = st->plans.find(key);
     if (it == st->plans.end()) {
         Plan plan;
-        plan.cfg = select_config(p, cus);
-        void* fptr = nullptr;
-        s = get_function(plan.cfg, &fptr);
-        if (s != DG_OK) return s;
-        plan.fn = static_cast<hipFunction_t>(fptr);
-        plan.items = num_work_items(plan.cfg, p.rows);
-        if (plan.items > INT_MAX) return set_error(DG_ERR_UNSUPPORTED, "too many tiles");
-        int occ = 1;
-        if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, plan.fn, plan.cfg.threads(), 0) != hipSuccess ||
-            occ < 1)
-            occ = 1;
-        plan.grid = (int)std::min<int64_t>(plan.items, (int64_t)cus * occ);
+        for (const KernelConfig& c : select_plan(p, cus)) {
+            Segment seg;
+            seg.cfg = c;
+            void* fptr = nullptr;
+            s = get_function(c, &fptr);
+            if (s != DG_OK) return s;
+            seg.fn = static_cast<hipFunction_t>(fptr);
+            seg.items = num_work_items(c, p.rows);
+            if (seg.items > INT_MAX) return set_error(DG_ERR_UNSUPPORTED, "too many tiles");
+            int occ = 1;
+            if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, seg.fn, c.threads(), 0) != hipSuccess ||
+                occ < 1)
+                occ = 1;
+            seg.grid = (int)std::min<int64_t>(seg.items, (int64_t)cus * occ);
+            plan.segs.push_back(seg);
+        }
         it = st->plans.emplace(key, plan).first;
     }
-    const Plan& plan = it->second;
-    const KernelConfig& cfg = plan.cfg;
-    hipFunction_t f = plan.fn;
-    const int64_t items = plan.items;
-    const int grid = plan.grid;
-    if (items <= 0) return DG_OK;
-
-    LaunchParams lp{};
-    lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
-    lp.M = p.rows;
-    lp.num_tiles = (int)items;
-    if (cfg.splitk > 1) {
-        const int64_t mn = items / cfg.splitk;
-        Workspace* w = nullptr;
-        s = ensure_workspace(*st, stream, (size_t)items * cfg.bm * cfg.bn * sizeof(float),
-                             (size_t)mn * sizeof(uint32_t), &w);
-        if (s != DG_OK) return s;
-        lp.ws = w->partials;
-        lp.counters = w->counters;
+    // Launches of one call run in stream order, so they can share the split-K
+    // workspace (each leaves its arrival counters at zero).
+    for (const Segment& seg : it->second.segs) {
+        const KernelConfig& cfg = seg.cfg;
+        if (seg.items <= 0) continue;
+        LaunchParams lp{};
+        lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
+        lp.M = p.rows;
+        lp.num_tiles = (int)seg.items;
+        if (cfg.splitk > 1) {
+            const int64_t mn = seg.items / cfg.splitk;
+            Workspace* w = nullptr;
+            s = ensure_workspace(*st, stream, (size_t)seg.items * cfg.bm * cfg.bn * sizeof(float),
+                                 (size_t)mn * sizeof(uint32_t), &w);
+            if (s != DG_OK) return s;
+            lp.ws = w->partials;
+            lp.counters = w->counters;
+        }
+        if (env_flag("DG_PRINT_CONFIGS"))
+            std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), seg.grid,
+                         cfg.threads(), (long long)seg.items, cfg.lds_bytes());
+        void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
+                        &lp.num_tiles};
+        hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
+        if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     }
-    if (env_flag("DG_PRINT_CONFIGS"))
-        std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), grid,
-                     cfg.threads(), (long long)items, cfg.lds_bytes());
-    void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M, &lp.num_tiles};
-    hipError_t e = hipModuleLaunchKernel(f, grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
-    if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     return DG_OK;
 }
 
@@ -251,9 +260,12 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
         return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
     Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
-    KernelConfig cfg = select_config(p, num_cus > 0 ? num_cus : 256);
-    std::vector<char> code;
-    return compile_code(cfg, &code);
+    for (const KernelConfig& cfg : select_plan(p, num_cus > 0 ? num_cus : 256)) {
+        std::vector<char> code;
+        dg_status s = compile_code(cfg, &code);
+        if (s != DG_OK) return s;
+    }
+    return DG_OK;
 }
 
 dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus, char* buf,
@@ -271,7 +283,8 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
         cus = effective_cus(*st);
     }
     Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
-    const std::string key = select_config(p, cus).key();
+    std::string key;
+    for (const KernelConfig& c : select_plan(p, cus)) key += (key.empty() ? "" : "+") + c.key();
     std::snprintf(buf, (size_t)len, "%s", key.c_str());
     return DG_OK;
 }

@@ -28,6 +28,11 @@ struct KernelConfig {
                                // 3: as 1, with an extra producer wave for A and no K-loop barrier
     int has_c = 0;
     int n = 0, k = 0, g = 1;
+    int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
+                               // launch two column ranges with different tile widths
+
+    int n_begin() const { return nb; }
+    int n_end() const { return ne > 0 ? ne : n; }
 
     int threads() const { return 64 * (wm * wn + (variant == 3 ? 1 : 0)); }   // variant 3: + producer wave
     int stage_bytes() const {
@@ -53,8 +58,9 @@ struct Problem {
     int has_c;
 };
 
-// Tile heuristics (heuristics.cpp).
-KernelConfig select_config(const Problem& p, int num_cus);
+// Tile heuristics (heuristics.cpp): the launches of one call, in order (one,
+// or two over disjoint column ranges).
+std::vector<KernelConfig> select_plan(const Problem& p, int num_cus);
 // Output tiles times splits, i.e. the launch's work items; for masked the
 // worst case (every row of every group valid).
 int64_t num_work_items(const KernelConfig& c, int rows);

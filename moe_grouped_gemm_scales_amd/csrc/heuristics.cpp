@@ -8,7 +8,8 @@
 // (tile, wave grid, LDS stages, split-K) tuples; the model charges each
 // candidate its wave-quantised MFMA time, its operand traffic and a fixed
 // per-tile cost, and the cheapest one wins.  DG_FORCE_CONFIG
-// ("bm,bn,wm,wn,stages,splitk[,kstep[,variant]]") overrides the choice for tuning sweeps.
+// ("bm,bn,wm,wn,stages,splitk[,kstep[,variant[,nb,ne]]]", launches separated
+// by ';') overrides the choice for tuning sweeps.
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -117,6 +118,8 @@ int unit_per_wave_v1(const KernelConfig& c) {
 // Mirrors the kernel's static_asserts, so a selected config always compiles.
 bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (16 * c.wm) || c.bn % (16 * c.wn)) return false;
+    if (c.ne > 0 && (c.nb < 0 || c.nb % 16 || c.nb >= c.ne || c.ne > p.n)) return false;
+    if (c.splitk < 1 || (c.splitk > 1 && p.kind != kDense)) return false;   // split-K: dense only
     if (c.variant < 0 || c.variant > 3) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
@@ -148,53 +151,89 @@ bool valid(const KernelConfig& c, const Problem& p) {
 // Configurations measured fastest on an MI355X (graph-replayed back-to-back
 // launches, tile/wave/stage/split sweeps) for the shapes of the DeepGEMM
 // launch article's benchmark tables; other shapes go through the model.
+// Consecutive rows of one shape with column ranges [nb, ne) are launched in
+// turn (none at present: 4096 x 7168 as 256 x 256 tiles over [0, 4096) then
+// 256 x 192 over [4096, 7168) fills two whole rounds of 256 CUs instead of
+// 1.75, yet measured the same as 448 tiles of 256 x 256, 459 us each: the
+// part runs at its power limit there, so idle CUs in a partial round are not
+// lost time).
 struct Tuned {
     int kind, rows, n, k, g, has_c;
     int bm, bn, wm, wn, stages, splitk, kstep, variant;
+    int nb, ne;
 };
 const Tuned kTuned[] = {
-    {kDense, 64, 2112, 7168, 1, 0, 64, 64, 1, 4, 4, 7, 1, 2},
-    {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3},
-    {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0},
-    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0},
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0},
-    {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3},
+    {kDense, 64, 2112, 7168, 1, 0, 64, 64, 1, 4, 4, 7, 1, 2, 0, 0},
+    {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3, 0, 0},
+    {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0, 0, 0},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
 };
 
-bool tuned(const Problem& p, int num_cus, KernelConfig* c) {
-    if (num_cus != 256) return false;       // measured on the full 256-CU part
+std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
+    std::vector<KernelConfig> out;
+    if (num_cus != 256) return out;       // measured on the full 256-CU part
     for (const Tuned& t : kTuned) {
         if (t.kind != p.kind || t.n != p.n || t.k != p.k || t.g != p.g || t.has_c != p.has_c) continue;
         if (t.rows >= 0 && t.rows != p.rows) continue;
         if (t.rows < 0 && p.rows < 4096) continue;   // contiguous: any large token count
-        c->bm = t.bm; c->bn = t.bn; c->wm = t.wm; c->wn = t.wn;
-        c->stages = t.stages; c->splitk = t.splitk; c->kstep = t.kstep; c->variant = t.variant;
-        return true;
+        KernelConfig c = base;
+        c.bm = t.bm; c.bn = t.bn; c.wm = t.wm; c.wn = t.wn;
+        c.stages = t.stages; c.splitk = t.splitk; c.kstep = t.kstep; c.variant = t.variant;
+        c.nb = t.nb; c.ne = t.ne;
+        out.push_back(c);
     }
-    return false;
+    return out;
 }
 
-bool parse_forced(KernelConfig* c) {
-    const char* s = std::getenv("DG_FORCE_CONFIG");
-    if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sk, ks = 1, var = 0;
-    int got = std::sscanf(s, "%d,%d,%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk, &ks, &var);
-    if (got < 6) return false;
-    c->bm = bm; c->bn = bn; c->wm = wm; c->wn = wn; c->stages = st; c->splitk = sk; c->kstep = ks;
-    c->variant = var;
-    return true;
+// DG_FORCE_CONFIG="bm,bn,wm,wn,stages,splitk[,kstep[,variant[,nb,ne]]]", or
+// several such launches over column ranges [nb, ne) separated by ';'.
+std::vector<KernelConfig> parse_forced(const KernelConfig& base) {
+    const char* env = std::getenv("DG_FORCE_CONFIG");
+    if (!env || !*env) return {};
+    std::vector<KernelConfig> out;
+    std::string all(env);
+    size_t pos = 0;
+    while (pos <= all.size()) {
+        size_t end = all.find(';', pos);
+        if (end == std::string::npos) end = all.size();
+        const std::string one = all.substr(pos, end - pos);
+        pos = end + 1;
+        int bm, bn, wm, wn, st, sk, ks = 1, var = 0, nb = 0, ne = 0;
+        int got = std::sscanf(one.c_str(), "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &bm, &bn, &wm, &wn, &st, &sk, &ks, &var,
+                              &nb, &ne);
+        if (got < 6 || got == 9) return {};
+        KernelConfig c = base;
+        c.bm = bm; c.bn = bn; c.wm = wm; c.wn = wn; c.stages = st; c.splitk = sk; c.kstep = ks;
+        c.variant = var;
+        c.nb = nb; c.ne = ne;
+        out.push_back(c);
+    }
+    return out;
+}
+
+// The launches cover [0, N) in order, each valid.
+bool valid_plan(const std::vector<KernelConfig>& plan, const Problem& p) {
+    if (plan.empty()) return false;
+    int next = 0;
+    for (const KernelConfig& c : plan) {
+        if (!valid(c, p) || c.n_begin() != next) return false;
+        next = c.n_end();
+    }
+    return next == p.n;
 }
 
 }  // namespace
 
 int64_t num_work_items(const KernelConfig& c, int rows) {
     const int64_t mt = (rows + c.bm - 1) / c.bm;
-    const int64_t nt = (c.n + c.bn - 1) / c.bn;
+    const int64_t nt = (c.n_end() - c.n_begin() + c.bn - 1) / c.bn;
     if (c.kind == kMasked) return mt * nt * c.g;
     return mt * nt * c.splitk;
 }
 
-KernelConfig select_config(const Problem& p, int num_cus) {
+std::vector<KernelConfig> select_plan(const Problem& p, int num_cus) {
     KernelConfig base;
     base.kind = p.kind;
     base.has_c = p.has_c;
@@ -202,13 +241,14 @@ KernelConfig select_config(const Problem& p, int num_cus) {
     base.k = p.k;
     base.g = (p.kind == kDense) ? 1 : p.g;
 
-    KernelConfig forced = base;
-    if (parse_forced(&forced) && valid(forced, p)) return forced;
-    KernelConfig table = base;
-    if (tuned(p, num_cus, &table) && valid(table, p)) {
+    std::vector<KernelConfig> forced = parse_forced(base);
+    if (valid_plan(forced, p)) return forced;
+    std::vector<KernelConfig> table = tuned(p, num_cus, base);
+    if (valid_plan(table, p)) {
         if (env_flag("DG_PRINT_CONFIGS"))
-            std::fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s (measured)\n", p.kind, p.rows, p.n, p.k,
-                         p.g, table.key().c_str());
+            for (const KernelConfig& c : table)
+                std::fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s (measured)\n", p.kind, p.rows, p.n,
+                             p.k, p.g, c.key().c_str());
         return table;
     }
 
@@ -268,7 +308,7 @@ KernelConfig select_config(const Problem& p, int num_cus) {
     if (env_flag("DG_PRINT_CONFIGS"))
         std::fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s (model %.2f us)\n", p.kind, p.rows, p.n,
                      p.k, p.g, best.cfg.key().c_str(), best.seconds * 1e6);
-    return best.cfg;
+    return {best.cfg};
 }
 
 }  // namespace dg

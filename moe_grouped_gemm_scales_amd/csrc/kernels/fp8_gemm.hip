@@ -59,6 +59,14 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 #ifndef DG_VARIANT
 #define DG_VARIANT 0
 #endif
+// Column range of D this kernel computes (a launch may cover part of N, so
+// that one call can use two tile widths and fill whole rounds of the grid)
+#ifndef DG_NB
+#define DG_NB 0
+#endif
+#ifndef DG_NE
+#define DG_NE DG_N
+#endif
 
 namespace dg {
 
@@ -76,10 +84,12 @@ constexpr int N = DG_N, K = DG_K, G = DG_G;
 constexpr int KBLK = 128;
 constexpr int KBLKS = K / KBLK;
 constexpr int NBLKS = (N + KBLK - 1) / KBLK;
-constexpr int NUM_NT = (N + BN - 1) / BN;     // n tiles
+constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D; N is the row pitch
+static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
+constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
 // WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N)
-constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0;
+constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0;
 
 static_assert(K % KBLK == 0, "K must be a multiple of 128");
 static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles must be 16-aligned");
@@ -207,7 +217,7 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         }
         tl.g = g;
         tl.m0 = mb * BM;
-        tl.n0 = nt * BN;
+        tl.n0 = N_BEGIN + nt * BN;
         tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
         tl.row_limit = valid - tl.m0;
         tl.mn = 0;
@@ -238,7 +248,7 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         int mt = first_m + (mn % width) % gsize;
         int nt = (mn % width) / gsize;
         tl.m0 = mt * BM;
-        tl.n0 = nt * BN;
+        tl.n0 = N_BEGIN + nt * BN;
         tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
         tl.row_limit = tl.rows;
         tl.kb0 = tl.split * (KBLKS / SPLITK);
@@ -343,17 +353,17 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
 #pragma unroll
         for (int b = 0; b < TN_; ++b) {
             const int n = tl.n0 + col0 + b * 16;
-            if (n >= N) continue;
+            if (n >= N_END) continue;
             const u64 off = row_base + (u64)r * N + n;
             v4f v = acc[a][b];
-            if constexpr (N % 4 == 0) {
+            if constexpr (N % 4 == 0 && N_END % 4 == 0) {
                 if constexpr (HAS_C) v += *(const v4f*)(p.C + off);
                 v4u16 o = {f32_to_bf16(v.x), f32_to_bf16(v.y), f32_to_bf16(v.z), f32_to_bf16(v.w)};
                 *(v4u16*)(p.D + off) = o;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (n + e < N) {
+                    if (n + e < N_END) {
                         float x = v[e];
                         if constexpr (HAS_C) x += p.C[off + e];
                         p.D[off + e] = f32_to_bf16(x);
@@ -487,7 +497,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             sfa_base = p.sfa;
         }
         a_rows_total = p.M;
-        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
         const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
@@ -944,7 +954,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             a_base = p.A + (u64)tl.m0 * K;
             sfa_base = p.sfa;
         }
-        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
         const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
         const int nb_t0 = tl.n0 / KBLK;
@@ -1259,7 +1269,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             a_base = p.A + (u64)tl.m0 * K;
             sfa_base = p.sfa;
         }
-        const int n_rows = N - tl.n0 < BN ? N - tl.n0 : BN;
+        const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
         const int nb_t0 = tl.n0 / KBLK;
 
         if (producer) {

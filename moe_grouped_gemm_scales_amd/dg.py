@@ -190,7 +190,7 @@ def precompile(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c:
 def describe_config(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,
                     num_cus: int = 0) -> str:
     """Key of the kernel configuration a call with these sizes selects."""
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(1024)
     _check(lib.dg_describe_config(kind, rows, N, K, num_groups, int(has_c), num_cus, buf, len(buf)))
     return buf.value.decode()
 

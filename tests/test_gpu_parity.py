@@ -264,3 +264,32 @@ def test_bdirect_grouped(oracle, monkeypatch, forced):
     D, sent = run(pc)
     ref, comp = oracle_rows(oracle, pc)
     _compare(pc, D, sent, ref, comp, what=f"contiguous {forced}")
+
+
+# ------------------------------------------------------------------ two launches over column ranges
+# (fields 9-10 of a launch: first and end column; launches separated by ';')
+SEGMENTS = [   # (launches, kinds they are valid for)
+    ("128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520", "dense masked contiguous"),
+    ("256,256,4,2,2,1,1,0,0,256;256,192,4,2,2,1,1,0,256,520", "dense masked"),
+    ("64,64,1,4,3,2,1,2,0,128;64,96,1,2,4,1,1,1,128,520", "dense"),
+    ("128,96,1,6,3,1,1,3,0,96;64,112,1,1,2,1,1,0,96,520", "dense masked contiguous"),
+]
+
+
+@pytest.mark.parametrize("forced,kinds", SEGMENTS)
+def test_column_range_plans(oracle, monkeypatch, forced, kinds):
+    import moe_grouped_gemm_scales_amd as dg
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    problems = {
+        "dense": gen.make_dense(300, 520, 1024, seed=12, with_c=True),
+        "masked": gen.make_masked(3, 200, 520, 512, seed=23, with_c=True, masked_m=[200, 0, 77]),
+        "contiguous": gen.make_contiguous([128, 0, 256, 100], 520, 384, seed=24, with_c=True, pad_rows=128),
+    }
+    for kind in kinds.split():
+        p = problems[kind]
+        # the forced launches are the ones used (two column ranges)
+        key = dg.describe_config({"dense": 0, "contiguous": 1, "masked": 2}[kind], p.M, p.N, p.K, p.G, True)
+        assert key.count("_cols") == 2, key
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"{kind} {forced}")
