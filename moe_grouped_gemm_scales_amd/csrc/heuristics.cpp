@@ -135,7 +135,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
         const int nkb = p.k / 128 / c.splitk, pre = std::min(c.stages - 1, nkb);
         if (c.variant == 1 && unit_per_wave_v1(c) * (c.stages - 2) > 63) return false;
         if (c.variant == 2 && (ub * (c.stages - 2) > 63 || ub * pre > 63)) return false;
-        if (c.variant == 3 && (ub * pre > 63 || c.splitk != 1 || c.bm * 128 + 256 > 78 * 1024)) return false;
+        if (c.variant == 3 && (ub * pre > 63 || c.bm * 128 + 256 > 78 * 1024)) return false;
         if (tm < 1 || tn < 1 || tm > 16 || tn > 4 || tm * tn > 32) return false;
         if (c.bm % 8) return false;
         return true;

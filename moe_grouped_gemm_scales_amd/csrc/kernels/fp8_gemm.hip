@@ -1175,8 +1175,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 // which the tests check, and never hang the device.
 static_assert(WM == 1, "variant 3 spreads its consumer waves along n only");
 static_assert(KSTEP == 1, "variant 3 stages one K block per slot");
-static_assert(SPLITK == 1, "variant 3 computes whole K ranges");
-constexpr int NKB = KBLKS;
+constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
 static_assert(NKB <= 64, "the whole K range of a work item is unrolled");
 constexpr int DEPTH = STAGES - 1;                 // K blocks of B requested ahead of use
 constexpr int UB = 2 * TN;                        // B loads per lane per K block
@@ -1326,6 +1325,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 wait_vmcnt<(NKB - 1 - kb) * PU>();
                 publish(kb);
             });
+            // the two workgroup barriers of the split-K hand-off in finish_tile
+            // (the producer holds no partial sums)
+            if constexpr (SPLITK > 1) {
+                __syncthreads();
+                __syncthreads();
+            }
             continue;
         }
 

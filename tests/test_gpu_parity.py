@@ -207,6 +207,8 @@ FORCED = [
     "128,96,1,6,3,1,1,3",
     "64,64,1,4,3,1,1,3",
     "32,48,1,1,2,1,1,3",
+    "64,64,1,4,3,2,1,3",
+    "32,48,1,1,2,4,1,3",
 ]
 
 
@@ -273,6 +275,7 @@ SEGMENTS = [   # (launches, kinds they are valid for)
     ("256,256,4,2,2,1,1,0,0,256;256,192,4,2,2,1,1,0,256,520", "dense masked"),
     ("64,64,1,4,3,2,1,2,0,128;64,96,1,2,4,1,1,1,128,520", "dense"),
     ("128,96,1,6,3,1,1,3,0,96;64,112,1,1,2,1,1,0,96,520", "dense masked contiguous"),
+    ("64,64,1,4,3,4,1,3,0,192;64,64,1,4,3,2,1,3,192,520", "dense"),
 ]
 
 
