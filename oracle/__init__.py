@@ -13,6 +13,9 @@ Semantics and citations are in the header of ``oracle.c``:
 * DeepGEMM launch article, section 2: per-block promotion into a
   higher-precision accumulator.
 * DeepGEMM README, "Grouped GEMM (contiguous layout)" and "(masked layout)".
+* DeepGEMM README, "Interfaces / Notes" (SM100) and the Ascend 950 article:
+  UE8M0 scale factors packed four to a 32-bit word; unpacked here to the FP32
+  scales they stand for (exactly), after which the GEMM is the FP32-scale one.
 """
 from __future__ import annotations
 
@@ -51,6 +54,12 @@ def _declare(lib):
     lib.oracle_e4m3_table.argtypes = [p]
     lib.oracle_bf16_rne.restype = c.c_uint16
     lib.oracle_bf16_rne.argtypes = [c.c_double]
+    lib.oracle_ue8m0_value.restype = c.c_double
+    lib.oracle_ue8m0_value.argtypes = [c.c_uint8]
+    lib.oracle_ue8m0_unpack_mn_major.restype = None
+    lib.oracle_ue8m0_unpack_mn_major.argtypes = [p, c.c_int64, c.c_int, c.c_int64, p]
+    lib.oracle_ue8m0_unpack_k_major.restype = None
+    lib.oracle_ue8m0_unpack_k_major.argtypes = [p, c.c_int64, c.c_int, p]
     lib.oracle_default_threads.restype = c.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_fp8_gemm_nt.restype = c.c_int
@@ -112,6 +121,46 @@ class Oracle:
     def bf16_rne(self, x: np.ndarray) -> np.ndarray:
         x = np.asarray(x, dtype=np.float64).ravel()
         return np.array([self.lib.oracle_bf16_rne(float(v)) for v in x], dtype=np.uint16)
+
+    # ---------------------------------------------------------- UE8M0 scales
+    def ue8m0_value(self, e: int) -> float:
+        return float(self.lib.oracle_ue8m0_value(int(e)))
+
+    def unpack_sfa_ue8m0(self, packed, Kb: int) -> np.ndarray:
+        """[..., ceil(Kb/4), M] int32 -> [..., Kb, M] fp32 (MN-major LHS scales)."""
+        pk = _c(packed, np.int32)
+        *lead, W, M = pk.shape
+        assert W == (Kb + 3) // 4
+        n = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, Kb, M), dtype=np.float32)
+        self.lib.oracle_ue8m0_unpack_mn_major(_ptr(pk), n, Kb, M, _ptr(out))
+        return out
+
+    def unpack_sfb_ue8m0(self, packed, Kb: int) -> np.ndarray:
+        """[..., Nb, ceil(Kb/4)] int32 -> [..., Nb, Kb] fp32 (K-contiguous RHS scales)."""
+        pk = _c(packed, np.int32)
+        *lead, W = pk.shape
+        assert W == (Kb + 3) // 4
+        n = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, Kb), dtype=np.float32)
+        self.lib.oracle_ue8m0_unpack_k_major(_ptr(pk), n, Kb, _ptr(out))
+        return out
+
+    def fp8_gemm_nt_ue8m0(self, A, sfa, B, sfb, C=None, rows=None, threads=0):
+        """Dense form with packed UE8M0 scales sfa [ceil(Kb/4), M], sfb [Nb, ceil(Kb/4)]."""
+        Kb = np.shape(A)[-1] // KBLOCK
+        return self.fp8_gemm_nt(A, self.unpack_sfa_ue8m0(sfa, Kb), B, self.unpack_sfb_ue8m0(sfb, Kb), C, rows,
+                                threads)
+
+    def m_grouped_contiguous_ue8m0(self, A, sfa, B, sfb, m_indices, C=None, rows=None, threads=0):
+        Kb = np.shape(A)[-1] // KBLOCK
+        return self.m_grouped_contiguous(A, self.unpack_sfa_ue8m0(sfa, Kb), B, self.unpack_sfb_ue8m0(sfb, Kb),
+                                         m_indices, C, rows, threads)
+
+    def m_grouped_masked_ue8m0(self, A, sfa, B, sfb, masked_m, C=None, rows=None, threads=0):
+        Kb = np.shape(A)[-1] // KBLOCK
+        return self.m_grouped_masked(A, self.unpack_sfa_ue8m0(sfa, Kb), B, self.unpack_sfb_ue8m0(sfb, Kb),
+                                     masked_m, C, rows, threads)
 
     def fp8_gemm_nt(self, A, sfa, B, sfb, C=None, rows=None, threads=0):
         """D (FP64) of the dense form; A [M,K] u8, sfa [K/128,M], B [N,K] u8, sfb [Nb,Kb]."""

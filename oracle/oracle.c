@@ -73,6 +73,57 @@ void oracle_e4m3_table(double *out256)
 }
 
 /* ------------------------------------------------------------------ */
+/* UE8M0 scale factors (DeepGEMM README, "Interfaces / Notes": on the  */
+/* SM100 path the scale factors are UE8M0, four of them packed into    */
+/* one 32-bit integer; the Ascend 950 article packs them along K).     */
+/* The format is the OCP MX E8M0 one: an unsigned 8-bit exponent e     */
+/* with bias 127, value 2^(e - 127); e = 255 is NaN.  Reading of the   */
+/* packing: byte j (bits 8j..8j+7) of word w holds the scale of K      */
+/* block 4w + j; bytes past the last K block are ignored.              */
+/* Every value 2^-127 .. 2^127 is exact in FP32 (2^-127 as a           */
+/* subnormal), so unpacking to FP32 scales loses nothing and the GEMM  */
+/* is then the FP32-scale one.                                         */
+/* ------------------------------------------------------------------ */
+double oracle_ue8m0_value(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+static uint8_t ue8m0_byte(int32_t word, int j)
+{
+    return (uint8_t)(((uint32_t)word >> (8 * j)) & 0xFFu);
+}
+
+/*
+ * LHS layout (MN-major, like the FP32 sfa): packed [n_mats][ceil(Kb/4)][M] ->
+ * out [n_mats][Kb][M] FP32.
+ */
+void oracle_ue8m0_unpack_mn_major(const int32_t *packed, int64_t n_mats, int Kb, int64_t M, float *out)
+{
+    const int W = (Kb + 3) / 4;
+    for (int64_t g = 0; g < n_mats; ++g)
+        for (int kb = 0; kb < Kb; ++kb)
+            for (int64_t m = 0; m < M; ++m) {
+                int32_t w = packed[(g * W + kb / 4) * M + m];
+                out[(g * Kb + kb) * M + m] = (float)oracle_ue8m0_value(ue8m0_byte(w, kb % 4));
+            }
+}
+
+/*
+ * RHS layout (K-contiguous, like the FP32 sfb): packed [n_rows][ceil(Kb/4)] ->
+ * out [n_rows][Kb] FP32, where n_rows counts 128-row blocks of B (times groups).
+ */
+void oracle_ue8m0_unpack_k_major(const int32_t *packed, int64_t n_rows, int Kb, float *out)
+{
+    const int W = (Kb + 3) / 4;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int kb = 0; kb < Kb; ++kb)
+            out[r * Kb + kb] = (float)oracle_ue8m0_value(ue8m0_byte(packed[r * W + kb / 4], kb % 4));
+}
+
+/* ------------------------------------------------------------------ */
 /* BF16 (1 sign, 8 exponent bits with bias 127, 7 mantissa bits),     */
 /* round-to-nearest, ties-to-even, straight from a double.  The        */
 /* outputs of all three operations are BF16.                           */

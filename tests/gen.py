@@ -14,6 +14,13 @@ on the input side:
 * scale = amax/448 in FP32 (1.0 for an all-zero block), code =
   E4M3FN(clamp(x/scale, -448, 448)), rounded to nearest-even by torch's cast.
 
+UE8M0 scales (DeepGEMM README, "Interfaces / Notes": SM100 takes UE8M0 scale
+factors, four packed into one 32-bit integer): the block scale is rounded up to
+a power of two, s = 2^ceil(log2(amax/448)) (so |x/s| <= 448 still holds), and
+its biased exponent e = 127 + log2(s) is stored as one byte; byte j of a word
+holds K block 4w + j (unused bytes hold 127).  LHS words are MN-major,
+``sfa[ceil(K/512)][M]``; RHS words ``sfb[ceil(N/128)][ceil(K/512)]``.
+
 Workload recipe (sizes from the DeepGEMM launch article, section 3 tables):
 values ~N(0,1) from ``torch.Generator('cpu')`` seeded with ``1000 + config``,
 drawn in the order A, B, C, masked_m.
@@ -35,19 +42,44 @@ def _cast_e4m3(x: torch.Tensor) -> torch.Tensor:
     return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def quantize_1x128(x: torch.Tensor):
-    """x [..., M, K] fp32 -> (codes u8 [..., M, K], sfa fp32 [..., K/128, M])."""
+def _block_scale(amax: torch.Tensor, ue8m0: bool):
+    """(scale fp32, biased exponent int32 or None) of blocks with the given amax."""
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    if not ue8m0:
+        return s, None
+    m, e = torch.frexp(s)                      # s = m * 2^e, m in [0.5, 1)
+    e = (e - (m == 0.5).to(e.dtype)).to(torch.int32)   # ceil(log2 s)
+    return torch.ldexp(torch.ones_like(s), e), e + 127
+
+
+def pack_ue8m0(e: torch.Tensor) -> torch.Tensor:
+    """[..., Kb] biased exponents -> [..., ceil(Kb/4)] int32, byte j = K block 4w + j."""
+    *lead, Kb = e.shape
+    W = (Kb + 3) // 4
+    pad = torch.full((*lead, 4 * W - Kb), 127, dtype=torch.int64)
+    b = torch.cat([e.to(torch.int64), pad], dim=-1).reshape(*lead, W, 4)
+    w = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    return w.to(torch.uint32).view(torch.int32) if hasattr(torch, "uint32") else \
+        torch.where(w >= 2**31, w - 2**32, w).to(torch.int32)
+
+
+def quantize_1x128(x: torch.Tensor, ue8m0: bool = False):
+    """x [..., M, K] fp32 -> (codes u8 [..., M, K], sfa [..., K/128, M] fp32, or
+    [..., ceil(K/512), M] int32 packed UE8M0)."""
     *lead, M, K = x.shape
     assert K % KBLOCK == 0
     xb = x.reshape(*lead, M, K // KBLOCK, KBLOCK)
     amax = xb.abs().amax(dim=-1)
-    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    s, e = _block_scale(amax, ue8m0)
     q = _cast_e4m3(xb / s.unsqueeze(-1)).reshape(*lead, M, K)
+    if ue8m0:
+        return q.contiguous(), pack_ue8m0(e).transpose(-1, -2).contiguous()
     return q.contiguous(), s.transpose(-1, -2).contiguous()
 
 
-def quantize_128x128(x: torch.Tensor):
-    """x [..., N, K] fp32 -> (codes u8 [..., N, K], sfb fp32 [..., ceil(N/128), K/128])."""
+def quantize_128x128(x: torch.Tensor, ue8m0: bool = False):
+    """x [..., N, K] fp32 -> (codes u8 [..., N, K], sfb [..., ceil(N/128), K/128] fp32,
+    or [..., ceil(N/128), ceil(K/512)] int32 packed UE8M0)."""
     *lead, N, K = x.shape
     assert K % KBLOCK == 0
     Nb = (N + KBLOCK - 1) // KBLOCK
@@ -55,8 +87,10 @@ def quantize_128x128(x: torch.Tensor):
     xp = torch.nn.functional.pad(x, (0, 0, 0, pad)) if pad else x
     xb = xp.reshape(*lead, Nb, KBLOCK, K // KBLOCK, KBLOCK)
     amax = xb.abs().amax(dim=(-3, -1))
-    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    s, e = _block_scale(amax, ue8m0)
     q = _cast_e4m3(xb / s[..., :, None, :, None]).reshape(*lead, Nb * KBLOCK, K)
+    if ue8m0:
+        return q[..., :N, :].contiguous(), pack_ue8m0(e).contiguous()
     return q[..., :N, :].contiguous(), s.contiguous()
 
 
@@ -72,6 +106,7 @@ class Problem:
     m_indices: Optional[torch.Tensor] = None   # int32 [M] (contiguous)
     masked_m: Optional[torch.Tensor] = None    # int32 [G] (masked)
     seed: int = 0
+    ue8m0: bool = False             # sfa/sfb are packed UE8M0 int32 words
 
     @property
     def M(self):
@@ -96,19 +131,19 @@ def _gen(seed):
     return g
 
 
-def make_dense(M, N, K, seed, with_c=False) -> Problem:
+def make_dense(M, N, K, seed, with_c=False, ue8m0=False) -> Problem:
     g = _gen(seed)
     a = torch.randn(M, K, generator=g, dtype=torch.float32)
     b = torch.randn(N, K, generator=g, dtype=torch.float32)
     c = torch.randn(M, N, generator=g, dtype=torch.float32) if with_c else None
-    A, sfa = quantize_1x128(a)
+    A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b)
+    B, sfb = quantize_128x128(b, ue8m0)
     del b
-    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed)
+    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed, ue8m0=ue8m0)
 
 
-def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128) -> Problem:
+def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128, ue8m0=False) -> Problem:
     """Experts' tokens concatenated along M, each segment padded to ``align`` rows.
 
     group_rows[g] valid rows for expert g; padding rows get index -1.  With
@@ -126,14 +161,14 @@ def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=1
     for e, (r, s) in enumerate(zip(group_rows, seg)):
         idx[off:off + r] = e
         off += s
-    A, sfa = quantize_1x128(a)
+    A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b)
+    B, sfb = quantize_128x128(b, ue8m0)
     del b
-    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed)
+    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed, ue8m0=ue8m0)
 
 
-def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None) -> Problem:
+def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False) -> Problem:
     g = _gen(seed)
     a = torch.randn(G, M_max, K, generator=g, dtype=torch.float32)
     b = torch.randn(G, N, K, generator=g, dtype=torch.float32)
@@ -142,11 +177,11 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None) -> Problem:
         mm = torch.randint(0, M_max + 1, (G,), generator=g, dtype=torch.int32)
     else:
         mm = torch.as_tensor(masked_m, dtype=torch.int32)
-    A, sfa = quantize_1x128(a)
+    A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b)
+    B, sfb = quantize_128x128(b, ue8m0)
     del b
-    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed)
+    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0)
 
 
 # ---------------------------------------------------------------- the five workloads
@@ -174,14 +209,14 @@ def workload_seed(cfg) -> int:
     return 1000 + (1 if cfg == "1c" else int(cfg))
 
 
-def make_workload(cfg) -> Problem:
+def make_workload(cfg, ue8m0=False) -> Problem:
     c = WORKLOADS[cfg]
     seed = workload_seed(cfg)
     if c["kind"] == "dense":
-        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False))
+        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False), ue8m0=ue8m0)
     if c["kind"] == "contiguous":
-        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed)
-    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed)
+        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed, ue8m0=ue8m0)
+    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed, ue8m0=ue8m0)
 
 
 # ---------------------------------------------------------------- structured inputs for pins

@@ -274,3 +274,71 @@ def test_masked_negative_and_subset(oracle):
     ds, cs = oracle.m_grouped_masked(npd["A"], npd["sfa"], npd["B"], npd["sfb"], npd["masked_m"], rows=rows)
     assert np.array_equal(cs, comp[rows])
     assert np.array_equal(ds[cs], d[rows][cs])
+
+
+# ------------------------------------------------------------------ UE8M0 scales
+def test_ue8m0_points_from_format(oracle):
+    """Decode of single E8M0 bytes against values fixed by the OCP MX definition."""
+    pts = json.load(open(os.path.join(GOLDEN, "ue8m0_points.json")))["points"]
+    for code, val in pts.items():
+        got = oracle.ue8m0_value(int(code, 16))
+        if val == "nan":
+            assert np.isnan(got), code
+        else:
+            assert got == float(val), (code, got, val)
+    # monotone, each step exactly doubles (no gaps or repeats in 0..254)
+    vals = np.array([oracle.ue8m0_value(e) for e in range(255)])
+    assert np.all(vals[1:] == 2.0 * vals[:-1])
+
+
+def test_ue8m0_packing_byte_order_and_layouts(oracle):
+    """Byte j of a word is K block 4w + j; LHS words [W][M] (MN-major), RHS [Nb][W]."""
+    Kb, M = 6, 3
+    e = np.array([[120 + kb + 10 * m for m in range(M)] for kb in range(Kb)])   # [Kb][M]
+    words = np.zeros((2, M), dtype=np.int64)
+    for kb in range(Kb):
+        words[kb // 4] |= e[kb] << (8 * (kb % 4))
+    words[1] |= (77 << 16) | (78 << 24)                 # bytes past the last K block: ignored
+    sfa = oracle.unpack_sfa_ue8m0(words.astype(np.uint32).view(np.int32), Kb)
+    assert sfa.shape == (Kb, M)
+    assert np.array_equal(sfa, np.ldexp(1.0, e - 127).astype(np.float32))
+    sfb = oracle.unpack_sfb_ue8m0(words.T.copy().astype(np.uint32).view(np.int32), Kb)   # [M as Nb][W]
+    assert np.array_equal(sfb, np.ldexp(1.0, e.T - 127).astype(np.float32))
+    # grouped leading dimension
+    g2 = np.stack([words, words + 1]).astype(np.uint32).view(np.int32)
+    u = oracle.unpack_sfa_ue8m0(g2, Kb)
+    assert u.shape == (2, Kb, M) and np.array_equal(u[0], sfa)
+    assert np.array_equal(u[1, 0], np.ldexp(1.0, e[0] + 1 - 127).astype(np.float32))
+
+
+def test_ue8m0_all_ones_closed_form(oracle):
+    """All-ones codes: D[m,n] = 128 * sum_kb 2^(ea[kb,m]-127) * 2^(eb[n/128,kb]-127) + C, exactly."""
+    g = torch.Generator().manual_seed(8)
+    M, N, K = 7, 300, 896
+    Kb, Nb = K // 128, (N + 127) // 128
+    ea = torch.randint(120, 135, (Kb, M), generator=g)
+    eb = torch.randint(118, 131, (Nb, Kb), generator=g)
+    sfa = gen.pack_ue8m0(ea.T).T.contiguous()               # [W][M]
+    sfb = gen.pack_ue8m0(eb)                                # [Nb][W]
+    A = torch.full((M, K), gen.E4M3_ONE, dtype=torch.uint8)
+    B = torch.full((N, K), gen.E4M3_ONE, dtype=torch.uint8)
+    C = torch.randn(M, N, generator=g)
+    d = oracle.fp8_gemm_nt_ue8m0(A.numpy(), sfa.numpy(), B.numpy(), sfb.numpy(), C.numpy())
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            want[m, n] = 128.0 * sum(2.0 ** (int(ea[kb, m]) - 127) * 2.0 ** (int(eb[n // 128, kb]) - 127)
+                                     for kb in range(Kb)) + float(C[m, n])
+    assert np.array_equal(d, want)
+
+
+def test_ue8m0_generator_scales(oracle):
+    """The UE8M0 quantiser picks the least power of two >= amax/448 and keeps codes in range."""
+    p = gen.make_dense(33, 260, 768, seed=41, ue8m0=True)
+    x = torch.randn(33, 768, generator=gen._gen(41))
+    sfa = oracle.unpack_sfa_ue8m0(p.sfa.numpy(), 6)                  # [Kb][M]
+    amax = x.reshape(33, 6, 128).abs().amax(-1).numpy().T / 448.0    # [Kb][M]
+    assert np.all(sfa >= amax) and np.all(sfa < 2 * amax)
+    assert np.all(np.log2(sfa) == np.round(np.log2(sfa)))
+    dec = torch_decode_table()
+    assert np.all(np.abs(dec[p.A.numpy()]) <= 448.0)

@@ -31,6 +31,11 @@ MUTANTS = [
     ("masked_off_by_one", "if (m >= valid) {", "if (m > valid) {"),
     ("bf16_ties_up", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     ("scale_squared", "acc += scale * s;", "acc += scale * scale * s;"),
+    ("ue8m0_bias_128", "return ldexp(1.0, (int)e - 127);", "return ldexp(1.0, (int)e - 128);"),
+    ("ue8m0_big_endian", "return (uint8_t)(((uint32_t)word >> (8 * j)) & 0xFFu);",
+     "return (uint8_t)(((uint32_t)word >> (8 * (3 - j))) & 0xFFu);"),
+    ("ue8m0_sfa_k_major", "int32_t w = packed[(g * W + kb / 4) * M + m];",
+     "int32_t w = packed[(g * M + m) * W + kb / 4];"),
 ]
 
 
@@ -46,7 +51,9 @@ def _pin_calls(o):
               pins.test_rows_subset_equals_full, pins.test_c_is_added,
               pins.test_contiguous_segments_equal_dense,
               pins.test_contiguous_group_independence_and_permutation,
-              pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset):
+              pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset,
+              pins.test_ue8m0_points_from_format, pins.test_ue8m0_packing_byte_order_and_layouts,
+              pins.test_ue8m0_all_ones_closed_form):
         calls.append(lambda f=f: f(o))
     return calls
 
