@@ -49,6 +49,8 @@ def algorithmic(p) -> tuple[float, float, int]:
     """(FLOPs, bytes, computed rows) of one call, by the pages' convention."""
     K, N = p.K, p.N
     Kb, Nb = K // 128, (N + 127) // 128
+    if p.ue8m0:
+        Kb = (Kb + 3) // 4          # one packed 4-byte word per four K blocks
     if p.kind == "dense":
         rows, groups_used = p.M, 1
     elif p.kind == "contiguous":
@@ -71,14 +73,14 @@ def kind_id(kind: str) -> int:
     return {"dense": 0, "contiguous": 1, "masked": 2}[kind]
 
 
-def bench_workload(cfg, steps: int, warmup: int, graph: bool):
+def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False):
     import torch
 
     import moe_grouped_gemm_scales_amd as dg
     from tests import gen
     from tests.gpu_util import out_shape, to_dev
 
-    p = gen.make_workload(cfg)
+    p = gen.make_workload(cfg, ue8m0=ue8m0)
     flops, nbytes, rows = algorithmic(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
     ws += math.prod(out_shape(p)) * 2
@@ -96,7 +98,8 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool):
             dg.dg_m_grouped_fp8_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"], D)
 
     rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
-    kernel = dg.describe_config(kind_id(p.kind), rows_arg, p.N, p.K, p.G, p.C is not None)
+    kernel = dg.describe_config(kind_id(p.kind) | (dg.SCALE_UE8M0 if ue8m0 else 0), rows_arg, p.N, p.K, p.G,
+                                p.C is not None)
     # everything runs on one non-default stream (HIP graphs cannot capture the null stream)
     stream = torch.cuda.Stream()
     start = torch.cuda.Event(enable_timing=True)
@@ -204,7 +207,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="1", help="0, 1, 1c, 2, 3 or 4 (default 1)")
-    ap.add_argument("--all", action="store_true", help="also run every workload, one stderr line each")
+    ap.add_argument("--all", action="store_true",
+                    help="also run every workload, one stderr line each (FP32 scales, then packed UE8M0 scales)")
+    ap.add_argument("--ue8m0", action="store_true",
+                    help="time the chosen workload with packed UE8M0 scales instead of FP32 ones")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--copy-kernel", action="store_true",
@@ -239,10 +245,11 @@ def main():
     cfg = args.workload if args.workload == "1c" else int(args.workload)
     per_shape = []
     if args.all:
-        for c in [0, 1, "1c", 2, 3, 4]:
+        for c, e8 in [(c, False) for c in [0, 1, "1c", 2, 3, 4]] + [(c, True) for c in [0, 1, 2, 3, 4]]:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
-            r = bench_workload(c, steps, min(args.warmup, steps), not args.eager)
-            line = dict(workload=gen.WORKLOAD_NAMES[c], kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
+            r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=e8)
+            wl = gen.WORKLOAD_NAMES[c] + ("_ue8m0" if e8 else "")
+            line = dict(workload=wl, kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
                         roofline_frac=round(r["frac"], 4), step_us=round(r["ms_per_step"] * 1e3, 3),
                         rows=r["rows"], copies=r["copies"])
@@ -251,18 +258,18 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    r = bench_workload(cfg, args.steps, args.warmup, not args.eager)
+    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0)
     p = r["problem"]
-    name = gen.WORKLOAD_NAMES[cfg]
+    name = gen.WORKLOAD_NAMES[cfg] + ("_ue8m0" if args.ue8m0 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    cpu = None if (args.no_cpu_baseline or args.ue8m0) else cpu_baseline(cfg)
     value = r["step_tflops"]
-    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) else None
+    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not args.ue8m0 else None
     out = {
         "metric": METRIC,
         "value": round(value, 3),

@@ -104,6 +104,32 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void *A, const float *sfa, const
                                           const float *C, void *D, int M_max, int N, int K,
                                           int num_groups, void *stream);
 
+/*
+ * The same three forms with packed UE8M0 scale factors (DeepGEMM README,
+ * "Interfaces / Notes": on the SM100 path the scale factors are UE8M0, four
+ * of them packed into one 32-bit integer; the Ascend 950 article packs them
+ * along K as well).  A UE8M0 byte e stands for the scale 2^(e - 127) (OCP MX
+ * E8M0; e = 255 is NaN).  Reading of the packing: byte j (bits 8j..8j+7) of a
+ * word holds the scale of K block 4w + j; bytes past the last K block are
+ * ignored.  With W = ceil(K/512):
+ *   sfa int32 [W][M] (masked: [G][W][M_max]), MN-major like the FP32 sfa;
+ *   sfb int32 [Nb][W] (grouped: [G][Nb][W]), K-contiguous like the FP32 sfb.
+ * Block sizes, layouts of A, B, C, D, the group and mask rules, ownership and
+ * errors are those of the FP32-scale entry points above; the result is
+ * D = C + sum_kb 2^(ea-127) 2^(eb-127) P_kb, rounded once to BF16.  On gfx950
+ * the MFMA applies these scales itself, so no promotion step is needed.
+ */
+dg_status dg_fp8_gemm_nt_ue8m0(const void *A, const int32_t *sfa, const void *B, const int32_t *sfb,
+                               const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void *A, const int32_t *sfa, const void *B,
+                                                    const int32_t *sfb, const int32_t *m_indices,
+                                                    const float *C, void *D, int M, int N, int K,
+                                                    int num_groups, void *stream);
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *A, const int32_t *sfa, const void *B,
+                                                const int32_t *sfb, const int32_t *masked_m,
+                                                const float *C, void *D, int M_max, int N, int K,
+                                                int num_groups, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);
 
@@ -129,10 +155,14 @@ int dg_get_num_cus(void);
  */
 dg_status dg_init(void);
 
+/* Flag OR-ed into `kind` below for the packed-UE8M0 entry points. */
+#define DG_SCALE_UE8M0 4
+
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these
  * arguments would use, without launching anything.  kind: 0 dense,
- * 1 contiguous, 2 masked; has_c: 0/1; rows = M (dense/contiguous) or M_max.
+ * 1 contiguous, 2 masked (| DG_SCALE_UE8M0 for packed UE8M0 scales); has_c:
+ * 0/1; rows = M (dense/contiguous) or M_max.
  * Needs no GPU: the code object is built for gfx950 and stored in the cache
  * directory (DG_CACHE_DIR, else <library dir>/jit_cache).
  */

@@ -4,4 +4,5 @@ thin Python binding.  See include/dg.h for the contract."""
 from .dg import (DGError, describe_config, dg_fp8_gemm_nt, dg_m_grouped_fp8_gemm_nt_contiguous,  # noqa: F401
                  dg_m_grouped_fp8_gemm_nt_masked, fp8_gemm_nt, get_mk_alignment_for_contiguous_layout,
                  get_num_cus, init, m_grouped_fp8_gemm_nt_contiguous, m_grouped_fp8_gemm_nt_masked,
-                 precompile, set_num_cus)
+                 precompile, set_num_cus, SCALE_UE8M0, dg_fp8_gemm_nt_ue8m0,
+                 dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0, dg_m_grouped_fp8_gemm_nt_masked_ue8m0)

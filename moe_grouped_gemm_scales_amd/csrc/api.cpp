@@ -24,9 +24,9 @@ thread_local std::string t_last_error;
 // The kernel's arguments, in order.
 struct LaunchParams {
     const void* A;
-    const float* sfa;
+    const void* sfa;
     const void* B;
-    const float* sfb;
+    const void* sfb;
     const float* C;
     void* D;
     const int32_t* grp;
@@ -56,7 +56,7 @@ struct Plan {
     std::vector<Segment> segs;
 };
 
-using PlanKey = std::tuple<int, int, int, int, int, int, int, std::string>;
+using PlanKey = std::tuple<int, int, int, int, int, int, int, int, std::string>;
 
 struct DeviceState {
     int num_cus = 0;
@@ -132,7 +132,7 @@ dg_status ensure_workspace(DeviceState& st, hipStream_t stream, size_t partial_b
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-dg_status check_common(const void* A, const float* sfa, const void* B, const float* sfb, const float* C,
+dg_status check_common(const void* A, const void* sfa, const void* B, const void* sfb, const float* C,
                        const void* D, int rows, int N, int K) {
     if (!A || !sfa || !B || !sfb || !D) return set_error(DG_ERR_INVALID_ARG, "A, sfa, B, sfb and D must be non-NULL");
     if (rows < 0 || N <= 0 || K <= 0)
@@ -147,7 +147,7 @@ dg_status check_common(const void* A, const float* sfa, const void* B, const flo
     return DG_OK;
 }
 
-dg_status launch(const Problem& p, const void* A, const float* sfa, const void* B, const float* sfb,
+dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B, const void* sfb,
                  const int32_t* grp, const float* C, void* D, void* stream_ptr) {
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     std::lock_guard<std::mutex> lock(g_mu);
@@ -157,7 +157,7 @@ dg_status launch(const Problem& p, const void* A, const float* sfa, const void* 
     if (s != DG_OK) return s;
     const int cus = effective_cus(*st);
     const char* forced = std::getenv("DG_FORCE_CONFIG");
-    PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, cus, forced ? forced : ""};
+    PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, p.sf, cus, forced ? forced : ""};
     auto it = st->plans.find(key);
     if (it == st->plans.end()) {
         Plan plan;
@@ -225,6 +225,47 @@ bool env_flag(const char* name) {
 
 using namespace dg;
 
+namespace {
+
+// The three forms, for either scale format (sf: 0 FP32, 1 packed UE8M0; the
+// scale pointers are only passed through to the kernel).
+dg_status dense(const void* A, const void* sfa, const void* B, const void* sfb, const float* C, void* D, int M,
+                int N, int K, int sf, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (M == 0) return DG_OK;
+    Problem p{kDense, M, N, K, 1, C ? 1 : 0, sf};
+    return launch(p, A, sfa, B, sfb, nullptr, C, D, stream);
+}
+
+dg_status contiguous(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* m_indices,
+                     const float* C, void* D, int M, int N, int K, int num_groups, int sf, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (!m_indices) return set_error(DG_ERR_INVALID_ARG, "m_indices must be non-NULL");
+    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+    if (!aligned(m_indices, 4)) return set_error(DG_ERR_ALIGNMENT, "m_indices must be 4-byte aligned");
+    if (M % dg_get_mk_alignment_for_contiguous_layout() != 0)
+        return set_error(DG_ERR_ALIGNMENT, "contiguous M must be a multiple of the M alignment (128)");
+    if (M == 0) return DG_OK;
+    Problem p{kContiguous, M, N, K, num_groups, C ? 1 : 0, sf};
+    return launch(p, A, sfa, B, sfb, m_indices, C, D, stream);
+}
+
+dg_status masked(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* masked_m,
+                 const float* C, void* D, int M_max, int N, int K, int num_groups, int sf, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M_max, N, K);
+    if (s != DG_OK) return s;
+    if (!masked_m) return set_error(DG_ERR_INVALID_ARG, "masked_m must be non-NULL");
+    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+    if (!aligned(masked_m, 4)) return set_error(DG_ERR_ALIGNMENT, "masked_m must be 4-byte aligned");
+    if (M_max == 0) return DG_OK;
+    Problem p{kMasked, M_max, N, K, num_groups, C ? 1 : 0, sf};
+    return launch(p, A, sfa, B, sfb, masked_m, C, D, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* dg_last_error(void) { return t_last_error.c_str(); }
@@ -256,10 +297,12 @@ dg_status dg_init(void) {
 }
 
 dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus) {
+    const int sf = (kind & DG_SCALE_UE8M0) ? 1 : 0;
+    kind &= ~DG_SCALE_UE8M0;
     if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
-    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
+    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
     for (const KernelConfig& cfg : select_plan(p, num_cus > 0 ? num_cus : 256)) {
         std::vector<char> code;
         dg_status s = compile_code(cfg, &code);
@@ -270,6 +313,8 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
 
 dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus, char* buf,
                              int len) {
+    const int sf = (kind & DG_SCALE_UE8M0) ? 1 : 0;
+    kind &= ~DG_SCALE_UE8M0;
     if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_describe_config: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
@@ -282,7 +327,7 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
         if (s != DG_OK) return s;
         cus = effective_cus(*st);
     }
-    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0};
+    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
     std::string key;
     for (const KernelConfig& c : select_plan(p, cus)) key += (key.empty() ? "" : "+") + c.key();
     std::snprintf(buf, (size_t)len, "%s", key.c_str());
@@ -291,39 +336,36 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
 
 dg_status dg_fp8_gemm_nt(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
                          int M, int N, int K, void* stream) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
-    if (s != DG_OK) return s;
-    if (M == 0) return DG_OK;
-    Problem p{kDense, M, N, K, 1, C ? 1 : 0};
-    return launch(p, A, sfa, B, sfb, nullptr, C, D, stream);
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 0, stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const float* sfa, const void* B, const float* sfb,
                                               const int32_t* m_indices, const float* C, void* D, int M, int N, int K,
                                               int num_groups, void* stream) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
-    if (s != DG_OK) return s;
-    if (!m_indices) return set_error(DG_ERR_INVALID_ARG, "m_indices must be non-NULL");
-    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
-    if (!aligned(m_indices, 4)) return set_error(DG_ERR_ALIGNMENT, "m_indices must be 4-byte aligned");
-    if (M % dg_get_mk_alignment_for_contiguous_layout() != 0)
-        return set_error(DG_ERR_ALIGNMENT, "contiguous M must be a multiple of the M alignment (128)");
-    if (M == 0) return DG_OK;
-    Problem p{kContiguous, M, N, K, num_groups, C ? 1 : 0};
-    return launch(p, A, sfa, B, sfb, m_indices, C, D, stream);
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 0, stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const float* sfa, const void* B, const float* sfb,
                                           const int32_t* masked_m, const float* C, void* D, int M_max, int N, int K,
                                           int num_groups, void* stream) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M_max, N, K);
-    if (s != DG_OK) return s;
-    if (!masked_m) return set_error(DG_ERR_INVALID_ARG, "masked_m must be non-NULL");
-    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
-    if (!aligned(masked_m, 4)) return set_error(DG_ERR_ALIGNMENT, "masked_m must be 4-byte aligned");
-    if (M_max == 0) return DG_OK;
-    Problem p{kMasked, M_max, N, K, num_groups, C ? 1 : 0};
-    return launch(p, A, sfa, B, sfb, masked_m, C, D, stream);
+    return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 0, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0(const void* A, const int32_t* sfa, const void* B, const int32_t* sfb, const float* C,
+                               void* D, int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 1, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* A, const int32_t* sfa, const void* B,
+                                                    const int32_t* sfb, const int32_t* m_indices, const float* C,
+                                                    void* D, int M, int N, int K, int num_groups, void* stream) {
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 1, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const int32_t* sfa, const void* B,
+                                                const int32_t* sfb, const int32_t* masked_m, const float* C,
+                                                void* D, int M_max, int N, int K, int num_groups, void* stream) {
+    return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 1, stream);
 }
 
 }  // extern "C"

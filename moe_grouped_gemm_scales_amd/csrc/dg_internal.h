@@ -28,6 +28,7 @@ struct KernelConfig {
                                // 3: as 1, with an extra producer wave for A and no K-loop barrier
     int has_c = 0;
     int n = 0, k = 0, g = 1;
+    int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0
     int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
                                // launch two column ranges with different tile widths
 
@@ -56,6 +57,7 @@ struct Problem {
     int rows;      // M (dense, contiguous) or M_max (masked)
     int n, k, g;
     int has_c;
+    int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0
 };
 
 // Tile heuristics (heuristics.cpp): the launches of one call, in order (one,

@@ -11,6 +11,7 @@
 // ("bm,bn,wm,wn,stages,splitk[,kstep[,variant[,nb,ne]]]", launches separated
 // by ';') overrides the choice for tuning sweeps.
 #include <algorithm>
+#include <iterator>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -120,6 +121,8 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (16 * c.wm) || c.bn % (16 * c.wn)) return false;
     if (c.ne > 0 && (c.nb < 0 || c.nb % 16 || c.nb >= c.ne || c.ne > p.n)) return false;
     if (c.splitk < 1 || (c.splitk > 1 && p.kind != kDense)) return false;   // split-K: dense only
+    if (c.sf != p.sf) return false;
+    if (c.sf && (c.variant != 0 || c.kstep != 1)) return false;   // UE8M0: variant 0, one K block a stage
     if (c.variant < 0 || c.variant > 3) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
@@ -171,10 +174,18 @@ const Tuned kTuned[] = {
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
 };
 
+// Packed UE8M0 scales (variant 0 only; no promotion in the K loop)
+const Tuned kTunedE8[] = {
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+};
+
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
     std::vector<KernelConfig> out;
     if (num_cus != 256) return out;       // measured on the full 256-CU part
-    for (const Tuned& t : kTuned) {
+    const Tuned* first = p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
+    const Tuned* last = p.sf ? std::end(kTunedE8) : std::end(kTuned);
+    for (const Tuned* it = first; it != last; ++it) {
+        const Tuned& t = *it;
         if (t.kind != p.kind || t.n != p.n || t.k != p.k || t.g != p.g || t.has_c != p.has_c) continue;
         if (t.rows >= 0 && t.rows != p.rows) continue;
         if (t.rows < 0 && p.rows < 4096) continue;   // contiguous: any large token count
@@ -237,6 +248,7 @@ std::vector<KernelConfig> select_plan(const Problem& p, int num_cus) {
     KernelConfig base;
     base.kind = p.kind;
     base.has_c = p.has_c;
+    base.sf = p.sf;
     base.n = p.n;
     base.k = p.k;
     base.g = (p.kind == kDense) ? 1 : p.g;
@@ -286,7 +298,7 @@ std::vector<KernelConfig> select_plan(const Problem& p, int num_cus) {
                     if (!tiny) continue;
                 }
                 for (int sk = 1; sk <= 16; ++sk) {
-                  for (int ks = 1; ks <= 2; ++ks) {
+                  for (int ks = 1; ks <= (p.sf ? 1 : 2); ++ks) {
                     if (sk > 1 && (p.kind != kDense || kb % sk || kb / sk < 2)) continue;
                     if (sk > 1 && out_tiles_128 * 2 >= num_cus) continue;
                     if (sk > 1 && bm * bn < 64 * 128) continue;   // small split tiles measured slow

@@ -65,6 +65,7 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     def("DG_K", c.k);
     def("DG_G", c.g);
     def("DG_VARIANT", c.variant);
+    def("DG_SF", c.sf);
     if (c.ne > 0) {
         def("DG_NB", c.nb);
         def("DG_NE", c.ne);
@@ -181,6 +182,7 @@ std::string KernelConfig::key() const {
     s << "k" << kind << (variant ? "v" + std::to_string(variant) : std::string()) << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
       << "_sk" << splitk
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
+    if (sf) s << "_e8m0";
     if (ne > 0) s << "_cols" << nb << "-" << ne;
     return s.str();
 }

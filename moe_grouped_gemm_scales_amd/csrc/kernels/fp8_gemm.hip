@@ -59,6 +59,14 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 #ifndef DG_VARIANT
 #define DG_VARIANT 0
 #endif
+// Scale format: 0 = FP32 scales (sfa [K/128][rows], sfb [ceil(N/128)][K/128]);
+// 1 = UE8M0 (DeepGEMM README, "Interfaces / Notes", SM100: four UE8M0 scale
+// factors packed into one 32-bit integer): byte j of a word is K block 4w + j,
+// sfa words [ceil(K/512)][rows], sfb words [ceil(N/128)][ceil(K/512)].  The
+// MFMA applies UE8M0 block scales itself, so there is no promotion step.
+#ifndef DG_SF
+#define DG_SF 0
+#endif
 // Column range of D this kernel computes (a launch may cover part of N, so
 // that one call can use two tile widths and fill whole rounds of the grid)
 #ifndef DG_NB
@@ -87,6 +95,9 @@ constexpr int NBLKS = (N + KBLK - 1) / KBLK;
 constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D; N is the row pitch
 static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
 constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
+constexpr bool SF_E8 = DG_SF != 0;
+constexpr int KW = (KBLKS + 3) / 4;           // packed UE8M0 words per row of scales
+constexpr int SF_KB = SF_E8 ? KW : KBLKS;     // scale entries (floats or words) along K
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
 // WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N)
 constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0;
@@ -418,6 +429,7 @@ constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
 constexpr int NT_INS = KSTEP;
 constexpr int STAGE_BYTES = T_OFF + KSTEP * 256;
 static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
+static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
@@ -491,7 +503,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         int a_rows_total;        // rows of this A (for sfa stride)
         if constexpr (kKind == 2) {
             a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
-            sfa_base = p.sfa + (u64)tl.g * KBLKS * p.M;
+            sfa_base = p.sfa + (u64)tl.g * SF_KB * p.M;
         } else {
             a_base = p.A + (u64)tl.m0 * K;
             sfa_base = p.sfa;
@@ -501,8 +513,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
-        const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * a_rows_total * 4u);
-        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)SF_KB * a_rows_total * 4u);
+        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
         const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
         // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
@@ -538,11 +550,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         for (int j = 0; j < IT; ++j) {
             const int h = min(wave + j * NWAVES, NT_INS - 1);
             const int nb = min(nb_t0 + lane, NBLKS - 1);
-            voff_t[j] = (u32)nb * KBLKS * 4u + (u32)h * 4u;
+            voff_t[j] = (u32)nb * SF_KB * 4u + (u32)h * 4u;
         }
 
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
         // (kb: first K block of the stage)
+        // index along K of the scales of K block kb (a word holds four UE8M0 scales)
+        auto sf_row = [](int kb) { return SF_E8 ? kb >> 2 : kb; };
         // live = false: a placeholder load whose buffer size is zero, so it moves
         // no data (every lane is out of range) but keeps the vmcnt count fixed.
         auto issue_one = [&](int j, int kb, int stage, bool live = true) {
@@ -561,11 +575,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                       __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
-                dma4(lim(rs_s), voff_s[j - IA - IB], __builtin_amdgcn_readfirstlane((u32)kb * a_rows_total * 4u),
+                dma4(lim(rs_s), voff_s[j - IA - IB], __builtin_amdgcn_readfirstlane((u32)sf_row(kb) * a_rows_total * 4u),
                      st + S_OFF + i * 256);
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
-                dma4(lim(rs_t), voff_t[j - IA - IB - IS], __builtin_amdgcn_readfirstlane((u32)kb * 4u), st + T_OFF + h * 256);
+                dma4(lim(rs_t), voff_t[j - IA - IB - IS], __builtin_amdgcn_readfirstlane((u32)sf_row(kb) * 4u),
+                     st + T_OFF + h * 256);
             }
         };
         auto issue_stage = [&](int kb, int stage, bool live = true) {
@@ -681,9 +696,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 lds_u8* const kbn = kblock_base(st_next, h_next);
 
                 float sab[TM];           // sa * sb for the uniform case
-                if constexpr (SB_UNIFORM) {
+                if constexpr (SB_UNIFORM && !SF_E8) {
 #pragma unroll
                     for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                }
+                // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
+                int ea[TM], eb[TN];
+                if constexpr (SF_E8) {
+                    const u32 sh = 8u * (u32)((tl.kb0 + it) & 3);
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
+#pragma unroll
+                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
                 }
 
                 // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
@@ -709,7 +733,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     float sc_prev[TM], s_last[TM];
 #pragma unroll
                     for (int a = 0; a < TM; ++a) {
-                        if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
+                        if constexpr (SF_E8) sc_prev[a] = s_last[a] = 0.f;
+                        else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
                         else {
                             sc_prev[a] = b > 0 ? sa[a] * sb[b > 0 ? b - 1 : 0] : 0.f;
                             s_last[a] = sa[a] * sb[b];
@@ -729,11 +754,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     for (int a = 0; a < TM; ++a) prev[a] = pr[a];
 #pragma unroll
                     for (int a = 0; a < TM; ++a) {
-                        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-                        // P[n][m] over this 128-wide K block: exact products, FP32 sums
-                        pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
-                        if (b == 0) acc[a][TN - 1] += p_carry[a] * s_carry[a];
-                        else acc[a][b - 1] += prev[a] * sc_prev[a];
+                        if constexpr (SF_E8) {
+                            // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
+                            // scales (its srcA is B, scaled by eb; its srcB is A, by ea)
+                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                fb, fa[a], acc[a][b], 0, 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
+                        } else {
+                            const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                            // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                            pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                            if (b == 0) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                            else acc[a][b - 1] += prev[a] * sc_prev[a];
+                        }
                         // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
                         // (after the tile's last block these reads are unused)
                         if (last) fa[a] = lds_read_frag(kbn + a_frag, kbn + a_frag_hi, A_OFF + a * 16 * ROWB);
@@ -801,9 +833,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
 
                 float sab[TM];           // sa * sb for the uniform case
-                if constexpr (SB_UNIFORM) {
+                if constexpr (SB_UNIFORM && !SF_E8) {
 #pragma unroll
                     for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                }
+                // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
+                int ea[TM], eb[TN];
+                if constexpr (SF_E8) {
+                    const u32 sh = 8u * (u32)((tl.kb0 + it) & 3);
+#pragma unroll
+                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
+#pragma unroll
+                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
                 }
 
                 // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
@@ -849,8 +890,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 }   // K blocks of the stage
             }
         }
+        if constexpr (!SF_E8) {
 #pragma unroll
-        for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+            for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+        }
 
         finish_tile<TM, TN>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag);
     }
@@ -872,6 +915,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 //              work item (it must fit), so the K loop has no barrier at all
 //              and the waves run independently.
 constexpr bool ARES = DG_VARIANT == 2;
+static_assert(!SF_E8, "UE8M0 scales are built for variant 0");
 static_assert(WM == 1, "variants 1 and 2 spread their waves along n only");
 static_assert(KSTEP == 1, "variants 1 and 2 stage one K block at a time");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
@@ -1174,6 +1218,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 // flag is also bounded, so a fault in this protocol would cost correctness,
 // which the tests check, and never hang the device.
 static_assert(WM == 1, "variant 3 spreads its consumer waves along n only");
+static_assert(!SF_E8, "UE8M0 scales are built for variant 0");
 static_assert(KSTEP == 1, "variant 3 stages one K block per slot");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
 static_assert(NKB <= 64, "the whole K range of a work item is unrolled");

@@ -43,7 +43,12 @@ def _load():
     lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
-    for f in (lib.dg_fp8_gemm_nt, lib.dg_m_grouped_fp8_gemm_nt_contiguous, lib.dg_m_grouped_fp8_gemm_nt_masked):
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    for f in (lib.dg_fp8_gemm_nt, lib.dg_m_grouped_fp8_gemm_nt_contiguous, lib.dg_m_grouped_fp8_gemm_nt_masked,
+              lib.dg_fp8_gemm_nt_ue8m0, lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0,
+              lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0):
         f.restype = i32
     lib.dg_last_error.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -98,6 +103,27 @@ def _f32(t: torch.Tensor, name: str, shape):
     _dev(t, name)
 
 
+def _scales(sfa, sfb, sfa_kb_mn, sfb_nb_kb, lead=()):
+    """Check the scale tensors; True for packed UE8M0 (int32), False for FP32.
+
+    FP32: sfa [*lead, Kb, M] and sfb [*lead, Nb, Kb].  UE8M0: the same with Kb
+    replaced by ceil(Kb/4) words, four K blocks to a word.
+    """
+    (kb, m), (nb, _) = sfa_kb_mn, sfb_nb_kb
+    if sfa.dtype == torch.int32:
+        w = _cdiv(kb, 4)
+        for t, name, shape in ((sfa, "sfa", (*lead, w, m)), (sfb, "sfb", (*lead, nb, w))):
+            if t.dtype != torch.int32:
+                raise TypeError(f"{name} must be int32 (packed UE8M0) like sfa, got {t.dtype}")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+            _dev(t, name)
+        return True
+    _f32(sfa, "sfa", (*lead, kb, m))
+    _f32(sfb, "sfb", (*lead, nb, kb))
+    return False
+
+
 def _out(d: torch.Tensor, shape):
     if d.dtype != torch.bfloat16:
         raise TypeError(f"D must be bfloat16, got {d.dtype}")
@@ -111,18 +137,22 @@ def _cdiv(a, b):
 
 
 def dg_fp8_gemm_nt(A, sfa, B, sfb, C, D, stream=None):
-    """D = C + A @ B.T (C may be None).  A [M,K], sfa [K/128,M], B [N,K], sfb [ceil(N/128),K/128]."""
+    """D = C + A @ B.T (C may be None).  A [M,K], sfa [K/128,M], B [N,K], sfb [ceil(N/128),K/128].
+
+    With int32 scale tensors (packed UE8M0, sfa [ceil(K/512),M], sfb [ceil(N/128),ceil(K/512)])
+    this calls dg_fp8_gemm_nt_ue8m0.
+    """
     _fp8(A, "A"); _fp8(B, "B")
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K:
         raise ValueError("A and B must share K")
-    _f32(sfa, "sfa", (_cdiv(K, 128), M))
-    _f32(sfb, "sfb", (_cdiv(N, 128), _cdiv(K, 128)))
+    e8 = _scales(sfa, sfb, (_cdiv(K, 128), M), (_cdiv(N, 128), _cdiv(K, 128)))
     if C is not None:
         _f32(C, "C", (M, N))
     _out(D, (M, N))
-    _check(lib.dg_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K, _stream(stream)))
+    f = lib.dg_fp8_gemm_nt_ue8m0 if e8 else lib.dg_fp8_gemm_nt
+    _check(f(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K, _stream(stream)))
     return D
 
 
@@ -133,16 +163,23 @@ def dg_m_grouped_fp8_gemm_nt_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=
     G, N = B.shape[0], B.shape[1]
     if B.shape[2] != K:
         raise ValueError("A and B must share K")
-    _f32(sfa, "sfa", (_cdiv(K, 128), M))
-    _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
+    if sfa.dtype == torch.int32:       # packed UE8M0; sfa has no group dimension here
+        e8 = _scales(sfa, sfb[0], (_cdiv(K, 128), M), (_cdiv(N, 128), _cdiv(K, 128)))
+        if tuple(sfb.shape) != (G, _cdiv(N, 128), _cdiv(_cdiv(K, 128), 4)):
+            raise ValueError("sfb must be int32 [G, ceil(N/128), ceil(K/512)]")
+    else:
+        e8 = False
+        _f32(sfa, "sfa", (_cdiv(K, 128), M))
+        _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
     if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
         raise ValueError("m_indices must be int32 [M]")
     _dev(m_indices, "m_indices")
     if C is not None:
         _f32(C, "C", (M, N))
     _out(D, (M, N))
-    _check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
-                                                   _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if e8 else lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    _check(f(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices), _ptr(C), _ptr(D), M, N, K, G,
+             _stream(stream)))
     return D
 
 
@@ -153,16 +190,16 @@ def dg_m_grouped_fp8_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream=None)
     N = B.shape[1]
     if B.shape[0] != G or B.shape[2] != K:
         raise ValueError("B must be [G, N, K]")
-    _f32(sfa, "sfa", (G, _cdiv(K, 128), M_max))
-    _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
+    e8 = _scales(sfa, sfb, (_cdiv(K, 128), M_max), (_cdiv(N, 128), _cdiv(K, 128)), lead=(G,))
     if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
         raise ValueError("masked_m must be int32 [G]")
     _dev(masked_m, "masked_m")
     if C is not None:
         _f32(C, "C", (G, M_max, N))
     _out(D, (G, M_max, N))
-    _check(lib.dg_m_grouped_fp8_gemm_nt_masked(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m),
-                                               _ptr(C), _ptr(D), M_max, N, K, G, _stream(stream)))
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if e8 else lib.dg_m_grouped_fp8_gemm_nt_masked
+    _check(f(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m), _ptr(C), _ptr(D), M_max, N, K, G,
+             _stream(stream)))
     return D
 
 
@@ -193,6 +230,29 @@ def describe_config(kind: int, rows: int, N: int, K: int, num_groups: int = 1, h
     buf = ctypes.create_string_buffer(1024)
     _check(lib.dg_describe_config(kind, rows, N, K, num_groups, int(has_c), num_cus, buf, len(buf)))
     return buf.value.decode()
+
+
+# The packed-UE8M0 entry points by their C names (the functions above also
+# dispatch to them when given int32 scale tensors)
+SCALE_UE8M0 = 4      # DG_SCALE_UE8M0: OR into `kind` of precompile / describe_config
+
+
+def dg_fp8_gemm_nt_ue8m0(A, sfa, B, sfb, C, D, stream=None):
+    if sfa.dtype != torch.int32:
+        raise TypeError("dg_fp8_gemm_nt_ue8m0 takes packed UE8M0 int32 scales")
+    return dg_fp8_gemm_nt(A, sfa, B, sfb, C, D, stream)
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    if sfa.dtype != torch.int32:
+        raise TypeError("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 takes packed UE8M0 int32 scales")
+    return dg_m_grouped_fp8_gemm_nt_contiguous(A, sfa, B, sfb, m_indices, C, D, stream)
+
+
+def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(A, sfa, B, sfb, masked_m, C, D, stream=None):
+    if sfa.dtype != torch.int32:
+        raise TypeError("dg_m_grouped_fp8_gemm_nt_masked_ue8m0 takes packed UE8M0 int32 scales")
+    return dg_m_grouped_fp8_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream)
 
 
 # names without the C prefix, as on the pages

@@ -44,6 +44,10 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
 def oracle_rows(oracle, p: gen.Problem, rows=None, threads=0):
     """(reference FP64 [rows, N], computed mask [rows]) for flat row indices."""
     d = gen.to_numpy(p)
+    if p.ue8m0:       # packed UE8M0 scales: the oracle unpacks them to the FP32 scales they stand for
+        Kb = p.K // 128
+        d["sfa"] = oracle.unpack_sfa_ue8m0(d["sfa"], Kb)
+        d["sfb"] = oracle.unpack_sfb_ue8m0(d["sfb"], Kb)
     if p.kind == "dense":
         ref = oracle.fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], rows=rows, threads=threads)
         return ref, np.ones(ref.shape[0], dtype=bool)

@@ -296,3 +296,66 @@ def test_column_range_plans(oracle, monkeypatch, forced, kinds):
         D, sent = run(p)
         ref, comp = oracle_rows(oracle, p)
         _compare(p, D, sent, ref, comp, what=f"{kind} {forced}")
+
+
+# ------------------------------------------------------------------ packed UE8M0 scales
+UE8M0_DENSE = [(1, 16, 128, False), (5, 129, 640, True), (100, 300, 512, True), (257, 515, 1152, False),
+               (300, 1000, 2048, True)]
+
+
+@pytest.mark.parametrize("M,N,K,with_c", UE8M0_DENSE)
+def test_ue8m0_dense(oracle, M, N, K, with_c):
+    p = gen.make_dense(M, N, K, seed=M + N + K + 5, with_c=with_c, ue8m0=True)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"ue8m0 dense {M}x{N}x{K}")
+
+
+def test_ue8m0_integer_data_bitwise(oracle):
+    """Integer codes and power-of-two scales: every sum is exact, so D is the oracle's BF16 bit for bit."""
+    g = torch.Generator().manual_seed(78)
+    M, N, K = 96, 400, 1664          # 13 K blocks: the last word is partly unused
+    A = gen.integer_codes((M, K), g, max_abs=8)
+    B = gen.integer_codes((N, K), g, max_abs=8)
+    ea = torch.randint(125, 130, (K // 128, M), generator=g)
+    eb = torch.randint(125, 130, ((N + 127) // 128, K // 128), generator=g)
+    p = gen.Problem("dense", A, gen.pack_ue8m0(ea.T).T.contiguous(), B, gen.pack_ue8m0(eb), ue8m0=True)
+    D, _ = run(p)
+    ref, _ = oracle_rows(oracle, p)
+    assert np.array_equal(check.bf16_bits(D), oracle.bf16_rne(ref).reshape(M, N))
+
+
+def test_ue8m0_grouped(oracle):
+    pm = gen.make_masked(3, 200, 333, 640, seed=31, with_c=True, masked_m=[200, 0, 77], ue8m0=True)
+    D, sent = run(pm)
+    ref, comp = oracle_rows(oracle, pm)
+    _compare(pm, D, sent, ref, comp, what="ue8m0 masked")
+    pc = gen.make_contiguous([128, 0, 256, 100], 333, 640, seed=32, with_c=True, pad_rows=128, ue8m0=True)
+    D, sent = run(pc)
+    ref, comp = oracle_rows(oracle, pc)
+    _compare(pc, D, sent, ref, comp, what="ue8m0 contiguous")
+
+
+UE8M0_FORCED = ["128,128,4,2,2,1,1,0", "256,256,4,2,2,1,1,0", "64,96,2,2,4,2,1,0", "256,224,4,2,2,1,1,0",
+                "32,64,1,2,3,4,1,0", "128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520"]
+
+
+@pytest.mark.parametrize("forced", UE8M0_FORCED)
+def test_ue8m0_forced_tile_configs(oracle, monkeypatch, forced):
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    p = gen.make_dense(300, 520, 1024, seed=13, with_c=True, ue8m0=True)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"ue8m0 forced {forced}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_ue8m0_workloads(oracle, cfg):
+    p = gen.make_workload(cfg, ue8m0=True)
+    D, sent = run(p)
+    if p.kind == "masked":
+        rows = np.arange(p.A.shape[0] * p.A.shape[1])
+    else:
+        rows = sample_rows(p.M, 48, seed=5, block=128)
+    ref, comp = oracle_rows(oracle, p, rows=rows)
+    _compare(p, D, sent, ref, comp, rows=rows, what="ue8m0 " + gen.WORKLOAD_NAMES[cfg])
