@@ -176,7 +176,11 @@ const Tuned kTuned[] = {
 
 // Packed UE8M0 scales (variant 0 only; no promotion in the K loop)
 const Tuned kTunedE8[] = {
+    {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
+    {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
