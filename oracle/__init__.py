@@ -16,6 +16,9 @@ Semantics and citations are in the header of ``oracle.c``:
 * DeepGEMM README, "Interfaces / Notes" (SM100) and the Ascend 950 article:
   UE8M0 scale factors packed four to a 32-bit word; unpacked here to the FP32
   scales they stand for (exactly), after which the GEMM is the FP32-scale one.
+* DeepGEMM-Ascend hub page (precision table: FP8 x FP4) and README news
+  2026.04.16 (FP8xFP4 GEMM; FP4 weights with UE8M0 scale factors): E2M1
+  weights with one UE8M0 scale per 1x32 block, A as in the UE8M0 form.
 """
 from __future__ import annotations
 
@@ -60,6 +63,11 @@ def _declare(lib):
     lib.oracle_ue8m0_unpack_mn_major.argtypes = [p, c.c_int64, c.c_int, c.c_int64, p]
     lib.oracle_ue8m0_unpack_k_major.restype = None
     lib.oracle_ue8m0_unpack_k_major.argtypes = [p, c.c_int64, c.c_int, p]
+    lib.oracle_e2m1_value.restype = c.c_double
+    lib.oracle_e2m1_value.argtypes = [c.c_uint8]
+    lib.oracle_fp8_fp4_gemm.restype = c.c_int
+    lib.oracle_fp8_fp4_gemm.argtypes = [c.c_int, p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                        p, c.c_int64, p, p, c.c_int]
     lib.oracle_default_threads.restype = c.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_fp8_gemm_nt.restype = c.c_int
@@ -161,6 +169,37 @@ class Oracle:
         Kb = np.shape(A)[-1] // KBLOCK
         return self.m_grouped_masked(A, self.unpack_sfa_ue8m0(sfa, Kb), B, self.unpack_sfb_ue8m0(sfb, Kb),
                                      masked_m, C, rows, threads)
+
+    # ---------------------------------------------------------- FP8 x FP4
+    def e2m1_value(self, nibble: int) -> float:
+        return float(self.lib.oracle_e2m1_value(int(nibble)))
+
+    def fp8_fp4_gemm(self, kind: str, A, sfa, B, sfb, group_info=None, C=None, rows=None, threads=0):
+        """(D FP64 [rows, N], computed [rows]) of an FP8 x FP4 GEMM.
+
+        kind "dense" | "contiguous" | "masked".  A E4M3 codes ([M,K] or [G,M_max,K]); sfa packed
+        UE8M0 words ([ceil(Kb/4),M] or [G,ceil(Kb/4),M_max]); B E2M1 pairs [(G,)N,K/2] u8 (element
+        2i in the low nibble of byte i); sfb [(G,)N,Kb] int32 (byte j: K elements 128 kb + 32 j ..+32).
+        """
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.int32); sfb = _c(sfb, np.int32); C = _c(C, np.float32)
+        gi = _c(group_info, np.int32)
+        k = {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+        if kind == "masked":
+            G, M, K = A.shape
+        else:
+            M, K = A.shape
+            G = B.shape[0] if B.ndim == 3 else 1
+        N = B.shape[-2]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else (G * M if kind == "masked" else M)
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_fp8_fp4_gemm(k, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(gi), _ptr(C), M, N, K, G,
+                                          _ptr(r), nr, _ptr(out), _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_fp8_fp4_gemm: bad sizes")
+        return out, comp.astype(bool)
 
     def fp8_gemm_nt(self, A, sfa, B, sfb, C=None, rows=None, threads=0):
         """D (FP64) of the dense form; A [M,K] u8, sfa [K/128,M], B [N,K] u8, sfb [Nb,Kb]."""

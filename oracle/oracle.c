@@ -124,6 +124,24 @@ void oracle_ue8m0_unpack_k_major(const int32_t *packed, int64_t n_rows, int Kb, 
 }
 
 /* ------------------------------------------------------------------ */
+/* FP4 E2M1 (OCP MX FP4; the pages' FP8 x FP4 GEMM takes FP4 weights:  */
+/* DeepGEMM-Ascend hub page, precision table; README news 2026.04.16). */
+/* Bits: sign = bit 3, exponent = bits 2..1 (bias 1), mantissa bit 0.  */
+/*   e == 0   : (-1)^s * m * 0.5                (0 or 0.5)             */
+/*   e in 1..3: (-1)^s * (1 + m/2) * 2^(e-1)    (1, 1.5, 2, 3, 4, 6)   */
+/* No infinities or NaN.  Two per byte, element 2i in the low nibble   */
+/* of byte i (reading: the OCP MX packing order).                      */
+/* ------------------------------------------------------------------ */
+double oracle_e2m1_value(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int m = nibble & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -1.0 * mag : mag;
+}
+
+/* ------------------------------------------------------------------ */
 /* BF16 (1 sign, 8 exponent bits with bias 127, 7 mantissa bits),     */
 /* round-to-nearest, ties-to-even, straight from a double.  The        */
 /* outputs of all three operations are BF16.                           */
@@ -201,6 +219,53 @@ static void compute_row(const row_job *j)
 }
 
 /* ------------------------------------------------------------------ */
+/* FP8 x FP4 row: A in E4M3 with one UE8M0 scale per 1x128 block (the  */
+/* packed LHS words above), B in E2M1 with one UE8M0 scale per 1x32    */
+/* block of its row (reading: the OCP MX block of FP4, 32 elements),   */
+/* four 32-blocks of one 128-wide K block packed into one word:        */
+/*   D[n] = C[n] + sum_kb sum_j sa(kb) * sb(n, kb, j) * S[n, kb, j],   */
+/*   S = sum over the 32 k of block j of e4m3(A[m,k]) * e2m1(B[n,k])   */
+/* in FP64 (each S is exact: every term is a multiple of 2^-10 below   */
+/* 448 * 6, so 32 of them need far fewer than 53 bits).                */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const double *dec;      /* E4M3 table */
+    double dec4[16];        /* E2M1 table */
+    const uint8_t *a_row;   /* K codes */
+    const int32_t *sa;      /* packed LHS words of this row; word w at sa[w * sa_stride] */
+    int64_t sa_stride;
+    const uint8_t *b;       /* B of the group, [N][K/2] bytes */
+    const int32_t *sfb;     /* [N][Kb] words of the group */
+    const float *c_row;
+    int N, K;
+    double *out;
+} row_job4;
+
+static void compute_row_fp4(const row_job4 *j)
+{
+    const int Kb = j->K / ORACLE_KBLOCK;
+    for (int n = 0; n < j->N; ++n) {
+        const uint8_t *b_row = j->b + (int64_t)n * (j->K / 2);
+        double acc = 0.0;
+        for (int kb = 0; kb != Kb; ++kb) {
+            double sa = oracle_ue8m0_value(ue8m0_byte(j->sa[(kb / 4) * j->sa_stride], kb % 4));
+            int32_t wb = j->sfb[(int64_t)n * Kb + kb];
+            for (int blk = 0; blk < 4; ++blk) {
+                double s = 0.0;
+                for (int t = 0; t < 32; ++t) {
+                    int k = kb * ORACLE_KBLOCK + blk * 32 + t;
+                    uint8_t byte = b_row[k / 2];
+                    uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+                    s += j->dec[j->a_row[k]] * j->dec4[nib];
+                }
+                acc += sa * oracle_ue8m0_value(ue8m0_byte(wb, blk)) * s;
+            }
+        }
+        j->out[n] = (j->c_row ? (double)j->c_row[n] : 0.0) + acc;
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Row scheduling over threads.                                        */
 /* ------------------------------------------------------------------ */
 enum { KIND_DENSE = 0, KIND_CONTIG = 1, KIND_MASKED = 2 };
@@ -215,6 +280,7 @@ typedef struct {
     const int64_t *rows; int64_t n_rows;
     double *out; uint8_t *computed;
     double dec[256];
+    int fp4;                     /* FP8 x FP4: sfa/sfb are packed UE8M0 words, B is E2M1 */
 } problem;
 
 typedef struct { const problem *p; int64_t r0, r1; } slice;
@@ -261,7 +327,26 @@ static void do_row(const problem *p, int64_t i)
         j.sfb = p->sfb + g * Nb * (int64_t)Kb;
         j.c_row = p->C ? p->C + r * p->N : NULL;
     }
-    compute_row(&j);
+    if (p->fp4) {
+        /* same row selection; scales and B reinterpreted for FP8 x FP4 */
+        const int W = (Kb + 3) / 4;
+        row_job4 j4;
+        j4.dec = p->dec; j4.N = p->N; j4.K = p->K; j4.out = out; j4.a_row = j.a_row; j4.c_row = j.c_row;
+        for (int c = 0; c < 16; ++c) j4.dec4[c] = oracle_e2m1_value((uint8_t)c);
+        const int32_t *sfa4 = (const int32_t *)p->sfa;
+        const int32_t *sfb4 = (const int32_t *)p->sfb;
+        const uint8_t *B4 = p->B;
+        int64_t g = 0, m = r;
+        if (p->kind == KIND_CONTIG) g = p->group_info[r];
+        if (p->kind == KIND_MASKED) { g = r / p->M; m = r % p->M; }
+        j4.sa = sfa4 + (p->kind == KIND_MASKED ? g * W * p->M : 0) + m;
+        j4.sa_stride = p->M;
+        j4.b = B4 + g * (int64_t)p->N * (p->K / 2);
+        j4.sfb = sfb4 + g * (int64_t)p->N * Kb;
+        compute_row_fp4(&j4);
+    } else {
+        compute_row(&j);
+    }
     if (p->computed) p->computed[i] = 1;
 }
 
@@ -372,5 +457,27 @@ int oracle_m_grouped_masked(const uint8_t *A, const float *sfa, const uint8_t *B
     p.group_info = masked_m; p.M = M_max; p.N = N; p.K = K; p.G = G;
     p.rows = rows; p.n_rows = rows ? n_rows : (int64_t)G * M_max; p.out = out; p.computed = computed;
     if (G <= 0) return -1;
+    return run(&p, n_threads);
+}
+
+/*
+ * FP8 x FP4 (all three forms; kind 0 dense, 1 contiguous, 2 masked):
+ *   A as in the FP32-scale forms; sfa packed UE8M0 words [ceil(Kb/4)][M]
+ *   (masked: [G][ceil(Kb/4)][M_max]); B [G][N][K/2] E2M1 pairs (dense: G = 1);
+ *   sfb [G][N][Kb] words, byte j = scale of K elements [128 kb + 32 j, +32);
+ *   group_info: m_indices (contiguous) or masked_m (masked), NULL for dense.
+ */
+int oracle_fp8_fp4_gemm(int kind, const uint8_t *A, const int32_t *sfa, const uint8_t *B, const int32_t *sfb,
+                        const int32_t *group_info, const float *C, int64_t M, int N, int K, int G,
+                        const int64_t *rows, int64_t n_rows, double *out, uint8_t *computed, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    if (kind < 0 || kind > 2 || G <= 0) return -1;
+    p.kind = kind; p.A = A; p.sfa = (const float *)sfa; p.B = B; p.sfb = (const float *)sfb; p.C = C;
+    p.group_info = group_info; p.M = M; p.N = N; p.K = K; p.G = G; p.fp4 = 1;
+    p.rows = rows;
+    p.n_rows = rows ? n_rows : (kind == KIND_MASKED ? (int64_t)G * M : M);
+    p.out = out; p.computed = computed;
     return run(&p, n_threads);
 }

@@ -94,6 +94,42 @@ def quantize_128x128(x: torch.Tensor, ue8m0: bool = False):
     return q[..., :N, :].contiguous(), s.contiguous()
 
 
+# ---------------------------------------------------------------- FP4 weights
+E2M1_MAX = 6.0
+E2M1_MAGS = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _cast_e2m1(x: torch.Tensor) -> torch.Tensor:
+    """Nearest E2M1 code (ties to the even mantissa) of x, |x| <= 6: u8 nibbles 0..15."""
+    a = x.abs().clamp(max=E2M1_MAX)
+    d = (a.unsqueeze(-1) - E2M1_MAGS).abs()
+    best = d.min(dim=-1, keepdim=True).values
+    # among equally near magnitudes take the even code (mantissa bit 0)
+    cand = (d == best) & (torch.arange(8) % 2 == 0)
+    code = torch.where(cand.any(-1), cand.to(torch.int8).argmax(-1), (d == best).to(torch.int8).argmax(-1))
+    return (code.to(torch.uint8) | ((x < 0).to(torch.uint8) << 3)) * (a > 0).to(torch.uint8)
+
+
+def quantize_fp4_1x32(x: torch.Tensor):
+    """x [..., N, K] fp32 -> (E2M1 pairs u8 [..., N, K/2], sfb int32 [..., N, K/128]).
+
+    One UE8M0 scale per 1x32 block, s = 2^ceil(log2(amax/6)); element 2i in the low
+    nibble of byte i; byte j of word [n][kb] holds the scale of K elements 128 kb + 32 j ..+32.
+    """
+    *lead, N, K = x.shape
+    assert K % KBLOCK == 0
+    xb = x.reshape(*lead, N, K // 32, 32)
+    amax = xb.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / E2M1_MAX, torch.ones_like(amax))
+    m, e = torch.frexp(s)
+    e = (e - (m == 0.5).to(e.dtype)).to(torch.int32)
+    s = torch.ldexp(torch.ones_like(s), e)
+    q = _cast_e2m1(xb / s.unsqueeze(-1)).reshape(*lead, N, K)
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).contiguous()
+    words = pack_ue8m0((e + 127).reshape(*lead, N, K // KBLOCK, 4).reshape(*lead, N * (K // KBLOCK), 4))
+    return packed, words.reshape(*lead, N, K // KBLOCK).contiguous()
+
+
 # ---------------------------------------------------------------- problems
 @dataclasses.dataclass
 class Problem:
@@ -107,6 +143,7 @@ class Problem:
     masked_m: Optional[torch.Tensor] = None    # int32 [G] (masked)
     seed: int = 0
     ue8m0: bool = False             # sfa/sfb are packed UE8M0 int32 words
+    fp4: bool = False               # B holds E2M1 pairs [.., N, K/2], sfb [.., N, K/128] words (1x32 blocks)
 
     @property
     def M(self):
@@ -131,19 +168,26 @@ def _gen(seed):
     return g
 
 
-def make_dense(M, N, K, seed, with_c=False, ue8m0=False) -> Problem:
+def _quant_b(b, ue8m0, fp4):
+    return quantize_fp4_1x32(b) if fp4 else quantize_128x128(b, ue8m0)
+
+
+def make_dense(M, N, K, seed, with_c=False, ue8m0=False, fp4=False) -> Problem:
+    """fp4: FP8 x FP4 (B as E2M1 with 1x32 UE8M0 scales; A with UE8M0 scales)."""
+    ue8m0 = ue8m0 or fp4
     g = _gen(seed)
     a = torch.randn(M, K, generator=g, dtype=torch.float32)
     b = torch.randn(N, K, generator=g, dtype=torch.float32)
     c = torch.randn(M, N, generator=g, dtype=torch.float32) if with_c else None
     A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b, ue8m0)
+    B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed, ue8m0=ue8m0)
+    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed, ue8m0=ue8m0, fp4=fp4)
 
 
-def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128, ue8m0=False) -> Problem:
+def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128, ue8m0=False,
+                    fp4=False) -> Problem:
     """Experts' tokens concatenated along M, each segment padded to ``align`` rows.
 
     group_rows[g] valid rows for expert g; padding rows get index -1.  With
@@ -161,14 +205,15 @@ def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=1
     for e, (r, s) in enumerate(zip(group_rows, seg)):
         idx[off:off + r] = e
         off += s
+    ue8m0 = ue8m0 or fp4
     A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b, ue8m0)
+    B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed, ue8m0=ue8m0)
+    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed, ue8m0=ue8m0, fp4=fp4)
 
 
-def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False) -> Problem:
+def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, fp4=False) -> Problem:
     g = _gen(seed)
     a = torch.randn(G, M_max, K, generator=g, dtype=torch.float32)
     b = torch.randn(G, N, K, generator=g, dtype=torch.float32)
@@ -177,11 +222,12 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False) 
         mm = torch.randint(0, M_max + 1, (G,), generator=g, dtype=torch.int32)
     else:
         mm = torch.as_tensor(masked_m, dtype=torch.int32)
+    ue8m0 = ue8m0 or fp4
     A, sfa = quantize_1x128(a, ue8m0)
     del a
-    B, sfb = quantize_128x128(b, ue8m0)
+    B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0)
+    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0, fp4=fp4)
 
 
 # ---------------------------------------------------------------- the five workloads
@@ -209,14 +255,14 @@ def workload_seed(cfg) -> int:
     return 1000 + (1 if cfg == "1c" else int(cfg))
 
 
-def make_workload(cfg, ue8m0=False) -> Problem:
+def make_workload(cfg, ue8m0=False, fp4=False) -> Problem:
     c = WORKLOADS[cfg]
     seed = workload_seed(cfg)
     if c["kind"] == "dense":
-        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False), ue8m0=ue8m0)
+        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False), ue8m0=ue8m0, fp4=fp4)
     if c["kind"] == "contiguous":
-        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed, ue8m0=ue8m0)
-    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed, ue8m0=ue8m0)
+        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed, ue8m0=ue8m0, fp4=fp4)
+    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed, ue8m0=ue8m0, fp4=fp4)
 
 
 # ---------------------------------------------------------------- structured inputs for pins

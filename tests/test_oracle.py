@@ -342,3 +342,110 @@ def test_ue8m0_generator_scales(oracle):
     assert np.all(np.log2(sfa) == np.round(np.log2(sfa)))
     dec = torch_decode_table()
     assert np.all(np.abs(dec[p.A.numpy()]) <= 448.0)
+
+
+# ------------------------------------------------------------------ FP8 x FP4
+def _e2m1_golden():
+    pts = json.load(open(os.path.join(GOLDEN, "e2m1_points.json")))["points"]
+    return np.array([float(pts[f"0x{c:x}"]) for c in range(16)])
+
+
+def test_e2m1_points_from_format(oracle):
+    table = _e2m1_golden()
+    for c in range(16):
+        got = oracle.e2m1_value(c)
+        assert got == table[c] and np.signbit(got) == np.signbit(table[c]), c
+
+
+def _fp4_dequant_ref(p):
+    """numpy FP64 dequantise-and-matmul of a dense FP8 x FP4 problem, from the golden
+    E2M1 table, torch's E4M3 decode and 2^(e-127) per byte (independent of the oracle)."""
+    dec8 = torch_decode_table()
+    t4 = _e2m1_golden()
+    A = dec8[p.A.numpy()]
+    M, K = A.shape
+    Bb = p.B.numpy()
+    B = np.empty((Bb.shape[0], K))
+    B[:, 0::2] = t4[Bb & 0xF]
+    B[:, 1::2] = t4[Bb >> 4]
+    wa = p.sfa.numpy().view(np.uint32)                       # [W][M]
+    ea = np.stack([(wa[kb // 4] >> (8 * (kb % 4))) & 0xFF for kb in range(K // 128)])   # [Kb][M]
+    wb = p.sfb.numpy().view(np.uint32)                       # [N][Kb]
+    eb = np.stack([(wb >> (8 * j)) & 0xFF for j in range(4)], axis=-1).reshape(wb.shape[0], -1)   # [N][K/32]
+    sa = np.repeat(np.ldexp(1.0, ea.astype(np.int64) - 127).T, 128, axis=1)
+    sb = np.repeat(np.ldexp(1.0, eb.astype(np.int64) - 127), 32, axis=1)
+    ref = (A * sa) @ (B * sb).T
+    if p.C is not None:
+        ref = ref + p.C.numpy().astype(np.float64)
+    return ref
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 256), (17, 130, 640)])
+def test_fp8_fp4_vs_numpy_dequant_matmul(oracle, M, N, K):
+    p = gen.make_dense(M, N, K, seed=M + N, with_c=True, fp4=True)
+    d, comp = oracle.fp8_fp4_gemm("dense", p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(), C=p.C.numpy())
+    assert comp.all()
+    ref = _fp4_dequant_ref(p)
+    assert np.allclose(d, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_fp8_fp4_nibble_order_and_block_scales(oracle):
+    """One-hot pairs: A[m, k] = 1 and B[n, k] = 1 only at k = m + n; B's 32-blocks scaled 2^j."""
+    M, N, K = 4, 6, 256
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K // 2), np.uint8)
+    for m in range(M):
+        A[m, 31 * m + 1] = gen.E4M3_ONE
+    for n in range(N):
+        k = 31 * (n % M) + 1
+        B[n, k // 2] |= (0x2 << 4) if k & 1 else 0x2      # E2M1 1.0 at element k
+    sfa = np.full((1, M), 0x7F7F7F7F, np.uint32).view(np.int32)
+    eb = np.array([127 + j for j in range(8)])            # per 32-block of K: 2^j
+    sfb = np.stack([eb[0:4], eb[4:8]]).astype(np.uint32)
+    sfb = (sfb[:, 0] | (sfb[:, 1] << 8) | (sfb[:, 2] << 16) | (sfb[:, 3] << 24)).view(np.int32)
+    sfb = np.tile(sfb, (N, 1))
+    d, _ = oracle.fp8_fp4_gemm("dense", A, sfa, B, sfb)
+    for m in range(M):
+        for n in range(N):
+            k = 31 * m + 1
+            assert d[m, n] == (2.0 ** (k // 32) if n % M == m else 0.0), (m, n, d[m, n])
+
+
+def test_fp8_fp4_grouped_equal_dense(oracle):
+    pm = gen.make_masked(2, 40, 70, 384, seed=5, masked_m=[40, 17], fp4=True)
+    d, comp = oracle.fp8_fp4_gemm("masked", pm.A.numpy(), pm.sfa.numpy(), pm.B.numpy(), pm.sfb.numpy(),
+                                  pm.masked_m.numpy())
+    assert comp.sum() == 57
+    for g in range(2):
+        dg_, _ = oracle.fp8_fp4_gemm("dense", pm.A[g].numpy(), pm.sfa[g].numpy(), pm.B[g].numpy(), pm.sfb[g].numpy())
+        valid = int(pm.masked_m[g])
+        assert np.array_equal(d[g * 40:g * 40 + valid], dg_[:valid])
+    pc = gen.make_contiguous([128, 0, 100], 70, 256, seed=6, fp4=True)
+    d, comp = oracle.fp8_fp4_gemm("contiguous", pc.A.numpy(), pc.sfa.numpy(), pc.B.numpy(), pc.sfb.numpy(),
+                                  pc.m_indices.numpy())
+    idx = pc.m_indices.numpy()
+    assert np.array_equal(comp, (idx >= 0))
+    for e in (0, 2):
+        rows = np.nonzero(idx == e)[0]
+        de, _ = oracle.fp8_fp4_gemm("dense", pc.A.numpy()[rows], pc.sfa.numpy()[:, rows], pc.B[e].numpy(),
+                                    pc.sfb[e].numpy())
+        assert np.array_equal(d[rows], de)
+
+
+def test_fp4_quantiser_rounds_to_nearest(oracle):
+    """Every E2M1 code the generator picks is a nearest representable value of x / s."""
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(8, 256, generator=g) * 3
+    B, sfb = gen.quantize_fp4_1x32(x)
+    t4 = _e2m1_golden()
+    q = np.empty((8, 256))
+    q[:, 0::2] = t4[B.numpy() & 0xF]
+    q[:, 1::2] = t4[B.numpy() >> 4]
+    w = sfb.numpy().view(np.uint32)
+    e = np.stack([(w >> (8 * j)) & 0xFF for j in range(4)], -1).reshape(8, -1)
+    s = np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+    y = x.numpy().astype(np.float64) / s
+    mags = np.unique(np.abs(t4))
+    err = np.abs(np.abs(y)[..., None] - mags).min(-1)
+    assert np.allclose(np.abs(np.abs(q) - np.abs(y)), err)
+    assert np.all(np.abs(y) <= 6.0)

@@ -36,6 +36,15 @@ MUTANTS = [
      "return (uint8_t)(((uint32_t)word >> (8 * (3 - j))) & 0xFFu);"),
     ("ue8m0_sfa_k_major", "int32_t w = packed[(g * W + kb / 4) * M + m];",
      "int32_t w = packed[(g * M + m) * W + kb / 4];"),
+    ("fp4_drop_last_k_block", "for (int kb = 0; kb != Kb; ++kb) {", "for (int kb = 0; kb != Kb - 1; ++kb) {"),
+    ("fp4_c_ignored", "j->out[n] = (j->c_row ? (double)j->c_row[n] : 0.0) + acc;", "j->out[n] = acc;"),
+    ("e2m1_lost_sign", "return s ? -1.0 * mag : mag;", "return mag;"),
+    ("e2m1_bias_2", "double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);",
+     "double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 2);"),
+    ("fp4_nibbles_swapped", "uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);",
+     "uint8_t nib = (k & 1) ? (byte & 0xF) : (byte >> 4);"),
+    ("fp4_scale_block_64", "acc += sa * oracle_ue8m0_value(ue8m0_byte(wb, blk)) * s;",
+     "acc += sa * oracle_ue8m0_value(ue8m0_byte(wb, blk / 2)) * s;"),
 ]
 
 
@@ -46,6 +55,7 @@ def _pin_calls(o):
     calls.append(lambda: pins.test_bf16_rne_matches_torch_cast(o))
     for M, N, K in [(3, 129, 384), (129, 3, 128), (5, 128, 384)]:
         calls.append(lambda M=M, N=N, K=K: pins.test_dense_vs_numpy_dequant_matmul(o, M, N, K))
+    calls.append(lambda: pins.test_fp8_fp4_vs_numpy_dequant_matmul(o, 17, 130, 640))
     for f in (pins.test_dense_integer_data_exact_vs_int64, pins.test_all_ones_closed_form,
               pins.test_one_hot_rows, pins.test_sign_flip_and_pow2_scaling,
               pins.test_rows_subset_equals_full, pins.test_c_is_added,
@@ -53,7 +63,8 @@ def _pin_calls(o):
               pins.test_contiguous_group_independence_and_permutation,
               pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset,
               pins.test_ue8m0_points_from_format, pins.test_ue8m0_packing_byte_order_and_layouts,
-              pins.test_ue8m0_all_ones_closed_form):
+              pins.test_ue8m0_all_ones_closed_form, pins.test_e2m1_points_from_format,
+              pins.test_fp8_fp4_nibble_order_and_block_scales, pins.test_fp8_fp4_grouped_equal_dense):
         calls.append(lambda f=f: f(o))
     return calls
 
