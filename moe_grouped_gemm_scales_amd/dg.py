@@ -4,7 +4,7 @@ Every function here checks the torch tensors' dtypes, shapes, devices and
 contiguity, then calls the C entry point of the same name with raw device
 pointers and the current HIP stream.  All arithmetic runs in the library's
 HIP kernels; there is no other code path.  If libdg.so is missing the import
-fails loudly (build it with ``python -m moe_grouped_gemm_scales_amd.build``).
+fails loudly (build it with ``python moe_grouped_gemm_scales_amd/build.py``).
 
 Layouts (DeepGEMM README, "Interfaces / Notes"): D = C + A @ B.T with A
 [M, K] and B [N, K] in FP8 E4M3 (torch.float8_e4m3fn or raw uint8 codes),
@@ -37,7 +37,7 @@ class DGError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m moe_grouped_gemm_scales_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python moe_grouped_gemm_scales_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
