@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOPS + HBM GB/s per shape (FP8 block-scaled GEMM), % of roofline"
 PEAK_HBM_GBS = 8000.0
-PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP8_TFLOPS = 5000.0    # also the peak used for FP8 x FP4: each MFMA there has an FP8 operand
 RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 # The pages' H800 numbers for the same shapes (DeepGEMM launch article,
 # section 3 dense table): other hardware, context only.
@@ -49,8 +49,13 @@ def algorithmic(p) -> tuple[float, float, int]:
     """(FLOPs, bytes, computed rows) of one call, by the pages' convention."""
     K, N = p.K, p.N
     Kb, Nb = K // 128, (N + 127) // 128
+    Kb_b = Kb                       # B scale entries along K per scale row
     if p.ue8m0:
         Kb = (Kb + 3) // 4          # one packed 4-byte word per four K blocks
+        Kb_b = Kb
+    if p.fp4:
+        Kb_b = K // 128             # FP4 B: one word (four 1x32 scales) per row and K block
+        Nb = N
     if p.kind == "dense":
         rows, groups_used = p.M, 1
     elif p.kind == "contiguous":
@@ -62,10 +67,11 @@ def algorithmic(p) -> tuple[float, float, int]:
         rows = int(mm.sum())
         groups_used = int((mm > 0).sum())
     flops = 2.0 * rows * N * K
-    nbytes = rows * K + groups_used * N * K + rows * N * 2
+    b_row = K // 2 if p.fp4 else K  # E2M1 B: two codes per byte
+    nbytes = rows * K + groups_used * N * b_row + rows * N * 2
     if p.C is not None:
         nbytes += rows * N * 4
-    nbytes += rows * Kb * 4 + groups_used * Nb * Kb * 4
+    nbytes += rows * Kb * 4 + groups_used * Nb * Kb_b * 4
     return flops, float(nbytes), rows
 
 
@@ -73,14 +79,14 @@ def kind_id(kind: str) -> int:
     return {"dense": 0, "contiguous": 1, "masked": 2}[kind]
 
 
-def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False):
+def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False, fp4: bool = False):
     import torch
 
     import moe_grouped_gemm_scales_amd as dg
     from tests import gen
     from tests.gpu_util import out_shape, to_dev
 
-    p = gen.make_workload(cfg, ue8m0=ue8m0)
+    p = gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
     flops, nbytes, rows = algorithmic(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
     ws += math.prod(out_shape(p)) * 2
@@ -90,7 +96,16 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
 
     def call(i):
         d, D = devs[i % copies], outs[i % copies]
-        if p.kind == "dense":
+        if fp4:
+            if p.kind == "dense":
+                dg.dg_fp8_fp4_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
+            elif p.kind == "contiguous":
+                dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["m_indices"],
+                                                           d["C"], D)
+            else:
+                dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"],
+                                                       D)
+        elif p.kind == "dense":
             dg.dg_fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
         elif p.kind == "contiguous":
             dg.dg_m_grouped_fp8_gemm_nt_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["m_indices"], d["C"], D)
@@ -98,7 +113,8 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
             dg.dg_m_grouped_fp8_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"], D)
 
     rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
-    kernel = dg.describe_config(kind_id(p.kind) | (dg.SCALE_UE8M0 if ue8m0 else 0), rows_arg, p.N, p.K, p.G,
+    flag = dg.SCALE_FP8_FP4 if fp4 else (dg.SCALE_UE8M0 if ue8m0 else 0)
+    kernel = dg.describe_config(kind_id(p.kind) | flag, rows_arg, p.N, p.K, p.G,
                                 p.C is not None)
     # everything runs on one non-default stream (HIP graphs cannot capture the null stream)
     stream = torch.cuda.Stream()
@@ -208,9 +224,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="1", help="0, 1, 1c, 2, 3 or 4 (default 1)")
     ap.add_argument("--all", action="store_true",
-                    help="also run every workload, one stderr line each (FP32 scales, then packed UE8M0 scales)")
+                    help="also run every workload, one stderr line each (FP32 scales, packed UE8M0 scales, "
+                         "then FP8 x FP4)")
     ap.add_argument("--ue8m0", action="store_true",
                     help="time the chosen workload with packed UE8M0 scales instead of FP32 ones")
+    ap.add_argument("--fp4", action="store_true",
+                    help="time the chosen workload as FP8 x FP4 (E2M1 B with 1x32 UE8M0 scales)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--copy-kernel", action="store_true",
@@ -245,10 +264,13 @@ def main():
     cfg = args.workload if args.workload == "1c" else int(args.workload)
     per_shape = []
     if args.all:
-        for c, e8 in [(c, False) for c in [0, 1, "1c", 2, 3, 4]] + [(c, True) for c in [0, 1, 2, 3, 4]]:
+        modes = [(c, "") for c in [0, 1, "1c", 2, 3, 4]] + [(c, "_ue8m0") for c in [0, 1, 2, 3, 4]] + \
+            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]]
+        for c, mode in modes:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
-            r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=e8)
-            wl = gen.WORKLOAD_NAMES[c] + ("_ue8m0" if e8 else "")
+            r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=mode == "_ue8m0",
+                               fp4=mode == "_fp4")
+            wl = gen.WORKLOAD_NAMES[c] + mode
             line = dict(workload=wl, kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
                         roofline_frac=round(r["frac"], 4), step_us=round(r["ms_per_step"] * 1e3, 3),
@@ -258,18 +280,18 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0)
+    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4)
     p = r["problem"]
-    name = gen.WORKLOAD_NAMES[cfg] + ("_ue8m0" if args.ue8m0 else "")
+    name = gen.WORKLOAD_NAMES[cfg] + ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))
-    cpu = None if (args.no_cpu_baseline or args.ue8m0) else cpu_baseline(cfg)
+    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4) else cpu_baseline(cfg)
     value = r["step_tflops"]
-    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not args.ue8m0 else None
+    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not (args.ue8m0 or args.fp4) else None
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -281,7 +303,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / pages, 4) if pages else None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": name, "kind": p.kind, "M": p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
                    "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],

@@ -130,6 +130,36 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *A, const int32_t *sf
                                                 const float *C, void *D, int M_max, int N, int K,
                                                 int num_groups, void *stream);
 
+/*
+ * FP8 x FP4: the same three forms with FP4 weights (DeepGEMM-Ascend hub page,
+ * precision table "FP8 x FP4"; DeepGEMM README, news of 2026.04.16: an
+ * FP8 x FP4 GEMM with FP4 weights and UE8M0 scale factors).
+ *   A, sfa: as in the packed-UE8M0 entry points above (E4M3, one UE8M0 scale
+ *     per 1x128 block, sfa int32 [W][M], masked [G][W][M_max]).
+ *   B uint8 [N][K/2] (grouped: [G][N][K/2]): OCP MX E2M1 codes, two per
+ *     byte, element 2i in the low nibble of byte i (reading: the OCP packing
+ *     order).  E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *     magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN.
+ *   sfb int32 [N][Kb] (grouped: [G][N][Kb]): one UE8M0 scale per 1x32 block
+ *     of each row of B (reading: the OCP MX block of 32); byte j of word
+ *     [n][kb] scales K elements 128 kb + 32 j .. 128 kb + 32 j + 31.
+ *   D = C + sum over 32-wide K blocks j of 2^(ea-127) 2^(eb-127) S_j, S_j the
+ *   exact block dot product, rounded once to BF16 (the matrix core applies
+ *   both scales; FP32 accumulation).
+ * C, D, the group and mask rules, ownership and errors are those of the
+ * entry points above; B must be 16-byte aligned.
+ */
+dg_status dg_fp8_fp4_gemm_nt(const void *A, const int32_t *sfa, const void *B, const int32_t *sfb,
+                             const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void *A, const int32_t *sfa, const void *B,
+                                                  const int32_t *sfb, const int32_t *m_indices,
+                                                  const float *C, void *D, int M, int N, int K,
+                                                  int num_groups, void *stream);
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void *A, const int32_t *sfa, const void *B,
+                                              const int32_t *sfb, const int32_t *masked_m,
+                                              const float *C, void *D, int M_max, int N, int K,
+                                              int num_groups, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);
 
@@ -155,13 +185,15 @@ int dg_get_num_cus(void);
  */
 dg_status dg_init(void);
 
-/* Flag OR-ed into `kind` below for the packed-UE8M0 entry points. */
+/* Flags OR-ed into `kind` below for the packed-UE8M0 and the FP8 x FP4 entry points. */
 #define DG_SCALE_UE8M0 4
+#define DG_SCALE_FP8_FP4 8
 
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these
  * arguments would use, without launching anything.  kind: 0 dense,
- * 1 contiguous, 2 masked (| DG_SCALE_UE8M0 for packed UE8M0 scales); has_c:
+ * 1 contiguous, 2 masked (| DG_SCALE_UE8M0 for packed UE8M0 scales,
+ * | DG_SCALE_FP8_FP4 for FP8 x FP4); has_c:
  * 0/1; rows = M (dense/contiguous) or M_max.
  * Needs no GPU: the code object is built for gfx950 and stored in the cache
  * directory (DG_CACHE_DIR, else <library dir>/jit_cache).

@@ -227,8 +227,8 @@ using namespace dg;
 
 namespace {
 
-// The three forms, for either scale format (sf: 0 FP32, 1 packed UE8M0; the
-// scale pointers are only passed through to the kernel).
+// The three forms, for each scale format (sf: 0 FP32, 1 packed UE8M0, 2 FP8 x
+// FP4 with E2M1 B; the scale pointers are only passed through to the kernel).
 dg_status dense(const void* A, const void* sfa, const void* B, const void* sfb, const float* C, void* D, int M,
                 int N, int K, int sf, void* stream) {
     dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
@@ -296,9 +296,15 @@ dg_status dg_init(void) {
     return ensure_workspace(*st, nullptr, 0, 0, &w);
 }
 
+// Scale format encoded in `kind` by the DG_SCALE_* flags
+int scale_format(int* kind) {
+    const int sf = (*kind & DG_SCALE_FP8_FP4) ? 2 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
+    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4);
+    return sf;
+}
+
 dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus) {
-    const int sf = (kind & DG_SCALE_UE8M0) ? 1 : 0;
-    kind &= ~DG_SCALE_UE8M0;
+    const int sf = scale_format(&kind);
     if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
@@ -313,8 +319,7 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
 
 dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus, char* buf,
                              int len) {
-    const int sf = (kind & DG_SCALE_UE8M0) ? 1 : 0;
-    kind &= ~DG_SCALE_UE8M0;
+    const int sf = scale_format(&kind);
     if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_describe_config: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
@@ -366,6 +371,23 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const int32_t* sf
                                                 const int32_t* sfb, const int32_t* masked_m, const float* C,
                                                 void* D, int M_max, int N, int K, int num_groups, void* stream) {
     return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 1, stream);
+}
+
+dg_status dg_fp8_fp4_gemm_nt(const void* A, const int32_t* sfa, const void* B, const int32_t* sfb, const float* C,
+                             void* D, int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 2, stream);
+}
+
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void* A, const int32_t* sfa, const void* B,
+                                                  const int32_t* sfb, const int32_t* m_indices, const float* C,
+                                                  void* D, int M, int N, int K, int num_groups, void* stream) {
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 2, stream);
+}
+
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* A, const int32_t* sfa, const void* B,
+                                              const int32_t* sfb, const int32_t* masked_m, const float* C, void* D,
+                                              int M_max, int N, int K, int num_groups, void* stream) {
+    return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 2, stream);
 }
 
 }  // extern "C"

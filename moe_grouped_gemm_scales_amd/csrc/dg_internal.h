@@ -28,7 +28,7 @@ struct KernelConfig {
                                // 3: as 1, with an extra producer wave for A and no K-loop barrier
     int has_c = 0;
     int n = 0, k = 0, g = 1;
-    int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0
+    int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0)
     int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
                                // launch two column ranges with different tile widths
 
@@ -38,6 +38,7 @@ struct KernelConfig {
     int threads() const { return 64 * (wm * wn + (variant == 3 ? 1 : 0)); }   // variant 3: + producer wave
     int stage_bytes() const {
         if (variant == 1) return bm * 128 + (bm + 63) / 64 * 256 + 256;
+        if (sf == 2) return bm * 128 + bn * 64 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
     int lds_bytes() const {
@@ -57,7 +58,7 @@ struct Problem {
     int rows;      // M (dense, contiguous) or M_max (masked)
     int n, k, g;
     int has_c;
-    int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0
+    int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4
 };
 
 // Tile heuristics (heuristics.cpp): the launches of one call, in order (one,

@@ -84,7 +84,7 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
     const double t_compute = (compute_cyc + stage_cyc) / kClockHz;
     // operand tiles mostly come from L2/MALL (they are shared between tiles);
     // the HBM bound of the whole launch is applied below
-    const double t_load = (double)(c.bm + c.bn) * kspan / (kCuLoadBytesPerS / occ);
+    const double t_load = (c.bm + (c.sf == 2 ? 0.5 : 1.0) * c.bn) * kspan / (kCuLoadBytesPerS / occ);
     // pipeline fill, epilogue and scheduling per tile; split-K adds a round trip
     double t_fixed = 1.2e-6 + (c.splitk > 1 ? 1.0e-6 * c.splitk + c.bm * c.bn * 8.0 * c.splitk / kCuLoadBytesPerS : 0.0);
     double t = waves * (std::max(t_compute, t_load) + t_fixed);
@@ -96,7 +96,8 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
     const double rows_per_group = valid_rows / groups_b;
     const double b_reads = rows_per_group <= 512 ? std::ceil(rows_per_group / c.bm)
                                                  : std::max(1.0, std::ceil(rows_per_group / c.bm) / 8.0);
-    const double bytes = valid_rows * p.k + b_reads * groups_b * p.n * p.k +
+    const double b_row_bytes = p.sf == 2 ? p.k / 2.0 : (double)p.k;
+    const double bytes = valid_rows * p.k + b_reads * groups_b * p.n * b_row_bytes +
                          valid_rows * p.n * (2.0 + 4.0 * p.has_c);
     t = std::max(t, bytes / kHbmBytesPerS);
     return t;
@@ -105,8 +106,9 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
 int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
     const int rpi = 8 / c.kstep;
-    const int na = c.bm / rpi, nb = c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
-    return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (c.kstep + nw - 1) / nw;
+    const int na = c.bm / rpi, nb = c.sf == 2 ? c.bn / 16 : c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
+    const int nt = c.sf == 2 ? (c.bn + 63) / 64 : c.kstep;
+    return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (nt + nw - 1) / nw;
 }
 
 // Vector-memory instructions per wave per K block of variant 1 (A/sfa DMA
@@ -122,7 +124,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.ne > 0 && (c.nb < 0 || c.nb % 16 || c.nb >= c.ne || c.ne > p.n)) return false;
     if (c.splitk < 1 || (c.splitk > 1 && p.kind != kDense)) return false;   // split-K: dense only
     if (c.sf != p.sf) return false;
-    if (c.sf && (c.variant != 0 || c.kstep != 1)) return false;   // UE8M0: variant 0, one K block a stage
+    if (c.sf && (c.variant != 0 || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
     if (c.variant < 0 || c.variant > 3) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
@@ -183,11 +185,20 @@ const Tuned kTunedE8[] = {
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
+// FP8 x FP4 (variant 0; B tiles are half the bytes of the FP8 ones)
+const Tuned kTunedF4[] = {
+    {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
+    {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
+};
+
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
     std::vector<KernelConfig> out;
     if (num_cus != 256) return out;       // measured on the full 256-CU part
-    const Tuned* first = p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
-    const Tuned* last = p.sf ? std::end(kTunedE8) : std::end(kTuned);
+    const Tuned* first = p.sf == 2 ? std::begin(kTunedF4) : p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
+    const Tuned* last = p.sf == 2 ? std::end(kTunedF4) : p.sf ? std::end(kTunedE8) : std::end(kTuned);
     for (const Tuned* it = first; it != last; ++it) {
         const Tuned& t = *it;
         if (t.kind != p.kind || t.n != p.n || t.k != p.k || t.g != p.g || t.has_c != p.has_c) continue;

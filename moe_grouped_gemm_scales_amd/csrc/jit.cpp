@@ -182,7 +182,8 @@ std::string KernelConfig::key() const {
     s << "k" << kind << (variant ? "v" + std::to_string(variant) : std::string()) << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
       << "_sk" << splitk
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
-    if (sf) s << "_e8m0";
+    if (sf == 1) s << "_e8m0";
+    if (sf == 2) s << "_f8f4";
     if (ne > 0) s << "_cols" << nb << "-" << ne;
     return s.str();
 }

@@ -64,6 +64,11 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 // factors packed into one 32-bit integer): byte j of a word is K block 4w + j,
 // sfa words [ceil(K/512)][rows], sfb words [ceil(N/128)][ceil(K/512)].  The
 // MFMA applies UE8M0 block scales itself, so there is no promotion step.
+// 2 = FP8 x FP4 (DeepGEMM-Ascend hub page, precision table; DeepGEMM README
+// news 2026.04.16): A and sfa as for 1; B holds OCP E2M1 codes, two per byte
+// (element 2i in the low nibble of byte i), [N][K/2]; sfb holds one UE8M0
+// scale per 1x32 block of each row of B, the four of a 128-wide K block in
+// one word, [N][K/128] (byte j: K elements 128 kb + 32 j .. + 32).
 #ifndef DG_SF
 #define DG_SF 0
 #endif
@@ -96,11 +101,14 @@ constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D;
 static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
 constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
 constexpr bool SF_E8 = DG_SF != 0;
+constexpr bool FP4B = DG_SF == 2;             // B in E2M1 with per-row 1x32 UE8M0 scales
 constexpr int KW = (KBLKS + 3) / 4;           // packed UE8M0 words per row of scales
 constexpr int SF_KB = SF_E8 ? KW : KBLKS;     // scale entries (floats or words) along K
+constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
-// WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N)
-constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0;
+// WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N);
+// FP4 B has a scale per row, never one per wave
+constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0 && !FP4B;
 
 static_assert(K % KBLK == 0, "K must be a multiple of 128");
 static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles must be 16-aligned");
@@ -184,6 +192,12 @@ __device__ __forceinline__ v8i lds_read_frag(lds_u8* lo, lds_u8* hi, int off) {
     return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 __device__ __forceinline__ float lds_read_f32(lds_u8* base, int off) { return *(lds_f32*)(base + off); }
+// FP4 fragment: 32 E2M1 codes in 16 bytes; the MFMA reads only the low four
+// registers of an FP4 operand.
+__device__ __forceinline__ v8i lds_read_frag4(lds_u8* p, int off) {
+    const v4i a = *(lds_v4i*)(p + off);
+    return v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+}
 
 // ------------------------------------------------------------ tile decode
 struct Tile {
@@ -284,6 +298,16 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
 template <int TM_, int TN_>
 __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f (&acc)[TM_][TN_], int row0,
                                             int col0, int tid, int* s_flag) {
+    // An MFMA reads the operands of every lane of its wave, whatever EXEC
+    // holds.  Pin every accumulator here, while the whole wave is active:
+    // otherwise, when the K loop is short enough to be laid out straight, the
+    // compiler may sink the last MFMAs, with the per-lane values feeding them
+    // (scale shifts, fragment reads), into the row-guarded stores below, where
+    // those values are only computed for the lanes of rows that are stored.
+#pragma unroll
+    for (int a = 0; a < TM_; ++a)
+#pragma unroll
+        for (int b = 0; b < TN_; ++b) asm volatile("" : "+v"(acc[a][b]));
     // ---- split-K: publish the partial, the last arrival sums all in split order
     if constexpr (SPLITK > 1) {
         float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
@@ -415,23 +439,28 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_impl(f, typename 
 // far better in 256-byte than in 128-byte pieces.
 constexpr int ROWB = 128 * KSTEP;               // bytes of one tile row in a stage
 constexpr int RPI = 1024 / ROWB;                // tile rows per 1 KB DMA instruction
+// FP4 B: a K block of a row is 64 bytes, 16 rows per instruction, its four
+// 16-byte chunks XOR-swizzled by (row >> 2) & 3
+constexpr int ROWB_B = FP4B ? 64 : ROWB;
+constexpr int RPI_B = 1024 / ROWB_B;
 constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
-constexpr int NB_INS = BN / RPI;                // ... for B
+constexpr int NB_INS = BN / RPI_B;              // ... for B
 constexpr int NS_PER_KB = (BM + 63) / 64;       // 256 B DMA instructions for one K block of sfa
 constexpr int NS_INS = NS_PER_KB * KSTEP;
 constexpr int A_OFF = 0;
 constexpr int B_OFF = BM * ROWB;
-constexpr int S_OFF = B_OFF + BN * ROWB;
+constexpr int S_OFF = B_OFF + BN * ROWB_B;
 constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
 // sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
-// DMA per K block, so the K loop issues no scalar loads
+// DMA per K block, so the K loop issues no scalar loads; FP4 B: one word per
+// row of the tile, 64 rows per DMA
 constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
-constexpr int NT_INS = KSTEP;
-constexpr int STAGE_BYTES = T_OFF + KSTEP * 256;
+constexpr int NT_INS = FP4B ? (BN + 63) / 64 : KSTEP;
+constexpr int STAGE_BYTES = T_OFF + NT_INS * 256;
 static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles are loaded RPI rows per instruction");
+static_assert(BM % RPI == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 
 // Every wave issues the same number of DMA instructions per stage, so one
@@ -486,11 +515,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
     // has to agree between the two operands, and it does: both use this map);
     // with chunks XOR-swizzled by row & 7 these reads are free of LDS bank
     // conflicts on gfx950, where chunks 2q, 2q + 1 were not.
+    // The matrix core pairs the operands by its own K index: in an E4M3
+    // operand, bytes 0-15 of lane group q are K 16q .. 16q+15 and bytes 16-31
+    // are K 64+16q .. 64+16q+15 (the map above, so these are those K); in an
+    // E2M1 operand, the 32 codes of lane group q are K 32q .. 32q+31, which is
+    // 16-byte chunk q of B's 64-byte row, and the lane's scale byte applies
+    // to them: exactly one 1x32 scale block (mapped with one-hot rows of A).
     const int sw = l16 & 7;
     const u32 chunk_lo = (u32)((q ^ sw) << 4);
     const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
     const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * ROWB;
-    const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * ROWB;
+    const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * ROWB_B;
+    const u32 b_chunk_lo = FP4B ? (u32)((q ^ ((l16 >> 2) & 3)) << 4) : chunk_lo;
 
 #pragma unroll 1
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
@@ -510,11 +546,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         }
         a_rows_total = p.M;
         const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
-        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * K;
+        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * KB_B;
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
-        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * K);
+        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
         const v4i rs_s = make_rsrc(sfa_base, (u32)SF_KB * a_rows_total * 4u);
-        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
+        const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
+                              : make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
         const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
         // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
@@ -536,6 +573,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         u32 voff_rows[NPAR];
 #pragma unroll
         for (int par = 0; par < NPAR; ++par) voff_rows[par] = lane_voff(par);
+        // FP4 B: lane l writes row l / 4 of the instruction's 16, physical chunk
+        // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
+        // swizzle term does not depend on the instruction (16 rows each)
+        const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
         u32 voff_s[IS];          // A scales: clamped rows (the offset includes the K block's row of sfa)
 #pragma unroll
         for (int j = 0; j < IS; ++j) {
@@ -549,8 +590,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int h = min(wave + j * NWAVES, NT_INS - 1);
-            const int nb = min(nb_t0 + lane, NBLKS - 1);
-            voff_t[j] = (u32)nb * SF_KB * 4u + (u32)h * 4u;
+            if constexpr (FP4B) {
+                // word [n0 + 64 h + lane][kb]; rows past the tile read as zero
+                voff_t[j] = (u32)(64 * h + lane) * KBLKS * 4u;
+            } else {
+                const int nb = min(nb_t0 + lane, NBLKS - 1);
+                voff_t[j] = (u32)nb * SF_KB * 4u + (u32)h * 4u;
+            }
         }
 
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
@@ -571,16 +617,20 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                       __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
             } else if (j < IA + IB) {
                 const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
-                dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
-                      __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+                if constexpr (FP4B)
+                    dma16(lim(rs_b), voff_b4 + (u32)__builtin_amdgcn_readfirstlane(i * RPI_B * KB_B),
+                          __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + B_OFF + i * 1024);
+                else
+                    dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                          __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
                 dma4(lim(rs_s), voff_s[j - IA - IB], __builtin_amdgcn_readfirstlane((u32)sf_row(kb) * a_rows_total * 4u),
                      st + S_OFF + i * 256);
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
-                dma4(lim(rs_t), voff_t[j - IA - IB - IS], __builtin_amdgcn_readfirstlane((u32)sf_row(kb) * 4u),
-                     st + T_OFF + h * 256);
+                dma4(lim(rs_t), voff_t[j - IA - IB - IS],
+                     __builtin_amdgcn_readfirstlane((u32)(FP4B ? kb : sf_row(kb)) * 4u), st + T_OFF + h * 256);
             }
         };
         auto issue_stage = [&](int kb, int stage, bool live = true) {
@@ -629,8 +679,17 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             // One K block per stage: the barrier sits in the last n sub-tile, where
             // the next K block's fragments are fetched while its MFMAs run.
             // LDS bases of one K block (stage slot, K block h inside the stage)
-            const u32 b_frag = b_frag_off + chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
+            const u32 b_frag = b_frag_off + b_chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
             const u32 a_frag = a_frag_off + chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
+            // B fragment of the sub-tile at byte offset off of a K block (lo/hi:
+            // the block's base plus this lane's chunk offsets)
+            auto read_fb = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
+                if constexpr (FP4B) return lds_read_frag4(lo, off);
+                else return lds_read_frag(lo, hi, off);
+            };
+            // FP4 B scales: this lane's row of each n sub-tile, one word per K block
+            const int sb4_off = (wn * WAVE_N + l16) * 4;
+            const u32 sh_q = 8u * (u32)q;    // lane group q takes byte q (its 32-wide K block)
             auto kblock_base = [&](int stage, int h) __attribute__((always_inline)) {
                 return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + h * 128);
             };
@@ -649,7 +708,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             float sb[TN];
             auto read_scales = [&](int stage, int h) __attribute__((always_inline)) {
                 lds_u8* const sb_p = kblock_sfb(stage, h);
-                if constexpr (SB_UNIFORM) {
+                if constexpr (FP4B) {
+#pragma unroll
+                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
+                } else if constexpr (SB_UNIFORM) {
                     sb[0] = lds_read_f32(sb_p, sb_off[0]);
                 } else {
 #pragma unroll
@@ -669,7 +731,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 read_scales(0, 0);
 #pragma unroll
                 for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(kb0 + a_frag, kb0 + a_frag_hi, A_OFF + a * 16 * ROWB);
-                fb = lds_read_frag(kb0 + b_frag, kb0 + b_frag_hi, B_OFF);
+                fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, B_OFF);
             }
 
 #pragma unroll 1
@@ -707,7 +769,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
                     for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
 #pragma unroll
-                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
+                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
+                        eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> (FP4B ? sh_q : sh));
                 }
 
                 // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
@@ -727,7 +790,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     }
                     const bool last = b + 1 == TN;
                     v8i fb_next;
-                    if (!last) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
+                    if (!last) fb_next = read_fb(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB_B);
                     // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
                     // b itself (carried), taken before the next K block's replace them
                     float sc_prev[TM], s_last[TM];
@@ -756,9 +819,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     for (int a = 0; a < TM; ++a) {
                         if constexpr (SF_E8) {
                             // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
-                            // scales (its srcA is B, scaled by eb; its srcB is A, by ea)
+                            // scales (its srcA is B, scaled by eb; its srcB is A, by ea).
+                            // srcA format: 0 = E4M3, 4 = E2M1 (FP4 B)
                             acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                fb, fa[a], acc[a][b], 0, 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
+                                fb, fa[a], acc[a][b], FP4B ? 4 : 0, 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
                         } else {
                             const v4f zero = {0.f, 0.f, 0.f, 0.f};
                             // P[n][m] over this 128-wide K block: exact products, FP32 sums
@@ -774,7 +838,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     if (!last) {
                         fb = fb_next;
                     } else {
-                        fb = lds_read_frag(kbn + b_frag, kbn + b_frag_hi, B_OFF);
+                        fb = read_fb(kbn + b_frag, kbn + b_frag_hi, B_OFF);
 #pragma unroll
                         for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
                     }

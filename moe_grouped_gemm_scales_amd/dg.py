@@ -46,9 +46,13 @@ def _load():
     lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    lib.dg_fp8_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
+    lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_m_grouped_fp8_fp4_gemm_nt_masked.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
     for f in (lib.dg_fp8_gemm_nt, lib.dg_m_grouped_fp8_gemm_nt_contiguous, lib.dg_m_grouped_fp8_gemm_nt_masked,
               lib.dg_fp8_gemm_nt_ue8m0, lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0,
-              lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0):
+              lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0, lib.dg_fp8_fp4_gemm_nt,
+              lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous, lib.dg_m_grouped_fp8_fp4_gemm_nt_masked):
         f.restype = i32
     lib.dg_last_error.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -259,3 +263,84 @@ def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(A, sfa, B, sfb, masked_m, C, D, stream
 fp8_gemm_nt = dg_fp8_gemm_nt
 m_grouped_fp8_gemm_nt_contiguous = dg_m_grouped_fp8_gemm_nt_contiguous
 m_grouped_fp8_gemm_nt_masked = dg_m_grouped_fp8_gemm_nt_masked
+
+
+# ---------------------------------------------------------------- FP8 x FP4
+SCALE_FP8_FP4 = 8    # DG_SCALE_FP8_FP4: OR into `kind` of precompile / describe_config
+
+
+def _i32(t: torch.Tensor, name: str, shape):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32 (packed UE8M0), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _dev(t, name)
+
+
+def _fp4(t: torch.Tensor, name: str, shape):
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 (two E2M1 codes per byte), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _dev(t, name)
+
+
+def dg_fp8_fp4_gemm_nt(A, sfa, B, sfb, C, D, stream=None):
+    """D = C + A @ B.T with E2M1 B.  A [M,K] E4M3, sfa int32 [ceil(K/512),M] (UE8M0, 1x128),
+    B uint8 [N,K/2] (element 2i in the low nibble of byte i), sfb int32 [N,K/128] (UE8M0, 1x32)."""
+    _fp8(A, "A")
+    M, K = A.shape
+    N = B.shape[0]
+    _fp4(B, "B", (N, K // 2))
+    _i32(sfa, "sfa", (_cdiv(_cdiv(K, 128), 4), M))
+    _i32(sfb, "sfb", (N, _cdiv(K, 128)))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_fp8_fp4_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K,
+                                  _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    """Contiguous M-grouped FP8 x FP4: B uint8 [G,N,K/2], sfb int32 [G,N,K/128]; A/sfa as the dense form."""
+    _fp8(A, "A")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _fp4(B, "B", (G, N, K // 2))
+    _i32(sfa, "sfa", (_cdiv(_cdiv(K, 128), 4), M))
+    _i32(sfb, "sfb", (G, N, _cdiv(K, 128)))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
+                                                       _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream=None):
+    """Masked M-grouped FP8 x FP4: A [G,M_max,K], sfa int32 [G,ceil(K/512),M_max], B uint8 [G,N,K/2],
+    sfb int32 [G,N,K/128]."""
+    _fp8(A, "A")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _fp4(B, "B", (G, N, K // 2))
+    _i32(sfa, "sfa", (G, _cdiv(_cdiv(K, 128), 4), M_max))
+    _i32(sfb, "sfb", (G, N, _cdiv(K, 128)))
+    if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be int32 [G]")
+    _dev(masked_m, "masked_m")
+    if C is not None:
+        _f32(C, "C", (G, M_max, N))
+    _out(D, (G, M_max, N))
+    _check(lib.dg_m_grouped_fp8_fp4_gemm_nt_masked(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m),
+                                                   _ptr(C), _ptr(D), M_max, N, K, G, _stream(stream)))
+    return D
+
+
+fp8_fp4_gemm_nt = dg_fp8_fp4_gemm_nt
+m_grouped_fp8_fp4_gemm_nt_contiguous = dg_m_grouped_fp8_fp4_gemm_nt_contiguous
+m_grouped_fp8_fp4_gemm_nt_masked = dg_m_grouped_fp8_fp4_gemm_nt_masked

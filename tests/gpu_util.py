@@ -29,7 +29,16 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
         D = sent.to("cuda")
     else:
         D.copy_(sent.to("cuda"))
-    if p.kind == "dense":
+    if p.fp4:
+        if p.kind == "dense":
+            dg.dg_fp8_fp4_gemm_nt(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
+        elif p.kind == "contiguous":
+            dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(dev["A"], dev["sfa"], dev["B"], dev["sfb"],
+                                                       dev["m_indices"], dev["C"], D)
+        else:
+            dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["masked_m"],
+                                                   dev["C"], D)
+    elif p.kind == "dense":
         dg.dg_fp8_gemm_nt(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
     elif p.kind == "contiguous":
         dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["m_indices"],
@@ -44,6 +53,11 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
 def oracle_rows(oracle, p: gen.Problem, rows=None, threads=0):
     """(reference FP64 [rows, N], computed mask [rows]) for flat row indices."""
     d = gen.to_numpy(p)
+    if p.fp4:         # FP8 x FP4: E2M1 B with 1x32 UE8M0 scales
+        gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
+        ref, comp = oracle.fp8_fp4_gemm(p.kind, d["A"], d["sfa"], d["B"], d["sfb"], gi, d["C"], rows=rows,
+                                        threads=threads)
+        return ref, comp
     if p.ue8m0:       # packed UE8M0 scales: the oracle unpacks them to the FP32 scales they stand for
         Kb = p.K // 128
         d["sfa"] = oracle.unpack_sfa_ue8m0(d["sfa"], Kb)
