@@ -19,6 +19,9 @@ Semantics and citations are in the header of ``oracle.c``:
 * DeepGEMM-Ascend hub page (precision table: FP8 x FP4) and README news
   2026.04.16 (FP8xFP4 GEMM; FP4 weights with UE8M0 scale factors): E2M1
   weights with one UE8M0 scale per 1x32 block, A as in the UE8M0 form.
+* DeepGEMM README, "Grouped GEMM (contiguous layout)": the K-axis grouped TN
+  call for the MoE weight backward (M and N fixed), both operands K-outermost
+  with one FP32 scale per 128 K rows of each column.
 """
 from __future__ import annotations
 
@@ -67,6 +70,9 @@ def _declare(lib):
     lib.oracle_e2m1_value.argtypes = [c.c_uint8]
     lib.oracle_fp8_fp4_gemm.restype = c.c_int
     lib.oracle_fp8_fp4_gemm.argtypes = [c.c_int, p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                        p, c.c_int64, p, p, c.c_int]
+    lib.oracle_k_grouped_tn.restype = c.c_int
+    lib.oracle_k_grouped_tn.argtypes = [p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
                                         p, c.c_int64, p, p, c.c_int]
     lib.oracle_default_threads.restype = c.c_int
     lib.oracle_default_threads.argtypes = []
@@ -199,6 +205,30 @@ class Oracle:
                                           _ptr(r), nr, _ptr(out), _ptr(comp), threads)
         if rc != 0:
             raise ValueError("oracle_fp8_fp4_gemm: bad sizes")
+        return out, comp.astype(bool)
+
+    # ---------------------------------------------------------- K-grouped TN
+    def k_grouped_tn(self, A, sfa, B, sfb, ks, C=None, rows=None, threads=0):
+        """(D FP64 [rows, N], computed [rows]) of the K-grouped TN GEMM.
+
+        A [K,M] and B [K,N] E4M3 codes (K outermost), sfa [K/128,M] and sfb [K/128,N] FP32,
+        ks [G] int32 K rows per group (consecutive segments), C None or [G,M,N] FP32.
+        Rows are flat g*M + m (all G*M by default); every row is computed.
+        """
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32); C = _c(C, np.float32)
+        ks = _c(ks, np.int32)
+        K, M = A.shape
+        N = B.shape[1]
+        G = ks.shape[0]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else G * M
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_k_grouped_tn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(ks), _ptr(C), M, N, K, G,
+                                          _ptr(r), nr, _ptr(out), _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_k_grouped_tn: bad sizes")
         return out, comp.astype(bool)
 
     def fp8_gemm_nt(self, A, sfa, B, sfb, C=None, rows=None, threads=0):

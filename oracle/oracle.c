@@ -25,6 +25,9 @@
  *    at S.1111.111), because the workloads scale blocks by amax/448.
  *  - Block sizes: A scales per 1x128 (one row, one K block), B scales per
  *    128x128 (128 rows of B, one K block).
+ *  - DeepGEMM README, "Grouped GEMM (contiguous layout)": a K-axis grouped
+ *    call (k_grouped_fp8_gemm_tn_contiguous) for the MoE weight backward,
+ *    M and N fixed; see compute_row_kgrouped for its reading.
  *
  * What is computed, for every output row m that is computed and every n:
  *     S[m,n,kb] = sum_{k in block kb} e4m3(A[m,k]) * e4m3(B[n,k])      (FP64)
@@ -268,7 +271,7 @@ static void compute_row_fp4(const row_job4 *j)
 /* ------------------------------------------------------------------ */
 /* Row scheduling over threads.                                        */
 /* ------------------------------------------------------------------ */
-enum { KIND_DENSE = 0, KIND_CONTIG = 1, KIND_MASKED = 2 };
+enum { KIND_DENSE = 0, KIND_CONTIG = 1, KIND_MASKED = 2, KIND_KGROUP = 3 };
 
 typedef struct {
     int kind;
@@ -281,7 +284,52 @@ typedef struct {
     double *out; uint8_t *computed;
     double dec[256];
     int fp4;                     /* FP8 x FP4: sfa/sfb are packed UE8M0 words, B is E2M1 */
+    const int64_t *k_off;        /* K-grouped: first K row of each group's segment ([G + 1]) */
 } problem;
+
+/* ------------------------------------------------------------------ */
+/* K-grouped TN (DeepGEMM README, "Grouped GEMM (contiguous layout)":  */
+/* a K-axis grouped call for the weight backward of MoE, M and N       */
+/* fixed).  Both operands are stored K-outermost ("TN": A [K][M],       */
+/* B [K][N]) and group g owns the K rows [k_off[g], k_off[g + 1]):      */
+/*   D[g][m][n] = C[g][m][n]                                           */
+/*              + sum_{kb in g} sfa[kb][m] * sfb[kb][n] * S[kb][m][n], */
+/*   S = sum over the 128 k of block kb of e4m3(A[k][m]) e4m3(B[k][n]) */
+/* (reading: both operands carry one FP32 scale per 128 K rows of each */
+/* column, 1x128 along K, the granularity of the A scales of the other */
+/* forms).  S is exact in FP64 as for the other forms; the outer sum   */
+/* runs in ascending kb.  The block sums of all n are formed together  */
+/* (k outer, n inner), which changes nothing: each is exact.           */
+/* ------------------------------------------------------------------ */
+static void compute_row_kgrouped(const problem *p, int64_t g, int64_t m, double *out)
+{
+    const int N = p->N;
+    const int64_t M = p->M;
+    const int64_t kb_first = p->k_off[g] / ORACLE_KBLOCK, kb_end = p->k_off[g + 1] / ORACLE_KBLOCK;
+    double *s = (double *)malloc(sizeof(double) * (size_t)N);
+    for (int n = 0; n < N; ++n)
+        out[n] = 0.0;
+    for (int64_t kb = kb_first; kb < kb_end; ++kb) {
+        for (int n = 0; n < N; ++n)
+            s[n] = 0.0;
+        for (int64_t k = kb * ORACLE_KBLOCK; k < (kb + 1) * ORACLE_KBLOCK; ++k) {
+            const double a = p->dec[p->A[k * M + m]];
+            const uint8_t *b_row = p->B + k * (int64_t)N;
+            for (int n = 0; n < N; ++n)
+                s[n] += a * p->dec[b_row[n]];
+        }
+        const double sa = (double)p->sfa[kb * M + m];
+        const float *sb = p->sfb + kb * (int64_t)N;
+        for (int n = 0; n < N; ++n)
+            out[n] += sa * (double)sb[n] * s[n];
+    }
+    free(s);
+    if (p->C) {
+        const float *c_row = p->C + (g * M + m) * (int64_t)N;
+        for (int n = 0; n < N; ++n)
+            out[n] += (double)c_row[n];
+    }
+}
 
 typedef struct { const problem *p; int64_t r0, r1; } slice;
 
@@ -294,6 +342,11 @@ static void do_row(const problem *p, int64_t i)
     row_job j;
     j.dec = p->dec; j.N = p->N; j.K = p->K; j.out = out;
 
+    if (p->kind == KIND_KGROUP) {            /* flat row r = g * M + m */
+        compute_row_kgrouped(p, r / p->M, r % p->M, out);
+        if (p->computed) p->computed[i] = 1;
+        return;
+    }
     if (p->kind == KIND_DENSE) {
         j.a_row = p->A + r * p->K;
         j.sa = p->sfa + r; j.sa_stride = p->M;
@@ -480,4 +533,36 @@ int oracle_fp8_fp4_gemm(int kind, const uint8_t *A, const int32_t *sfa, const ui
     p.n_rows = rows ? n_rows : (kind == KIND_MASKED ? (int64_t)G * M : M);
     p.out = out; p.computed = computed;
     return run(&p, n_threads);
+}
+
+/*
+ * K-grouped TN contiguous (see compute_row_kgrouped):
+ *   A [K][M] e4m3 codes, sfa [K/128][M], B [K][N] codes, sfb [K/128][N] fp32,
+ *   ks [G] int32: K rows of each group, in order (reading: each a multiple of
+ *   128; a negative count is 0; segments are cut at K), C NULL or [G][M][N].
+ *   rows: flat indices g*M + m (NULL: all G*M rows); out [rows][N] FP64.
+ *   Returns 0, or -1 on bad sizes (K not a multiple of 128, a segment not
+ *   starting on a multiple of 128).
+ */
+int oracle_k_grouped_tn(const uint8_t *A, const float *sfa, const uint8_t *B, const float *sfb,
+                        const int32_t *ks, const float *C, int64_t M, int N, int K, int G,
+                        const int64_t *rows, int64_t n_rows, double *out, uint8_t *computed, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    if (G <= 0 || K <= 0 || K % ORACLE_KBLOCK != 0) return -1;
+    int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    off[0] = 0;
+    for (int g = 0; g < G; ++g) {
+        int64_t k = ks[g] < 0 ? 0 : ks[g];
+        int64_t end = off[g] + k;
+        off[g + 1] = end > K ? K : end;
+        if (off[g + 1] % ORACLE_KBLOCK != 0) { free(off); return -1; }
+    }
+    p.kind = KIND_KGROUP; p.A = A; p.sfa = sfa; p.B = B; p.sfb = sfb; p.C = C;
+    p.M = M; p.N = N; p.K = K; p.G = G; p.k_off = off;
+    p.rows = rows; p.n_rows = rows ? n_rows : (int64_t)G * M; p.out = out; p.computed = computed;
+    int rc = run(&p, n_threads);
+    free(off);
+    return rc;
 }

@@ -230,6 +230,57 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, 
     return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0, fp4=fp4)
 
 
+# ---------------------------------------------------------------- K-grouped TN
+@dataclasses.dataclass
+class KGroupedProblem:
+    """K-grouped TN: both operands K-outermost, one FP32 scale per 128 K rows of each column."""
+    A: torch.Tensor                 # u8 codes [K, M]
+    sfa: torch.Tensor               # fp32 [K/128, M]
+    B: torch.Tensor                 # u8 codes [K, N]
+    sfb: torch.Tensor               # fp32 [K/128, N]
+    ks: torch.Tensor                # int32 [G]: K rows of each group, consecutive segments
+    C: Optional[torch.Tensor] = None   # fp32 [G, M, N]
+    seed: int = 0
+    kind: str = "k_grouped"
+
+    @property
+    def M(self):
+        return self.A.shape[1]
+
+    @property
+    def N(self):
+        return self.B.shape[1]
+
+    @property
+    def K(self):
+        return self.A.shape[0]
+
+    @property
+    def G(self):
+        return self.ks.shape[0]
+
+
+def quantize_k_blocks(x: torch.Tensor):
+    """x [K, M] fp32 -> (codes u8 [K, M], scales fp32 [K/128, M]): one scale per 128 K rows
+    of each column (the 1x128 rule of quantize_1x128, applied along K)."""
+    q, s = quantize_1x128(x.t().contiguous())
+    return q.t().contiguous(), s
+
+
+def make_k_grouped(ks, M, N, seed, with_c=False) -> KGroupedProblem:
+    """Groups g of ks[g] K rows each (multiples of 128), values ~N(0,1) drawn A, B, C."""
+    g = _gen(seed)
+    K = int(sum(ks))
+    a = torch.randn(K, M, generator=g, dtype=torch.float32)
+    b = torch.randn(K, N, generator=g, dtype=torch.float32)
+    c = torch.randn(len(ks), M, N, generator=g, dtype=torch.float32) if with_c else None
+    A, sfa = quantize_k_blocks(a)
+    del a
+    B, sfb = quantize_k_blocks(b)
+    del b
+    return KGroupedProblem(A, sfa, B, sfb, torch.as_tensor(ks, dtype=torch.int32), C=c, seed=seed)
+
+
 # ---------------------------------------------------------------- the five workloads
 # (shapes: DeepGEMM launch article, section 3, dense table and MoE table)
 WORKLOADS = {

@@ -449,3 +449,80 @@ def test_fp4_quantiser_rounds_to_nearest(oracle):
     err = np.abs(np.abs(y)[..., None] - mags).min(-1)
     assert np.allclose(np.abs(np.abs(q) - np.abs(y)), err)
     assert np.all(np.abs(y) <= 6.0)
+
+
+# ------------------------------------------------------------------ K-grouped TN
+def _kg_dequant_ref(p):
+    """numpy FP64 per group: C_g + (A_seg * sfa)^T @ (B_seg * sfb), from torch's E4M3 decode."""
+    dec = torch_decode_table()
+    A = dec[p.A.numpy()] * np.repeat(p.sfa.numpy().astype(np.float64), 128, axis=0)   # [K, M]
+    B = dec[p.B.numpy()] * np.repeat(p.sfb.numpy().astype(np.float64), 128, axis=0)   # [K, N]
+    out, off = [], 0
+    for g, k in enumerate(p.ks.tolist()):
+        d = A[off:off + k].T @ B[off:off + k]
+        if p.C is not None:
+            d = d + p.C[g].numpy().astype(np.float64)
+        out.append(d)
+        off += k
+    return np.concatenate(out, axis=0)
+
+
+@pytest.mark.parametrize("ks,M,N", [([128, 256, 0, 384], 37, 129), ([512], 1, 5), ([0, 128], 130, 64)])
+def test_k_grouped_vs_numpy_dequant_matmul(oracle, ks, M, N):
+    p = gen.make_k_grouped(ks, M, N, seed=sum(ks) + M + N, with_c=True)
+    got, comp = oracle.k_grouped_tn(p.A, p.sfa, p.B, p.sfb, p.ks, p.C)
+    assert comp.all()
+    ref = _kg_dequant_ref(p)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-9)
+
+
+def test_k_grouped_equals_dense_nt_on_transposed_operands(oracle):
+    """With B scales constant over each 128 columns, group g is the dense NT GEMM of
+    A_seg^T and B_seg^T with sfb[nb][kb]: the same exact block sums in the same order,
+    so the results agree bit for bit (a different oracle entry point, pinned above)."""
+    g = torch.Generator().manual_seed(61)
+    ks, M, N = [256, 384], 70, 200
+    p = gen.make_k_grouped(ks, M, N, seed=62, with_c=True)
+    Kb = sum(ks) // 128
+    sb_blocks = gen.pow2_scales((Kb, (N + 127) // 128), g)
+    sfb = torch.repeat_interleave(sb_blocks, 128, dim=1)[:, :N].contiguous()
+    got, _ = oracle.k_grouped_tn(p.A, p.sfa, p.B, sfb, p.ks, p.C)
+    got = got.reshape(len(ks), M, N)
+    off = 0
+    for gi, k in enumerate(ks):
+        A = p.A[off:off + k].t().contiguous()
+        B = p.B[off:off + k].t().contiguous()
+        sfa = p.sfa[off // 128:(off + k) // 128].contiguous()
+        sfb_nt = sb_blocks[off // 128:(off + k) // 128].t().contiguous()
+        ref = oracle.fp8_gemm_nt(A.numpy(), sfa.numpy(), B.numpy(), sfb_nt.numpy(), p.C[gi].numpy())
+        assert np.array_equal(got[gi], ref)
+        off += k
+
+
+def test_k_grouped_operand_swap_transposes(oracle):
+    p = gen.make_k_grouped([128, 256], 45, 77, seed=63)
+    d, _ = oracle.k_grouped_tn(p.A, p.sfa, p.B, p.sfb, p.ks)
+    e, _ = oracle.k_grouped_tn(p.B, p.sfb, p.A, p.sfa, p.ks)
+    assert np.array_equal(d.reshape(2, 45, 77), e.reshape(2, 77, 45).transpose(0, 2, 1))
+
+
+def test_k_grouped_empty_group_and_closed_form(oracle):
+    """ks = 0 gives D = C exactly; all-ones codes (E4M3 1.0) with constant power-of-two
+    scales give D = ks[g] * sA * sB exactly."""
+    ks, M, N = [256, 0, 128], 9, 33
+    K = sum(ks)
+    ones_a = torch.full((K, M), gen.E4M3_ONE, dtype=torch.uint8)
+    ones_b = torch.full((K, N), gen.E4M3_ONE, dtype=torch.uint8)
+    sfa = torch.full((K // 128, M), 0.25)
+    sfb = torch.full((K // 128, N), 8.0)
+    C = torch.randn(3, M, N, generator=torch.Generator().manual_seed(64))
+    d, _ = oracle.k_grouped_tn(ones_a, sfa, ones_b, sfb, torch.tensor(ks, dtype=torch.int32), C)
+    d = d.reshape(3, M, N)
+    for g, k in enumerate(ks):
+        assert np.array_equal(d[g], k * 2.0 + C[g].numpy().astype(np.float64))
+
+
+def test_k_grouped_bad_segments_rejected(oracle):
+    p = gen.make_k_grouped([128, 128], 4, 4, seed=65)
+    with pytest.raises(ValueError):
+        oracle.k_grouped_tn(p.A, p.sfa, p.B, p.sfb, torch.tensor([64, 192], dtype=torch.int32))

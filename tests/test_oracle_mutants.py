@@ -45,6 +45,15 @@ MUTANTS = [
      "uint8_t nib = (k & 1) ? (byte & 0xF) : (byte >> 4);"),
     ("fp4_scale_block_64", "acc += sa * oracle_ue8m0_value(ue8m0_byte(wb, blk)) * s;",
      "acc += sa * oracle_ue8m0_value(ue8m0_byte(wb, blk / 2)) * s;"),
+    ("kg_drop_last_k_block", "for (int64_t kb = kb_first; kb < kb_end; ++kb) {",
+     "for (int64_t kb = kb_first; kb < kb_end - 1; ++kb) {"),
+    ("kg_previous_segment", "const int64_t kb_first = p->k_off[g] / ORACLE_KBLOCK,",
+     "const int64_t kb_first = p->k_off[g > 0 ? g - 1 : 0] / ORACLE_KBLOCK,"),
+    ("kg_a_k_contiguous", "const double a = p->dec[p->A[k * M + m]];",
+     "const double a = p->dec[p->A[m * (int64_t)p->K + k]];"),
+    ("kg_sfb_first_block", "const float *sb = p->sfb + kb * (int64_t)N;",
+     "const float *sb = p->sfb + kb_first * (int64_t)N;"),
+    ("kg_c_ignored", "            out[n] += (double)c_row[n];", "            out[n] += 0.0 * (double)c_row[n];"),
 ]
 
 
@@ -64,8 +73,11 @@ def _pin_calls(o):
               pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset,
               pins.test_ue8m0_points_from_format, pins.test_ue8m0_packing_byte_order_and_layouts,
               pins.test_ue8m0_all_ones_closed_form, pins.test_e2m1_points_from_format,
-              pins.test_fp8_fp4_nibble_order_and_block_scales, pins.test_fp8_fp4_grouped_equal_dense):
+              pins.test_fp8_fp4_nibble_order_and_block_scales, pins.test_fp8_fp4_grouped_equal_dense,
+              pins.test_k_grouped_equals_dense_nt_on_transposed_operands,
+              pins.test_k_grouped_operand_swap_transposes, pins.test_k_grouped_empty_group_and_closed_form):
         calls.append(lambda f=f: f(o))
+    calls.append(lambda: pins.test_k_grouped_vs_numpy_dequant_matmul(o, [128, 256, 0, 384], 37, 129))
     return calls
 
 
