@@ -160,6 +160,36 @@ dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void *A, const int32_t *sfa,
                                               const float *C, void *D, int M_max, int N, int K,
                                               int num_groups, void *stream);
 
+/*
+ * K-grouped, TN, contiguous (MoE weight backward).  DeepGEMM README, "Grouped
+ * GEMM (contiguous layout)": a K-axis grouped call (k_grouped_fp8_gemm_tn_contiguous)
+ * with M and N fixed; the groups' K segments are concatenated along K.  The
+ * page names the call only, so its layout is a reading:
+ *   A uint8 (E4M3) [K][M] and B uint8 (E4M3) [K][N]: both K-outermost ("TN";
+ *     row k of A holds the M values of K index k), the layout in which token
+ *     gradients and activations are stored for a weight gradient;
+ *   sfa float [K/128][M], sfb float [K/128][N]: one FP32 scale per 128 K rows
+ *     of each column (1x128 along K for both operands);
+ *   ks int32 [G] (device): K rows of each group, in order; group g owns rows
+ *     [ks[0] + ... + ks[g-1], + ks[g]).  Each count must be a multiple of 128
+ *     (a negative count is taken as 0; the segments are cut at K; a count
+ *     that is not a multiple of 128 gives undefined values for that group and
+ *     the later ones, but no access outside the buffers);
+ *   C float [G][M][N] or NULL, D bf16 [G][M][N]:
+ *     D[g] = C[g] + sum over the K blocks kb of group g of
+ *            sfa[kb][m] * sfb[kb][n] * (exact block dot product of column m of A
+ *            and column n of B), rounded once to BF16.
+ * An empty group gets D[g] = C[g] (or zeros).  K must be a multiple of 128.
+ * The library rewrites A and B K-contiguous into a per-stream device buffer of
+ * (M + N) * ceil(K/1024)*1024 bytes (allocated on the first call of a size,
+ * kept until exit), then runs the GEMM on it.  Ownership, streams and errors
+ * as above.
+ */
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const void *A, const float *sfa, const void *B,
+                                              const float *sfb, const int32_t *ks, const float *C,
+                                              void *D, int M, int N, int K, int num_groups,
+                                              void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);
 
@@ -192,7 +222,8 @@ dg_status dg_init(void);
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these
  * arguments would use, without launching anything.  kind: 0 dense,
- * 1 contiguous, 2 masked (| DG_SCALE_UE8M0 for packed UE8M0 scales,
+ * 1 contiguous, 2 masked, 3 K-grouped (K = the K rows; the FP32 scale form
+ * only) (| DG_SCALE_UE8M0 for packed UE8M0 scales,
  * | DG_SCALE_FP8_FP4 for FP8 x FP4); has_c:
  * 0/1; rows = M (dense/contiguous) or M_max.
  * Needs no GPU: the code object is built for gfx950 and stored in the cache

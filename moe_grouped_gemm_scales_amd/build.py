@@ -54,7 +54,7 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
-# kind, rows, N, K, groups, has_c: the five benchmark workloads (plus C variant)
+# kind, rows, N, K, groups, has_c: the five benchmark workloads (plus C variant) and the K-grouped one
 STANDARD_SHAPES = [
     (0, 64, 2112, 7168, 1, 0),
     (0, 128, 24576, 1536, 1, 0),
@@ -62,6 +62,7 @@ STANDARD_SHAPES = [
     (0, 4096, 7168, 16384, 1, 0),
     (1, 32768, 4096, 7168, 4, 0),
     (2, 256, 7168, 2048, 4, 0),
+    (3, 4096, 7168, 32768, 4, 0),     # K-grouped: the weight gradient of the contiguous workload
 ]
 
 

@@ -34,6 +34,7 @@ struct LaunchParams {
     uint32_t* counters;
     int M;
     int num_tiles;
+    int kt;
 };
 
 struct Workspace {
@@ -41,6 +42,8 @@ struct Workspace {
     size_t partial_bytes = 0;
     uint32_t* counters = nullptr;
     size_t counter_bytes = 0;
+    uint8_t* kmajor = nullptr;       // K-grouped operands rewritten K-contiguous
+    size_t kmajor_bytes = 0;
 };
 
 // One kernel launch of a call.
@@ -54,6 +57,7 @@ struct Segment {
 // launches in order (two when the columns are split between tile widths).
 struct Plan {
     std::vector<Segment> segs;
+    hipFunction_t transpose = nullptr;   // K-grouped: the K-contiguous rewrite of the operands
 };
 
 using PlanKey = std::tuple<int, int, int, int, int, int, int, int, std::string>;
@@ -130,6 +134,25 @@ dg_status ensure_workspace(DeviceState& st, hipStream_t stream, size_t partial_b
     return DG_OK;
 }
 
+// Grow (never shrink) the stream's buffer for the K-contiguous K-grouped operands.
+dg_status ensure_kmajor(DeviceState& st, hipStream_t stream, size_t bytes, uint8_t** out) {
+    Workspace& w = st.ws[stream];
+    if (w.kmajor_bytes < bytes) {
+        if (w.kmajor) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(w.kmajor);
+            w.kmajor = nullptr;
+            w.kmajor_bytes = 0;
+        }
+        hipError_t e = hipMalloc((void**)&w.kmajor, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(K-contiguous operands)");
+        w.kmajor_bytes = bytes;
+    }
+    *out = w.kmajor;
+    return DG_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 dg_status check_common(const void* A, const void* sfa, const void* B, const void* sfb, const float* C,
@@ -177,7 +200,37 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
             seg.grid = (int)std::min<int64_t>(seg.items, (int64_t)cus * occ);
             plan.segs.push_back(seg);
         }
+        if (p.kind == kKGrouped) {
+            void* fptr = nullptr;
+            s = get_function(plan.segs.front().cfg, &fptr, "dg_transpose_k_major");
+            if (s != DG_OK) return s;
+            plan.transpose = static_cast<hipFunction_t>(fptr);
+        }
         it = st->plans.emplace(key, plan).first;
+    }
+    // K-grouped: rewrite A [kt][M] and B [kt][N] as [M][k] and [N][k] (k: the
+    // padded pitch) in the stream's workspace; the GEMM reads those
+    if (p.kind == kKGrouped) {
+        uint8_t* buf = nullptr;
+        s = ensure_kmajor(*st, stream, ((size_t)p.rows + (size_t)p.n) * (size_t)p.k, &buf);
+        if (s != DG_OK) return s;
+        uint8_t* at = buf;
+        uint8_t* bt = buf + (size_t)p.rows * (size_t)p.k;
+        const void* srcs[2] = {A, B};
+        uint8_t* dsts[2] = {at, bt};
+        int cols[2] = {p.rows, p.n};
+        for (int i = 0; i < 2; ++i) {
+            const void* x = srcs[i];
+            void* xt = dsts[i];
+            int rows_k = p.kt;
+            int c = cols[i];
+            void* args[] = {&x, &xt, &rows_k, &c};
+            hipError_t e = hipModuleLaunchKernel(it->second.transpose, (unsigned)(p.kt / 64), (unsigned)((c + 63) / 64),
+                                                 1, 256, 1, 1, 0, stream, args, nullptr);
+            if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(transpose)");
+        }
+        A = at;
+        B = bt;
     }
     // Launches of one call run in stream order, so they can share the split-K
     // workspace (each leaves its arrival counters at zero).
@@ -188,6 +241,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
         lp.M = p.rows;
         lp.num_tiles = (int)seg.items;
+        lp.kt = p.kt;
         if (cfg.splitk > 1) {
             const int64_t mn = seg.items / cfg.splitk;
             Workspace* w = nullptr;
@@ -201,7 +255,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
             std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), seg.grid,
                          cfg.threads(), (long long)seg.items, cfg.lds_bytes());
         void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
-                        &lp.num_tiles};
+                        &lp.num_tiles, &lp.kt};
         hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
         if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     }
@@ -264,6 +318,24 @@ dg_status masked(const void* A, const void* sfa, const void* B, const void* sfb,
     return launch(p, A, sfa, B, sfb, masked_m, C, D, stream);
 }
 
+dg_status k_grouped(const void* A, const float* sfa, const void* B, const float* sfb, const int32_t* ks,
+                    const float* C, void* D, int M, int N, int K, int num_groups, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (!ks) return set_error(DG_ERR_INVALID_ARG, "ks must be non-NULL");
+    if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+    if (!aligned(ks, 4)) return set_error(DG_ERR_ALIGNMENT, "ks must be 4-byte aligned");
+    const int pitch = k_grouped_pitch(K);
+    // the K-contiguous operands are addressed with 32-bit offsets per 256-row slab, the
+    // B scales as one buffer
+    if ((uint64_t)pitch * 256u >= (1ull << 32) || (uint64_t)(K / 128) * (uint64_t)N * 4u >= (1ull << 32))
+        return set_error(DG_ERR_UNSUPPORTED, "sizes exceed 32-bit buffer offsets");
+    if (M == 0) return DG_OK;
+    Problem p{kKGrouped, M, N, pitch, num_groups, C ? 1 : 0, 0};
+    p.kt = K;
+    return launch(p, A, sfa, B, sfb, ks, C, D, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,10 +377,11 @@ int scale_format(int* kind) {
 
 dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus) {
     const int sf = scale_format(&kind);
-    if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
+    if (kind < 0 || kind > 3 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
-    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
+    Problem p{kind, rows, N, kind == kKGrouped ? k_grouped_pitch(K) : K, kind == kDense ? 1 : num_groups,
+              has_c ? 1 : 0, sf};
     for (const KernelConfig& cfg : select_plan(p, num_cus > 0 ? num_cus : 256)) {
         std::vector<char> code;
         dg_status s = compile_code(cfg, &code);
@@ -320,7 +393,7 @@ dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int ha
 dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus, char* buf,
                              int len) {
     const int sf = scale_format(&kind);
-    if (kind < 0 || kind > 2 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
+    if (kind < 0 || kind > 3 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_describe_config: bad arguments");
     if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
     int cus = num_cus;
@@ -332,7 +405,8 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
         if (s != DG_OK) return s;
         cus = effective_cus(*st);
     }
-    Problem p{kind, rows, N, K, kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
+    Problem p{kind, rows, N, kind == kKGrouped ? k_grouped_pitch(K) : K, kind == kDense ? 1 : num_groups,
+              has_c ? 1 : 0, sf};
     std::string key;
     for (const KernelConfig& c : select_plan(p, cus)) key += (key.empty() ? "" : "+") + c.key();
     std::snprintf(buf, (size_t)len, "%s", key.c_str());
@@ -388,6 +462,12 @@ dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* A, const int32_t* sfa,
                                               const int32_t* sfb, const int32_t* masked_m, const float* C, void* D,
                                               int M_max, int N, int K, int num_groups, void* stream) {
     return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 2, stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const void* A, const float* sfa, const void* B, const float* sfb,
+                                              const int32_t* ks, const float* C, void* D, int M, int N, int K,
+                                              int num_groups, void* stream) {
+    return k_grouped(A, sfa, B, sfb, ks, C, D, M, N, K, num_groups, stream);
 }
 
 }  // extern "C"

@@ -10,7 +10,7 @@
 
 namespace dg {
 
-enum Kind : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+enum Kind : int { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 
 // One compiled specialisation of the kernel.  Everything here becomes a -D
 // macro of the hipRTC compile; N and K are compile-time constants (the
@@ -39,6 +39,7 @@ struct KernelConfig {
     int stage_bytes() const {
         if (variant == 1) return bm * 128 + (bm + 63) / 64 * 256 + 256;
         if (sf == 2) return bm * 128 + bn * 64 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
+        if (kind == kKGrouped) return (bm + bn) * 128 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
     int lds_bytes() const {
@@ -59,6 +60,7 @@ struct Problem {
     int n, k, g;
     int has_c;
     int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4
+    int kt = 0;    // K-grouped: K rows of the operands (n, k above: N and the padded pitch)
 };
 
 // Tile heuristics (heuristics.cpp): the launches of one call, in order (one,
@@ -69,9 +71,14 @@ std::vector<KernelConfig> select_plan(const Problem& p, int num_cus);
 int64_t num_work_items(const KernelConfig& c, int rows);
 
 // JIT (jit.cpp).  compile_code() needs no GPU; get_function() loads on the
-// current device.
+// current device (the GEMM kernel, or another kernel of the same module).
 dg_status compile_code(const KernelConfig& c, std::vector<char>* code);
-dg_status get_function(const KernelConfig& c, void** function /* hipFunction_t */);
+dg_status get_function(const KernelConfig& c, void** function /* hipFunction_t */,
+                       const char* name = "dg_fp8_gemm_nt_kernel");
+
+// K-grouped operands are rewritten K-contiguous with this row pitch (the
+// compile-time K of the kernels; a new pitch means a new compile)
+inline int k_grouped_pitch(int k) { return (k + 1023) / 1024 * 1024; }
 std::string cache_dir();
 
 // Errors (api.cpp).

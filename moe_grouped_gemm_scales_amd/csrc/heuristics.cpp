@@ -58,13 +58,14 @@ struct Estimate {
 
 double estimate(const Problem& p, const KernelConfig& c, int num_cus, double valid_rows) {
     const int mt = (p.kind == kMasked) ? (int)std::ceil(valid_rows / std::max(p.g, 1) / c.bm) * p.g
-                                       : (p.rows + c.bm - 1) / c.bm;
+                                       : (p.rows + c.bm - 1) / c.bm * (p.kind == kKGrouped ? p.g : 1);
     const int nt = (p.n + c.bn - 1) / c.bn;
     const double tiles = (double)mt * nt * c.splitk;
     const int occ = occupancy(c);
     const double slots = (double)num_cus * occ;
     const double waves = std::ceil(tiles / slots);
-    const double kspan = (double)p.k / c.splitk;
+    // K-grouped: a tile covers one group's share of K (taken as an even split)
+    const double kspan = (double)p.k / c.splitk / (p.kind == kKGrouped ? std::max(p.g, 1) : 1);
     const double kblocks = kspan / 128.0;
     const int nw = c.wm * c.wn;
     const double waves_per_simd = std::max(1.0, occ * nw / 4.0);
@@ -107,7 +108,7 @@ int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
     const int rpi = 8 / c.kstep;
     const int na = c.bm / rpi, nb = c.sf == 2 ? c.bn / 16 : c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
-    const int nt = c.sf == 2 ? (c.bn + 63) / 64 : c.kstep;
+    const int nt = (c.sf == 2 || c.kind == kKGrouped) ? (c.bn + 63) / 64 : c.kstep;
     return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (nt + nw - 1) / nw;
 }
 
@@ -125,6 +126,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.splitk < 1 || (c.splitk > 1 && p.kind != kDense)) return false;   // split-K: dense only
     if (c.sf != p.sf) return false;
     if (c.sf && (c.variant != 0 || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
+    if (p.kind == kKGrouped && (c.sf || c.variant != 0 || c.kstep != 1)) return false;   // K-grouped: the same
     if (c.variant < 0 || c.variant > 3) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
@@ -174,6 +176,9 @@ const Tuned kTuned[] = {
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
     {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
+    // K-grouped weight gradient of the contiguous workload (K: the row pitch of the
+    // K-contiguous operands, 4 x 8192 tokens)
+    {kKGrouped, 4096, 7168, 32768, 4, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
 };
 
 // Packed UE8M0 scales (variant 0 only; no promotion in the K loop)
@@ -255,7 +260,7 @@ bool valid_plan(const std::vector<KernelConfig>& plan, const Problem& p) {
 int64_t num_work_items(const KernelConfig& c, int rows) {
     const int64_t mt = (rows + c.bm - 1) / c.bm;
     const int64_t nt = (c.n_end() - c.n_begin() + c.bn - 1) / c.bn;
-    if (c.kind == kMasked) return mt * nt * c.g;
+    if (c.kind == kMasked || c.kind == kKGrouped) return mt * nt * c.g;
     return mt * nt * c.splitk;
 }
 

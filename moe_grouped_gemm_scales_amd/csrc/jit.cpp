@@ -205,11 +205,11 @@ dg_status compile_code(const KernelConfig& c, std::vector<char>* code) {
     return compile_locked(c, code);
 }
 
-dg_status get_function(const KernelConfig& c, void** function) {
+dg_status get_function(const KernelConfig& c, void** function, const char* name) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return set_error(DG_ERR_HIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_pair(dev, c.key());
+    auto key = std::make_pair(dev, c.key() + "/" + name);
     auto it = g_funcs.find(key);
     if (it != g_funcs.end()) {
         *function = (void*)it->second;
@@ -224,7 +224,7 @@ dg_status get_function(const KernelConfig& c, void** function) {
     if (e != hipSuccess)
         return set_error(DG_ERR_JIT, std::string("hipModuleLoadData failed: ") + hipGetErrorString(e));
     hipFunction_t f;
-    e = hipModuleGetFunction(&f, mod, "dg_fp8_gemm_nt_kernel");
+    e = hipModuleGetFunction(&f, mod, name);
     if (e != hipSuccess)
         return set_error(DG_ERR_JIT, std::string("hipModuleGetFunction failed: ") + hipGetErrorString(e));
     if (env_flag("DG_PRINT_COMPILE")) {

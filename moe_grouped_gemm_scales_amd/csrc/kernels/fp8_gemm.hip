@@ -20,6 +20,12 @@
 //     expert from its first row, rows whose index differs are left untouched.
 //   2 M-grouped masked (README "Grouped GEMM (masked layout)"): A/D are
 //     [G][M_max][.]; grp = masked_m[G]; rows >= clamp(masked_m[g]) untouched.
+//   3 K-grouped (README "Grouped GEMM (contiguous layout)": the K-axis grouped
+//     call of the MoE weight backward, M and N fixed): D[g] = C[g] + the sum
+//     over the K blocks of group g only; grp = ks[G], the K rows of each group
+//     in order.  A and B here are the operands already made K-contiguous
+//     ([M][K], [N][K] with K the padded row pitch) by dg_transpose_k_major
+//     below; B has one FP32 scale per column and K block, sfb[K/128][N].
 //
 // Layout of the work (MI355X-specific, not from the pages):
 //   * MFMA orientation is swapped: the MFMA "row" operand is a 16-row slice of
@@ -108,7 +114,9 @@ constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
 // WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N);
 // FP4 B has a scale per row, never one per wave
-constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0 && !FP4B;
+constexpr bool KG = kKind == 3;                // K-grouped: per-column B scales, per-group K ranges
+constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0 && !FP4B && !KG;
+static_assert(!KG || (!SF_E8 && DG_SPLITK == 1 && DG_KSTEP == 1), "K-grouped: FP32 scales, no split-K, one K block a stage");
 
 static_assert(K % KBLK == 0, "K must be a multiple of 128");
 static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles must be 16-aligned");
@@ -136,7 +144,17 @@ struct Params {
     u32* counters;         // split-K arrival counters, zero between calls
     int M;                 // rows of A (dense, contiguous) or M_max (masked)
     int num_tiles;         // total work items for this launch
+    int kt;                // K-grouped: K rows of the operands (the groups' segments are cut there)
 };
+
+// Promotion scale of one MFMA result: one FP32 per (row, 128-row block of B),
+// or, K-grouped, one per column, i.e. a vector over the lane's four columns.
+template <bool V> struct ScaleType { typedef float type; };
+template <> struct ScaleType<true> { typedef v4f type; };
+typedef ScaleType<KG>::type sc_t;
+// the first (or only) scale, and its bits (for branches the K-grouped form never takes)
+__device__ __forceinline__ float first(float x) { return x; }
+__device__ __forceinline__ float first(v4f x) { return x.x; }
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ v4i make_rsrc(const void* base, u32 num_bytes) {
@@ -245,6 +263,31 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         tl.n0 = N_BEGIN + nt * BN;
         tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
         tl.row_limit = valid - tl.m0;
+        tl.mn = 0;
+    } else if constexpr (kKind == 3) {
+        // K-grouped: every group has the same output tiles; its K range is the
+        // prefix sum of ks (negative counts taken as 0, cut at kt; a count that
+        // is not a multiple of 128 makes this and later groups' values
+        // undefined, never an access out of bounds)
+        const int num_mt = (p.M + BM - 1) / BM;
+        const int per_g = num_mt * NUM_NT;
+        const int g = t / per_g;
+        const int local = t % per_g;
+        int off = 0;
+        for (int h = 0; h < g; ++h) off += p.grp[h] > 0 ? p.grp[h] : 0;
+        int len = p.grp[g] > 0 ? p.grp[g] : 0;
+        const int kbt = p.kt / KBLK;
+        int kb0 = off / KBLK, kb1 = (off + len) / KBLK;
+        kb0 = kb0 < kbt ? kb0 : kbt;
+        kb1 = kb1 < kbt ? kb1 : kbt;
+        const int mt = local % num_mt, nt = local / num_mt;   // row blocks fastest: they share B
+        tl.g = g;
+        tl.m0 = mt * BM;
+        tl.n0 = N_BEGIN + nt * BN;
+        tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
+        tl.row_limit = tl.rows;
+        tl.kb0 = kb0;
+        tl.kb1 = kb1 > kb0 ? kb1 : kb0;
         tl.mn = 0;
     } else {
         const int num_mt = (p.M + BM - 1) / BM;
@@ -377,7 +420,7 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
 
     // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
     u64 row_base;      // element offset of row 0 of this tile in C/D
-    if constexpr (kKind == 2) row_base = ((u64)tl.g * p.M + tl.m0) * N;
+    if constexpr (kKind == 2 || kKind == 3) row_base = ((u64)tl.g * p.M + tl.m0) * N;
     else row_base = (u64)tl.m0 * N;
 #pragma unroll
     for (int a = 0; a < TM_; ++a) {
@@ -453,9 +496,9 @@ constexpr int S_OFF = B_OFF + BN * ROWB_B;
 constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
 // sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
 // DMA per K block, so the K loop issues no scalar loads; FP4 B: one word per
-// row of the tile, 64 rows per DMA
+// row of the tile, K-grouped: one float per column, 64 per DMA
 constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
-constexpr int NT_INS = FP4B ? (BN + 63) / 64 : KSTEP;
+constexpr int NT_INS = (FP4B || KG) ? (BN + 63) / 64 : KSTEP;
 constexpr int STAGE_BYTES = T_OFF + NT_INS * 256;
 static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
@@ -492,8 +535,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THR
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+                      int num_tiles, int kt) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -546,11 +589,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         }
         a_rows_total = p.M;
         const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
-        const u8* b_base = p.B + ((u64)tl.g * N + tl.n0) * KB_B;
+        const u8* b_base = p.B + ((u64)(KG ? 0 : tl.g) * N + tl.n0) * KB_B;
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
         const v4i rs_s = make_rsrc(sfa_base, (u32)SF_KB * a_rows_total * 4u);
         const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
+                         : KG ? make_rsrc(p.sfb, (u32)(p.kt / KBLK) * N * 4u)
                               : make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
         const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
@@ -593,6 +637,9 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             if constexpr (FP4B) {
                 // word [n0 + 64 h + lane][kb]; rows past the tile read as zero
                 voff_t[j] = (u32)(64 * h + lane) * KBLKS * 4u;
+            } else if constexpr (KG) {
+                // sfb[kb][n0 + 64 h + lane], columns past N clamped (never stored)
+                voff_t[j] = (u32)min(tl.n0 + 64 * h + lane, N - 1) * 4u;
             } else {
                 const int nb = min(nb_t0 + lane, NBLKS - 1);
                 voff_t[j] = (u32)nb * SF_KB * 4u + (u32)h * 4u;
@@ -630,7 +677,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
                 dma4(lim(rs_t), voff_t[j - IA - IB - IS],
-                     __builtin_amdgcn_readfirstlane((u32)(FP4B ? kb : sf_row(kb)) * 4u), st + T_OFF + h * 256);
+                     __builtin_amdgcn_readfirstlane((u32)(FP4B ? kb : KG ? kb * N : sf_row(kb)) * 4u),
+                     st + T_OFF + h * 256);
             }
         };
         auto issue_stage = [&](int kb, int stage, bool live = true) {
@@ -647,7 +695,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         // MFMA results of the last n sub-tile of the previous K block and their
         // scales: promoted while the next K block's first MFMAs run.
         v4f p_carry[TM];
-        float s_carry[TM];
+        sc_t s_carry[TM];
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
             p_carry[a] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -705,12 +753,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             v8i fa[TM];
             v8i fb;
             float sa[TM];
-            float sb[TN];
+            sc_t sb[TN];
+            // K-grouped B scales: the lane's four columns of each n sub-tile
+            const int sbk_off = (wn * WAVE_N + 4 * q) * 4;
             auto read_scales = [&](int stage, int h) __attribute__((always_inline)) {
                 lds_u8* const sb_p = kblock_sfb(stage, h);
                 if constexpr (FP4B) {
 #pragma unroll
                     for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
+                } else if constexpr (KG) {
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        sb[b] = *(__attribute__((address_space(3))) const sc_t*)(sb_p + sbk_off + b * 64);
                 } else if constexpr (SB_UNIFORM) {
                     sb[0] = lds_read_f32(sb_p, sb_off[0]);
                 } else {
@@ -760,7 +814,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 float sab[TM];           // sa * sb for the uniform case
                 if constexpr (SB_UNIFORM && !SF_E8) {
 #pragma unroll
-                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * first(sb[0]);
                 }
                 // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
                 int ea[TM], eb[TN];
@@ -770,7 +824,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
 #pragma unroll
                     for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
-                        eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> (FP4B ? sh_q : sh));
+                        eb[b] = (int)(__builtin_bit_cast(u32, first(sb[b])) >> (FP4B ? sh_q : sh));
                 }
 
                 // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
@@ -793,13 +847,14 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     if (!last) fb_next = read_fb(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB_B);
                     // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
                     // b itself (carried), taken before the next K block's replace them
-                    float sc_prev[TM], s_last[TM];
+                    sc_t sc_prev[TM], s_last[TM];
 #pragma unroll
                     for (int a = 0; a < TM; ++a) {
                         if constexpr (SF_E8) sc_prev[a] = s_last[a] = 0.f;
                         else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
                         else {
-                            sc_prev[a] = b > 0 ? sa[a] * sb[b > 0 ? b - 1 : 0] : 0.f;
+                            sc_prev[a] = sa[a] * sb[b > 0 ? b - 1 : 0];
+                            if (b == 0) sc_prev[a] = 0.f;
                             s_last[a] = sa[a] * sb[b];
                         }
                     }
@@ -979,7 +1034,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 //              work item (it must fit), so the K loop has no barrier at all
 //              and the waves run independently.
 constexpr bool ARES = DG_VARIANT == 2;
-static_assert(!SF_E8, "UE8M0 scales are built for variant 0");
+static_assert(!SF_E8 && !KG, "UE8M0 scales and the K-grouped form are built for variant 0");
 static_assert(WM == 1, "variants 1 and 2 spread their waves along n only");
 static_assert(KSTEP == 1, "variants 1 and 2 stage one K block at a time");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
@@ -1026,8 +1081,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THR
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+                      int num_tiles, int kt) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -1282,7 +1337,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 // flag is also bounded, so a fault in this protocol would cost correctness,
 // which the tests check, and never hang the device.
 static_assert(WM == 1, "variant 3 spreads its consumer waves along n only");
-static_assert(!SF_E8, "UE8M0 scales are built for variant 0");
+static_assert(!SF_E8 && !KG, "UE8M0 scales and the K-grouped form are built for variant 0");
 static_assert(KSTEP == 1, "variant 3 stages one K block per slot");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
 static_assert(NKB <= 64, "the whole K range of a work item is unrolled");
@@ -1332,8 +1387,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, V3_MAX_
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles};
+                      int num_tiles, int kt) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -1552,6 +1607,51 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         acc[TM - 1][TN - 1] += p_carry * s_carry;
 
         finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+    }
+}
+#endif
+
+#if DG_KIND == 3
+// ============================================================ K-grouped: operands made K-contiguous
+// The K-grouped operands arrive K-outermost (X [rows_k][cols] bytes: a row per
+// K index).  The matrix core takes each lane's K values from consecutive
+// bytes, so before the GEMM each operand is rewritten as Xt [cols][K] (row
+// pitch K, the padded compile-time size; bytes past rows_k are never read).
+// One workgroup moves a 64 x 64 byte block through LDS: four lanes read the 64
+// bytes of a K row, then each lane gathers 16 K values of one column from LDS
+// and writes them as one 16-byte store.  Bound by HBM bandwidth.
+extern "C" __global__ void __launch_bounds__(256)
+dg_transpose_k_major(const u8* __restrict__ X, u8* __restrict__ Xt, int rows_k, int cols) {
+    __shared__ __attribute__((aligned(16))) u8 tile[64][68];   // 68: rows start on different banks
+    const int tid = threadIdx.x;
+    const int k0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const int r = tid >> 2, piece = (tid & 3) * 16;
+    {
+        const int k = k0 + r, c = c0 + piece;
+        u32 w[4] = {0u, 0u, 0u, 0u};
+        if (k < rows_k) {
+            const u8* src = X + (u64)k * (u64)cols + c;
+            if ((cols & 15) == 0 && c + 16 <= cols) {
+                const v4i x = *(const v4i*)src;           // 16-byte aligned: cols and c are multiples of 16
+                w[0] = (u32)x.x; w[1] = (u32)x.y; w[2] = (u32)x.z; w[3] = (u32)x.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (c + i < cols) w[i >> 2] |= (u32)src[i] << (8 * (i & 3));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(u32*)&tile[r][piece + 4 * j] = w[j];
+    }
+    __syncthreads();
+    const int c = c0 + r;
+    if (c < cols && k0 + piece < rows_k) {
+        u32 w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = (u32)tile[piece + 4 * j][r] | ((u32)tile[piece + 4 * j + 1][r] << 8) |
+                   ((u32)tile[piece + 4 * j + 2][r] << 16) | ((u32)tile[piece + 4 * j + 3][r] << 24);
+        *(v4i*)(Xt + (u64)c * K + k0 + piece) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
 }
 #endif

@@ -46,6 +46,8 @@ def _load():
     lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
     lib.dg_fp8_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
     lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_m_grouped_fp8_fp4_gemm_nt_masked.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
@@ -344,3 +346,35 @@ def dg_m_grouped_fp8_fp4_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream=N
 fp8_fp4_gemm_nt = dg_fp8_fp4_gemm_nt
 m_grouped_fp8_fp4_gemm_nt_contiguous = dg_m_grouped_fp8_fp4_gemm_nt_contiguous
 m_grouped_fp8_fp4_gemm_nt_masked = dg_m_grouped_fp8_fp4_gemm_nt_masked
+
+
+# ---------------------------------------------------------------- K-grouped TN
+KIND_K_GROUPED = 3   # `kind` of precompile / describe_config for the K-grouped call
+
+
+def dg_k_grouped_fp8_gemm_tn_contiguous(A, sfa, B, sfb, ks, C, D, stream=None):
+    """D[g] = C[g] + A[seg g]^T @ B[seg g] (FP32 scales per 128 K rows of each column).
+
+    A [K,M] and B [K,N] E4M3 (K outermost), sfa [K/128,M] and sfb [K/128,N] float32,
+    ks int32 [G] (device) K rows per group, C None or float32 [G,M,N], D bfloat16 [G,M,N].
+    """
+    _fp8(A, "A"); _fp8(B, "B")
+    K, M = A.shape
+    if B.shape[0] != K:
+        raise ValueError("A and B must share K (their first dimension)")
+    N = B.shape[1]
+    _f32(sfa, "sfa", (_cdiv(K, 128), M))
+    _f32(sfb, "sfb", (_cdiv(K, 128), N))
+    if ks.dtype != torch.int32 or ks.dim() != 1:
+        raise ValueError("ks must be int32 [G]")
+    _dev(ks, "ks")
+    G = ks.shape[0]
+    if C is not None:
+        _f32(C, "C", (G, M, N))
+    _out(D, (G, M, N))
+    _check(lib.dg_k_grouped_fp8_gemm_tn_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(ks), _ptr(C),
+                                                   _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+k_grouped_fp8_gemm_tn_contiguous = dg_k_grouped_fp8_gemm_tn_contiguous
