@@ -48,6 +48,13 @@ def kernel_source_hash() -> str:
 def algorithmic(p) -> tuple[float, float, int]:
     """(FLOPs, bytes, computed rows) of one call, by the pages' convention."""
     K, N = p.K, p.N
+    if p.kind == "k_grouped":
+        # each group's D [M, N] is computed; A [K, M] and B [K, N] are read once
+        M, G = p.M, p.G
+        nbytes = K * M + K * N + G * M * N * 2 + (K // 128) * (M + N) * 4
+        if p.C is not None:
+            nbytes += G * M * N * 4
+        return 2.0 * M * N * K, float(nbytes), G * M
     Kb, Nb = K // 128, (N + 127) // 128
     Kb_b = Kb                       # B scale entries along K per scale row
     if p.ue8m0:
@@ -76,7 +83,7 @@ def algorithmic(p) -> tuple[float, float, int]:
 
 
 def kind_id(kind: str) -> int:
-    return {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+    return {"dense": 0, "contiguous": 1, "masked": 2, "k_grouped": 3}[kind]
 
 
 def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False, fp4: bool = False):
@@ -86,17 +93,24 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
     from tests import gen
     from tests.gpu_util import out_shape, to_dev
 
-    p = gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
+    p = gen.make_k_grouped_workload() if cfg == "kg" else gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
     flops, nbytes, rows = algorithmic(p)
+    oshape = (p.G, p.M, p.N) if p.kind == "k_grouped" else out_shape(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
-    ws += math.prod(out_shape(p)) * 2
+    ws += math.prod(oshape) * 2
     copies = max(1, min(64, math.ceil(512e6 / ws)))
-    devs = [to_dev(p) for _ in range(copies)]
-    outs = [torch.empty(out_shape(p), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    if p.kind == "k_grouped":
+        f = lambda t: None if t is None else t.to("cuda")
+        devs = [dict(A=f(p.A), sfa=f(p.sfa), B=f(p.B), sfb=f(p.sfb), C=f(p.C), ks=f(p.ks)) for _ in range(copies)]
+    else:
+        devs = [to_dev(p) for _ in range(copies)]
+    outs = [torch.empty(oshape, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
 
     def call(i):
         d, D = devs[i % copies], outs[i % copies]
-        if fp4:
+        if p.kind == "k_grouped":
+            dg.dg_k_grouped_fp8_gemm_tn_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["ks"], d["C"], D)
+        elif fp4:
             if p.kind == "dense":
                 dg.dg_fp8_fp4_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
             elif p.kind == "contiguous":
@@ -222,7 +236,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="1", help="0, 1, 1c, 2, 3 or 4 (default 1)")
+    ap.add_argument("--workload", default="1",
+                    help="0, 1, 1c, 2, 3, 4 or kg (the K-grouped weight gradient of 3) (default 1)")
     ap.add_argument("--all", action="store_true",
                     help="also run every workload, one stderr line each (FP32 scales, packed UE8M0 scales, "
                          "then FP8 x FP4)")
@@ -261,16 +276,18 @@ def main():
         sys.exit(1)
     from tests import gen
 
-    cfg = args.workload if args.workload == "1c" else int(args.workload)
+    cfg = args.workload if args.workload in ("1c", "kg") else int(args.workload)
     per_shape = []
     if args.all:
         modes = [(c, "") for c in [0, 1, "1c", 2, 3, 4]] + [(c, "_ue8m0") for c in [0, 1, 2, 3, 4]] + \
-            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]]
+            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]] + [("kg", "")]
         for c, mode in modes:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
+            if c == "kg":
+                steps = max(5, args.steps // 20)
             r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=mode == "_ue8m0",
                                fp4=mode == "_fp4")
-            wl = gen.WORKLOAD_NAMES[c] + mode
+            wl = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[c] + mode
             line = dict(workload=wl, kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
                         roofline_frac=round(r["frac"], 4), step_us=round(r["ms_per_step"] * 1e3, 3),
@@ -282,14 +299,15 @@ def main():
 
     r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4)
     p = r["problem"]
-    name = gen.WORKLOAD_NAMES[cfg] + ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "")
+    name = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[cfg] + \
+        ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))
-    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4) else cpu_baseline(cfg)
+    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4 or cfg == "kg") else cpu_baseline(cfg)
     value = r["step_tflops"]
     pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not (args.ue8m0 or args.fp4) else None
     out = {
@@ -305,7 +323,7 @@ def main():
         "vs_baseline": round(value / pages, 4) if pages else None,
         "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": name, "kind": p.kind, "M": p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
+        "config": {"workload": name, "kind": p.kind, "M": p.M if p.kind == "k_grouped" else p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
                    "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],
                    "hip_graph": bool(not args.eager)},
         "kernel_us": round(r["kernel_ms"] * 1e3, 3),

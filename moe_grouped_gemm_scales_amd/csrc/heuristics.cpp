@@ -178,7 +178,7 @@ const Tuned kTuned[] = {
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
     // K-grouped weight gradient of the contiguous workload (K: the row pitch of the
     // K-contiguous operands, 4 x 8192 tokens)
-    {kKGrouped, 4096, 7168, 32768, 4, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    {kKGrouped, 4096, 7168, 32768, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
 // Packed UE8M0 scales (variant 0 only; no promotion in the K loop)

@@ -271,6 +271,15 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         // undefined, never an access out of bounds)
         const int num_mt = (p.M + BM - 1) / BM;
         const int per_g = num_mt * NUM_NT;
+        // the XCD-aware spread of each full round of the grid, as for dense below
+        const int grid = gridDim.x;
+        if (grid % 8 == 0) {
+            const int r0 = t - t % grid;
+            if (r0 + grid <= p.num_tiles) {
+                const int b = t - r0;
+                t = r0 + (b % 8) * (grid / 8) + b / 8;
+            }
+        }
         const int g = t / per_g;
         const int local = t % per_g;
         int off = 0;
@@ -280,7 +289,12 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         int kb0 = off / KBLK, kb1 = (off + len) / KBLK;
         kb0 = kb0 < kbt ? kb0 : kbt;
         kb1 = kb1 < kbt ? kb1 : kbt;
-        const int mt = local % num_mt, nt = local / num_mt;   // row blocks fastest: they share B
+        // grouped order inside the group: 8 row blocks per column sweep
+        constexpr int GROUP_M = 8;
+        const int width = GROUP_M * NUM_NT;
+        const int first_m = local / width * GROUP_M;
+        const int gsize = num_mt - first_m < GROUP_M ? num_mt - first_m : GROUP_M;
+        const int mt = first_m + (local % width) % gsize, nt = (local % width) / gsize;
         tl.g = g;
         tl.m0 = mt * BM;
         tl.n0 = N_BEGIN + nt * BN;

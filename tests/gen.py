@@ -281,6 +281,14 @@ def make_k_grouped(ks, M, N, seed, with_c=False) -> KGroupedProblem:
     return KGroupedProblem(A, sfa, B, sfb, torch.as_tensor(ks, dtype=torch.int32), C=c, seed=seed)
 
 
+def make_k_grouped_workload() -> KGroupedProblem:
+    """The weight gradient of the contiguous workload: 4 experts x 8192 tokens, M = 4096, N = 7168."""
+    return make_k_grouped([8192] * 4, 4096, 7168, seed=1005)
+
+
+WORKLOAD_NAMES_EXTRA = {"kg": "k_grouped_4x8192_4096x7168"}
+
+
 # ---------------------------------------------------------------- the five workloads
 # (shapes: DeepGEMM launch article, section 3, dense table and MoE table)
 WORKLOADS = {
