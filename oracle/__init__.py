@@ -207,6 +207,28 @@ class Oracle:
             raise ValueError("oracle_fp8_fp4_gemm: bad sizes")
         return out, comp.astype(bool)
 
+    # ---------------------------------------------------------- NN / TN / TT layouts
+    def fp8_gemm_layout(self, layout: str, A, sfa, B, sfb, C=None, m_indices=None, G=1, rows=None, threads=0):
+        """(D FP64, computed) of D = C + A_l . B_l^T for a stored layout (DeepGEMM README,
+        "Normal dense GEMM": fp8_gemm_{nt, nn, tn, tt}; "Grouped GEMM (contiguous layout)":
+        m_grouped_fp8_gemm_{nt, nn}_contiguous).
+
+        The first letter is how A is stored (N: [M, K], T: [K, M]), the second how B is
+        (T: [N, K] or [G, N, K], N: [K, N] or [G, K, N]); the scales keep their logical
+        layouts (sfa [K/128, M], sfb [(G,) ceil(N/128), K/128]).  A stored operand is put
+        back in the NT arrangement with a plain transpose, then the NT definition applies.
+        m_indices given: the contiguous grouped form.
+        """
+        a_t, b_n = layout[0] == "t", layout[1] == "n"
+        A = np.ascontiguousarray(np.asarray(A).T) if a_t else np.asarray(A)
+        B = np.asarray(B)
+        if b_n:
+            B = np.ascontiguousarray(np.swapaxes(B, -1, -2))
+        if m_indices is None:
+            out = self.fp8_gemm_nt(A, sfa, B, sfb, C, rows=rows, threads=threads)
+            return out, np.ones(out.shape[0], dtype=bool)
+        return self.m_grouped_contiguous(A, sfa, B, sfb, m_indices, C, rows=rows, threads=threads)
+
     # ---------------------------------------------------------- K-grouped TN
     def k_grouped_tn(self, A, sfa, B, sfb, ks, C=None, rows=None, threads=0):
         """(D FP64 [rows, N], computed [rows]) of the K-grouped TN GEMM.

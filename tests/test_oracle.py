@@ -526,3 +526,42 @@ def test_k_grouped_bad_segments_rejected(oracle):
     p = gen.make_k_grouped([128, 128], 4, 4, seed=65)
     with pytest.raises(ValueError):
         oracle.k_grouped_tn(p.A, p.sfa, p.B, p.sfb, torch.tensor([64, 192], dtype=torch.int32))
+
+
+# ------------------------------------------------------------------ NN / TN / TT layouts
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("M,N,K", [(3, 129, 384), (130, 5, 256)])
+def test_layouts_vs_numpy_on_stored_operands(oracle, layout, M, N, K):
+    """The stored operands, dequantised in place with numpy (no transposes on the oracle's
+    side of the comparison): D = C + A_deq @ B_deq^T (nt), A_deq @ B_deq (nn), and so on."""
+    p = gen.make_dense(M, N, K, seed=M * N + K, with_c=True)
+    dec = torch_decode_table()
+    sa = np.repeat(p.sfa.numpy().astype(np.float64), 128, axis=0)                     # [K, M]
+    sb = np.repeat(np.repeat(p.sfb.numpy().astype(np.float64), 128, axis=0)[:N], 128, axis=1)   # [N, K]
+    A = p.A.numpy() if layout[0] == "n" else np.ascontiguousarray(p.A.numpy().T)      # stored
+    B = p.B.numpy() if layout[1] == "t" else np.ascontiguousarray(p.B.numpy().T)
+    Ad = dec[A] * (sa.T if layout[0] == "n" else sa)
+    Bd = dec[B] * (sb if layout[1] == "t" else sb.T)
+    lhs = Ad if layout[0] == "n" else Ad.T                                            # [M, K]
+    rhs = Bd.T if layout[1] == "t" else Bd                                            # [K, N]
+    ref = lhs @ rhs + p.C.numpy().astype(np.float64)
+    got, comp = oracle.fp8_gemm_layout(layout, A, p.sfa.numpy(), B, p.sfb.numpy(), p.C.numpy())
+    assert comp.all()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-9)
+
+
+def test_layout_nn_contiguous_vs_numpy(oracle):
+    p = gen.make_contiguous([128, 0, 100], 129, 256, seed=71, with_c=True, pad_rows=128)
+    Bn = np.ascontiguousarray(np.swapaxes(p.B.numpy(), -1, -2))                        # [G, K, N]
+    got, comp = oracle.fp8_gemm_layout("nn", p.A.numpy(), p.sfa.numpy(), Bn, p.sfb.numpy(), p.C.numpy(),
+                                       m_indices=p.m_indices.numpy())
+    dec = torch_decode_table()
+    Ad = dec[p.A.numpy()] * np.repeat(p.sfa.numpy().astype(np.float64).T, 128, axis=1)
+    for m in range(p.M):
+        g = int(p.m_indices[m])
+        assert comp[m] == (0 <= g < 3)
+        if not comp[m]:
+            continue
+        sb = np.repeat(np.repeat(p.sfb[g].numpy().astype(np.float64), 128, axis=0)[:129], 128, axis=1)  # [N, K]
+        ref = Ad[m] @ (dec[Bn[g]] * sb.T) + p.C[m].numpy().astype(np.float64)
+        assert np.allclose(got[m], ref, rtol=1e-12, atol=1e-9)
