@@ -105,6 +105,30 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void *A, const float *sfa, const
                                           int num_groups, void *stream);
 
 /*
+ * Storage layouts other than NT (DeepGEMM README, "Normal dense GEMM":
+ * fp8_gemm_{nt, nn, tn, tt}; "Grouped GEMM (contiguous layout)":
+ * m_grouped_fp8_gemm_{nt, nn}_contiguous).  The operation is the same
+ * D = C + A . B^T over the logical A [M][K] and B [N][K]; the letters say how
+ * the operands are stored (reading, the pages name the calls only): the first
+ * is A, N = [M][K] (K-contiguous), T = [K][M]; the second is B, T = [N][K],
+ * N = [K][N] (grouped: [G][K][N]).  The scales keep their logical layouts and
+ * block shapes (sfa [Kb][M], sfb [(G)][Nb][Kb]).  An operand stored K-outermost
+ * is rewritten K-contiguous into a per-stream device buffer (rows x K bytes,
+ * allocated on the first call of a size, kept until exit), then the NT kernels
+ * run on it.  Everything else as for the NT calls.
+ */
+dg_status dg_fp8_gemm_nn(const void *A, const float *sfa, const void *B, const float *sfb,
+                         const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_fp8_gemm_tn(const void *A, const float *sfa, const void *B, const float *sfb,
+                         const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_fp8_gemm_tt(const void *A, const float *sfa, const void *B, const float *sfb,
+                         const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const void *A, const float *sfa, const void *B,
+                                              const float *sfb, const int32_t *m_indices,
+                                              const float *C, void *D, int M, int N, int K,
+                                              int num_groups, void *stream);
+
+/*
  * The same three forms with packed UE8M0 scale factors (DeepGEMM README,
  * "Interfaces / Notes": on the SM100 path the scale factors are UE8M0, four
  * of them packed into one 32-bit integer; the Ascend 950 article packs them

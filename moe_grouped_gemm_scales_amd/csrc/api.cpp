@@ -200,13 +200,40 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
             seg.grid = (int)std::min<int64_t>(seg.items, (int64_t)cus * occ);
             plan.segs.push_back(seg);
         }
-        if (p.kind == kKGrouped) {
-            void* fptr = nullptr;
-            s = get_function(plan.segs.front().cfg, &fptr, "dg_transpose_k_major");
-            if (s != DG_OK) return s;
-            plan.transpose = static_cast<hipFunction_t>(fptr);
-        }
         it = st->plans.emplace(key, plan).first;
+    }
+    const bool rewrite = p.kind == kKGrouped || p.a_k_outer || p.b_k_outer;
+    if (rewrite && !it->second.transpose) {
+        void* fptr = nullptr;
+        s = get_function(it->second.segs.front().cfg, &fptr, "dg_transpose_k_major");
+        if (s != DG_OK) return s;
+        it->second.transpose = static_cast<hipFunction_t>(fptr);
+    }
+    // rewrite of a K-outermost operand X [groups][rows_k][cols] as [groups][cols][pitch]
+    auto rewrite_k_major = [&](const void* x, void* xt, int rows_k, int cols, int groups) -> dg_status {
+        void* args[] = {&x, &xt, &rows_k, &cols};
+        hipError_t e = hipModuleLaunchKernel(it->second.transpose, (unsigned)(rows_k / 64), (unsigned)((cols + 63) / 64),
+                                             (unsigned)groups, 256, 1, 1, 0, stream, args, nullptr);
+        return e == hipSuccess ? DG_OK : hip_fail(e, "hipModuleLaunchKernel(transpose)");
+    };
+    // TN / NN / TT layouts: the K-outermost operand(s) rewritten K-contiguous in the
+    // stream's workspace, then the NT kernels run on them
+    if (p.kind != kKGrouped && (p.a_k_outer || p.b_k_outer)) {
+        const size_t a_bytes = p.a_k_outer ? (size_t)p.rows * (size_t)p.k : 0;
+        const size_t b_bytes = p.b_k_outer ? (size_t)p.g * (size_t)p.n * (size_t)p.k : 0;
+        uint8_t* buf = nullptr;
+        s = ensure_kmajor(*st, stream, a_bytes + b_bytes, &buf);
+        if (s != DG_OK) return s;
+        if (p.a_k_outer) {
+            s = rewrite_k_major(A, buf, p.k, p.rows, 1);
+            if (s != DG_OK) return s;
+            A = buf;
+        }
+        if (p.b_k_outer) {
+            s = rewrite_k_major(B, buf + a_bytes, p.k, p.n, p.g);
+            if (s != DG_OK) return s;
+            B = buf + a_bytes;
+        }
     }
     // K-grouped: rewrite A [kt][M] and B [kt][N] as [M][k] and [N][k] (k: the
     // padded pitch) in the stream's workspace; the GEMM reads those
@@ -216,19 +243,10 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         if (s != DG_OK) return s;
         uint8_t* at = buf;
         uint8_t* bt = buf + (size_t)p.rows * (size_t)p.k;
-        const void* srcs[2] = {A, B};
-        uint8_t* dsts[2] = {at, bt};
-        int cols[2] = {p.rows, p.n};
-        for (int i = 0; i < 2; ++i) {
-            const void* x = srcs[i];
-            void* xt = dsts[i];
-            int rows_k = p.kt;
-            int c = cols[i];
-            void* args[] = {&x, &xt, &rows_k, &c};
-            hipError_t e = hipModuleLaunchKernel(it->second.transpose, (unsigned)(p.kt / 64), (unsigned)((c + 63) / 64),
-                                                 1, 256, 1, 1, 0, stream, args, nullptr);
-            if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(transpose)");
-        }
+        s = rewrite_k_major(A, at, p.kt, p.rows, 1);
+        if (s != DG_OK) return s;
+        s = rewrite_k_major(B, bt, p.kt, p.n, 1);
+        if (s != DG_OK) return s;
         A = at;
         B = bt;
     }
@@ -284,16 +302,19 @@ namespace {
 // The three forms, for each scale format (sf: 0 FP32, 1 packed UE8M0, 2 FP8 x
 // FP4 with E2M1 B; the scale pointers are only passed through to the kernel).
 dg_status dense(const void* A, const void* sfa, const void* B, const void* sfb, const float* C, void* D, int M,
-                int N, int K, int sf, void* stream) {
+                int N, int K, int sf, void* stream, int a_k_outer = 0, int b_k_outer = 0) {
     dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
     if (s != DG_OK) return s;
     if (M == 0) return DG_OK;
     Problem p{kDense, M, N, K, 1, C ? 1 : 0, sf};
+    p.a_k_outer = a_k_outer;
+    p.b_k_outer = b_k_outer;
     return launch(p, A, sfa, B, sfb, nullptr, C, D, stream);
 }
 
 dg_status contiguous(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* m_indices,
-                     const float* C, void* D, int M, int N, int K, int num_groups, int sf, void* stream) {
+                     const float* C, void* D, int M, int N, int K, int num_groups, int sf, void* stream,
+                     int b_k_outer = 0) {
     dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
     if (s != DG_OK) return s;
     if (!m_indices) return set_error(DG_ERR_INVALID_ARG, "m_indices must be non-NULL");
@@ -303,6 +324,7 @@ dg_status contiguous(const void* A, const void* sfa, const void* B, const void* 
         return set_error(DG_ERR_ALIGNMENT, "contiguous M must be a multiple of the M alignment (128)");
     if (M == 0) return DG_OK;
     Problem p{kContiguous, M, N, K, num_groups, C ? 1 : 0, sf};
+    p.b_k_outer = b_k_outer;
     return launch(p, A, sfa, B, sfb, m_indices, C, D, stream);
 }
 
@@ -468,6 +490,29 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const void* A, const float* sfa, c
                                               const int32_t* ks, const float* C, void* D, int M, int N, int K,
                                               int num_groups, void* stream) {
     return k_grouped(A, sfa, B, sfb, ks, C, D, M, N, K, num_groups, stream);
+}
+
+// Layout letters: the first says how A is stored (N [M][K], T [K][M]), the
+// second how B is (T [N][K], N [K][N]); the K-outermost ones are rewritten.
+dg_status dg_fp8_gemm_nn(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
+                         int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 0, stream, 0, 1);
+}
+
+dg_status dg_fp8_gemm_tn(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
+                         int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 0, stream, 1, 1);
+}
+
+dg_status dg_fp8_gemm_tt(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
+                         int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 0, stream, 1, 0);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const void* A, const float* sfa, const void* B, const float* sfb,
+                                              const int32_t* m_indices, const float* C, void* D, int M, int N, int K,
+                                              int num_groups, void* stream) {
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 0, stream, 1);
 }
 
 }  // extern "C"

@@ -61,6 +61,7 @@ struct Problem {
     int has_c;
     int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4
     int kt = 0;    // K-grouped: K rows of the operands (n, k above: N and the padded pitch)
+    int a_k_outer = 0, b_k_outer = 0;   // A stored [K][rows] (T), B stored [(G)][K][N] (N)
 };
 
 // Tile heuristics (heuristics.cpp): the launches of one call, in order (one,

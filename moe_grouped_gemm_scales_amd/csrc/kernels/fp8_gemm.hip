@@ -1625,12 +1625,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 }
 #endif
 
-#if DG_KIND == 3
-// ============================================================ K-grouped: operands made K-contiguous
-// The K-grouped operands arrive K-outermost (X [rows_k][cols] bytes: a row per
-// K index).  The matrix core takes each lane's K values from consecutive
-// bytes, so before the GEMM each operand is rewritten as Xt [cols][K] (row
-// pitch K, the padded compile-time size; bytes past rows_k are never read).
+// ============================================================ operands stored K-outermost
+// The K-grouped operands, and A or B of the TN / NN / TT layouts, arrive
+// K-outermost (X [rows_k][cols] bytes: a row per K index).  The matrix core
+// takes each lane's K values from consecutive bytes, so before the GEMM such an
+// operand is rewritten as Xt [cols][K] (row pitch K, the compile-time size;
+// K-grouped: padded, and bytes past rows_k are never read); blockIdx.z walks
+// the groups of a grouped B ([G][rows_k][cols] -> [G][cols][K]).
 // One workgroup moves a 64 x 64 byte block through LDS: four lanes read the 64
 // bytes of a K row, then each lane gathers 16 K values of one column from LDS
 // and writes them as one 16-byte store.  Bound by HBM bandwidth.
@@ -1639,6 +1640,8 @@ dg_transpose_k_major(const u8* __restrict__ X, u8* __restrict__ Xt, int rows_k, 
     __shared__ __attribute__((aligned(16))) u8 tile[64][68];   // 68: rows start on different banks
     const int tid = threadIdx.x;
     const int k0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    X += (u64)blockIdx.z * (u64)rows_k * (u64)cols;
+    Xt += (u64)blockIdx.z * (u64)cols * (u64)K;
     const int r = tid >> 2, piece = (tid & 3) * 16;
     {
         const int k = k0 + r, c = c0 + piece;
@@ -1668,6 +1671,5 @@ dg_transpose_k_major(const u8* __restrict__ X, u8* __restrict__ Xt, int rows_k, 
         *(v4i*)(Xt + (u64)c * K + k0 + piece) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
 }
-#endif
 
 }  // namespace dg

@@ -46,6 +46,11 @@ def _load():
     lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        getattr(lib, name).argtypes = lib.dg_fp8_gemm_nt.argtypes
+        getattr(lib, name).restype = i32
+    lib.dg_m_grouped_fp8_gemm_nn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_m_grouped_fp8_gemm_nn_contiguous.restype = i32
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
     lib.dg_fp8_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
@@ -378,3 +383,60 @@ def dg_k_grouped_fp8_gemm_tn_contiguous(A, sfa, B, sfb, ks, C, D, stream=None):
 
 
 k_grouped_fp8_gemm_tn_contiguous = dg_k_grouped_fp8_gemm_tn_contiguous
+
+
+# ---------------------------------------------------------------- NN / TN / TT layouts
+def _dense_layout(layout, A, sfa, B, sfb, C, D, stream):
+    """D = C + A_l @ B_l.T where A is stored [M,K] (n) or [K,M] (t) and B [N,K] (t) or [K,N] (n)."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape if layout[0] == "n" else A.shape[::-1]
+    N, Kb_ = B.shape if layout[1] == "t" else B.shape[::-1]
+    if Kb_ != K:
+        raise ValueError("A and B must share K")
+    _f32(sfa, "sfa", (_cdiv(K, 128), M))
+    _f32(sfb, "sfb", (_cdiv(N, 128), _cdiv(K, 128)))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    f = getattr(lib, f"dg_fp8_gemm_{layout}")
+    _check(f(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K, _stream(stream)))
+    return D
+
+
+def dg_fp8_gemm_nn(A, sfa, B, sfb, C, D, stream=None):
+    """A [M,K], B stored [K,N]."""
+    return _dense_layout("nn", A, sfa, B, sfb, C, D, stream)
+
+
+def dg_fp8_gemm_tn(A, sfa, B, sfb, C, D, stream=None):
+    """A stored [K,M], B stored [K,N]."""
+    return _dense_layout("tn", A, sfa, B, sfb, C, D, stream)
+
+
+def dg_fp8_gemm_tt(A, sfa, B, sfb, C, D, stream=None):
+    """A stored [K,M], B [N,K]."""
+    return _dense_layout("tt", A, sfa, B, sfb, C, D, stream)
+
+
+def dg_m_grouped_fp8_gemm_nn_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    """Contiguous M-grouped with B stored [G,K,N]; otherwise as the NT form."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[2]
+    if B.shape[1] != K:
+        raise ValueError("B must be [G, K, N]")
+    _f32(sfa, "sfa", (_cdiv(K, 128), M))
+    _f32(sfb, "sfb", (G, _cdiv(N, 128), _cdiv(K, 128)))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_fp8_gemm_nn_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
+                                                   _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+fp8_gemm_nn, fp8_gemm_tn, fp8_gemm_tt = dg_fp8_gemm_nn, dg_fp8_gemm_tn, dg_fp8_gemm_tt
+m_grouped_fp8_gemm_nn_contiguous = dg_m_grouped_fp8_gemm_nn_contiguous
