@@ -74,6 +74,11 @@ def _declare(lib):
     lib.oracle_k_grouped_tn.restype = c.c_int
     lib.oracle_k_grouped_tn.argtypes = [p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
                                         p, c.c_int64, p, p, c.c_int]
+    lib.oracle_bf16_value.restype = c.c_double
+    lib.oracle_bf16_value.argtypes = [c.c_uint16]
+    lib.oracle_bf16_gemm.restype = c.c_int
+    lib.oracle_bf16_gemm.argtypes = [c.c_int, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                     p, c.c_int64, p, p, c.c_int]
     lib.oracle_default_threads.restype = c.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_fp8_gemm_nt.restype = c.c_int
@@ -205,6 +210,35 @@ class Oracle:
                                           _ptr(r), nr, _ptr(out), _ptr(comp), threads)
         if rc != 0:
             raise ValueError("oracle_fp8_fp4_gemm: bad sizes")
+        return out, comp.astype(bool)
+
+    # ---------------------------------------------------------- BF16 x BF16
+    def bf16_value(self, bits: int) -> float:
+        return float(self.lib.oracle_bf16_value(int(bits)))
+
+    def bf16_gemm(self, kind: str, A, B, group_info=None, C=None, rows=None, threads=0):
+        """(D FP64 [rows, N], computed [rows]) of the unscaled BF16 GEMM D = C + A . B^T.
+
+        A, B: BF16 bit patterns as uint16 (or int16), A [M,K] (masked [G,M_max,K]), B [(G,)N,K];
+        group_info: m_indices (contiguous) or masked_m (masked).
+        """
+        A = _c(np.asarray(A).view(np.uint16), np.uint16); B = _c(np.asarray(B).view(np.uint16), np.uint16)
+        C = _c(C, np.float32); gi = _c(group_info, np.int32)
+        k = {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+        if kind == "masked":
+            G, M, K = A.shape
+        else:
+            M, K = A.shape
+            G = B.shape[0] if B.ndim == 3 else 1
+        N = B.shape[-2]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else (G * M if kind == "masked" else M)
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_bf16_gemm(k, _ptr(A), _ptr(B), _ptr(gi), _ptr(C), M, N, K, G, _ptr(r), nr, _ptr(out),
+                                       _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_bf16_gemm: bad sizes")
         return out, comp.astype(bool)
 
     # ---------------------------------------------------------- NN / TN / TT layouts

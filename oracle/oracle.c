@@ -566,3 +566,117 @@ int oracle_k_grouped_tn(const uint8_t *A, const float *sfa, const uint8_t *B, co
     free(off);
     return rc;
 }
+
+/* ------------------------------------------------------------------ */
+/* BF16 x BF16 (DeepGEMM-Ascend hub page, precision table: BF16 x BF16 */
+/* for ordinary-precision training; DeepGEMM README intro: GEMM in     */
+/* FP8, FP4 and BF16): D = C + A . B^T with no scale factors.          */
+/* BF16 decoded from its bit fields: sign bit 15, exponent bits 14..7  */
+/* (bias 127), mantissa bits 6..0; exponent 0: subnormal m * 2^-133;   */
+/* exponent 255: Inf (m = 0) or NaN.                                   */
+/* ------------------------------------------------------------------ */
+double oracle_bf16_value(uint16_t bits)
+{
+    int s = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int m = bits & 0x7F;
+    double mag;
+    if (e == 0xFF)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -133);
+    else
+        mag = ldexp(1.0 + (double)m / 128.0, e - 127);
+    return s ? -mag : mag;
+}
+
+typedef struct {
+    const uint16_t *A, *B;       /* [rows][K], [G][N][K] */
+    const float *C;
+    const int32_t *group_info;   /* m_indices (kind 1) or masked_m (kind 2) */
+    int kind;
+    int64_t M;                   /* rows of A (dense, contiguous) or M_max (masked) */
+    int N, K, G;
+    const int64_t *rows;
+    int64_t n_rows;
+    double *out;
+    uint8_t *computed;
+} bf16_problem;
+
+typedef struct { const bf16_problem *p; int64_t r0, r1; } bf16_slice;
+
+/* One output row: D[n] = C[n] + sum_k bf16(A[m][k]) * bf16(B[n][k]) in FP64,
+ * ascending k (every product is exact in FP64; the sum rounds far below the
+ * BF16 output's resolution). */
+static void *bf16_worker(void *arg)
+{
+    const bf16_slice *sl = (const bf16_slice *)arg;
+    const bf16_problem *p = sl->p;
+    double *a = (double *)malloc(sizeof(double) * (size_t)p->K);
+    for (int64_t i = sl->r0; i < sl->r1; ++i) {
+        int64_t r = p->rows ? p->rows[i] : i;
+        double *out = p->out + i * (int64_t)p->N;
+        int64_t g = 0;
+        if (p->kind == KIND_CONTIG) {
+            g = p->group_info[r];
+            if (g < 0 || g >= p->G) {
+                for (int n = 0; n < p->N; ++n) out[n] = NAN;
+                if (p->computed) p->computed[i] = 0;
+                continue;
+            }
+        } else if (p->kind == KIND_MASKED) {
+            int64_t valid = p->group_info[r / p->M];
+            valid = valid < 0 ? 0 : (valid > p->M ? p->M : valid);
+            g = r / p->M;
+            if (r % p->M >= valid) {
+                for (int n = 0; n < p->N; ++n) out[n] = NAN;
+                if (p->computed) p->computed[i] = 0;
+                continue;
+            }
+        }
+        for (int k = 0; k < p->K; ++k)
+            a[k] = oracle_bf16_value(p->A[r * p->K + k]);
+        const uint16_t *b = p->B + g * (int64_t)p->N * p->K;
+        for (int n = 0; n < p->N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < p->K; ++k)
+                acc += a[k] * oracle_bf16_value(b[(int64_t)n * p->K + k]);
+            out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);
+        }
+        if (p->computed) p->computed[i] = 1;
+    }
+    free(a);
+    return NULL;
+}
+
+/*
+ * BF16 GEMM, kind 0 dense / 1 contiguous / 2 masked, layouts as the FP8 forms
+ * with 2-byte elements and no scales: A [rows][K] (masked [G][M_max][K]),
+ * B [G][N][K] (dense: G = 1), C NULL or like D.  rows: flat row indices
+ * (NULL: all).  Returns 0, or -1 on bad sizes.
+ */
+int oracle_bf16_gemm(int kind, const uint16_t *A, const uint16_t *B, const int32_t *group_info, const float *C,
+                     int64_t M, int N, int K, int G, const int64_t *rows, int64_t n_rows, double *out,
+                     uint8_t *computed, int n_threads)
+{
+    if (kind < 0 || kind > 2 || M <= 0 || N <= 0 || K <= 0 || G <= 0) return -1;
+    bf16_problem p = {A, B, C, group_info, kind, M, N, K, G, rows, 0, out, computed};
+    p.n_rows = rows ? n_rows : (kind == KIND_MASKED ? (int64_t)G * M : M);
+    if (n_threads <= 0) n_threads = oracle_default_threads();
+    if (n_threads > 256) n_threads = 256;
+    if (n_threads > p.n_rows) n_threads = (int)(p.n_rows > 0 ? p.n_rows : 1);
+    pthread_t tid[256];
+    bf16_slice sl[256];
+    int started[256];
+    int64_t per = (p.n_rows + n_threads - 1) / n_threads;
+    for (int t = 0; t < n_threads; ++t) {
+        sl[t].p = &p;
+        sl[t].r0 = t * per < p.n_rows ? t * per : p.n_rows;
+        sl[t].r1 = (t + 1) * per < p.n_rows ? (t + 1) * per : p.n_rows;
+        started[t] = sl[t].r0 < sl[t].r1 && pthread_create(&tid[t], NULL, bf16_worker, &sl[t]) == 0;
+        if (!started[t] && sl[t].r0 < sl[t].r1) bf16_worker(&sl[t]);
+    }
+    for (int t = 0; t < n_threads; ++t)
+        if (started[t]) pthread_join(tid[t], NULL);
+    return 0;
+}

@@ -144,6 +144,7 @@ class Problem:
     seed: int = 0
     ue8m0: bool = False             # sfa/sfb are packed UE8M0 int32 words
     fp4: bool = False               # B holds E2M1 pairs [.., N, K/2], sfb [.., N, K/128] words (1x32 blocks)
+    bf16: bool = False              # A and B are torch.bfloat16, no scales (sfa, sfb None)
 
     @property
     def M(self):
@@ -228,6 +229,41 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, 
     B, sfb = _quant_b(b, ue8m0, fp4)
     del b
     return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0, fp4=fp4)
+
+
+# ---------------------------------------------------------------- BF16 x BF16 (unscaled)
+def _bf16(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.bfloat16).contiguous()
+
+
+def make_bf16(kind, seed, M=None, N=None, K=None, with_c=False, group_rows=None, G=None, M_max=None,
+              masked_m=None, pad_rows=None) -> Problem:
+    """BF16 operands ~N(0,1) rounded to BF16 (nearest-even), drawn A, B, C, masked_m."""
+    g = _gen(seed)
+    if kind == "dense":
+        a = torch.randn(M, K, generator=g)
+        b = torch.randn(N, K, generator=g)
+        c = torch.randn(M, N, generator=g) if with_c else None
+        return Problem("dense", _bf16(a), None, _bf16(b), None, C=c, seed=seed, bf16=True)
+    if kind == "contiguous":
+        G = len(group_rows)
+        seg = [((r + 127) // 128) * 128 for r in group_rows]
+        Mt = sum(seg) + (pad_rows or 0)
+        a = torch.randn(Mt, K, generator=g)
+        b = torch.randn(G, N, K, generator=g)
+        c = torch.randn(Mt, N, generator=g) if with_c else None
+        idx = torch.full((Mt,), -1, dtype=torch.int32)
+        off = 0
+        for e, (r, sg) in enumerate(zip(group_rows, seg)):
+            idx[off:off + r] = e
+            off += sg
+        return Problem("contiguous", _bf16(a), None, _bf16(b), None, C=c, m_indices=idx, seed=seed, bf16=True)
+    a = torch.randn(G, M_max, K, generator=g)
+    b = torch.randn(G, N, K, generator=g)
+    c = torch.randn(G, M_max, N, generator=g) if with_c else None
+    mm = torch.randint(0, M_max + 1, (G,), generator=g, dtype=torch.int32) if masked_m is None else \
+        torch.as_tensor(masked_m, dtype=torch.int32)
+    return Problem("masked", _bf16(a), None, _bf16(b), None, C=c, masked_m=mm, seed=seed, bf16=True)
 
 
 # ---------------------------------------------------------------- K-grouped TN
@@ -347,6 +383,6 @@ def sentinel_like(shape, seed) -> torch.Tensor:
 
 def to_numpy(p: Problem):
     """numpy views of a problem's tensors (for the oracle)."""
-    f = lambda t: None if t is None else t.numpy()
+    f = lambda t: None if t is None else (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).numpy()
     return dict(A=f(p.A), sfa=f(p.sfa), B=f(p.B), sfb=f(p.sfb), C=f(p.C),
                 m_indices=f(p.m_indices), masked_m=f(p.masked_m))

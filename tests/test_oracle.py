@@ -565,3 +565,53 @@ def test_layout_nn_contiguous_vs_numpy(oracle):
         sb = np.repeat(np.repeat(p.sfb[g].numpy().astype(np.float64), 128, axis=0)[:129], 128, axis=1)  # [N, K]
         ref = Ad[m] @ (dec[Bn[g]] * sb.T) + p.C[m].numpy().astype(np.float64)
         assert np.allclose(got[m], ref, rtol=1e-12, atol=1e-9)
+
+
+# ------------------------------------------------------------------ BF16 x BF16
+def test_bf16_decode_matches_torch_for_every_code(oracle):
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = np.array([oracle.bf16_value(c) for c in range(65536)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5, 64), (37, 129, 200), (130, 3, 128)])
+def test_bf16_gemm_vs_numpy(oracle, M, N, K):
+    p = gen.make_bf16("dense", seed=M + N + K, M=M, N=N, K=K, with_c=True)
+    A = p.A.float().numpy().astype(np.float64)
+    B = p.B.float().numpy().astype(np.float64)
+    ref = A @ B.T + p.C.numpy().astype(np.float64)
+    d = gen.to_numpy(p)
+    got, comp = oracle.bf16_gemm("dense", d["A"], d["B"], C=d["C"])
+    assert comp.all()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-10)
+
+
+def test_bf16_gemm_integer_data_exact(oracle):
+    g = torch.Generator().manual_seed(88)
+    A = torch.randint(-20, 21, (50, 256), generator=g)
+    B = torch.randint(-20, 21, (70, 256), generator=g)
+    got, _ = oracle.bf16_gemm("dense", A.to(torch.bfloat16).view(torch.int16).numpy(),
+                              B.to(torch.bfloat16).view(torch.int16).numpy())
+    assert np.array_equal(got, (A.to(torch.int64) @ B.to(torch.int64).T).numpy().astype(np.float64))
+
+
+def test_bf16_grouped_equal_dense(oracle):
+    pc = gen.make_bf16("contiguous", seed=81, N=65, K=96, group_rows=[128, 0, 60], with_c=True, pad_rows=128)
+    d = gen.to_numpy(pc)
+    got, comp = oracle.bf16_gemm("contiguous", d["A"], d["B"], d["m_indices"], d["C"])
+    for m in np.flatnonzero(comp):
+        g = int(pc.m_indices[m])
+        ref, _ = oracle.bf16_gemm("dense", d["A"][m:m + 1], d["B"][g], C=d["C"][m:m + 1])
+        assert np.array_equal(got[m], ref[0])
+    assert np.array_equal(comp, (pc.m_indices.numpy() >= 0))
+    pm = gen.make_bf16("masked", seed=82, N=40, K=64, G=3, M_max=20, masked_m=[20, 0, 7])
+    d = gen.to_numpy(pm)
+    got, comp = oracle.bf16_gemm("masked", d["A"], d["B"], d["masked_m"])
+    assert comp.reshape(3, 20).sum(1).tolist() == [20, 0, 7]
+    for g in range(3):
+        ref, _ = oracle.bf16_gemm("dense", d["A"][g], d["B"][g])
+        valid = comp.reshape(3, 20)[g]
+        assert np.array_equal(got.reshape(3, 20, 40)[g][valid], ref[valid])

@@ -54,6 +54,13 @@ MUTANTS = [
     ("kg_sfb_first_block", "const float *sb = p->sfb + kb * (int64_t)N;",
      "const float *sb = p->sfb + kb_first * (int64_t)N;"),
     ("kg_c_ignored", "            out[n] += (double)c_row[n];", "            out[n] += 0.0 * (double)c_row[n];"),
+    ("bf16_bias_128", "mag = ldexp(1.0 + (double)m / 128.0, e - 127);", "mag = ldexp(1.0 + (double)m / 128.0, e - 128);"),
+    ("bf16_subnormal_scale", "mag = ldexp((double)m, -133);", "mag = ldexp((double)m, -132);"),
+    ("bf16_drop_last_k", "            for (int k = 0; k < p->K; ++k)\n                acc += a[k]",
+     "            for (int k = 0; k < p->K - 1; ++k)\n                acc += a[k]"),
+    ("bf16_c_ignored", "out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);", "out[n] = acc;"),
+    ("bf16_masked_group0", "        const uint16_t *b = p->B + g * (int64_t)p->N * p->K;",
+     "        const uint16_t *b = p->B;"),
 ]
 
 
@@ -78,6 +85,9 @@ def _pin_calls(o):
               pins.test_k_grouped_operand_swap_transposes, pins.test_k_grouped_empty_group_and_closed_form):
         calls.append(lambda f=f: f(o))
     calls.append(lambda: pins.test_k_grouped_vs_numpy_dequant_matmul(o, [128, 256, 0, 384], 37, 129))
+    calls.append(lambda: pins.test_bf16_decode_matches_torch_for_every_code(o))
+    calls.append(lambda: pins.test_bf16_gemm_vs_numpy(o, 37, 129, 200))
+    calls.append(lambda: pins.test_bf16_grouped_equal_dense(o))
     return calls
 
 
