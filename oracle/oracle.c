@@ -587,7 +587,7 @@ double oracle_bf16_value(uint16_t bits)
         mag = ldexp((double)m, -133);
     else
         mag = ldexp(1.0 + (double)m / 128.0, e - 127);
-    return s ? -mag : mag;
+    return s ? 0.0 - mag : mag;
 }
 
 typedef struct {

@@ -58,6 +58,7 @@ MUTANTS = [
     ("bf16_subnormal_scale", "mag = ldexp((double)m, -133);", "mag = ldexp((double)m, -132);"),
     ("bf16_drop_last_k", "            for (int k = 0; k < p->K; ++k)\n                acc += a[k]",
      "            for (int k = 0; k < p->K - 1; ++k)\n                acc += a[k]"),
+    ("bf16_lost_sign", "return s ? 0.0 - mag : mag;", "return mag;"),
     ("bf16_c_ignored", "out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);", "out[n] = acc;"),
     ("bf16_masked_group0", "        const uint16_t *b = p->B + g * (int64_t)p->N * p->K;",
      "        const uint16_t *b = p->B;"),
