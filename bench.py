@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOPS + HBM GB/s per shape (FP8 block-scaled GEMM), % of roofline"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0    # also the peak used for FP8 x FP4: each MFMA there has an FP8 operand
+PEAK_BF16_TFLOPS = 2500.0   # dense BF16 MFMA peak (the unscaled BF16 GEMM)
 RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 # The pages' H800 numbers for the same shapes (DeepGEMM launch article,
 # section 3 dense table): other hardware, context only.
@@ -48,6 +49,19 @@ def kernel_source_hash() -> str:
 def algorithmic(p) -> tuple[float, float, int]:
     """(FLOPs, bytes, computed rows) of one call, by the pages' convention."""
     K, N = p.K, p.N
+    if getattr(p, "bf16", False):
+        # 2-byte A, B and D, no scales
+        if p.kind == "dense":
+            rows, groups_used = p.M, 1
+        elif p.kind == "contiguous":
+            idx = p.m_indices
+            rows = int(((idx >= 0) & (idx < p.G)).sum())
+            groups_used = int(idx[(idx >= 0) & (idx < p.G)].unique().numel())
+        else:
+            mm = p.masked_m.clamp(0, p.A.shape[1])
+            rows, groups_used = int(mm.sum()), int((mm > 0).sum())
+        nbytes = rows * K * 2 + groups_used * N * K * 2 + rows * N * 2 + (rows * N * 4 if p.C is not None else 0)
+        return 2.0 * rows * N * K, float(nbytes), rows
     if p.kind == "k_grouped":
         # each group's D [M, N] is computed; A [K, M] and B [K, N] are read once
         M, G = p.M, p.G
@@ -86,14 +100,23 @@ def kind_id(kind: str) -> int:
     return {"dense": 0, "contiguous": 1, "masked": 2, "k_grouped": 3}[kind]
 
 
-def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False, fp4: bool = False):
+def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False, fp4: bool = False,
+                   bf16: bool = False):
     import torch
 
     import moe_grouped_gemm_scales_amd as dg
     from tests import gen
     from tests.gpu_util import out_shape, to_dev
 
-    p = gen.make_k_grouped_workload() if cfg == "kg" else gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
+    if cfg == "kg":
+        p = gen.make_k_grouped_workload()
+    elif bf16:
+        c = gen.WORKLOADS[cfg]
+        assert c["kind"] == "dense", "the BF16 bench covers the dense workloads"
+        p = gen.make_bf16("dense", seed=gen.workload_seed(cfg), M=c["M"], N=c["N"], K=c["K"],
+                          with_c=c.get("with_c", False))
+    else:
+        p = gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
     flops, nbytes, rows = algorithmic(p)
     oshape = (p.G, p.M, p.N) if p.kind == "k_grouped" else out_shape(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
@@ -110,6 +133,8 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
         d, D = devs[i % copies], outs[i % copies]
         if p.kind == "k_grouped":
             dg.dg_k_grouped_fp8_gemm_tn_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["ks"], d["C"], D)
+        elif bf16:
+            dg.dg_bf16_gemm_nt(d["A"], d["B"], d["C"], D)
         elif fp4:
             if p.kind == "dense":
                 dg.dg_fp8_fp4_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
@@ -127,7 +152,7 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
             dg.dg_m_grouped_fp8_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"], D)
 
     rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
-    flag = dg.SCALE_FP8_FP4 if fp4 else (dg.SCALE_UE8M0 if ue8m0 else 0)
+    flag = dg.KIND_BF16 if bf16 else dg.SCALE_FP8_FP4 if fp4 else (dg.SCALE_UE8M0 if ue8m0 else 0)
     kernel = dg.describe_config(kind_id(p.kind) | flag, rows_arg, p.N, p.K, p.G,
                                 p.C is not None)
     # everything runs on one non-default stream (HIP graphs cannot capture the null stream)
@@ -170,12 +195,13 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
     kernel_ms = start.elapsed_time(end) / n_launch
     ms_per_step = wall * 1e3 / n_launch
     t_kernel = kernel_ms * 1e-3
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP8_TFLOPS
     ai = flops / nbytes
-    bound = "mfma" if ai >= RIDGE else "hbm"
+    bound = "mfma" if ai >= peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     tflops = flops / t_kernel / 1e12
     gbs = nbytes / t_kernel / 1e9
-    frac = (tflops / PEAK_FP8_TFLOPS) if bound == "mfma" else (gbs / PEAK_HBM_GBS)
-    return dict(problem=p, flops=flops, bytes=nbytes, rows=rows, kernel=kernel, copies=copies,
+    frac = (tflops / peak) if bound == "mfma" else (gbs / PEAK_HBM_GBS)
+    return dict(problem=p, peak=peak, flops=flops, bytes=nbytes, rows=rows, kernel=kernel, copies=copies,
                 kernel_ms=kernel_ms, ms_per_step=ms_per_step, wall_s=wall, tflops=tflops, gbs=gbs,
                 bound=bound, frac=frac, jit_s=t_jit, step_tflops=flops / (ms_per_step * 1e-3) / 1e12)
 
@@ -280,13 +306,13 @@ def main():
     per_shape = []
     if args.all:
         modes = [(c, "") for c in [0, 1, "1c", 2, 3, 4]] + [(c, "_ue8m0") for c in [0, 1, 2, 3, 4]] + \
-            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]] + [("kg", "")]
+            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]] + [("kg", ""), (2, "_bf16")]
         for c, mode in modes:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
             if c == "kg":
                 steps = max(5, args.steps // 20)
             r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=mode == "_ue8m0",
-                               fp4=mode == "_fp4")
+                               fp4=mode == "_fp4", bf16=mode == "_bf16")
             wl = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[c] + mode
             line = dict(workload=wl, kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
@@ -303,7 +329,7 @@ def main():
         ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
-                peak=PEAK_FP8_TFLOPS if r["bound"] == "mfma" else PEAK_HBM_GBS,
+                peak=r["peak"] if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))

@@ -214,6 +214,27 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const void *A, const float *sfa, c
                                               void *D, int M, int N, int K, int num_groups,
                                               void *stream);
 
+/*
+ * BF16 x BF16 without scale factors (DeepGEMM-Ascend hub page, precision
+ * table "BF16 x BF16" for ordinary-precision training; DeepGEMM README intro:
+ * GEMM in FP8, FP4 and BF16): D = C + A . B^T with A and B in BF16, FP32
+ * accumulation, BF16 D (round-to-nearest-even, once).  Layouts as the FP8 NT
+ * forms with 2-byte elements and no sfa/sfb: dense A [M][K], B [N][K];
+ * contiguous A [M][K], B [G][N][K], m_indices [M]; masked A [G][M_max][K],
+ * B [G][N][K], masked_m [G]; C float like D or NULL.  K must be a multiple of
+ * 64 (one 128-byte block; reading, the pages give no rule), M of the
+ * contiguous form a multiple of 128.  Ownership, streams, group and mask rules
+ * and errors as for the FP8 forms.
+ */
+dg_status dg_bf16_gemm_nt(const void *A, const void *B, const float *C, void *D, int M, int N, int K,
+                          void *stream);
+dg_status dg_m_grouped_bf16_gemm_nt_contiguous(const void *A, const void *B, const int32_t *m_indices,
+                                               const float *C, void *D, int M, int N, int K,
+                                               int num_groups, void *stream);
+dg_status dg_m_grouped_bf16_gemm_nt_masked(const void *A, const void *B, const int32_t *masked_m,
+                                           const float *C, void *D, int M_max, int N, int K,
+                                           int num_groups, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);
 
@@ -242,6 +263,7 @@ dg_status dg_init(void);
 /* Flags OR-ed into `kind` below for the packed-UE8M0 and the FP8 x FP4 entry points. */
 #define DG_SCALE_UE8M0 4
 #define DG_SCALE_FP8_FP4 8
+#define DG_BF16 16           /* BF16 x BF16 without scales (K in elements) */
 
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these

@@ -340,6 +340,27 @@ dg_status masked(const void* A, const void* sfa, const void* B, const void* sfb,
     return launch(p, A, sfa, B, sfb, masked_m, C, D, stream);
 }
 
+// BF16 x BF16, the three M forms: no scales; the kernels count K in bytes
+dg_status bf16_gemm(int kind, const void* A, const void* B, const int32_t* grp, const float* C, void* D, int rows,
+                    int N, int K, int num_groups, void* stream) {
+    if (!A || !B || !D) return set_error(DG_ERR_INVALID_ARG, "A, B and D must be non-NULL");
+    if (rows < 0 || N <= 0 || K <= 0) return set_error(DG_ERR_INVALID_ARG, "sizes must be positive (M may be 0)");
+    if (K % 64 != 0) return set_error(DG_ERR_UNSUPPORTED, "BF16: K must be a multiple of 64 (one 128-byte block)");
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
+        return set_error(DG_ERR_ALIGNMENT, "A, B, C and D must be 16-byte aligned");
+    if ((uint64_t)K * 2u * 256u >= (1ull << 32)) return set_error(DG_ERR_UNSUPPORTED, "sizes exceed 32-bit buffer offsets");
+    if (kind != kDense) {
+        if (!grp) return set_error(DG_ERR_INVALID_ARG, "m_indices / masked_m must be non-NULL");
+        if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
+        if (!aligned(grp, 4)) return set_error(DG_ERR_ALIGNMENT, "m_indices / masked_m must be 4-byte aligned");
+    }
+    if (kind == kContiguous && rows % dg_get_mk_alignment_for_contiguous_layout() != 0)
+        return set_error(DG_ERR_ALIGNMENT, "contiguous M must be a multiple of the M alignment (128)");
+    if (rows == 0) return DG_OK;
+    Problem p{kind, rows, N, 2 * K, kind == kDense ? 1 : num_groups, C ? 1 : 0, 3};
+    return launch(p, A, nullptr, B, nullptr, grp, C, D, stream);
+}
+
 dg_status k_grouped(const void* A, const float* sfa, const void* B, const float* sfb, const int32_t* ks,
                     const float* C, void* D, int M, int N, int K, int num_groups, void* stream) {
     dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
@@ -392,18 +413,23 @@ dg_status dg_init(void) {
 
 // Scale format encoded in `kind` by the DG_SCALE_* flags
 int scale_format(int* kind) {
-    const int sf = (*kind & DG_SCALE_FP8_FP4) ? 2 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
-    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4);
+    const int sf = (*kind & DG_BF16) ? 3 : (*kind & DG_SCALE_FP8_FP4) ? 2 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
+    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4 | DG_BF16);
     return sf;
+}
+
+// the kernels' K: BF16 rows are counted in bytes; K-grouped operands use the padded pitch
+int kernel_k(int kind, int sf, int K) {
+    if (sf == 3) return 2 * K;
+    return kind == kKGrouped ? k_grouped_pitch(K) : K;
 }
 
 dg_status dg_precompile(int kind, int rows, int N, int K, int num_groups, int has_c, int num_cus) {
     const int sf = scale_format(&kind);
     if (kind < 0 || kind > 3 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_precompile: bad arguments");
-    if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
-    Problem p{kind, rows, N, kind == kKGrouped ? k_grouped_pitch(K) : K, kind == kDense ? 1 : num_groups,
-              has_c ? 1 : 0, sf};
+    if (K % (sf == 3 ? 64 : 128)) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128 (BF16: 64)");
+    Problem p{kind, rows, N, kernel_k(kind, sf, K), kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
     for (const KernelConfig& cfg : select_plan(p, num_cus > 0 ? num_cus : 256)) {
         std::vector<char> code;
         dg_status s = compile_code(cfg, &code);
@@ -417,7 +443,7 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
     const int sf = scale_format(&kind);
     if (kind < 0 || kind > 3 || rows <= 0 || N <= 0 || K <= 0 || num_groups <= 0 || !buf || len <= 0)
         return set_error(DG_ERR_INVALID_ARG, "dg_describe_config: bad arguments");
-    if (K % 128) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128");
+    if (K % (sf == 3 ? 64 : 128)) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128 (BF16: 64)");
     int cus = num_cus;
     if (cus <= 0) {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -427,8 +453,7 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
         if (s != DG_OK) return s;
         cus = effective_cus(*st);
     }
-    Problem p{kind, rows, N, kind == kKGrouped ? k_grouped_pitch(K) : K, kind == kDense ? 1 : num_groups,
-              has_c ? 1 : 0, sf};
+    Problem p{kind, rows, N, kernel_k(kind, sf, K), kind == kDense ? 1 : num_groups, has_c ? 1 : 0, sf};
     std::string key;
     for (const KernelConfig& c : select_plan(p, cus)) key += (key.empty() ? "" : "+") + c.key();
     std::snprintf(buf, (size_t)len, "%s", key.c_str());
@@ -513,6 +538,20 @@ dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const void* A, const float* sfa, c
                                               const int32_t* m_indices, const float* C, void* D, int M, int N, int K,
                                               int num_groups, void* stream) {
     return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 0, stream, 1);
+}
+
+dg_status dg_bf16_gemm_nt(const void* A, const void* B, const float* C, void* D, int M, int N, int K, void* stream) {
+    return bf16_gemm(kDense, A, B, nullptr, C, D, M, N, K, 1, stream);
+}
+
+dg_status dg_m_grouped_bf16_gemm_nt_contiguous(const void* A, const void* B, const int32_t* m_indices, const float* C,
+                                               void* D, int M, int N, int K, int num_groups, void* stream) {
+    return bf16_gemm(kContiguous, A, B, m_indices, C, D, M, N, K, num_groups, stream);
+}
+
+dg_status dg_m_grouped_bf16_gemm_nt_masked(const void* A, const void* B, const int32_t* masked_m, const float* C,
+                                           void* D, int M_max, int N, int K, int num_groups, void* stream) {
+    return bf16_gemm(kMasked, A, B, masked_m, C, D, M_max, N, K, num_groups, stream);
 }
 
 }  // extern "C"

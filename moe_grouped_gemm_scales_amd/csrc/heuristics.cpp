@@ -107,8 +107,9 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
 int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
     const int rpi = 8 / c.kstep;
-    const int na = c.bm / rpi, nb = c.sf == 2 ? c.bn / 16 : c.bn / rpi, ns = (c.bm + 63) / 64 * c.kstep;
-    const int nt = (c.sf == 2 || c.kind == kKGrouped) ? (c.bn + 63) / 64 : c.kstep;
+    const int na = c.bm / rpi, nb = c.sf == 2 ? c.bn / 16 : c.bn / rpi;
+    const int ns = c.sf == 3 ? 0 : (c.bm + 63) / 64 * c.kstep;
+    const int nt = c.sf == 3 ? 0 : (c.sf == 2 || c.kind == kKGrouped) ? (c.bn + 63) / 64 : c.kstep;
     return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (nt + nw - 1) / nw;
 }
 
@@ -199,11 +200,18 @@ const Tuned kTunedF4[] = {
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
+// BF16 x BF16 (variant 0; k here is the row length in bytes, 2 x K)
+const Tuned kTunedBF16[] = {
+    {kDense, 4096, 7168, 32768, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+};
+
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
     std::vector<KernelConfig> out;
     if (num_cus != 256) return out;       // measured on the full 256-CU part
-    const Tuned* first = p.sf == 2 ? std::begin(kTunedF4) : p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
-    const Tuned* last = p.sf == 2 ? std::end(kTunedF4) : p.sf ? std::end(kTunedE8) : std::end(kTuned);
+    const Tuned* first = p.sf == 3 ? std::begin(kTunedBF16) : p.sf == 2 ? std::begin(kTunedF4)
+                       : p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
+    const Tuned* last = p.sf == 3 ? std::end(kTunedBF16) : p.sf == 2 ? std::end(kTunedF4)
+                      : p.sf ? std::end(kTunedE8) : std::end(kTuned);
     for (const Tuned* it = first; it != last; ++it) {
         const Tuned& t = *it;
         if (t.kind != p.kind || t.n != p.n || t.k != p.k || t.g != p.g || t.has_c != p.has_c) continue;

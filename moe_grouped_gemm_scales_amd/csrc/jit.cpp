@@ -184,6 +184,7 @@ std::string KernelConfig::key() const {
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
     if (sf == 1) s << "_e8m0";
     if (sf == 2) s << "_f8f4";
+    if (sf == 3) s << "_bf16";
     if (ne > 0) s << "_cols" << nb << "-" << ne;
     return s.str();
 }

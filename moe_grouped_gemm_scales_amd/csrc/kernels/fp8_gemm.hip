@@ -75,6 +75,10 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 // (element 2i in the low nibble of byte i), [N][K/2]; sfb holds one UE8M0
 // scale per 1x32 block of each row of B, the four of a 128-wide K block in
 // one word, [N][K/128] (byte j: K elements 128 kb + 32 j .. + 32).
+// 3 = BF16 x BF16 without scales (DeepGEMM-Ascend hub page, precision table;
+// DeepGEMM README intro: GEMM in FP8, FP4 and BF16): A [rows][K], B [N][K]
+// BF16, D = C + A . B^T.  DG_K is then the row length in BYTES (2 x K), so a
+// 128-byte "K block" is 64 BF16 elements, two v_mfma_f32_16x16x32_bf16.
 #ifndef DG_SF
 #define DG_SF 0
 #endif
@@ -106,8 +110,9 @@ constexpr int NBLKS = (N + KBLK - 1) / KBLK;
 constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D; N is the row pitch
 static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
 constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
-constexpr bool SF_E8 = DG_SF != 0;
+constexpr bool SF_E8 = DG_SF == 1 || DG_SF == 2;
 constexpr bool FP4B = DG_SF == 2;             // B in E2M1 with per-row 1x32 UE8M0 scales
+constexpr bool BF16 = DG_SF == 3;             // BF16 operands, no scales
 constexpr int KW = (KBLKS + 3) / 4;           // packed UE8M0 words per row of scales
 constexpr int SF_KB = SF_E8 ? KW : KBLKS;     // scale entries (floats or words) along K
 constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
@@ -115,7 +120,8 @@ constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
 // WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N);
 // FP4 B has a scale per row, never one per wave
 constexpr bool KG = kKind == 3;                // K-grouped: per-column B scales, per-group K ranges
-constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0 && !FP4B && !KG;
+constexpr bool SB_UNIFORM = (KBLK % WAVE_N) == 0 && (DG_NB % WAVE_N) == 0 && !FP4B && !KG && !BF16;
+static_assert(!BF16 || (DG_KSTEP == 1 && kKind != 3), "BF16: one K block a stage, M-grouped or dense");
 static_assert(!KG || (!SF_E8 && DG_SPLITK == 1 && DG_KSTEP == 1), "K-grouped: FP32 scales, no split-K, one K block a stage");
 
 static_assert(K % KBLK == 0, "K must be a multiple of 128");
@@ -202,6 +208,10 @@ __device__ __forceinline__ u32 lds_addr(const void* p) {
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
 typedef __attribute__((address_space(3))) const float lds_f32;
 typedef __attribute__((address_space(3))) const u8 lds_u8;
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// the two 16-byte halves of a fragment as BF16 MFMA operands (8 elements each)
+__device__ __forceinline__ v8bf bf_lo(v8i x) { return __builtin_bit_cast(v8bf, v4i{x[0], x[1], x[2], x[3]}); }
+__device__ __forceinline__ v8bf bf_hi(v8i x) { return __builtin_bit_cast(v8bf, v4i{x[4], x[5], x[6], x[7]}); }
 // Fragment read: two 16-byte chunks at lane-specific bases plus a constant
 // offset, written as pointer arithmetic so the offset folds into ds_read_b128.
 __device__ __forceinline__ v8i lds_read_frag(lds_u8* lo, lds_u8* hi, int off) {
@@ -502,7 +512,7 @@ constexpr int ROWB_B = FP4B ? 64 : ROWB;
 constexpr int RPI_B = 1024 / ROWB_B;
 constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
 constexpr int NB_INS = BN / RPI_B;              // ... for B
-constexpr int NS_PER_KB = (BM + 63) / 64;       // 256 B DMA instructions for one K block of sfa
+constexpr int NS_PER_KB = BF16 ? 0 : (BM + 63) / 64;   // 256 B DMA instructions for one K block of sfa
 constexpr int NS_INS = NS_PER_KB * KSTEP;
 constexpr int A_OFF = 0;
 constexpr int B_OFF = BM * ROWB;
@@ -512,10 +522,11 @@ constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
 // DMA per K block, so the K loop issues no scalar loads; FP4 B: one word per
 // row of the tile, K-grouped: one float per column, 64 per DMA
 constexpr int T_OFF = S_OFF + KSTEP * S_BYTES;
-constexpr int NT_INS = (FP4B || KG) ? (BN + 63) / 64 : KSTEP;
+constexpr int NT_INS = BF16 ? 0 : (FP4B || KG) ? (BN + 63) / 64 : KSTEP;
 constexpr int STAGE_BYTES = T_OFF + NT_INS * 256;
 static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
+static_assert(!BF16 || (KBLKS >= 1 && K % 128 == 0), "BF16: K bytes a multiple of 128");
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 static_assert(BM % RPI == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
@@ -635,7 +646,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
         // swizzle term does not depend on the instruction (16 rows each)
         const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-        u32 voff_s[IS];          // A scales: clamped rows (the offset includes the K block's row of sfa)
+        u32 voff_s[IS > 0 ? IS : 1];   // A scales: clamped rows (the offset includes the K block's row of sfa)
 #pragma unroll
         for (int j = 0; j < IS; ++j) {
             const int i = min(wave + j * NWAVES, NS_INS - 1);
@@ -644,7 +655,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
             voff_s[j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
         }
-        u32 voff_t[IT];
+        u32 voff_t[IT > 0 ? IT : 1];
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
             const int h = min(wave + j * NWAVES, NT_INS - 1);
@@ -771,6 +782,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             // K-grouped B scales: the lane's four columns of each n sub-tile
             const int sbk_off = (wn * WAVE_N + 4 * q) * 4;
             auto read_scales = [&](int stage, int h) __attribute__((always_inline)) {
+                if constexpr (BF16) return;       // no scales
                 lds_u8* const sb_p = kblock_sfb(stage, h);
                 if constexpr (FP4B) {
 #pragma unroll
@@ -864,7 +876,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     sc_t sc_prev[TM], s_last[TM];
 #pragma unroll
                     for (int a = 0; a < TM; ++a) {
-                        if constexpr (SF_E8) sc_prev[a] = s_last[a] = 0.f;
+                        if constexpr (SF_E8 || BF16) sc_prev[a] = s_last[a] = 0.f;
                         else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
                         else {
                             sc_prev[a] = sa[a] * sb[b > 0 ? b - 1 : 0];
@@ -892,6 +904,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                             // srcA format: 0 = E4M3, 4 = E2M1 (FP4 B)
                             acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 fb, fa[a], acc[a][b], FP4B ? 4 : 0, 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
+                        } else if constexpr (BF16) {
+                            // 64 BF16 elements: K chunks q (elements 8q..8q+7) then q+4 (32+8q..)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_lo(fb), bf_lo(fa[a]), acc[a][b], 0, 0, 0);
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_hi(fb), bf_hi(fa[a]), acc[a][b], 0, 0, 0);
                         } else {
                             const v4f zero = {0.f, 0.f, 0.f, 0.f};
                             // P[n][m] over this 128-wide K block: exact products, FP32 sums
@@ -1023,7 +1039,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 }   // K blocks of the stage
             }
         }
-        if constexpr (!SF_E8) {
+        if constexpr (!SF_E8 && !BF16) {
 #pragma unroll
             for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
         }
@@ -1048,7 +1064,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 //              work item (it must fit), so the K loop has no barrier at all
 //              and the waves run independently.
 constexpr bool ARES = DG_VARIANT == 2;
-static_assert(!SF_E8 && !KG, "UE8M0 scales and the K-grouped form are built for variant 0");
+static_assert(!SF_E8 && !KG && !BF16, "UE8M0 scales, BF16 and the K-grouped form are built for variant 0");
 static_assert(WM == 1, "variants 1 and 2 spread their waves along n only");
 static_assert(KSTEP == 1, "variants 1 and 2 stage one K block at a time");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
@@ -1351,7 +1367,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 // flag is also bounded, so a fault in this protocol would cost correctness,
 // which the tests check, and never hang the device.
 static_assert(WM == 1, "variant 3 spreads its consumer waves along n only");
-static_assert(!SF_E8 && !KG, "UE8M0 scales and the K-grouped form are built for variant 0");
+static_assert(!SF_E8 && !KG && !BF16, "UE8M0 scales, BF16 and the K-grouped form are built for variant 0");
 static_assert(KSTEP == 1, "variant 3 stages one K block per slot");
 constexpr int NKB = KBLKS / SPLITK;               // K blocks of one work item
 static_assert(NKB <= 64, "the whole K range of a work item is unrolled");

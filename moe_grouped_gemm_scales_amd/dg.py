@@ -51,6 +51,12 @@ def _load():
         getattr(lib, name).restype = i32
     lib.dg_m_grouped_fp8_gemm_nn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_m_grouped_fp8_gemm_nn_contiguous.restype = i32
+    vp_ = ctypes.c_void_p
+    lib.dg_bf16_gemm_nt.argtypes = [vp_, vp_, vp_, vp_, i32, i32, i32, vp_]
+    lib.dg_m_grouped_bf16_gemm_nt_contiguous.argtypes = [vp_, vp_, vp_, vp_, vp_, i32, i32, i32, i32, vp_]
+    lib.dg_m_grouped_bf16_gemm_nt_masked.argtypes = [vp_, vp_, vp_, vp_, vp_, i32, i32, i32, i32, vp_]
+    for f in (lib.dg_bf16_gemm_nt, lib.dg_m_grouped_bf16_gemm_nt_contiguous, lib.dg_m_grouped_bf16_gemm_nt_masked):
+        f.restype = i32
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
     lib.dg_fp8_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
@@ -440,3 +446,64 @@ def dg_m_grouped_fp8_gemm_nn_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=
 
 fp8_gemm_nn, fp8_gemm_tn, fp8_gemm_tt = dg_fp8_gemm_nn, dg_fp8_gemm_tn, dg_fp8_gemm_tt
 m_grouped_fp8_gemm_nn_contiguous = dg_m_grouped_fp8_gemm_nn_contiguous
+
+
+# ---------------------------------------------------------------- BF16 x BF16 (unscaled)
+KIND_BF16 = 16       # DG_BF16: OR into `kind` of precompile / describe_config (K in elements)
+
+
+def _bf(t: torch.Tensor, name: str, shape):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _dev(t, name)
+
+
+def dg_bf16_gemm_nt(A, B, C, D, stream=None):
+    """D = C + A @ B.T in BF16 without scales.  A [M,K], B [N,K] bfloat16, C None or float32 [M,N]."""
+    M, K = A.shape
+    N = B.shape[0]
+    _bf(A, "A", (M, K)); _bf(B, "B", (N, K))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_bf16_gemm_nt(_ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_bf16_gemm_nt_contiguous(A, B, m_indices, C, D, stream=None):
+    """Contiguous M-grouped BF16: A [M,K], B [G,N,K], m_indices int32 [M]."""
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _bf(A, "A", (M, K)); _bf(B, "B", (G, N, K))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_bf16_gemm_nt_contiguous(_ptr(A), _ptr(B), _ptr(m_indices), _ptr(C), _ptr(D), M, N, K, G,
+                                                    _stream(stream)))
+    return D
+
+
+def dg_m_grouped_bf16_gemm_nt_masked(A, B, masked_m, C, D, stream=None):
+    """Masked M-grouped BF16: A [G,M_max,K], B [G,N,K], masked_m int32 [G]."""
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _bf(A, "A", (G, M_max, K)); _bf(B, "B", (G, N, K))
+    if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be int32 [G]")
+    _dev(masked_m, "masked_m")
+    if C is not None:
+        _f32(C, "C", (G, M_max, N))
+    _out(D, (G, M_max, N))
+    _check(lib.dg_m_grouped_bf16_gemm_nt_masked(_ptr(A), _ptr(B), _ptr(masked_m), _ptr(C), _ptr(D), M_max, N, K, G,
+                                                _stream(stream)))
+    return D
+
+
+bf16_gemm_nt = dg_bf16_gemm_nt
+m_grouped_bf16_gemm_nt_contiguous = dg_m_grouped_bf16_gemm_nt_contiguous
+m_grouped_bf16_gemm_nt_masked = dg_m_grouped_bf16_gemm_nt_masked

@@ -29,7 +29,14 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
         D = sent.to("cuda")
     else:
         D.copy_(sent.to("cuda"))
-    if p.fp4:
+    if p.bf16:
+        if p.kind == "dense":
+            dg.dg_bf16_gemm_nt(dev["A"], dev["B"], dev["C"], D)
+        elif p.kind == "contiguous":
+            dg.dg_m_grouped_bf16_gemm_nt_contiguous(dev["A"], dev["B"], dev["m_indices"], dev["C"], D)
+        else:
+            dg.dg_m_grouped_bf16_gemm_nt_masked(dev["A"], dev["B"], dev["masked_m"], dev["C"], D)
+    elif p.fp4:
         if p.kind == "dense":
             dg.dg_fp8_fp4_gemm_nt(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
         elif p.kind == "contiguous":
@@ -53,6 +60,9 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
 def oracle_rows(oracle, p: gen.Problem, rows=None, threads=0):
     """(reference FP64 [rows, N], computed mask [rows]) for flat row indices."""
     d = gen.to_numpy(p)
+    if p.bf16:        # unscaled BF16 GEMM
+        gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
+        return oracle.bf16_gemm(p.kind, d["A"], d["B"], gi, d["C"], rows=rows, threads=threads)
     if p.fp4:         # FP8 x FP4: E2M1 B with 1x32 UE8M0 scales
         gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
         ref, comp = oracle.fp8_fp4_gemm(p.kind, d["A"], d["sfa"], d["B"], d["sfb"], gi, d["C"], rows=rows,
