@@ -271,6 +271,8 @@ def main():
                     help="time the chosen workload with packed UE8M0 scales instead of FP32 ones")
     ap.add_argument("--fp4", action="store_true",
                     help="time the chosen workload as FP8 x FP4 (E2M1 B with 1x32 UE8M0 scales)")
+    ap.add_argument("--bf16", action="store_true",
+                    help="time the chosen dense workload as an unscaled BF16 GEMM")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--copy-kernel", action="store_true",
@@ -323,19 +325,19 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4)
+    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4, bf16=args.bf16)
     p = r["problem"]
     name = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[cfg] + \
-        ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "")
+        ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "_bf16" if args.bf16 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=r["peak"] if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))
-    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4 or cfg == "kg") else cpu_baseline(cfg)
+    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4 or args.bf16 or cfg == "kg") else cpu_baseline(cfg)
     value = r["step_tflops"]
-    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not (args.ue8m0 or args.fp4) else None
+    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not (args.ue8m0 or args.fp4 or args.bf16) else None
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -347,7 +349,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / pages, 4) if pages else None,
-        "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "fp8_e4m3",
+        "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "bf16" if args.bf16 else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": name, "kind": p.kind, "M": p.M if p.kind == "k_grouped" else p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
                    "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],

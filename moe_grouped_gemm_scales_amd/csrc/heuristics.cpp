@@ -151,7 +151,9 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.kstep != 1 && c.kstep != 2) return false;
     if (c.bm % (8 / c.kstep) || c.bn % (8 / c.kstep) || c.stages < 2) return false;
     if (dma_per_wave(c) * (c.stages - 1) > 63) return false;   // vmcnt field
-    if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > 32) return false;
+    // more than 32 sub-tiles per wave: only 4-wave groups without promotion (accumulators in AGPRs)
+    const bool agpr_acc = (c.sf == 1 || c.sf == 3) && c.wm * c.wn == 4;
+    if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > (agpr_acc ? 64 : 32)) return false;
     if ((p.k / 128) % (c.splitk * c.kstep)) return false;
     return true;
 }
@@ -202,7 +204,7 @@ const Tuned kTunedF4[] = {
 
 // BF16 x BF16 (variant 0; k here is the row length in bytes, 2 x K)
 const Tuned kTunedBF16[] = {
-    {kDense, 4096, 7168, 32768, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    {kDense, 4096, 7168, 32768, 1, 0, 256, 224, 4, 2, 2, 1, 1, 0, 0, 0},
 };
 
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {

@@ -136,7 +136,11 @@ static_assert(STAGES >= 2, "at least double buffering");
 // 256-lane maximum the compiler plans for one wave per SIMD, writes MFMA
 // results to AGPRs and copies every one back with v_accvgpr_read before the
 // promotion FMA, doubling the VALU work per MFMA.
-constexpr int MAX_THREADS_DECL = NTHREADS < 512 ? 512 : NTHREADS;
+// Exception: with no promotion step (UE8M0 scales applied by the MFMA, or BF16)
+// a 4-wave workgroup with more than 32 sub-tiles per wave keeps its accumulators
+// in AGPRs, which the MFMAs read and write directly; it declares its own size.
+constexpr bool ACC_IN_AGPR = (DG_SF == 1 || DG_SF == 3) && NTHREADS == 256 && TM * TN > 32;
+constexpr int MAX_THREADS_DECL = (NTHREADS < 512 && !ACC_IN_AGPR) ? 512 : NTHREADS;
 
 struct Params {
     const u8* A;

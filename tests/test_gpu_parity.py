@@ -337,7 +337,8 @@ def test_ue8m0_grouped(oracle):
 
 
 UE8M0_FORCED = ["128,128,4,2,2,1,1,0", "256,256,4,2,2,1,1,0", "64,96,2,2,4,2,1,0", "256,224,4,2,2,1,1,0",
-                "32,64,1,2,3,4,1,0", "128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520"]
+                "32,64,1,2,3,4,1,0", "128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520",
+                "256,192,2,2,2,1,1,0"]   # the last: 4 waves of 128 x 96, accumulators in AGPRs
 
 
 @pytest.mark.parametrize("forced", UE8M0_FORCED)
