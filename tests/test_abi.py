@@ -80,3 +80,53 @@ def test_binding_marshalling_errors():
         pkg.dg_fp8_gemm_nt(A, torch.zeros(1, 4), A, torch.zeros(1, 1), None, torch.zeros(4, 4, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         pkg.dg_fp8_gemm_nt(A.float(), torch.zeros(1, 4), A, torch.zeros(1, 1), None, None)
+
+
+def test_fp4_and_ue8m0_validation():
+    v = ctypes.c_void_p
+    f = dg.lib.dg_fp8_fp4_gemm_nt
+    assert f(v(FAKE), v(FAKE), None, v(FAKE), None, v(FAKE), 64, 64, 128, None) == -1      # B NULL
+    assert f(v(FAKE), v(FAKE), v(FAKE + 8), v(FAKE), None, v(FAKE), 64, 64, 128, None) == -3   # B misaligned
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 96, None) == -2    # K % 128
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 0, 64, 128, None) == 0     # M = 0: no-op
+    g = dg.lib.dg_m_grouped_fp8_fp4_gemm_nt_masked
+    assert g(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), 64, 64, 128, 2, None) == -1
+    h = dg.lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0
+    assert h(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 100, 64, 128, 2, None) == -3
+
+
+def test_k_grouped_validation():
+    v = ctypes.c_void_p
+    f = dg.lib.dg_k_grouped_fp8_gemm_tn_contiguous
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), 64, 64, 128, 2, None) == -1   # ks NULL
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 128, 0, None) == -1  # G = 0
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE + 2), None, v(FAKE), 64, 64, 128, 2, None) == -3
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 192, 2, None) == -2  # K % 128
+    assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 0, 64, 128, 2, None) == 0    # M = 0
+
+
+def test_layout_and_bf16_validation():
+    v = ctypes.c_void_p
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        f = getattr(dg.lib, name)
+        assert f(None, v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 128, None) == -1
+        assert f(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 100, None) == -2
+    c = dg.lib.dg_m_grouped_fp8_gemm_nn_contiguous
+    assert c(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 100, 64, 128, 2, None) == -3
+    b = dg.lib.dg_bf16_gemm_nt
+    assert b(None, v(FAKE), None, v(FAKE), 64, 64, 64, None) == -1
+    assert b(v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 96, None) == -2          # K % 64
+    assert b(v(FAKE), v(FAKE + 4), None, v(FAKE), 64, 64, 64, None) == -3      # B misaligned
+    assert b(v(FAKE), v(FAKE), None, v(FAKE), 0, 64, 64, None) == 0           # M = 0: no-op
+    bc = dg.lib.dg_m_grouped_bf16_gemm_nt_contiguous
+    assert bc(v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 100, 64, 64, 2, None) == -3   # M % 128
+    assert bc(v(FAKE), v(FAKE), None, None, v(FAKE), 128, 64, 64, 2, None) == -1      # m_indices NULL
+    bm = dg.lib.dg_m_grouped_bf16_gemm_nt_masked
+    assert bm(v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 64, 64, 64, 0, None) == -1    # G = 0
+
+
+def test_describe_config_for_new_forms():
+    assert pkg.describe_config(0 | pkg.SCALE_FP8_FP4, 128, 24576, 1536, num_cus=256).endswith("_f8f4")
+    assert pkg.describe_config(pkg.KIND_K_GROUPED, 4096, 7168, 32768, 4, num_cus=256).startswith("k3_")
+    key = pkg.describe_config(pkg.KIND_BF16, 4096, 7168, 16384, num_cus=256)
+    assert key.endswith("_bf16") and "_K32768_" in key       # BF16 rows counted in bytes
