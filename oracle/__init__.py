@@ -74,6 +74,8 @@ def _declare(lib):
     lib.oracle_k_grouped_tn.restype = c.c_int
     lib.oracle_k_grouped_tn.argtypes = [p, p, p, p, p, p, c.c_int64, c.c_int, c.c_int, c.c_int,
                                         p, c.c_int64, p, p, c.c_int]
+    lib.oracle_fp4_fp4_gemm.restype = c.c_int
+    lib.oracle_fp4_fp4_gemm.argtypes = lib.oracle_fp8_fp4_gemm.argtypes
     lib.oracle_bf16_value.restype = c.c_double
     lib.oracle_bf16_value.argtypes = [c.c_uint16]
     lib.oracle_bf16_gemm.restype = c.c_int
@@ -285,6 +287,30 @@ class Oracle:
                                           _ptr(r), nr, _ptr(out), _ptr(comp), threads)
         if rc != 0:
             raise ValueError("oracle_k_grouped_tn: bad sizes")
+        return out, comp.astype(bool)
+
+    def fp4_fp4_gemm(self, kind: str, A, sfa, B, sfb, group_info=None, C=None, rows=None, threads=0):
+        """(D FP64 [rows, N], computed [rows]) of an FP4 x FP4 GEMM: A E2M1 pairs [M,K/2] (masked
+        [G,M_max,K/2]) with sfa int32 [M,K/128] (masked [G,M_max,K/128]), B and sfb as fp8_fp4_gemm."""
+        A = _c(A, np.uint8); B = _c(B, np.uint8)
+        sfa = _c(sfa, np.int32); sfb = _c(sfb, np.int32); C = _c(C, np.float32)
+        gi = _c(group_info, np.int32)
+        k = {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+        if kind == "masked":
+            G, M, K2 = A.shape
+        else:
+            M, K2 = A.shape
+            G = B.shape[0] if B.ndim == 3 else 1
+        K = 2 * K2
+        N = B.shape[-2]
+        r, nr = _rows(rows)
+        n_out = nr if r is not None else (G * M if kind == "masked" else M)
+        out = np.empty((n_out, N), dtype=np.float64)
+        comp = np.zeros(n_out, dtype=np.uint8)
+        rc = self.lib.oracle_fp4_fp4_gemm(k, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(gi), _ptr(C), M, N, K, G,
+                                          _ptr(r), nr, _ptr(out), _ptr(comp), threads)
+        if rc != 0:
+            raise ValueError("oracle_fp4_fp4_gemm: bad sizes")
         return out, comp.astype(bool)
 
     def fp8_gemm_nt(self, A, sfa, B, sfb, C=None, rows=None, threads=0):

@@ -269,6 +269,45 @@ static void compute_row_fp4(const row_job4 *j)
 }
 
 /* ------------------------------------------------------------------ */
+/* FP4 x FP4 row (DeepGEMM-Ascend hub page, precision table: FP4 x FP4 */
+/* for ultra-low-bit inference): A and B both E2M1, two codes a byte,  */
+/* each row with one UE8M0 scale per 1x32 block (the four of a K block */
+/* in one word, sfa [rows][K/128] like sfb [N][K/128]):                */
+/*   D[n] = C[n] + sum_kb sum_j 2^(ea-127) 2^(eb-127) S[n, kb, j],     */
+/*   S = sum over the 32 k of block j of e2m1(A[m,k]) * e2m1(B[n,k]).  */
+/* ------------------------------------------------------------------ */
+static double e2m1_nibble(const uint8_t *row, int k, const double *dec4)
+{
+    const uint8_t byte = row[k >> 1];
+    return dec4[(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)];
+}
+
+static void compute_row_fp4x4(const uint8_t *a_row, const int32_t *sa_row, const uint8_t *b, const int32_t *sfb,
+                              const float *c_row, int N, int K, double *out)
+{
+    double dec4[16];
+    for (int c = 0; c < 16; ++c) dec4[c] = oracle_e2m1_value((uint8_t)c);
+    const int Kb = K / ORACLE_KBLOCK;
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *b_row = b + (int64_t)n * (K / 2);
+        double total = 0.0;
+        for (int kb = 0; kb < Kb; ++kb) {
+            for (int j = 0; j < 4; ++j) {
+                double blk = 0.0;
+                for (int t = 0; t < 32; ++t) {
+                    const int k = kb * ORACLE_KBLOCK + 32 * j + t;
+                    blk += e2m1_nibble(a_row, k, dec4) * e2m1_nibble(b_row, k, dec4);
+                }
+                const double sa = oracle_ue8m0_value(ue8m0_byte(sa_row[kb], j));
+                const double sb = oracle_ue8m0_value(ue8m0_byte(sfb[(int64_t)n * Kb + kb], j));
+                total += sa * sb * blk;
+            }
+        }
+        out[n] = total + (c_row ? (double)c_row[n] : 0.0);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Row scheduling over threads.                                        */
 /* ------------------------------------------------------------------ */
 enum { KIND_DENSE = 0, KIND_CONTIG = 1, KIND_MASKED = 2, KIND_KGROUP = 3 };
@@ -380,7 +419,17 @@ static void do_row(const problem *p, int64_t i)
         j.sfb = p->sfb + g * Nb * (int64_t)Kb;
         j.c_row = p->C ? p->C + r * p->N : NULL;
     }
-    if (p->fp4) {
+    if (p->fp4 == 2) {
+        /* FP4 x FP4: A rows are K/2 bytes with a word of scales per K block */
+        const int32_t *sfa44 = (const int32_t *)p->sfa;
+        const int32_t *sfb44 = (const int32_t *)p->sfb;
+        int64_t g44 = 0;
+        if (p->kind == KIND_CONTIG) g44 = p->group_info[r];
+        if (p->kind == KIND_MASKED) g44 = r / p->M;
+        compute_row_fp4x4(p->A + r * (int64_t)(p->K / 2), sfa44 + r * (int64_t)Kb,
+                          p->B + g44 * (int64_t)p->N * (p->K / 2), sfb44 + g44 * (int64_t)p->N * Kb, j.c_row,
+                          p->N, p->K, out);
+    } else if (p->fp4) {
         /* same row selection; scales and B reinterpreted for FP8 x FP4 */
         const int W = (Kb + 3) / 4;
         row_job4 j4;
@@ -679,4 +728,25 @@ int oracle_bf16_gemm(int kind, const uint16_t *A, const uint16_t *B, const int32
     for (int t = 0; t < n_threads; ++t)
         if (started[t]) pthread_join(tid[t], NULL);
     return 0;
+}
+
+/*
+ * FP4 x FP4 (all three forms; kind 0 dense, 1 contiguous, 2 masked):
+ *   A [rows][K/2] E2M1 pairs (masked [G][M_max][K/2]), sfa [rows][K/128] words
+ *   (masked [G][M_max][K/128]); B and sfb as for FP8 x FP4; C, group_info and
+ *   rows as for the other forms.
+ */
+int oracle_fp4_fp4_gemm(int kind, const uint8_t *A, const int32_t *sfa, const uint8_t *B, const int32_t *sfb,
+                        const int32_t *group_info, const float *C, int64_t M, int N, int K, int G,
+                        const int64_t *rows, int64_t n_rows, double *out, uint8_t *computed, int n_threads)
+{
+    problem p;
+    memset(&p, 0, sizeof(p));
+    if (kind < 0 || kind > 2 || G <= 0) return -1;
+    p.kind = kind; p.A = A; p.sfa = (const float *)sfa; p.B = B; p.sfb = (const float *)sfb; p.C = C;
+    p.group_info = group_info; p.M = M; p.N = N; p.K = K; p.G = G; p.fp4 = 2;
+    p.rows = rows;
+    p.n_rows = rows ? n_rows : (kind == KIND_MASKED ? (int64_t)G * M : M);
+    p.out = out; p.computed = computed;
+    return run(&p, n_threads);
 }

@@ -145,6 +145,7 @@ class Problem:
     ue8m0: bool = False             # sfa/sfb are packed UE8M0 int32 words
     fp4: bool = False               # B holds E2M1 pairs [.., N, K/2], sfb [.., N, K/128] words (1x32 blocks)
     bf16: bool = False              # A and B are torch.bfloat16, no scales (sfa, sfb None)
+    fp4a: bool = False              # A also E2M1 pairs [.., M, K/2] with sfa [.., M, K/128] words (FP4 x FP4)
 
     @property
     def M(self):
@@ -173,22 +174,28 @@ def _quant_b(b, ue8m0, fp4):
     return quantize_fp4_1x32(b) if fp4 else quantize_128x128(b, ue8m0)
 
 
-def make_dense(M, N, K, seed, with_c=False, ue8m0=False, fp4=False) -> Problem:
-    """fp4: FP8 x FP4 (B as E2M1 with 1x32 UE8M0 scales; A with UE8M0 scales)."""
+def _quant_a(a, ue8m0, fp4x4):
+    return quantize_fp4_1x32(a) if fp4x4 else quantize_1x128(a, ue8m0)
+
+
+def make_dense(M, N, K, seed, with_c=False, ue8m0=False, fp4=False, fp4x4=False) -> Problem:
+    """fp4: FP8 x FP4 (B as E2M1 with 1x32 UE8M0 scales; A with UE8M0 scales);
+    fp4x4: FP4 x FP4 (A as E2M1 with 1x32 UE8M0 scales per row, like B)."""
+    fp4 = fp4 or fp4x4
     ue8m0 = ue8m0 or fp4
     g = _gen(seed)
     a = torch.randn(M, K, generator=g, dtype=torch.float32)
     b = torch.randn(N, K, generator=g, dtype=torch.float32)
     c = torch.randn(M, N, generator=g, dtype=torch.float32) if with_c else None
-    A, sfa = quantize_1x128(a, ue8m0)
+    A, sfa = _quant_a(a, ue8m0, fp4x4)
     del a
     B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed, ue8m0=ue8m0, fp4=fp4)
+    return Problem("dense", A, sfa, B, sfb, C=c, seed=seed, ue8m0=ue8m0, fp4=fp4, fp4a=fp4x4)
 
 
 def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=128, ue8m0=False,
-                    fp4=False) -> Problem:
+                    fp4=False, fp4x4=False) -> Problem:
     """Experts' tokens concatenated along M, each segment padded to ``align`` rows.
 
     group_rows[g] valid rows for expert g; padding rows get index -1.  With
@@ -206,15 +213,17 @@ def make_contiguous(group_rows, N, K, seed, with_c=False, pad_rows=None, align=1
     for e, (r, s) in enumerate(zip(group_rows, seg)):
         idx[off:off + r] = e
         off += s
+    fp4 = fp4 or fp4x4
     ue8m0 = ue8m0 or fp4
-    A, sfa = quantize_1x128(a, ue8m0)
+    A, sfa = _quant_a(a, ue8m0, fp4x4)
     del a
     B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed, ue8m0=ue8m0, fp4=fp4)
+    return Problem("contiguous", A, sfa, B, sfb, C=c, m_indices=idx, seed=seed, ue8m0=ue8m0, fp4=fp4, fp4a=fp4x4)
 
 
-def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, fp4=False) -> Problem:
+def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, fp4=False,
+                fp4x4=False) -> Problem:
     g = _gen(seed)
     a = torch.randn(G, M_max, K, generator=g, dtype=torch.float32)
     b = torch.randn(G, N, K, generator=g, dtype=torch.float32)
@@ -223,12 +232,13 @@ def make_masked(G, M_max, N, K, seed, with_c=False, masked_m=None, ue8m0=False, 
         mm = torch.randint(0, M_max + 1, (G,), generator=g, dtype=torch.int32)
     else:
         mm = torch.as_tensor(masked_m, dtype=torch.int32)
+    fp4 = fp4 or fp4x4
     ue8m0 = ue8m0 or fp4
-    A, sfa = quantize_1x128(a, ue8m0)
+    A, sfa = _quant_a(a, ue8m0, fp4x4)
     del a
     B, sfb = _quant_b(b, ue8m0, fp4)
     del b
-    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0, fp4=fp4)
+    return Problem("masked", A, sfa, B, sfb, C=c, masked_m=mm, seed=seed, ue8m0=ue8m0, fp4=fp4, fp4a=fp4x4)
 
 
 # ---------------------------------------------------------------- BF16 x BF16 (unscaled)
@@ -350,14 +360,15 @@ def workload_seed(cfg) -> int:
     return 1000 + (1 if cfg == "1c" else int(cfg))
 
 
-def make_workload(cfg, ue8m0=False, fp4=False) -> Problem:
+def make_workload(cfg, ue8m0=False, fp4=False, fp4x4=False) -> Problem:
     c = WORKLOADS[cfg]
     seed = workload_seed(cfg)
+    kw = dict(ue8m0=ue8m0, fp4=fp4, fp4x4=fp4x4)
     if c["kind"] == "dense":
-        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False), ue8m0=ue8m0, fp4=fp4)
+        return make_dense(c["M"], c["N"], c["K"], seed, with_c=c.get("with_c", False), **kw)
     if c["kind"] == "contiguous":
-        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed, ue8m0=ue8m0, fp4=fp4)
-    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed, ue8m0=ue8m0, fp4=fp4)
+        return make_contiguous([c["rows_per_group"]] * c["G"], c["N"], c["K"], seed, **kw)
+    return make_masked(c["G"], c["M_max"], c["N"], c["K"], seed, **kw)
 
 
 # ---------------------------------------------------------------- structured inputs for pins

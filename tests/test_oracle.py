@@ -615,3 +615,51 @@ def test_bf16_grouped_equal_dense(oracle):
         ref, _ = oracle.bf16_gemm("dense", d["A"][g], d["B"][g])
         valid = comp.reshape(3, 20)[g]
         assert np.array_equal(got.reshape(3, 20, 40)[g][valid], ref[valid])
+
+
+# ------------------------------------------------------------------ FP4 x FP4
+def _e2m1_decode_np(packed):
+    """[..., K/2] bytes -> [..., K] values from the golden E2M1 table (element 2i: low nibble)."""
+    table = _e2m1_golden()
+    vals = np.array([table[c] for c in range(16)])
+    lo, hi = packed & 0x0F, packed >> 4
+    return vals[np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], -1)]
+
+
+def _per32_scales(words, K):
+    """[..., K/128] int32 words -> [..., K] FP64 scales 2^(e-127), byte j of word kb for K 128kb+32j.."""
+    w = words.astype(np.int64) & 0xFFFFFFFF
+    e = np.stack([(w >> (8 * j)) & 0xFF for j in range(4)], axis=-1).reshape(*words.shape[:-1], -1)
+    return np.repeat(np.ldexp(1.0, e - 127), 32, axis=-1)[..., :K]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5, 128), (17, 130, 384), (129, 3, 256)])
+def test_fp4_fp4_vs_numpy_dequant_matmul(oracle, M, N, K):
+    p = gen.make_dense(M, N, K, seed=M * 7 + N + K, with_c=True, fp4x4=True)
+    A = _e2m1_decode_np(p.A.numpy()) * _per32_scales(p.sfa.numpy(), K)
+    B = _e2m1_decode_np(p.B.numpy()) * _per32_scales(p.sfb.numpy(), K)
+    ref = A @ B.T + p.C.numpy().astype(np.float64)
+    got, comp = oracle.fp4_fp4_gemm("dense", p.A.numpy(), p.sfa.numpy(), p.B.numpy(), p.sfb.numpy(),
+                                    C=p.C.numpy())
+    assert comp.all()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-9)
+
+
+def test_fp4_fp4_operand_swap_and_grouped(oracle):
+    p = gen.make_dense(40, 72, 256, seed=97, fp4x4=True)
+    d, _ = oracle.fp4_fp4_gemm("dense", p.A, p.sfa, p.B, p.sfb)
+    e, _ = oracle.fp4_fp4_gemm("dense", p.B, p.sfb, p.A, p.sfa)
+    assert np.array_equal(d, e.T)
+    pm = gen.make_masked(3, 64, 48, 256, seed=98, masked_m=[64, 0, 9], fp4x4=True)
+    got, comp = oracle.fp4_fp4_gemm("masked", pm.A, pm.sfa, pm.B, pm.sfb, pm.masked_m)
+    assert comp.reshape(3, 64).sum(1).tolist() == [64, 0, 9]
+    for g in range(3):
+        ref, _ = oracle.fp4_fp4_gemm("dense", pm.A[g], pm.sfa[g], pm.B[g], pm.sfb[g])
+        valid = comp.reshape(3, 64)[g]
+        assert np.array_equal(got.reshape(3, 64, 48)[g][valid], ref[valid])
+    pc = gen.make_contiguous([128, 60], 48, 256, seed=99, fp4x4=True)
+    got, comp = oracle.fp4_fp4_gemm("contiguous", pc.A, pc.sfa, pc.B, pc.sfb, pc.m_indices)
+    for m in np.flatnonzero(comp):
+        g = int(pc.m_indices[m])
+        ref, _ = oracle.fp4_fp4_gemm("dense", pc.A[m:m + 1], pc.sfa[m:m + 1], pc.B[g], pc.sfb[g])
+        assert np.array_equal(got[m], ref[0])

@@ -59,6 +59,13 @@ MUTANTS = [
     ("bf16_drop_last_k", "            for (int k = 0; k < p->K; ++k)\n                acc += a[k]",
      "            for (int k = 0; k < p->K - 1; ++k)\n                acc += a[k]"),
     ("bf16_lost_sign", "return s ? 0.0 - mag : mag;", "return mag;"),
+    ("fp4x4_nibbles_swapped", "return dec4[(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)];",
+     "return dec4[(k % 2 == 0) ? (byte >> 4) : (byte & 0x0F)];"),
+    ("fp4x4_a_scale_block_64", "const double sa = oracle_ue8m0_value(ue8m0_byte(sa_row[kb], j));",
+     "const double sa = oracle_ue8m0_value(ue8m0_byte(sa_row[kb], j / 2));"),
+    ("fp4x4_a_scale_ignored", "                total += sa * sb * blk;", "                total += sb * blk;"),
+    ("fp4x4_last_block_dropped", "for (int j = 0; j < 4; ++j) {\n                double blk = 0.0;",
+     "for (int j = 0; j < 3; ++j) {\n                double blk = 0.0;"),
     ("bf16_c_ignored", "out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);", "out[n] = acc;"),
     ("bf16_masked_group0", "        const uint16_t *b = p->B + g * (int64_t)p->N * p->K;",
      "        const uint16_t *b = p->B;"),
@@ -89,6 +96,8 @@ def _pin_calls(o):
     calls.append(lambda: pins.test_bf16_decode_matches_torch_for_every_code(o))
     calls.append(lambda: pins.test_bf16_gemm_vs_numpy(o, 37, 129, 200))
     calls.append(lambda: pins.test_bf16_grouped_equal_dense(o))
+    calls.append(lambda: pins.test_fp4_fp4_vs_numpy_dequant_matmul(o, 17, 130, 384))
+    calls.append(lambda: pins.test_fp4_fp4_operand_swap_and_grouped(o))
     return calls
 
 
