@@ -291,7 +291,7 @@ static void compute_row_fp4x4(const uint8_t *a_row, const int32_t *sa_row, const
     for (int n = 0; n < N; ++n) {
         const uint8_t *b_row = b + (int64_t)n * (K / 2);
         double total = 0.0;
-        for (int kb = 0; kb < Kb; ++kb) {
+        for (int kb = 0; Kb > kb; ++kb) {
             for (int j = 0; j < 4; ++j) {
                 double blk = 0.0;
                 for (int t = 0; t < 32; ++t) {

@@ -59,8 +59,10 @@ MUTANTS = [
     ("bf16_drop_last_k", "            for (int k = 0; k < p->K; ++k)\n                acc += a[k]",
      "            for (int k = 0; k < p->K - 1; ++k)\n                acc += a[k]"),
     ("bf16_lost_sign", "return s ? 0.0 - mag : mag;", "return mag;"),
-    ("fp4x4_nibbles_swapped", "return dec4[(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)];",
-     "return dec4[(k % 2 == 0) ? (byte >> 4) : (byte & 0x0F)];"),
+    # (swapping the nibble order of both operands at once leaves every block sum unchanged;
+    # swapping it for A alone is a real mistake)
+    ("fp4x4_a_nibbles_swapped", "blk += e2m1_nibble(a_row, k, dec4) * e2m1_nibble(b_row, k, dec4);",
+     "blk += e2m1_nibble(a_row, k ^ 1, dec4) * e2m1_nibble(b_row, k, dec4);"),
     ("fp4x4_a_scale_block_64", "const double sa = oracle_ue8m0_value(ue8m0_byte(sa_row[kb], j));",
      "const double sa = oracle_ue8m0_value(ue8m0_byte(sa_row[kb], j / 2));"),
     ("fp4x4_a_scale_ignored", "                total += sa * sb * blk;", "                total += sb * blk;"),
