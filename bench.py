@@ -34,6 +34,7 @@ METRIC = "TFLOPS + HBM GB/s per shape (FP8 block-scaled GEMM), % of roofline"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0    # also the peak used for FP8 x FP4: each MFMA there has an FP8 operand
 PEAK_BF16_TFLOPS = 2500.0   # dense BF16 MFMA peak (the unscaled BF16 GEMM)
+PEAK_FP4_TFLOPS = 10100.0   # dense FP4 MFMA peak (FP4 x FP4)
 RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 # The pages' H800 numbers for the same shapes (DeepGEMM launch article,
 # section 3 dense table): other hardware, context only.
@@ -89,7 +90,10 @@ def algorithmic(p) -> tuple[float, float, int]:
         groups_used = int((mm > 0).sum())
     flops = 2.0 * rows * N * K
     b_row = K // 2 if p.fp4 else K  # E2M1 B: two codes per byte
-    nbytes = rows * K + groups_used * N * b_row + rows * N * 2
+    a_row = K // 2 if p.fp4a else K
+    if p.fp4a:
+        Kb = K // 128               # FP4 A: one word (four 1x32 scales) per row and K block
+    nbytes = rows * a_row + groups_used * N * b_row + rows * N * 2
     if p.C is not None:
         nbytes += rows * N * 4
     nbytes += rows * Kb * 4 + groups_used * Nb * Kb_b * 4
@@ -101,7 +105,7 @@ def kind_id(kind: str) -> int:
 
 
 def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = False, fp4: bool = False,
-                   bf16: bool = False):
+                   bf16: bool = False, fp4x4: bool = False):
     import torch
 
     import moe_grouped_gemm_scales_amd as dg
@@ -116,7 +120,7 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
         p = gen.make_bf16("dense", seed=gen.workload_seed(cfg), M=c["M"], N=c["N"], K=c["K"],
                           with_c=c.get("with_c", False))
     else:
-        p = gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4)
+        p = gen.make_workload(cfg, ue8m0=ue8m0, fp4=fp4, fp4x4=fp4x4)
     flops, nbytes, rows = algorithmic(p)
     oshape = (p.G, p.M, p.N) if p.kind == "k_grouped" else out_shape(p)
     ws = sum(t.numel() * t.element_size() for t in (p.A, p.sfa, p.B, p.sfb, p.C) if t is not None)
@@ -135,6 +139,15 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
             dg.dg_k_grouped_fp8_gemm_tn_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["ks"], d["C"], D)
         elif bf16:
             dg.dg_bf16_gemm_nt(d["A"], d["B"], d["C"], D)
+        elif fp4x4:
+            if p.kind == "dense":
+                dg.dg_fp4_fp4_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
+            elif p.kind == "contiguous":
+                dg.dg_m_grouped_fp4_fp4_gemm_nt_contiguous(d["A"], d["sfa"], d["B"], d["sfb"], d["m_indices"],
+                                                           d["C"], D)
+            else:
+                dg.dg_m_grouped_fp4_fp4_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"],
+                                                       D)
         elif fp4:
             if p.kind == "dense":
                 dg.dg_fp8_fp4_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D)
@@ -152,7 +165,8 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
             dg.dg_m_grouped_fp8_gemm_nt_masked(d["A"], d["sfa"], d["B"], d["sfb"], d["masked_m"], d["C"], D)
 
     rows_arg = p.A.shape[1] if p.kind == "masked" else p.M
-    flag = dg.KIND_BF16 if bf16 else dg.SCALE_FP8_FP4 if fp4 else (dg.SCALE_UE8M0 if ue8m0 else 0)
+    flag = dg.KIND_BF16 if bf16 else dg.SCALE_FP4_FP4 if fp4x4 else dg.SCALE_FP8_FP4 if fp4 else \
+        (dg.SCALE_UE8M0 if ue8m0 else 0)
     kernel = dg.describe_config(kind_id(p.kind) | flag, rows_arg, p.N, p.K, p.G,
                                 p.C is not None)
     # everything runs on one non-default stream (HIP graphs cannot capture the null stream)
@@ -195,7 +209,7 @@ def bench_workload(cfg, steps: int, warmup: int, graph: bool, ue8m0: bool = Fals
     kernel_ms = start.elapsed_time(end) / n_launch
     ms_per_step = wall * 1e3 / n_launch
     t_kernel = kernel_ms * 1e-3
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP8_TFLOPS
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP4_TFLOPS if fp4x4 else PEAK_FP8_TFLOPS
     ai = flops / nbytes
     bound = "mfma" if ai >= peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     tflops = flops / t_kernel / 1e12
@@ -271,6 +285,8 @@ def main():
                     help="time the chosen workload with packed UE8M0 scales instead of FP32 ones")
     ap.add_argument("--fp4", action="store_true",
                     help="time the chosen workload as FP8 x FP4 (E2M1 B with 1x32 UE8M0 scales)")
+    ap.add_argument("--fp4x4", action="store_true",
+                    help="time the chosen workload as FP4 x FP4 (E2M1 A and B, 1x32 UE8M0 scales)")
     ap.add_argument("--bf16", action="store_true",
                     help="time the chosen dense workload as an unscaled BF16 GEMM")
     ap.add_argument("--eager", action="store_true",
@@ -308,13 +324,14 @@ def main():
     per_shape = []
     if args.all:
         modes = [(c, "") for c in [0, 1, "1c", 2, 3, 4]] + [(c, "_ue8m0") for c in [0, 1, 2, 3, 4]] + \
-            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]] + [("kg", ""), (2, "_bf16")]
+            [(c, "_fp4") for c in [0, 1, "1c", 2, 3, 4]] + [("kg", ""), (2, "_bf16")] + \
+            [(c, "_fp4x4") for c in [1, 2, 4]]
         for c, mode in modes:
             steps = args.steps if c in (0, 1, "1c", 4) else max(10, args.steps // 10)
             if c == "kg":
                 steps = max(5, args.steps // 20)
             r = bench_workload(c, steps, min(args.warmup, steps), not args.eager, ue8m0=mode == "_ue8m0",
-                               fp4=mode == "_fp4", bf16=mode == "_bf16")
+                               fp4=mode == "_fp4", bf16=mode == "_bf16", fp4x4=mode == "_fp4x4")
             wl = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[c] + mode
             line = dict(workload=wl, kernel=r["kernel"], kernel_us=round(r["kernel_ms"] * 1e3, 3),
                         tflops=round(r["tflops"], 2), hbm_gbs=round(r["gbs"], 1), bound=r["bound"],
@@ -325,19 +342,21 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4, bf16=args.bf16)
+    r = bench_workload(cfg, args.steps, args.warmup, not args.eager, ue8m0=args.ue8m0, fp4=args.fp4, bf16=args.bf16,
+                       fp4x4=args.fp4x4)
     p = r["problem"]
     name = {**gen.WORKLOAD_NAMES, **gen.WORKLOAD_NAMES_EXTRA}[cfg] + \
-        ("_fp4" if args.fp4 else "_ue8m0" if args.ue8m0 else "_bf16" if args.bf16 else "")
+        ("_fp4" if args.fp4 else "_fp4x4" if args.fp4x4 else "_ue8m0" if args.ue8m0 else "_bf16" if args.bf16 else "")
     roof = dict(bound=r["bound"],
                 achieved=round(r["tflops"] if r["bound"] == "mfma" else r["gbs"], 3),
                 peak=r["peak"] if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
                 traffic=traffic_for(name))
-    cpu = None if (args.no_cpu_baseline or args.ue8m0 or args.fp4 or args.bf16 or cfg == "kg") else cpu_baseline(cfg)
+    alt = args.ue8m0 or args.fp4 or args.bf16 or args.fp4x4
+    cpu = None if (args.no_cpu_baseline or alt or cfg == "kg") else cpu_baseline(cfg)
     value = r["step_tflops"]
-    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not (args.ue8m0 or args.fp4 or args.bf16) else None
+    pages = PAGES_TFLOPS.get(cfg) if isinstance(cfg, int) and not alt else None
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -349,7 +368,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / pages, 4) if pages else None,
-        "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "bf16" if args.bf16 else "fp8_e4m3",
+        "dtype": "fp8_e4m3 x fp4_e2m1" if args.fp4 else "fp4_e2m1" if args.fp4x4 else "bf16" if args.bf16 else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": name, "kind": p.kind, "M": p.M if p.kind == "k_grouped" else p.A.shape[-2], "N": p.N, "K": p.K, "groups": p.G,
                    "with_c": p.C is not None, "kernel": r["kernel"], "input_copies": r["copies"],

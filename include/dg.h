@@ -235,6 +235,29 @@ dg_status dg_m_grouped_bf16_gemm_nt_masked(const void *A, const void *B, const i
                                            const float *C, void *D, int M_max, int N, int K,
                                            int num_groups, void *stream);
 
+/*
+ * FP4 x FP4 (DeepGEMM-Ascend hub page, precision table "FP4 x FP4" for
+ * ultra-low-bit inference; the page names no call, so the layout is a
+ * reading): A as well as B in OCP E2M1 (two codes a byte, element 2i in the
+ * low nibble of byte i), each row of each operand with one UE8M0 scale per
+ * 1x32 block, the four of a 128-wide K block in one word (byte j: K elements
+ * 128 kb + 32 j .. + 31):
+ *   A uint8 [M][K/2] (masked [G][M_max][K/2]), sfa int32 [M][K/128]
+ *     (masked [G][M_max][K/128]); B and sfb as for FP8 x FP4.
+ *   D = C + sum over 32-wide K blocks of 2^(ea-127) 2^(eb-127) S_j, rounded
+ *   once to BF16.  C, D, groups, masks, ownership and errors as above.
+ */
+dg_status dg_fp4_fp4_gemm_nt(const void *A, const int32_t *sfa, const void *B, const int32_t *sfb,
+                             const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_m_grouped_fp4_fp4_gemm_nt_contiguous(const void *A, const int32_t *sfa, const void *B,
+                                                  const int32_t *sfb, const int32_t *m_indices,
+                                                  const float *C, void *D, int M, int N, int K,
+                                                  int num_groups, void *stream);
+dg_status dg_m_grouped_fp4_fp4_gemm_nt_masked(const void *A, const int32_t *sfa, const void *B,
+                                              const int32_t *sfb, const int32_t *masked_m,
+                                              const float *C, void *D, int M_max, int N, int K,
+                                              int num_groups, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);
 
@@ -264,6 +287,7 @@ dg_status dg_init(void);
 #define DG_SCALE_UE8M0 4
 #define DG_SCALE_FP8_FP4 8
 #define DG_BF16 16           /* BF16 x BF16 without scales (K in elements) */
+#define DG_SCALE_FP4_FP4 32  /* FP4 x FP4 */
 
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these

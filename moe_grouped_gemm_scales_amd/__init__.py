@@ -1,5 +1,5 @@
 """MI355X (gfx950) block-scaled FP8 GEMM: D = C + A.B^T in dense, M-grouped
-contiguous and M-grouped masked forms (FP32 or UE8M0 scales, and FP8 x FP4),
+contiguous and M-grouped masked forms (FP32 or UE8M0 scales, FP8 x FP4 and FP4 x FP4),
 the NN/TN/TT storage layouts, the K-grouped TN form and an unscaled BF16 GEMM,
 as a C-ABI library (libdg.so) with a thin Python binding.  See include/dg.h
 for the contract."""
@@ -15,4 +15,6 @@ from .dg import (DGError, describe_config, dg_fp8_gemm_nt, dg_m_grouped_fp8_gemm
                  dg_m_grouped_fp8_gemm_nn_contiguous, fp8_gemm_nn, fp8_gemm_tn, fp8_gemm_tt,
                  m_grouped_fp8_gemm_nn_contiguous, KIND_BF16, dg_bf16_gemm_nt,
                  dg_m_grouped_bf16_gemm_nt_contiguous, dg_m_grouped_bf16_gemm_nt_masked, bf16_gemm_nt,
-                 m_grouped_bf16_gemm_nt_contiguous, m_grouped_bf16_gemm_nt_masked)
+                 m_grouped_bf16_gemm_nt_contiguous, m_grouped_bf16_gemm_nt_masked, SCALE_FP4_FP4,
+                 dg_fp4_fp4_gemm_nt, dg_m_grouped_fp4_fp4_gemm_nt_contiguous, dg_m_grouped_fp4_fp4_gemm_nt_masked,
+                 fp4_fp4_gemm_nt, m_grouped_fp4_fp4_gemm_nt_contiguous, m_grouped_fp4_fp4_gemm_nt_masked)

@@ -413,8 +413,9 @@ dg_status dg_init(void) {
 
 // Scale format encoded in `kind` by the DG_SCALE_* flags
 int scale_format(int* kind) {
-    const int sf = (*kind & DG_BF16) ? 3 : (*kind & DG_SCALE_FP8_FP4) ? 2 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
-    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4 | DG_BF16);
+    const int sf = (*kind & DG_SCALE_FP4_FP4) ? 4 : (*kind & DG_BF16) ? 3 : (*kind & DG_SCALE_FP8_FP4) ? 2
+                 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
+    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4 | DG_BF16 | DG_SCALE_FP4_FP4);
     return sf;
 }
 
@@ -552,6 +553,23 @@ dg_status dg_m_grouped_bf16_gemm_nt_contiguous(const void* A, const void* B, con
 dg_status dg_m_grouped_bf16_gemm_nt_masked(const void* A, const void* B, const int32_t* masked_m, const float* C,
                                            void* D, int M_max, int N, int K, int num_groups, void* stream) {
     return bf16_gemm(kMasked, A, B, masked_m, C, D, M_max, N, K, num_groups, stream);
+}
+
+dg_status dg_fp4_fp4_gemm_nt(const void* A, const int32_t* sfa, const void* B, const int32_t* sfb, const float* C,
+                             void* D, int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 4, stream);
+}
+
+dg_status dg_m_grouped_fp4_fp4_gemm_nt_contiguous(const void* A, const int32_t* sfa, const void* B,
+                                                  const int32_t* sfb, const int32_t* m_indices, const float* C,
+                                                  void* D, int M, int N, int K, int num_groups, void* stream) {
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 4, stream);
+}
+
+dg_status dg_m_grouped_fp4_fp4_gemm_nt_masked(const void* A, const int32_t* sfa, const void* B,
+                                              const int32_t* sfb, const int32_t* masked_m, const float* C, void* D,
+                                              int M_max, int N, int K, int num_groups, void* stream) {
+    return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 4, stream);
 }
 
 }  // extern "C"

@@ -29,7 +29,8 @@ struct KernelConfig {
     int has_c = 0;
     int n = 0, k = 0, g = 1;
     int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0),
-                               // 3 BF16 x BF16 without scales (k is then the row length in bytes)
+                               // 3 BF16 x BF16 without scales (k is then the row length in bytes),
+                               // 4 FP4 x FP4 (E2M1 A and B, 1x32 UE8M0 per row)
     int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
                                // launch two column ranges with different tile widths
 
@@ -41,6 +42,7 @@ struct KernelConfig {
         if (variant == 1) return bm * 128 + (bm + 63) / 64 * 256 + 256;
         if (sf == 2) return bm * 128 + bn * 64 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
         if (sf == 3) return (bm + bn) * 128;   // BF16: no scales
+        if (sf == 4) return (bm + bn) * 64 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;   // FP4 x FP4
         if (kind == kKGrouped) return (bm + bn) * 128 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }

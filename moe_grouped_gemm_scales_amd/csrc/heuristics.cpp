@@ -85,7 +85,8 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
     const double t_compute = (compute_cyc + stage_cyc) / kClockHz;
     // operand tiles mostly come from L2/MALL (they are shared between tiles);
     // the HBM bound of the whole launch is applied below
-    const double t_load = (c.bm + (c.sf == 2 ? 0.5 : 1.0) * c.bn) * kspan / (kCuLoadBytesPerS / occ);
+    const double t_load = ((c.sf == 4 ? 0.5 : 1.0) * c.bm + (c.sf == 2 || c.sf == 4 ? 0.5 : 1.0) * c.bn) * kspan /
+                          (kCuLoadBytesPerS / occ);
     // pipeline fill, epilogue and scheduling per tile; split-K adds a round trip
     double t_fixed = 1.2e-6 + (c.splitk > 1 ? 1.0e-6 * c.splitk + c.bm * c.bn * 8.0 * c.splitk / kCuLoadBytesPerS : 0.0);
     double t = waves * (std::max(t_compute, t_load) + t_fixed);
@@ -97,7 +98,7 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
     const double rows_per_group = valid_rows / groups_b;
     const double b_reads = rows_per_group <= 512 ? std::ceil(rows_per_group / c.bm)
                                                  : std::max(1.0, std::ceil(rows_per_group / c.bm) / 8.0);
-    const double b_row_bytes = p.sf == 2 ? p.k / 2.0 : (double)p.k;
+    const double b_row_bytes = (p.sf == 2 || p.sf == 4) ? p.k / 2.0 : (double)p.k;
     const double bytes = valid_rows * p.k + b_reads * groups_b * p.n * b_row_bytes +
                          valid_rows * p.n * (2.0 + 4.0 * p.has_c);
     t = std::max(t, bytes / kHbmBytesPerS);
@@ -107,9 +108,9 @@ double estimate(const Problem& p, const KernelConfig& c, int num_cus, double val
 int dma_per_wave(const KernelConfig& c) {
     const int nw = c.wm * c.wn;
     const int rpi = 8 / c.kstep;
-    const int na = c.bm / rpi, nb = c.sf == 2 ? c.bn / 16 : c.bn / rpi;
+    const int na = c.sf == 4 ? c.bm / 16 : c.bm / rpi, nb = (c.sf == 2 || c.sf == 4) ? c.bn / 16 : c.bn / rpi;
     const int ns = c.sf == 3 ? 0 : (c.bm + 63) / 64 * c.kstep;
-    const int nt = c.sf == 3 ? 0 : (c.sf == 2 || c.kind == kKGrouped) ? (c.bn + 63) / 64 : c.kstep;
+    const int nt = c.sf == 3 ? 0 : (c.sf == 2 || c.sf == 4 || c.kind == kKGrouped) ? (c.bn + 63) / 64 : c.kstep;
     return (na + nw - 1) / nw + (nb + nw - 1) / nw + (ns + nw - 1) / nw + (nt + nw - 1) / nw;
 }
 
@@ -210,9 +211,10 @@ const Tuned kTunedBF16[] = {
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {
     std::vector<KernelConfig> out;
     if (num_cus != 256) return out;       // measured on the full 256-CU part
-    const Tuned* first = p.sf == 3 ? std::begin(kTunedBF16) : p.sf == 2 ? std::begin(kTunedF4)
+    // FP4 x FP4 starts from the FP8 x FP4 table (same structure, A half the bytes)
+    const Tuned* first = p.sf == 3 ? std::begin(kTunedBF16) : (p.sf == 2 || p.sf == 4) ? std::begin(kTunedF4)
                        : p.sf ? std::begin(kTunedE8) : std::begin(kTuned);
-    const Tuned* last = p.sf == 3 ? std::end(kTunedBF16) : p.sf == 2 ? std::end(kTunedF4)
+    const Tuned* last = p.sf == 3 ? std::end(kTunedBF16) : (p.sf == 2 || p.sf == 4) ? std::end(kTunedF4)
                       : p.sf ? std::end(kTunedE8) : std::end(kTuned);
     for (const Tuned* it = first; it != last; ++it) {
         const Tuned& t = *it;

@@ -185,6 +185,7 @@ std::string KernelConfig::key() const {
     if (sf == 1) s << "_e8m0";
     if (sf == 2) s << "_f8f4";
     if (sf == 3) s << "_bf16";
+    if (sf == 4) s << "_f4f4";
     if (ne > 0) s << "_cols" << nb << "-" << ne;
     return s.str();
 }

@@ -79,6 +79,9 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 // DeepGEMM README intro: GEMM in FP8, FP4 and BF16): A [rows][K], B [N][K]
 // BF16, D = C + A . B^T.  DG_K is then the row length in BYTES (2 x K), so a
 // 128-byte "K block" is 64 BF16 elements, two v_mfma_f32_16x16x32_bf16.
+// 4 = FP4 x FP4 (DeepGEMM-Ascend hub page, precision table): A as well as B
+// in E2M1, [rows][K/2], each row with one UE8M0 scale per 1x32 block, sfa
+// [rows][K/128] words (masked [G][M_max][K/128]) laid out like sfb of 2.
 #ifndef DG_SF
 #define DG_SF 0
 #endif
@@ -110,12 +113,14 @@ constexpr int NBLKS = (N + KBLK - 1) / KBLK;
 constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D; N is the row pitch
 static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
 constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
-constexpr bool SF_E8 = DG_SF == 1 || DG_SF == 2;
-constexpr bool FP4B = DG_SF == 2;             // B in E2M1 with per-row 1x32 UE8M0 scales
+constexpr bool SF_E8 = DG_SF == 1 || DG_SF == 2 || DG_SF == 4;
+constexpr bool FP4B = DG_SF == 2 || DG_SF == 4;   // B in E2M1 with per-row 1x32 UE8M0 scales
+constexpr bool FP4A = DG_SF == 4;             // A in E2M1 with per-row 1x32 UE8M0 scales too
 constexpr bool BF16 = DG_SF == 3;             // BF16 operands, no scales
 constexpr int KW = (KBLKS + 3) / 4;           // packed UE8M0 words per row of scales
 constexpr int SF_KB = SF_E8 ? KW : KBLKS;     // scale entries (floats or words) along K
 constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
+constexpr int KB_A = FP4A ? K / 2 : K;        // ... of A
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
 // WAVE_N divides 128 (tiles start at multiples of BN, a multiple of WAVE_N);
 // FP4 B has a scale per row, never one per wave
@@ -514,12 +519,14 @@ constexpr int RPI = 1024 / ROWB;                // tile rows per 1 KB DMA instru
 // 16-byte chunks XOR-swizzled by (row >> 2) & 3
 constexpr int ROWB_B = FP4B ? 64 : ROWB;
 constexpr int RPI_B = 1024 / ROWB_B;
-constexpr int NA_INS = BM / RPI;                // 1 KB DMA instructions for A
+constexpr int ROWB_A = FP4A ? 64 : ROWB;        // FP4 A: the same 64-byte rows as FP4 B
+constexpr int RPI_A = 1024 / ROWB_A;
+constexpr int NA_INS = BM / RPI_A;              // 1 KB DMA instructions for A
 constexpr int NB_INS = BN / RPI_B;              // ... for B
 constexpr int NS_PER_KB = BF16 ? 0 : (BM + 63) / 64;   // 256 B DMA instructions for one K block of sfa
 constexpr int NS_INS = NS_PER_KB * KSTEP;
 constexpr int A_OFF = 0;
-constexpr int B_OFF = BM * ROWB;
+constexpr int B_OFF = BM * ROWB_A;
 constexpr int S_OFF = B_OFF + BN * ROWB_B;
 constexpr int S_BYTES = NS_PER_KB * 256;        // sfa bytes per K block
 // sfb of the (at most three) 128-row blocks of B a tile touches, one 256 B
@@ -532,7 +539,7 @@ static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
 static_assert(!BF16 || (KBLKS >= 1 && K % 128 == 0), "BF16: K bytes a multiple of 128");
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-static_assert(BM % RPI == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
+static_assert(BM % RPI_A == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 
 // Every wave issues the same number of DMA instructions per stage, so one
@@ -596,9 +603,10 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
     const int sw = l16 & 7;
     const u32 chunk_lo = (u32)((q ^ sw) << 4);
     const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
-    const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * ROWB;
+    const u32 a_frag_off = (u32)(wm * WAVE_M + l16) * ROWB_A;
     const u32 b_frag_off = (u32)(wn * WAVE_N + l16) * ROWB_B;
     const u32 b_chunk_lo = FP4B ? (u32)((q ^ ((l16 >> 2) & 3)) << 4) : chunk_lo;
+    const u32 a_chunk_lo = FP4A ? (u32)((q ^ ((l16 >> 2) & 3)) << 4) : chunk_lo;
 
 #pragma unroll 1
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
@@ -610,18 +618,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         const float* sfa_base;
         int a_rows_total;        // rows of this A (for sfa stride)
         if constexpr (kKind == 2) {
-            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
-            sfa_base = p.sfa + (u64)tl.g * SF_KB * p.M;
+            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * KB_A;
+            sfa_base = p.sfa + (u64)tl.g * (FP4A ? KBLKS : SF_KB) * p.M;
         } else {
-            a_base = p.A + (u64)tl.m0 * K;
+            a_base = p.A + (u64)tl.m0 * KB_A;
             sfa_base = p.sfa;
         }
         a_rows_total = p.M;
         const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
         const u8* b_base = p.B + ((u64)(KG ? 0 : tl.g) * N + tl.n0) * KB_B;
-        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
+        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * KB_A);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
-        const v4i rs_s = make_rsrc(sfa_base, (u32)SF_KB * a_rows_total * 4u);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)(FP4A ? KBLKS : SF_KB) * a_rows_total * 4u);
         const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
                          : KG ? make_rsrc(p.sfb, (u32)(p.kt / KBLK) * N * 4u)
                               : make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
@@ -650,6 +658,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
         // swizzle term does not depend on the instruction (16 rows each)
         const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+        const u32 voff_b4a = (u32)(lane >> 2) * KB_A + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);   // FP4 A
         u32 voff_s[IS > 0 ? IS : 1];   // A scales: clamped rows (the offset includes the K block's row of sfa)
 #pragma unroll
         for (int j = 0; j < IS; ++j) {
@@ -657,7 +666,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             const int h = i / NS_PER_KB;
             const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
-            voff_s[j] = (u32)mm * 4u + (u32)h * a_rows_total * 4u;
+            // FP4 A: word [m][kb] (row-major); otherwise sfa [kb][m] (MN-major)
+            voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * 4u + (u32)h * a_rows_total * 4u;
         }
         u32 voff_t[IT > 0 ? IT : 1];
 #pragma unroll
@@ -689,8 +699,12 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             };
             if (j < IA) {
                 const int i = min(wave + j * NWAVES, NA_INS - 1);
-                dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
-                      __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
+                if constexpr (FP4A)
+                    dma16(lim(rs_a), voff_b4a + (u32)__builtin_amdgcn_readfirstlane(i * RPI_A * KB_A),
+                          __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + A_OFF + i * 1024);
+                else
+                    dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                          __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
             } else if (j < IA + IB) {
                 const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
                 if constexpr (FP4B)
@@ -701,7 +715,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                           __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
-                dma4(lim(rs_s), voff_s[j - IA - IB], __builtin_amdgcn_readfirstlane((u32)sf_row(kb) * a_rows_total * 4u),
+                dma4(lim(rs_s), voff_s[j - IA - IB],
+                     __builtin_amdgcn_readfirstlane(FP4A ? (u32)kb * 4u : (u32)sf_row(kb) * a_rows_total * 4u),
                      st + S_OFF + i * 256);
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
@@ -757,11 +772,15 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             // the next K block's fragments are fetched while its MFMAs run.
             // LDS bases of one K block (stage slot, K block h inside the stage)
             const u32 b_frag = b_frag_off + b_chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
-            const u32 a_frag = a_frag_off + chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
+            const u32 a_frag = a_frag_off + a_chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
             // B fragment of the sub-tile at byte offset off of a K block (lo/hi:
             // the block's base plus this lane's chunk offsets)
             auto read_fb = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
                 if constexpr (FP4B) return lds_read_frag4(lo, off);
+                else return lds_read_frag(lo, hi, off);
+            };
+            auto read_fa = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
+                if constexpr (FP4A) return lds_read_frag4(lo, off);
                 else return lds_read_frag(lo, hi, off);
             };
             // FP4 B scales: this lane's row of each n sub-tile, one word per K block
@@ -814,7 +833,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 lds_u8* const kb0 = kblock_base(0, 0);
                 read_scales(0, 0);
 #pragma unroll
-                for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(kb0 + a_frag, kb0 + a_frag_hi, A_OFF + a * 16 * ROWB);
+                for (int a = 0; a < TM; ++a) fa[a] = read_fa(kb0 + a_frag, kb0 + a_frag_hi, A_OFF + a * 16 * ROWB_A);
                 fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, B_OFF);
             }
 
@@ -851,7 +870,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 if constexpr (SF_E8) {
                     const u32 sh = 8u * (u32)((tl.kb0 + it) & 3);
 #pragma unroll
-                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
+                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> (FP4A ? sh_q : sh));
 #pragma unroll
                     for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
                         eb[b] = (int)(__builtin_bit_cast(u32, first(sb[b])) >> (FP4B ? sh_q : sh));
@@ -905,9 +924,9 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                         if constexpr (SF_E8) {
                             // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
                             // scales (its srcA is B, scaled by eb; its srcB is A, by ea).
-                            // srcA format: 0 = E4M3, 4 = E2M1 (FP4 B)
+                            // operand formats: 0 = E4M3, 4 = E2M1 (srcA: B, srcB: A)
                             acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                fb, fa[a], acc[a][b], FP4B ? 4 : 0, 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
+                                fb, fa[a], acc[a][b], FP4B ? 4 : 0, FP4A ? 4 : 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
                         } else if constexpr (BF16) {
                             // 64 BF16 elements: K chunks q (elements 8q..8q+7) then q+4 (32+8q..)
                             acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_lo(fb), bf_lo(fa[a]), acc[a][b], 0, 0, 0);
@@ -921,7 +940,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                         }
                         // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
                         // (after the tile's last block these reads are unused)
-                        if (last) fa[a] = lds_read_frag(kbn + a_frag, kbn + a_frag_hi, A_OFF + a * 16 * ROWB);
+                        if (last) fa[a] = read_fa(kbn + a_frag, kbn + a_frag_hi, A_OFF + a * 16 * ROWB_A);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (!last) {

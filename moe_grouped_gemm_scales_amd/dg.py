@@ -57,6 +57,12 @@ def _load():
     lib.dg_m_grouped_bf16_gemm_nt_masked.argtypes = [vp_, vp_, vp_, vp_, vp_, i32, i32, i32, i32, vp_]
     for f in (lib.dg_bf16_gemm_nt, lib.dg_m_grouped_bf16_gemm_nt_contiguous, lib.dg_m_grouped_bf16_gemm_nt_masked):
         f.restype = i32
+    lib.dg_fp4_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
+    lib.dg_m_grouped_fp4_fp4_gemm_nt_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_m_grouped_fp4_fp4_gemm_nt_masked.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    for f in (lib.dg_fp4_fp4_gemm_nt, lib.dg_m_grouped_fp4_fp4_gemm_nt_contiguous,
+              lib.dg_m_grouped_fp4_fp4_gemm_nt_masked):
+        f.restype = i32
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
     lib.dg_fp8_fp4_gemm_nt.argtypes = lib.dg_fp8_gemm_nt.argtypes
@@ -507,3 +513,64 @@ def dg_m_grouped_bf16_gemm_nt_masked(A, B, masked_m, C, D, stream=None):
 bf16_gemm_nt = dg_bf16_gemm_nt
 m_grouped_bf16_gemm_nt_contiguous = dg_m_grouped_bf16_gemm_nt_contiguous
 m_grouped_bf16_gemm_nt_masked = dg_m_grouped_bf16_gemm_nt_masked
+
+
+# ---------------------------------------------------------------- FP4 x FP4
+SCALE_FP4_FP4 = 32   # DG_SCALE_FP4_FP4: OR into `kind` of precompile / describe_config
+
+
+def dg_fp4_fp4_gemm_nt(A, sfa, B, sfb, C, D, stream=None):
+    """D = C + A @ B.T with E2M1 A and B.  A uint8 [M,K/2], sfa int32 [M,K/128], B uint8 [N,K/2],
+    sfb int32 [N,K/128] (one UE8M0 scale per 1x32 block of each row, four to a word)."""
+    M, K2 = A.shape
+    K = 2 * K2
+    N = B.shape[0]
+    _fp4(A, "A", (M, K2)); _fp4(B, "B", (N, K2))
+    _i32(sfa, "sfa", (M, _cdiv(K, 128))); _i32(sfb, "sfb", (N, _cdiv(K, 128)))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_fp4_fp4_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K,
+                                  _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp4_fp4_gemm_nt_contiguous(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    """Contiguous M-grouped FP4 x FP4: A [M,K/2], sfa [M,K/128], B [G,N,K/2], sfb [G,N,K/128]."""
+    M, K2 = A.shape
+    K = 2 * K2
+    G, N = B.shape[0], B.shape[1]
+    _fp4(A, "A", (M, K2)); _fp4(B, "B", (G, N, K2))
+    _i32(sfa, "sfa", (M, _cdiv(K, 128))); _i32(sfb, "sfb", (G, N, _cdiv(K, 128)))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_fp4_fp4_gemm_nt_contiguous(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
+                                                       _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp4_fp4_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream=None):
+    """Masked M-grouped FP4 x FP4: A [G,M_max,K/2], sfa [G,M_max,K/128], B [G,N,K/2], sfb [G,N,K/128]."""
+    G, M_max, K2 = A.shape
+    K = 2 * K2
+    N = B.shape[1]
+    _fp4(A, "A", (G, M_max, K2)); _fp4(B, "B", (G, N, K2))
+    _i32(sfa, "sfa", (G, M_max, _cdiv(K, 128))); _i32(sfb, "sfb", (G, N, _cdiv(K, 128)))
+    if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be int32 [G]")
+    _dev(masked_m, "masked_m")
+    if C is not None:
+        _f32(C, "C", (G, M_max, N))
+    _out(D, (G, M_max, N))
+    _check(lib.dg_m_grouped_fp4_fp4_gemm_nt_masked(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m),
+                                                   _ptr(C), _ptr(D), M_max, N, K, G, _stream(stream)))
+    return D
+
+
+fp4_fp4_gemm_nt = dg_fp4_fp4_gemm_nt
+m_grouped_fp4_fp4_gemm_nt_contiguous = dg_m_grouped_fp4_fp4_gemm_nt_contiguous
+m_grouped_fp4_fp4_gemm_nt_masked = dg_m_grouped_fp4_fp4_gemm_nt_masked

@@ -157,7 +157,7 @@ class Problem:
 
     @property
     def K(self):
-        return self.A.shape[-1]
+        return self.A.shape[-1] * (2 if self.fp4a else 1)    # FP4 A holds two codes a byte
 
     @property
     def G(self):

@@ -17,7 +17,7 @@ def to_dev(p: gen.Problem, device="cuda"):
 def out_shape(p: gen.Problem):
     if p.kind == "masked":
         return (p.A.shape[0], p.A.shape[1], p.N)
-    return (p.M, p.N)
+    return (p.A.shape[0], p.N)
 
 
 def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
@@ -36,6 +36,15 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
             dg.dg_m_grouped_bf16_gemm_nt_contiguous(dev["A"], dev["B"], dev["m_indices"], dev["C"], D)
         else:
             dg.dg_m_grouped_bf16_gemm_nt_masked(dev["A"], dev["B"], dev["masked_m"], dev["C"], D)
+    elif p.fp4a:
+        if p.kind == "dense":
+            dg.dg_fp4_fp4_gemm_nt(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
+        elif p.kind == "contiguous":
+            dg.dg_m_grouped_fp4_fp4_gemm_nt_contiguous(dev["A"], dev["sfa"], dev["B"], dev["sfb"],
+                                                       dev["m_indices"], dev["C"], D)
+        else:
+            dg.dg_m_grouped_fp4_fp4_gemm_nt_masked(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["masked_m"],
+                                                   dev["C"], D)
     elif p.fp4:
         if p.kind == "dense":
             dg.dg_fp8_fp4_gemm_nt(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
@@ -63,6 +72,10 @@ def oracle_rows(oracle, p: gen.Problem, rows=None, threads=0):
     if p.bf16:        # unscaled BF16 GEMM
         gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
         return oracle.bf16_gemm(p.kind, d["A"], d["B"], gi, d["C"], rows=rows, threads=threads)
+    if p.fp4a:        # FP4 x FP4: both operands E2M1 with 1x32 UE8M0 scales per row
+        gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
+        return oracle.fp4_fp4_gemm(p.kind, d["A"], d["sfa"], d["B"], d["sfb"], gi, d["C"], rows=rows,
+                                   threads=threads)
     if p.fp4:         # FP8 x FP4: E2M1 B with 1x32 UE8M0 scales
         gi = {"dense": None, "contiguous": d["m_indices"], "masked": d["masked_m"]}[p.kind]
         ref, comp = oracle.fp8_fp4_gemm(p.kind, d["A"], d["sfa"], d["B"], d["sfb"], gi, d["C"], rows=rows,
