@@ -102,3 +102,43 @@ def test_k_grouped_workload_full_size(oracle):
     D = run_kg(p)
     rows = np.concatenate([g * 4096 + sample_rows(4096, 12, seed=g, block=256) for g in range(4)])
     compare(oracle, p, D, rows=rows, what="k-grouped 4x8192 x 4096x7168")
+
+
+def test_graph_replays_of_newer_forms_match_eager():
+    """K-grouped (its rewrite pass included), FP8 x FP4 masked and BF16 contiguous calls
+    captured into one HIP graph give the eager bits on every replay, with eager work
+    (which reuses the same rewrite buffer) between replays."""
+    import moe_grouped_gemm_scales_amd as dg
+    from tests.gpu_util import to_dev
+    pk = gen.make_k_grouped([256, 0, 384], 200, 136, seed=31, with_c=True)
+    pf = gen.make_masked(2, 128, 200, 512, seed=32, masked_m=[100, 7], fp4=True)
+    pb = gen.make_bf16("contiguous", seed=33, N=96, K=256, group_rows=[128, 50])
+    c = lambda t: None if t is None else t.to("cuda")
+    k = dict(A=c(pk.A), sfa=c(pk.sfa), B=c(pk.B), sfb=c(pk.sfb), ks=c(pk.ks), C=c(pk.C))
+    f, b = to_dev(pf), to_dev(pb)
+
+    def calls(Dk, Df, Db):
+        dg.dg_k_grouped_fp8_gemm_tn_contiguous(k["A"], k["sfa"], k["B"], k["sfb"], k["ks"], k["C"], Dk)
+        dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(f["A"], f["sfa"], f["B"], f["sfb"], f["masked_m"], None, Df)
+        dg.dg_m_grouped_bf16_gemm_nt_contiguous(b["A"], b["B"], b["m_indices"], None, Db)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs_e = (torch.empty(3, 200, 136, dtype=torch.bfloat16, device="cuda"),
+                  gen.sentinel_like((2, 128, 200), 5).to("cuda"),
+                  gen.sentinel_like((pb.M, 96), 6).to("cuda"))
+        calls(*outs_e)
+        torch.cuda.synchronize()
+        outs_g = (torch.empty_like(outs_e[0]), gen.sentinel_like((2, 128, 200), 5).to("cuda"),
+                  gen.sentinel_like((pb.M, 96), 6).to("cuda"))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            calls(*outs_g)
+        for rep in range(3):
+            outs_g[0].zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for i, (x, y) in enumerate(zip(outs_g, outs_e)):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"output {i}, replay {rep}"
+            calls(*outs_e)       # eager work between replays
+            torch.cuda.synchronize()
