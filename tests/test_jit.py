@@ -1,0 +1,110 @@
+"""The hipRTC build on the CPU: every kernel the measured tables select compiles for
+gfx950 with no scratch (spill) access in its K loop, a compile error comes back as
+DG_ERR_JIT, and a damaged cache entry is rebuilt.  Each check runs in a fresh
+process with its own cache directory (the library also caches code in memory)."""
+import glob
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+READELF = "/opt/rocm/llvm/bin/llvm-readelf"
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+
+# (kind | format flag, rows, N, K, groups, has_c): the benchmark workloads in every format
+SF_UE8M0, SF_FP8_FP4, SF_BF16, SF_FP4_FP4 = 4, 8, 16, 32
+PLANS = [
+    (0, 64, 2112, 7168, 1, 0), (0, 128, 24576, 1536, 1, 0), (0, 128, 24576, 1536, 1, 1),
+    (0, 4096, 7168, 16384, 1, 0), (1, 32768, 4096, 7168, 4, 0), (2, 256, 7168, 2048, 4, 0),
+    (3, 4096, 7168, 32768, 4, 0),
+    (0 | SF_UE8M0, 64, 2112, 7168, 1, 0), (0 | SF_UE8M0, 4096, 7168, 16384, 1, 0),
+    (1 | SF_UE8M0, 32768, 4096, 7168, 4, 0), (2 | SF_UE8M0, 256, 7168, 2048, 4, 0),
+    (0 | SF_FP8_FP4, 128, 24576, 1536, 1, 0), (0 | SF_FP8_FP4, 4096, 7168, 16384, 1, 0),
+    (2 | SF_FP8_FP4, 256, 7168, 2048, 4, 0),
+    (0 | SF_FP4_FP4, 128, 24576, 1536, 1, 0), (0 | SF_FP4_FP4, 4096, 7168, 16384, 1, 0),
+    (0 | SF_BF16, 4096, 7168, 16384, 1, 0),
+    # model-chosen small shapes (ragged, with C)
+    (0, 300, 520, 1024, 1, 1), (2, 200, 333, 640, 3, 1), (0 | SF_FP8_FP4, 5, 129, 640, 1, 1),
+]
+
+
+def _run(code, cache_dir, extra_env=None):
+    env = dict(os.environ, DG_CACHE_DIR=str(cache_dir), **(extra_env or {}))
+    return subprocess.run([sys.executable, "-c", textwrap.dedent(code)], cwd=ROOT, env=env,
+                          capture_output=True, text=True, timeout=600)
+
+
+PRECOMPILE = """
+    import ctypes, sys
+    import torch  # the hipRTC library a torch process resolves, as in build()
+    lib = ctypes.CDLL("moe_grouped_gemm_scales_amd/libdg.so")
+    lib.dg_last_error.restype = ctypes.c_char_p
+    for plan in {plans}:
+        rc = lib.dg_precompile(*plan, 256)
+        print(plan, rc, lib.dg_last_error().decode()[:300], flush=True)
+"""
+
+
+def _notes(path):
+    out = subprocess.run([READELF, "--notes", path], capture_output=True, text=True).stdout
+    vals = {}
+    for line in out.splitlines():
+        line = line.strip()
+        for key in (".vgpr_spill_count:", ".sgpr_spill_count:", ".private_segment_fixed_size:"):
+            if line.startswith(key):
+                vals.setdefault(key.strip(":."), []).append(int(line.split()[-1]))
+    return vals
+
+
+def _k_loop_scratch_ops(path):
+    """Scratch (spill) instructions between the first and the last MFMA of the GEMM kernel,
+    i.e. inside its K loop, in the AMD disassembly of this code object."""
+    out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", path], capture_output=True, text=True).stdout
+    body = out.split("<dg_fp8_gemm_nt_kernel>:", 1)[1].split("\n\n", 1)[0].splitlines()
+    mfma = [i for i, line in enumerate(body) if "v_mfma" in line]
+    assert mfma, "no MFMA in the GEMM kernel"
+    return [line.strip() for line in body[mfma[0]:mfma[-1] + 1] if "scratch_" in line]
+
+
+@pytest.mark.skipif(not (os.path.exists(READELF) and os.path.exists(OBJDUMP)), reason="LLVM tools not installed")
+def test_selected_kernels_keep_their_k_loop_out_of_scratch(tmp_path):
+    """No kernel a measured table selects touches scratch memory in its K loop.  (The
+    FP32-scale 256 x 256 kernel spills three VGPRs of per-tile set-up, stored and reloaded
+    once per tile before the loop; every other selected kernel has no spill at all.)"""
+    r = _run(PRECOMPILE.format(plans=repr(PLANS)), tmp_path)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert all(line.split(")")[1].split()[0] == "0" for line in r.stdout.strip().splitlines()), r.stdout
+    objs = glob.glob(str(tmp_path / "*.hsaco"))
+    assert len(objs) >= len(PLANS) - 2      # a few plans may share a code object
+    spilling = []
+    for path in objs:
+        v = _notes(path)
+        name = os.path.basename(path)
+        assert v, name
+        assert not _k_loop_scratch_ops(path), f"{name}: scratch access in the K loop"
+        if max(v.get("vgpr_spill_count", [0])) or max(v.get("private_segment_fixed_size", [0])):
+            spilling.append(name.rsplit("-", 1)[0])
+    assert set(spilling) <= {"k0_m256n256_w4x2_s2x1_sk1_c0_N7168_K16384_G1"}, spilling
+
+
+def test_compile_error_is_dg_err_jit(tmp_path):
+    r = _run(PRECOMPILE.format(plans=repr([(0, 64, 64, 128, 1, 0)])), tmp_path,
+             {"DG_JIT_EXTRA_OPTION": "-DDG_BM=not_a_number"})
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert " -4 " in r.stdout and "hipRTC compile" in r.stdout, r.stdout
+
+
+def test_damaged_cache_entry_is_rebuilt(tmp_path):
+    plan = [(0, 96, 200, 256, 1, 0)]
+    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path)
+    assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
+    (obj,) = glob.glob(str(tmp_path / "*.hsaco"))
+    with open(obj, "wb") as f:
+        f.write(b"not a code object")
+    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path)
+    assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
+    with open(obj, "rb") as f:
+        assert f.read(4) == b"\x7fELF"
