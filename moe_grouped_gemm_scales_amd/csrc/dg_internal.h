@@ -25,7 +25,8 @@ struct KernelConfig {
     int splitk = 1;            // K splits (dense only)
     int variant = 0;           // 0: A and B through LDS; 1: B straight into VGPRs, A through an LDS
                                // ring; 2: B straight into VGPRs, A of the K range resident in LDS;
-                               // 3: as 1, with an extra producer wave for A and no K-loop barrier
+                               // 3: as 1, with an extra producer wave for A and no K-loop barrier;
+                               // 4: as 0, with A requested one K block further ahead than B
     int has_c = 0;
     int n = 0, k = 0, g = 1;
     int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0),
@@ -47,6 +48,8 @@ struct KernelConfig {
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
     int lds_bytes() const {
+        if (variant == 4)   // three A slots (tile + sfa), two B slots (tile + sfb)
+            return (stages + 1) * (bm * 128 + (bm + 63) / 64 * 256) + stages * (bn * 128 + 256);
         if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
         if (variant == 3) {   // as many ring slots as fit (at most 16), see the kernel
             const int slot = bm * 128 + (bm + 63) / 64 * 256;

@@ -64,7 +64,8 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     def("DG_N", c.n);
     def("DG_K", c.k);
     def("DG_G", c.g);
-    def("DG_VARIANT", c.variant);
+    def("DG_VARIANT", c.variant == 4 ? 0 : c.variant);
+    if (c.variant == 4) def("DG_AAHEAD", 1);
     def("DG_SF", c.sf);
     if (c.ne > 0) {
         def("DG_NB", c.nb);

@@ -538,7 +538,20 @@ constexpr int STAGE_BYTES = T_OFF + NT_INS * 256;
 static_assert(BN <= 256, "a tile touches at most three 128-row blocks of B");
 static_assert(!SF_E8 || KSTEP == 1, "UE8M0 scales: one K block per stage");
 static_assert(!BF16 || (KBLKS >= 1 && K % 128 == 0), "BF16: K bytes a multiple of 128");
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+// A ahead (DG_AAHEAD, two-slot ring only): the A tiles and their scales get a ring
+// of their own with one slot more than B's, so A is requested two K blocks ahead
+// and B one; the rings then are [A slots x (A tile, sfa)][B slots x (B tile, sfb)].
+#ifndef DG_AAHEAD
+#define DG_AAHEAD 0
+#endif
+constexpr bool AAHEAD = DG_AAHEAD != 0;
+static_assert(!AAHEAD || (KSTEP == 1 && STAGES == 2), "A ahead: one K block a stage, two B slots");
+static_assert(!AAHEAD || (!FP4A && !FP4B && !KG && !BF16), "A ahead: FP8 operands with 128x128 B scales");
+constexpr int A_SLOT = BM * ROWB_A + S_BYTES;                 // A ahead: one A slot
+constexpr int B_SLOT = BN * ROWB_B + NT_INS * 256;            // A ahead: one B slot
+constexpr int A_SLOTS = STAGES + 1;
+constexpr int B_RING = A_SLOTS * A_SLOT;
+constexpr int LDS_BYTES = AAHEAD ? B_RING + STAGES * B_SLOT : STAGES * STAGE_BYTES;
 static_assert(BM % RPI_A == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 
@@ -729,6 +742,34 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
             for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage, live);
         };
+        // A ahead: instruction j of one iteration's issue, in the order B, sfb (K block
+        // kb_b into B slot sl_b), then A, sfa (K block kb_a into A slot sl_a), so that
+        // waiting until only the last IA + IS are in flight lands everything but A's.
+        auto issue_one_aa = [&](int j, int kb_a, int sl_a, bool live_a, int kb_b, int sl_b, bool live_b) {
+            auto lim = [&](v4i r, bool live) {
+                r.z = live ? r.z : 0;
+                return r;
+            };
+            const u32 sa_base = __builtin_amdgcn_readfirstlane(smem_base + sl_a * A_SLOT);
+            const u32 sb_base = __builtin_amdgcn_readfirstlane(smem_base + B_RING + sl_b * B_SLOT);
+            if (j < IB) {
+                const int i = min(wave + j * NWAVES, NB_INS - 1);
+                dma16(lim(rs_b, live_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                      __builtin_amdgcn_readfirstlane((u32)kb_b * KBLK), sb_base + i * 1024);
+            } else if (j < IB + IT) {
+                const int h = min(wave + (j - IB) * NWAVES, NT_INS - 1);
+                dma4(lim(rs_t, live_b), voff_t[j - IB], __builtin_amdgcn_readfirstlane((u32)sf_row(kb_b) * 4u),
+                     sb_base + BN * ROWB_B + h * 256);
+            } else if (j < IB + IT + IA) {
+                const int i = min(wave + (j - IB - IT) * NWAVES, NA_INS - 1);
+                dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                      __builtin_amdgcn_readfirstlane((u32)kb_a * KBLK), sa_base + i * 1024);
+            } else {
+                const int i = min(wave + (j - IB - IT - IA) * NWAVES, NS_INS - 1);
+                dma4(lim(rs_s, live_a), voff_s[j - IB - IT - IA],
+                     __builtin_amdgcn_readfirstlane((u32)sf_row(kb_a) * a_rows_total * 4u), sa_base + BM * ROWB_A + i * 256);
+            }
+        };
 
         // ---- accumulators
         v4f acc[TM][TN];
@@ -751,9 +792,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         __syncthreads();
 
         const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
+        if constexpr (AAHEAD) {
+            // B and A of K block 0, then A of K block 1 (placeholders past the tile)
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
+            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one_aa(j, tl.kb0, 0, nst > 0, tl.kb0, 0, nst > 0);
+#pragma unroll
+            for (int j = IB + IT; j < INS_PER_WAVE; ++j)
+                issue_one_aa(j, tl.kb0 + min(1, nst - 1), 1, nst > 1, tl.kb0, 0, false);
+        } else {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
+        }
 
         // row offsets of this lane's fragments inside a stage
         const int a_row0 = wm * WAVE_M + l16;   // + a*16
@@ -786,14 +836,23 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             // FP4 B scales: this lane's row of each n sub-tile, one word per K block
             const int sb4_off = (wn * WAVE_N + l16) * 4;
             const u32 sh_q = 8u * (u32)q;    // lane group q takes byte q (its 32-wide K block)
-            auto kblock_base = [&](int stage, int h) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + h * 128);
+            // LDS bases of the A tile, the B tile, the A scales and the B scales of a
+            // slot (one K block per stage here; with A ahead A and B have rings of their own)
+            auto a_tile = [&](int slot) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                    smem_base + (AAHEAD ? slot * A_SLOT : slot * STAGE_BYTES + A_OFF));
             };
-            auto kblock_scales = [&](int stage, int h) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + h * S_BYTES);
+            auto b_tile = [&](int slot) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                    smem_base + (AAHEAD ? B_RING + slot * B_SLOT : slot * STAGE_BYTES + B_OFF));
             };
-            auto kblock_sfb = [&](int stage, int h) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES + T_OFF + h * 256);
+            auto a_scales = [&](int slot) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                    smem_base + (AAHEAD ? slot * A_SLOT + BM * ROWB_A : slot * STAGE_BYTES + S_OFF));
+            };
+            auto b_scales = [&](int slot) __attribute__((always_inline)) {
+                return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                    smem_base + (AAHEAD ? B_RING + slot * B_SLOT + BN * ROWB_B : slot * STAGE_BYTES + T_OFF));
             };
             // Registers of the K block being multiplied: its A fragments, its first
             // (then current) B fragment and the scales.  They are read from LDS one K
@@ -804,9 +863,9 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             sc_t sb[TN];
             // K-grouped B scales: the lane's four columns of each n sub-tile
             const int sbk_off = (wn * WAVE_N + 4 * q) * 4;
-            auto read_scales = [&](int stage, int h) __attribute__((always_inline)) {
+            auto read_scales = [&](int slot_a, int slot_b) __attribute__((always_inline)) {
                 if constexpr (BF16) return;       // no scales
-                lds_u8* const sb_p = kblock_sfb(stage, h);
+                lds_u8* const sb_p = b_scales(slot_b);
                 if constexpr (FP4B) {
 #pragma unroll
                     for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
@@ -820,21 +879,23 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
                     for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
                 }
-                lds_u8* const sa_p = kblock_scales(stage, h) + a_row0 * 4;
+                lds_u8* const sa_p = a_scales(slot_a) + a_row0 * 4;
 #pragma unroll
-                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, a * 64);
             };
 
             // stage 0 in LDS (this wave's DMA, then everyone's), then its registers
-            if (STAGES - 1 <= nst) wait_stages<STAGES - 2>();
+            if constexpr (AAHEAD) wait_vmcnt<IA + IS>();     // all but A of K block 1
+            else if (STAGES - 1 <= nst) wait_stages<STAGES - 2>();
             else wait_vmcnt<0>();
             __syncthreads();
             {
-                lds_u8* const kb0 = kblock_base(0, 0);
+                lds_u8* const ka0 = a_tile(0);
+                lds_u8* const kb0 = b_tile(0);
                 read_scales(0, 0);
 #pragma unroll
-                for (int a = 0; a < TM; ++a) fa[a] = read_fa(kb0 + a_frag, kb0 + a_frag_hi, A_OFF + a * 16 * ROWB_A);
-                fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, B_OFF);
+                for (int a = 0; a < TM; ++a) fa[a] = read_fa(ka0 + a_frag, ka0 + a_frag_hi, a * 16 * ROWB_A);
+                fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, 0);
             }
 
 #pragma unroll 1
@@ -849,16 +910,22 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 const bool live = it + STAGES - 1 < nst;
                 const int kb_fill = tl.kb0 + min(it + STAGES - 1, nst - 1) * KSTEP;
                 const int slot_fill = (it + STAGES - 1) % STAGES;
+                // A ahead: A of K block it+2 into its A slot, B of it+1 into its B slot
+                const int a_fill_slot = (it + 2) % A_SLOTS;
+                const int a_fill_kb = tl.kb0 + min(it + 2, nst - 1);
+                const bool a_live = it + 2 < nst;
                 // the K block after the last one of this stage: first of the next stage
                 const int stage_next = (it + 1) % STAGES;
+                const int a_slot = AAHEAD ? it % A_SLOTS : stage;
+                const int a_slot_next = AAHEAD ? (it + 1) % A_SLOTS : stage_next;
 #pragma unroll
                 for (int h = 0; h < KSTEP; ++h) {
-                lds_u8* const kbp = kblock_base(stage, h);
+                lds_u8* const kbp = b_tile(stage);
                 lds_u8* const b_lo = kbp + b_frag;
                 lds_u8* const b_hi = kbp + b_frag_hi;
-                const int h_next = h + 1 < KSTEP ? h + 1 : 0;
-                const int st_next = h + 1 < KSTEP ? stage : stage_next;
-                lds_u8* const kbn = kblock_base(st_next, h_next);
+                lds_u8* const kan = a_tile(a_slot_next);
+                lds_u8* const kbn = b_tile(stage_next);
+                (void)a_slot;
 
                 float sab[TM];           // sa * sb for the uniform case
                 if constexpr (SB_UNIFORM && !SF_E8) {
@@ -883,7 +950,14 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 #pragma unroll
                 for (int b = 0; b < TN; ++b) {
                     if (h == 0) {
-                        if constexpr (SPREAD == 0) {
+                        if constexpr (AAHEAD) {
+                            const int nspread = SPREAD == 0 ? 1 : SPREAD;
+                            if (b < nspread) {
+#pragma unroll
+                                for (int j = b * INS_PER_WAVE / nspread; j < (b + 1) * INS_PER_WAVE / nspread; ++j)
+                                    issue_one_aa(j, a_fill_kb, a_fill_slot, a_live, kb_fill, slot_fill, live);
+                            }
+                        } else if constexpr (SPREAD == 0) {
                             if (b == 0) issue_stage(kb_fill, slot_fill, live);
                         } else if (b < SPREAD) {
 #pragma unroll
@@ -893,7 +967,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     }
                     const bool last = b + 1 == TN;
                     v8i fb_next;
-                    if (!last) fb_next = read_fb(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB_B);
+                    if (!last) fb_next = read_fb(b_lo, b_hi, (b + 1) * 16 * ROWB_B);
                     // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
                     // b itself (carried), taken before the next K block's replace them
                     sc_t sc_prev[TM], s_last[TM];
@@ -910,11 +984,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     if (last) {
                         if (h + 1 == KSTEP) {
                             // next stage landed (own DMA; the later stages pending), then
-                            // everyone's; all reads of this stage are in registers
-                            wait_stages<STAGES - 2>();
+                            // everyone's; all reads of this stage are in registers.  A ahead:
+                            // everything but A of K block it+2 (issued last) has landed
+                            if constexpr (AAHEAD) wait_vmcnt<IA + IS>();
+                            else wait_stages<STAGES - 2>();
                             __syncthreads();
                         }
-                        read_scales(st_next, h_next);
+                        read_scales(a_slot_next, stage_next);
                     }
                     v4f prev[TM];
 #pragma unroll
@@ -940,13 +1016,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                         }
                         // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
                         // (after the tile's last block these reads are unused)
-                        if (last) fa[a] = read_fa(kbn + a_frag, kbn + a_frag_hi, A_OFF + a * 16 * ROWB_A);
+                        if (last) fa[a] = read_fa(kan + a_frag, kan + a_frag_hi, a * 16 * ROWB_A);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (!last) {
                         fb = fb_next;
                     } else {
-                        fb = read_fb(kbn + b_frag, kbn + b_frag_hi, B_OFF);
+                        fb = read_fb(kbn + b_frag, kbn + b_frag_hi, 0);
 #pragma unroll
                         for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
                     }

@@ -254,6 +254,30 @@ def test_graph_replays_match_eager(oracle):
 
 
 # ------------------------------------------------------------------ variants 1 and 2 on the grouped forms
+@pytest.mark.parametrize("forced", ["128,128,4,2,2,1,1,4", "64,96,2,2,2,1,1,4", "256,224,4,2,2,1,1,4",
+                                    "128,128,4,2,2,2,1,4"])
+def test_a_ahead_variant(oracle, monkeypatch, forced):
+    """Variant 4 (A requested one K block further ahead than B, separate LDS rings) on
+    ragged dense (split-K included), masked and contiguous problems, FP32 and UE8M0 scales."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    for e8 in (False, True):
+        p = gen.make_dense(300, 520, 1024, seed=41, with_c=True, ue8m0=e8)
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"dense {forced} ue8m0={e8}")
+        if forced.split(",")[5] != "1":
+            continue                      # split-K is dense only
+        pm = gen.make_masked(3, 200, 333, 512, seed=42, with_c=True, masked_m=[200, 0, 77], ue8m0=e8)
+        D, sent = run(pm)
+        ref, comp = oracle_rows(oracle, pm)
+        _compare(pm, D, sent, ref, comp, what=f"masked {forced} ue8m0={e8}")
+        if int(forced.split(",")[0]) <= 128:
+            pc = gen.make_contiguous([128, 0, 256, 100], 200, 384, seed=43, with_c=True, pad_rows=128, ue8m0=e8)
+            D, sent = run(pc)
+            ref, comp = oracle_rows(oracle, pc)
+            _compare(pc, D, sent, ref, comp, what=f"contiguous {forced} ue8m0={e8}")
+
+
 @pytest.mark.parametrize("forced", ["128,128,1,8,5,1,1,1", "64,64,1,4,3,1,1,1", "64,128,1,4,4,1,1,2",
                                     "64,64,1,4,3,1,1,3"])
 def test_bdirect_grouped(oracle, monkeypatch, forced):
