@@ -48,8 +48,10 @@ struct KernelConfig {
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
     int lds_bytes() const {
-        if (variant == 4)   // three A slots (tile + sfa), two B slots (tile + sfb)
-            return (stages + 1) * (bm * 128 + (bm + 63) / 64 * 256) + stages * (bn * 128 + 256);
+        if (variant == 4) {   // three A slots (tile + sfa), two B slots (tile + sfb); BF16: no scales
+            const int sa = sf == 3 ? 0 : (bm + 63) / 64 * 256, sb = sf == 3 ? 0 : 256;
+            return (stages + 1) * (bm * 128 + sa) + stages * (bn * 128 + sb);
+        }
         if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
         if (variant == 3) {   // as many ring slots as fit (at most 16), see the kernel
             const int slot = bm * 128 + (bm + 63) / 64 * 256;

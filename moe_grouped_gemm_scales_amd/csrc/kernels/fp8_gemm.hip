@@ -546,7 +546,7 @@ static_assert(!BF16 || (KBLKS >= 1 && K % 128 == 0), "BF16: K bytes a multiple o
 #endif
 constexpr bool AAHEAD = DG_AAHEAD != 0;
 static_assert(!AAHEAD || (KSTEP == 1 && STAGES == 2), "A ahead: one K block a stage, two B slots");
-static_assert(!AAHEAD || (!FP4A && !FP4B && !KG && !BF16), "A ahead: FP8 operands with 128x128 B scales");
+static_assert(!AAHEAD || (!FP4A && !FP4B && !KG), "A ahead: FP8 (128x128 B scales) or BF16 operands");
 constexpr int A_SLOT = BM * ROWB_A + S_BYTES;                 // A ahead: one A slot
 constexpr int B_SLOT = BN * ROWB_B + NT_INS * 256;            // A ahead: one B slot
 constexpr int A_SLOTS = STAGES + 1;
