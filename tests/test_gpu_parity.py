@@ -278,6 +278,17 @@ def test_a_ahead_variant(oracle, monkeypatch, forced):
             _compare(pc, D, sent, ref, comp, what=f"contiguous {forced} ue8m0={e8}")
 
 
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_a_ahead_short_k(oracle, monkeypatch, K):
+    """Variant 4 with one, two and three K blocks per tile: the prologue's second A block
+    and the loop's refills are placeholders there."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", "64,96,2,2,2,1,1,4")
+    p = gen.make_dense(130, 200, K, seed=44 + K, with_c=True)
+    D, sent = run(p)
+    ref, comp = oracle_rows(oracle, p)
+    _compare(p, D, sent, ref, comp, what=f"a-ahead K={K}")
+
+
 @pytest.mark.parametrize("forced", ["128,128,1,8,5,1,1,1", "64,64,1,4,3,1,1,1", "64,128,1,4,4,1,1,2",
                                     "64,64,1,4,3,1,1,3"])
 def test_bdirect_grouped(oracle, monkeypatch, forced):
