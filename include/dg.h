@@ -33,10 +33,14 @@
  *     stream).  They never synchronise the host and never read device data
  *     (group indices, masks) on the host.
  *   - The library owns its compiled-kernel cache and a per-stream device
- *     workspace (split-K partials and arrival counters), created on first use
- *     (or by dg_init) and kept until process exit.  The first call for a new
- *     shape compiles a kernel (hipRTC) and may allocate; later calls with the
- *     same shape neither compile nor allocate.
+ *     workspace (split-K partials and arrival counters; the K-contiguous copies
+ *     of K-outermost operands), created on first use (or by dg_init) and kept
+ *     until process exit.  The first call for a new shape compiles a kernel
+ *     (hipRTC) and may allocate; later calls with the same shape neither
+ *     compile nor allocate.  A workspace a larger call outgrows is replaced by
+ *     one at least twice its size and is never freed, so a HIP graph that
+ *     captured calls keeps valid addresses; replay such a graph on the stream
+ *     it was captured on (calls on one stream share that stream's workspace).
  *   - Work queued on different streams must not share output buffers.
  *
  * Errors: every call validates its arguments on the host before touching the

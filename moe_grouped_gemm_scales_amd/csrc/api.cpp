@@ -44,6 +44,9 @@ struct Workspace {
     size_t counter_bytes = 0;
     uint8_t* kmajor = nullptr;       // K-grouped operands rewritten K-contiguous
     size_t kmajor_bytes = 0;
+    // Buffers a larger call outgrew.  They stay allocated until the process ends:
+    // a HIP graph captured earlier still holds their addresses.
+    std::vector<void*> retired;
 };
 
 // One kernel launch of a call.
@@ -97,33 +100,26 @@ int effective_cus(const DeviceState& st) {
     return st.num_cus;
 }
 
-// Grow (never shrink) the stream's workspace.  New arrival counters start at
-// zero; kernels leave them at zero again when they finish.
+// Grow (never shrink) the stream's workspace, at least doubling it.  An outgrown
+// buffer is retired, not freed, so graphs that captured it stay valid.  New
+// arrival counters start at zero; kernels leave them at zero again when they finish.
 dg_status ensure_workspace(DeviceState& st, hipStream_t stream, size_t partial_bytes, size_t counter_bytes,
                            Workspace** out) {
     Workspace& w = st.ws[stream];
     if (w.partial_bytes < partial_bytes) {
-        if (w.partials) {
-            hipError_t e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(w.partials);
-            w.partials = nullptr;
-            w.partial_bytes = 0;
-        }
-        size_t bytes = std::max<size_t>(partial_bytes, size_t(8) << 20);
+        if (w.partials) w.retired.push_back(w.partials);
+        w.partials = nullptr;
+        size_t bytes = std::max({partial_bytes, size_t(8) << 20, 2 * w.partial_bytes});
+        w.partial_bytes = 0;
         hipError_t e = hipMalloc((void**)&w.partials, bytes);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K workspace)");
         w.partial_bytes = bytes;
     }
     if (w.counter_bytes < counter_bytes) {
-        if (w.counters) {
-            hipError_t e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(w.counters);
-            w.counters = nullptr;
-            w.counter_bytes = 0;
-        }
-        size_t bytes = std::max<size_t>(counter_bytes, size_t(64) << 10);
+        if (w.counters) w.retired.push_back(w.counters);
+        w.counters = nullptr;
+        size_t bytes = std::max({counter_bytes, size_t(64) << 10, 2 * w.counter_bytes});
+        w.counter_bytes = 0;
         hipError_t e = hipMalloc((void**)&w.counters, bytes);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K counters)");
         e = hipMemset(w.counters, 0, bytes);
@@ -134,17 +130,15 @@ dg_status ensure_workspace(DeviceState& st, hipStream_t stream, size_t partial_b
     return DG_OK;
 }
 
-// Grow (never shrink) the stream's buffer for the K-contiguous K-grouped operands.
-dg_status ensure_kmajor(DeviceState& st, hipStream_t stream, size_t bytes, uint8_t** out) {
+// Grow (never shrink) the stream's buffer for operands rewritten K-contiguous,
+// retiring (not freeing) an outgrown one, as for the workspace above.
+dg_status ensure_kmajor(DeviceState& st, hipStream_t stream, size_t need, uint8_t** out) {
     Workspace& w = st.ws[stream];
-    if (w.kmajor_bytes < bytes) {
-        if (w.kmajor) {
-            hipError_t e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(w.kmajor);
-            w.kmajor = nullptr;
-            w.kmajor_bytes = 0;
-        }
+    if (w.kmajor_bytes < need) {
+        if (w.kmajor) w.retired.push_back(w.kmajor);
+        w.kmajor = nullptr;
+        const size_t bytes = std::max(need, 2 * w.kmajor_bytes);
+        w.kmajor_bytes = 0;
         hipError_t e = hipMalloc((void**)&w.kmajor, bytes);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(K-contiguous operands)");
         w.kmajor_bytes = bytes;

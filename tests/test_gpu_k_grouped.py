@@ -142,3 +142,46 @@ def test_graph_replays_of_newer_forms_match_eager():
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"output {i}, replay {rep}"
             calls(*outs_e)       # eager work between replays
             torch.cuda.synchronize()
+
+
+def test_graph_survives_workspace_growth(monkeypatch):
+    """A graph captures a K-grouped call (rewrite buffer) and a split-K call (partials);
+    larger eager calls on the same stream then grow both workspaces; every replay of
+    the graph still gives the eager bits (outgrown buffers stay allocated)."""
+    import os
+    import moe_grouped_gemm_scales_amd as dg
+    from tests.gpu_util import to_dev
+    c = lambda t: None if t is None else t.to("cuda")
+    small = gen.make_k_grouped([128, 256], 64, 80, seed=51)
+    large = gen.make_k_grouped([2048, 2048], 512, 640, seed=52)
+    ps = gen.make_dense(64, 2112, 7168, seed=53)          # split-K 7: 3.8 MB of partials
+    pl = gen.make_dense(1024, 2112, 8192, seed=54)        # split-K 8 forced below: 71 MB
+    ds, dl = to_dev(ps), to_dev(pl)
+    ks = {k: c(getattr(small, k)) for k in ("A", "sfa", "B", "sfb", "ks")}
+    kl = {k: c(getattr(large, k)) for k in ("A", "sfa", "B", "sfb", "ks")}
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Ke = torch.empty(2, 64, 80, dtype=torch.bfloat16, device="cuda")
+        De = torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda")
+        dg.dg_k_grouped_fp8_gemm_tn_contiguous(ks["A"], ks["sfa"], ks["B"], ks["sfb"], ks["ks"], None, Ke)
+        dg.dg_fp8_gemm_nt(ds["A"], ds["sfa"], ds["B"], ds["sfb"], None, De)
+        torch.cuda.synchronize()
+        Kg, Dg = torch.empty_like(Ke), torch.empty_like(De)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            dg.dg_k_grouped_fp8_gemm_tn_contiguous(ks["A"], ks["sfa"], ks["B"], ks["sfb"], ks["ks"], None, Kg)
+            dg.dg_fp8_gemm_nt(ds["A"], ds["sfa"], ds["B"], ds["sfb"], None, Dg)
+        KL = torch.empty(2, 512, 640, dtype=torch.bfloat16, device="cuda")
+        DL = torch.empty(1024, 2112, dtype=torch.bfloat16, device="cuda")
+        for rep in range(2):
+            # larger calls on the same stream: the rewrite buffer and the partials grow
+            dg.dg_k_grouped_fp8_gemm_tn_contiguous(kl["A"], kl["sfa"], kl["B"], kl["sfb"], kl["ks"], None, KL)
+            monkeypatch.setenv("DG_FORCE_CONFIG", "128,128,4,2,2,8,1,0")
+            dg.dg_fp8_gemm_nt(dl["A"], dl["sfa"], dl["B"], dl["sfb"], None, DL)
+            monkeypatch.delenv("DG_FORCE_CONFIG")
+            Kg.zero_(); Dg.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Kg.view(torch.int16), Ke.view(torch.int16)), f"k-grouped replay {rep}"
+            assert torch.equal(Dg.view(torch.int16), De.view(torch.int16)), f"split-K replay {rep}"
+            assert os.environ.get("DG_FORCE_CONFIG") is None
