@@ -713,18 +713,18 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             if (j < IA) {
                 const int i = min(wave + j * NWAVES, NA_INS - 1);
                 if constexpr (FP4A)
-                    dma16(lim(rs_a), voff_b4a + (u32)__builtin_amdgcn_readfirstlane(i * RPI_A * KB_A),
+                    dma16(lim(rs_a), voff_b4a + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_A) * (u32)KB_A),
                           __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + A_OFF + i * 1024);
                 else
-                    dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                    dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                           __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
             } else if (j < IA + IB) {
                 const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
                 if constexpr (FP4B)
-                    dma16(lim(rs_b), voff_b4 + (u32)__builtin_amdgcn_readfirstlane(i * RPI_B * KB_B),
+                    dma16(lim(rs_b), voff_b4 + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_B) * (u32)KB_B),
                           __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + B_OFF + i * 1024);
                 else
-                    dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                    dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                           __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
@@ -754,7 +754,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             const u32 sb_base = __builtin_amdgcn_readfirstlane(smem_base + B_RING + sl_b * B_SLOT);
             if (j < IB) {
                 const int i = min(wave + j * NWAVES, NB_INS - 1);
-                dma16(lim(rs_b, live_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                dma16(lim(rs_b, live_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                       __builtin_amdgcn_readfirstlane((u32)kb_b * KBLK), sb_base + i * 1024);
             } else if (j < IB + IT) {
                 const int h = min(wave + (j - IB) * NWAVES, NT_INS - 1);
@@ -762,7 +762,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                      sb_base + BN * ROWB_B + h * 256);
             } else if (j < IB + IT + IA) {
                 const int i = min(wave + (j - IB - IT) * NWAVES, NA_INS - 1);
-                dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane(i * RPI * K),
+                dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                       __builtin_amdgcn_readfirstlane((u32)kb_a * KBLK), sa_base + i * 1024);
             } else {
                 const int i = min(wave + (j - IB - IT - IA) * NWAVES, NS_INS - 1);
