@@ -44,13 +44,6 @@ int occupancy(const KernelConfig& c) {
     return std::max(1, std::min(by_lds, by_regs));
 }
 
-double mfma_efficiency(int tm, int tn) {
-    // fraction of MFMA peak one wave tile sustains: small tiles spend more issue
-    // slots on LDS reads, scale products and loop overhead per MFMA
-    double per_mfma_overhead = 2.0 / tm + 2.0 / tn;   // fragment reads per MFMA
-    return 0.85 / (1.0 + 0.25 * per_mfma_overhead);
-}
-
 struct Estimate {
     double seconds;
     KernelConfig cfg;
