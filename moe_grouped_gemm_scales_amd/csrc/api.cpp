@@ -174,7 +174,8 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
     if (s != DG_OK) return s;
     const int cus = effective_cus(*st);
     const char* forced = std::getenv("DG_FORCE_CONFIG");
-    PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, p.sf, cus, forced ? forced : ""};
+    PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, p.sf, cus,
+                std::string(forced ? forced : "") + "|" + jit_extra_option()};
     auto it = st->plans.find(key);
     if (it == st->plans.end()) {
         Plan plan;

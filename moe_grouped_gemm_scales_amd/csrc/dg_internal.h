@@ -83,6 +83,8 @@ int64_t num_work_items(const KernelConfig& c, int rows);
 // JIT (jit.cpp).  compile_code() needs no GPU; get_function() loads on the
 // current device (the GEMM kernel, or another kernel of the same module).
 dg_status compile_code(const KernelConfig& c, std::vector<char>* code);
+// DG_JIT_EXTRA_OPTION (one more hipRTC option), part of every cache key
+std::string jit_extra_option();
 dg_status get_function(const KernelConfig& c, void** function /* hipFunction_t */,
                        const char* name = "dg_fp8_gemm_nt_kernel");
 

@@ -131,15 +131,19 @@ void write_file_atomic(const std::string& path, const std::vector<char>& data) {
 }
 
 dg_status compile_locked(const KernelConfig& c, std::vector<char>* code) {
-    auto it = g_code.find(c.key());
+    std::vector<std::string> opts = compile_options(c);
+    // the extra option changes the code, so it is part of both cache keys
+    const std::string extra = jit_extra_option();
+    if (!extra.empty()) opts.push_back(extra);
+    const std::string mem_key = c.key() + (extra.empty() ? std::string() : "|" + extra);
+    auto it = g_code.find(mem_key);
     if (it != g_code.end()) {
         *code = it->second;
         return DG_OK;
     }
-    const std::vector<std::string> opts = compile_options(c);
     const std::string path = cache_file(c, opts);
     if (read_file(path, code)) {
-        g_code[c.key()] = *code;
+        g_code[mem_key] = *code;
         return DG_OK;
     }
     const bool verbose = env_flag("DG_PRINT_COMPILE");
@@ -149,8 +153,6 @@ dg_status compile_locked(const KernelConfig& c, std::vector<char>* code) {
         return set_error(DG_ERR_JIT, "hiprtcCreateProgram failed");
     std::vector<const char*> argv;
     for (const auto& s : opts) argv.push_back(s.c_str());
-    const char* bad = std::getenv("DG_JIT_EXTRA_OPTION");   // lets tests force a compile error
-    if (bad && *bad) argv.push_back(bad);
     hiprtcResult r = hiprtcCompileProgram(prog, (int)argv.size(), argv.data());
     size_t log_size = 0;
     hiprtcGetProgramLogSize(prog, &log_size);
@@ -171,7 +173,7 @@ dg_status compile_locked(const KernelConfig& c, std::vector<char>* code) {
         for (const auto& s : opts) cmd << ' ' << s;
         std::fprintf(stderr, "[dg] hipRTC %s (%.0f ms):%s\n", c.key().c_str(), ms, cmd.str().c_str());
     }
-    g_code[c.key()] = *code;
+    g_code[mem_key] = *code;
     write_file_atomic(path, *code);
     return DG_OK;
 }
@@ -203,6 +205,14 @@ std::string cache_dir() {
     return "jit_cache";
 }
 
+// One more hipRTC option from the environment: tests force a compile error with
+// it, experiments pass -D switches.  A build with it is never served to a caller
+// without it (or with another): the option is part of every cache key.
+std::string jit_extra_option() {
+    const char* v = std::getenv("DG_JIT_EXTRA_OPTION");
+    return v ? std::string(v) : std::string();
+}
+
 dg_status compile_code(const KernelConfig& c, std::vector<char>* code) {
     std::lock_guard<std::mutex> lock(g_mu);
     return compile_locked(c, code);
@@ -212,7 +222,8 @@ dg_status get_function(const KernelConfig& c, void** function, const char* name)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return set_error(DG_ERR_HIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_pair(dev, c.key() + "/" + name);
+    const std::string extra = jit_extra_option();
+    auto key = std::make_pair(dev, c.key() + "/" + name + (extra.empty() ? std::string() : "|" + extra));
     auto it = g_funcs.find(key);
     if (it != g_funcs.end()) {
         *function = (void*)it->second;

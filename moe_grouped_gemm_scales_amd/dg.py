@@ -114,6 +114,9 @@ def _fp8(t: torch.Tensor, name: str):
 def _dev(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device; another device's memory is not its operand
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 

@@ -108,3 +108,26 @@ def test_damaged_cache_entry_is_rebuilt(tmp_path):
     assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
     with open(obj, "rb") as f:
         assert f.read(4) == b"\x7fELF"
+
+
+def test_extra_option_is_part_of_the_cache_key(tmp_path):
+    """A build with DG_JIT_EXTRA_OPTION gets a cache entry of its own, on disk and in
+    memory: it is never served to a caller without the option (or with another)."""
+    plan = [(0, 96, 200, 256, 1, 0)]
+    count = lambda: len(glob.glob(str(tmp_path / "*.hsaco")))
+    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path)
+    assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
+    assert count() == 1
+    # another process with the option: a second code object, not the first one
+    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path, {"DG_JIT_EXTRA_OPTION": "-DDG_FA_AHEAD=2"})
+    assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
+    assert count() == 2
+    # one process that sets the option between two calls builds (and caches) a third
+    in_process = textwrap.dedent(PRECOMPILE.format(plans=repr(plan))) + textwrap.dedent("""
+        import os
+        os.environ["DG_JIT_EXTRA_OPTION"] = "-DDG_FA_AHEAD=3"
+        print("second", lib.dg_precompile(*{plan}, 256), flush=True)
+    """).format(plan=repr(plan[0]))
+    r = _run(in_process, tmp_path)
+    assert r.returncode == 0 and "second 0" in r.stdout, r.stdout + r.stderr[-2000:]
+    assert count() == 3
