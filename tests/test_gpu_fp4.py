@@ -108,7 +108,8 @@ def test_fp4_masked_edges(oracle, masked_m):
 
 
 FP4_FORCED = ["128,128,4,2,2,1,1,0", "256,256,4,2,2,1,1,0", "64,96,2,2,4,2,1,0", "256,224,4,2,2,1,1,0",
-              "32,64,1,2,3,4,1,0", "128,112,4,1,3,1,1,0", "128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520"]
+              "32,64,1,2,3,4,1,0", "128,112,4,1,3,1,1,0", "128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520",
+              "128,224,4,2,4,1,1,0"]
 
 
 @pytest.mark.parametrize("forced", FP4_FORCED)

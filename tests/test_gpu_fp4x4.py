@@ -76,7 +76,7 @@ def test_fp4x4_grouped(oracle):
 
 
 @pytest.mark.parametrize("forced", ["128,128,4,2,2,1,1,0", "256,256,4,2,2,1,1,0", "64,96,2,2,4,2,1,0",
-                                    "32,64,1,2,3,4,1,0"])
+                                    "32,64,1,2,3,4,1,0", "128,224,4,2,4,1,1,0"])
 def test_fp4x4_forced_tile_configs(oracle, monkeypatch, forced):
     monkeypatch.setenv("DG_FORCE_CONFIG", forced)
     p = gen.make_dense(300, 520, 1024, seed=26, with_c=True, fp4x4=True)
@@ -85,7 +85,7 @@ def test_fp4x4_forced_tile_configs(oracle, monkeypatch, forced):
     _compare(D, sent, ref, comp, what=f"fp4x4 forced {forced}")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_fp4x4_workloads(oracle, cfg):
     p = gen.make_workload(cfg, fp4x4=True)
     D, sent = run(p)

@@ -23,7 +23,7 @@ PLANS = [
     (0 | SF_UE8M0, 64, 2112, 7168, 1, 0), (0 | SF_UE8M0, 4096, 7168, 16384, 1, 0),
     (1 | SF_UE8M0, 32768, 4096, 7168, 4, 0), (2 | SF_UE8M0, 256, 7168, 2048, 4, 0),
     (0 | SF_FP8_FP4, 128, 24576, 1536, 1, 0), (0 | SF_FP8_FP4, 4096, 7168, 16384, 1, 0),
-    (2 | SF_FP8_FP4, 256, 7168, 2048, 4, 0),
+    (1 | SF_FP8_FP4, 32768, 4096, 7168, 4, 0), (2 | SF_FP8_FP4, 256, 7168, 2048, 4, 0),
     (0 | SF_FP4_FP4, 128, 24576, 1536, 1, 0), (0 | SF_FP4_FP4, 4096, 7168, 16384, 1, 0),
     (0 | SF_BF16, 4096, 7168, 16384, 1, 0),
     # model-chosen small shapes (ragged, with C)
