@@ -41,6 +41,8 @@
  *     one at least twice its size and is never freed, so a HIP graph that
  *     captured calls keeps valid addresses; replay such a graph on the stream
  *     it was captured on (calls on one stream share that stream's workspace).
+ *     A call that compiles or allocates cannot run under stream capture: make
+ *     the first call of each shape on each stream eagerly, then capture.
  *   - Work queued on different streams must not share output buffers.
  *
  * Errors: every call validates its arguments on the host before touching the
