@@ -205,10 +205,15 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         it->second.transpose = static_cast<hipFunction_t>(fptr);
     }
     // rewrite of a K-outermost operand X [groups][rows_k][cols] as [groups][cols][pitch]
+    // (one workgroup per 64 x 64 byte block, K blocks fastest; grid.z: groups)
     auto rewrite_k_major = [&](const void* x, void* xt, int rows_k, int cols, int groups) -> dg_status {
+        const uint64_t blocks = (uint64_t)(rows_k / 64) * (uint64_t)((cols + 63) / 64);
+        if (blocks >= (1ull << 31) || groups > 65535)
+            return set_error(DG_ERR_UNSUPPORTED, "operand too large for the K-contiguous rewrite");
+        if (blocks == 0) return DG_OK;
         void* args[] = {&x, &xt, &rows_k, &cols};
-        hipError_t e = hipModuleLaunchKernel(it->second.transpose, (unsigned)(rows_k / 64), (unsigned)((cols + 63) / 64),
-                                             (unsigned)groups, 256, 1, 1, 0, stream, args, nullptr);
+        hipError_t e = hipModuleLaunchKernel(it->second.transpose, (unsigned)blocks, 1, (unsigned)groups, 256, 1, 1, 0,
+                                             stream, args, nullptr);
         return e == hipSuccess ? DG_OK : hip_fail(e, "hipModuleLaunchKernel(transpose)");
     };
     // TN / NN / TT layouts: the K-outermost operand(s) rewritten K-contiguous in the

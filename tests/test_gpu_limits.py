@@ -10,7 +10,9 @@ through the C ABI:
 * 2^19 + 77 rows of A (dense, with C) and 2^19 rows over four experts
   (contiguous): grids of thousands of tiles, row offsets past 2^27 bytes;
 * 2^18 + 40 columns of B with 3 rows;
-* masked groups with a long K (2^17) and a partial mask.
+* masked groups with a long K (2^17) and a partial mask;
+* A stored K-outermost with 2^22 + 64 rows (its rewrite spans 65537 column
+  blocks).
 
 Outputs are checked on sampled rows (always the first and last and tile
 edges) with the bar of the other parity tests: |D - ref| <= 2^-7 |ref| +
@@ -126,3 +128,19 @@ def test_masked_long_k(oracle):
     rows = np.concatenate([sample_rows(M_max, 10, seed=5), M_max + sample_rows(M_max, 10, seed=6)])
     ref, comp = oracle_rows(oracle, p, rows=rows)
     _compare(D, sent, ref, comp, rows, f"masked {G}x{M_max}x{N}x{K}")
+
+
+def test_tt_layout_rewrite_of_many_rows(oracle):
+    """A stored K-outermost ([K][M]) with M = 2^22 + 64: its rewrite covers 65537 blocks
+    of 64 columns, past what one grid dimension of 65535 would hold."""
+    import moe_grouped_gemm_scales_amd as dg
+    M, N, K = (1 << 22) + 64, 16, 128
+    p = gen.make_dense(M, N, K, seed=82)
+    At = p.A.t().contiguous()
+    sent = gen.sentinel_like((M, N), 7)
+    D = sent.to("cuda")
+    dg.dg_fp8_gemm_tt(At.to("cuda"), p.sfa.to("cuda"), p.B.to("cuda"), p.sfb.to("cuda"), None, D)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 48, block=64, seed=8)
+    ref, comp = oracle_rows(oracle, p, rows=rows)
+    _compare(D.cpu(), sent, ref, comp, rows, f"tt layout {M}x{N}x{K}")
