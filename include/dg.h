@@ -87,8 +87,11 @@ dg_status dg_fp8_gemm_nt(const void *A, const float *sfa, const void *B, const f
  *   A [M][K], sfa [Kb][M], B [G][N][K], sfb [G][Nb][Kb], C NULL or [M][N], D [M][N],
  *   m_indices int32 [M] (device): expert of each row; a value outside [0, G)
  *   marks a padding row, which is not computed and whose D row is untouched.
- * M must be a multiple of the alignment.  All valid rows of one aligned
- * block must name the same expert (rows naming another are left untouched).
+ * M must be a multiple of the alignment.  Every valid row of an aligned block
+ * must name the block's expert, and padding rows come after them.  Outside
+ * that layout each row is either computed for its own expert or left
+ * untouched (which one depends on the tile size); no row is ever computed
+ * with another expert's weights.
  */
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void *A, const float *sfa, const void *B,
                                               const float *sfb, const int32_t *m_indices,

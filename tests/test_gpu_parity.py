@@ -160,6 +160,29 @@ def test_contiguous_groups_independent(oracle):
         (-D1.float())[idx == 1], D2.float()[idx == 1])
 
 
+@pytest.mark.parametrize("forced", [None, "128,128,4,2,2,1,1,0", "64,96,2,2,4,1,1,0", "32,64,1,2,3,1,1,0"])
+def test_contiguous_mixed_blocks_never_use_another_experts_weights(oracle, monkeypatch, forced):
+    """Aligned blocks that break the layout (rows naming another expert inside a
+    block, a block that starts with a padding row): whatever the tile size, every
+    row is either left untouched or holds its result for its own expert, padding
+    rows are untouched, and the blocks that keep the layout are computed in full."""
+    if forced:
+        monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    p = gen.make_contiguous([128, 128, 128], 160, 256, seed=61)
+    idx = p.m_indices.clone()
+    idx[40:60] = 2           # block 0 (expert 0) holds rows naming expert 2
+    idx[128] = -1            # block 1 starts with a padding row; rows 129.. still name expert 1
+    q = gen.Problem("contiguous", p.A, p.sfa, p.B, p.sfb, m_indices=idx)
+    D, sent = run(q)
+    ref, comp = oracle_rows(oracle, q)            # every row with a valid index, for its own expert
+    got, bits, sbits = check.bf16_to_f64(D), check.bf16_bits(D), check.bf16_bits(sent)
+    untouched = (bits == sbits).all(axis=1)
+    assert untouched[~comp].all(), "a padding row was written"
+    written = comp & ~untouched
+    check.assert_close(got[written], ref[written], f"contiguous, mixed blocks ({forced or 'default plan'})")
+    assert written[256:].all(), "the block that keeps the layout was not computed in full"
+
+
 # ------------------------------------------------------------------ masked, edge cases
 @pytest.mark.parametrize("masked_m", [[0, 0, 0], [96, 96, 96], [-3, 200, 17], [1, 95, 48]])
 def test_masked_edges(oracle, masked_m):
