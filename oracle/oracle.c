@@ -636,7 +636,8 @@ double oracle_bf16_value(uint16_t bits)
         mag = ldexp((double)m, -133);
     else
         mag = ldexp(1.0 + (double)m / 128.0, e - 127);
-    return s ? 0.0 - mag : mag;
+    /* the sign bit applies to zero as well: 0x8000 is -0 */
+    return copysign(mag, s ? -1.0 : 1.0);
 }
 
 typedef struct {
@@ -653,6 +654,15 @@ typedef struct {
 } bf16_problem;
 
 typedef struct { const bf16_problem *p; int64_t r0, r1; } bf16_slice;
+
+/* All 65536 codes decoded once by oracle_bf16_value (a lookup instead of a
+ * decode per multiply; the values are the same). */
+static double bf16_table[65536];
+static pthread_once_t bf16_table_once = PTHREAD_ONCE_INIT;
+static void bf16_table_fill(void)
+{
+    for (int c = 0; c < 65536; ++c) bf16_table[c] = oracle_bf16_value((uint16_t)c);
+}
 
 /* One output row: D[n] = C[n] + sum_k bf16(A[m][k]) * bf16(B[n][k]) in FP64,
  * ascending k (every product is exact in FP64; the sum rounds far below the
@@ -684,12 +694,12 @@ static void *bf16_worker(void *arg)
             }
         }
         for (int k = 0; k < p->K; ++k)
-            a[k] = oracle_bf16_value(p->A[r * p->K + k]);
+            a[k] = bf16_table[p->A[r * p->K + k]];
         const uint16_t *b = p->B + g * (int64_t)p->N * p->K;
         for (int n = 0; n < p->N; ++n) {
             double acc = 0.0;
             for (int k = 0; k < p->K; ++k)
-                acc += a[k] * oracle_bf16_value(b[(int64_t)n * p->K + k]);
+                acc += a[k] * bf16_table[b[(int64_t)n * p->K + k]];
             out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);
         }
         if (p->computed) p->computed[i] = 1;
@@ -709,6 +719,7 @@ int oracle_bf16_gemm(int kind, const uint16_t *A, const uint16_t *B, const int32
                      uint8_t *computed, int n_threads)
 {
     if (kind < 0 || kind > 2 || M <= 0 || N <= 0 || K <= 0 || G <= 0) return -1;
+    pthread_once(&bf16_table_once, bf16_table_fill);
     bf16_problem p = {A, B, C, group_info, kind, M, N, K, G, rows, 0, out, computed};
     p.n_rows = rows ? n_rows : (kind == KIND_MASKED ? (int64_t)G * M : M);
     if (n_threads <= 0) n_threads = oracle_default_threads();

@@ -570,11 +570,14 @@ def test_layout_nn_contiguous_vs_numpy(oracle):
 # ------------------------------------------------------------------ BF16 x BF16
 def test_bf16_decode_matches_torch_for_every_code(oracle):
     codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
-    ref = codes.view(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
     got = np.array([oracle.bf16_value(c) for c in range(65536)])
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert np.array_equal(got[ok], ref[ok])
+    # array_equal cannot see the sign of a zero: 0x8000 must decode to -0
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert np.signbit(got[0x8000]) and got[0x8000] == 0.0
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 5, 64), (37, 129, 200), (130, 3, 128)])

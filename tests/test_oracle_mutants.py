@@ -58,7 +58,7 @@ MUTANTS = [
     ("bf16_subnormal_scale", "mag = ldexp((double)m, -133);", "mag = ldexp((double)m, -132);"),
     ("bf16_drop_last_k", "            for (int k = 0; k < p->K; ++k)\n                acc += a[k]",
      "            for (int k = 0; k < p->K - 1; ++k)\n                acc += a[k]"),
-    ("bf16_lost_sign", "return s ? 0.0 - mag : mag;", "return mag;"),
+    ("bf16_lost_sign", "return copysign(mag, s ? -1.0 : 1.0);", "return mag;"),
     # (swapping the nibble order of both operands at once leaves every block sum unchanged;
     # swapping it for A alone is a real mistake)
     ("fp4x4_a_nibbles_swapped", "blk += e2m1_nibble(a_row, k, dec4) * e2m1_nibble(b_row, k, dec4);",
