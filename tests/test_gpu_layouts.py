@@ -70,7 +70,8 @@ def test_nn_contiguous(oracle):
 def test_layouts_large_dense(oracle, layout):
     """The compute-bound dense workload (4096 x 7168 x 16384) stored in another layout."""
     p = gen.make_workload(2)
-    check_layout(oracle, p, layout, rows=sample_rows(p.M, 32, seed=8, block=256))
+    # NN compared whole, TT on sampled rows
+    check_layout(oracle, p, layout, rows=None if layout == "nn" else sample_rows(p.M, 32, seed=8, block=256))
 
 
 def test_nn_contiguous_workload(oracle):

@@ -26,9 +26,10 @@ def _compare(p, D, sent, ref, comp, rows=None, what=""):
     Df = flat_rows(D)
     Sf = flat_rows(sent)
     idx = np.arange(Df.shape[0]) if rows is None else rows
-    got = check.bf16_to_f64(Df[torch.as_tensor(idx)])
     if comp.any():
-        check.assert_close(got[comp], ref[comp], what)
+        # only the computed rows are widened (the sentinel rows are compared as bits)
+        got = check.bf16_to_f64(Df[torch.as_tensor(idx[comp])])
+        check.assert_close(got, ref[comp], what)
     if (~comp).any():
         untouched = idx[~comp]
         assert np.array_equal(check.bf16_bits(Df[torch.as_tensor(untouched)]),
@@ -101,22 +102,21 @@ def test_dense_repeatable_and_stream(oracle):
 # ------------------------------------------------------------------ the five workloads at full size
 @pytest.mark.parametrize("cfg", [0, 1, "1c", 2])
 def test_workload_dense(oracle, cfg):
+    """Every element of D at full size (4096 x 7168 x 16384: ~1 TFLOP of FP64 oracle work)."""
     p = gen.make_workload(cfg)
     D, sent = run(p)
-    rows = np.arange(p.M) if p.M <= 128 else sample_rows(p.M, 48, seed=3)
-    ref, comp = oracle_rows(oracle, p, rows=rows)
-    _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[cfg])
-    # every row of a dense result is written: no sentinel survives in sampled-out rows either
-    assert not torch.equal(D.view(torch.int16)[-1], sent.view(torch.int16)[-1])
+    ref, comp = oracle_rows(oracle, p)
+    assert comp.all()
+    _compare(p, D, sent, ref, comp, what=gen.WORKLOAD_NAMES[cfg])
 
 
 def test_workload_contiguous(oracle):
+    """Every element of the 4 x 8192 x 4096 x 7168 contiguous result (~1.9 TFLOP of oracle work)."""
     p = gen.make_workload(3)
     D, sent = run(p)
-    rows = sample_rows(p.M, 48, seed=4, block=128)
-    ref, comp = oracle_rows(oracle, p, rows=rows)
+    ref, comp = oracle_rows(oracle, p)
     assert comp.all()
-    _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[3])
+    _compare(p, D, sent, ref, comp, what=gen.WORKLOAD_NAMES[3])
 
 
 def test_workload_masked(oracle):
@@ -412,9 +412,7 @@ def test_ue8m0_forced_tile_configs(oracle, monkeypatch, forced):
 def test_ue8m0_workloads(oracle, cfg):
     p = gen.make_workload(cfg, ue8m0=True)
     D, sent = run(p)
-    if p.kind == "masked":
-        rows = np.arange(p.A.shape[0] * p.A.shape[1])
-    else:
-        rows = sample_rows(p.M, 48, seed=5, block=128)
+    # the masked and the large dense result are compared whole, the contiguous one on sampled rows
+    rows = sample_rows(p.M, 48, seed=5, block=128) if p.kind == "contiguous" else None
     ref, comp = oracle_rows(oracle, p, rows=rows)
     _compare(p, D, sent, ref, comp, rows=rows, what="ue8m0 " + gen.WORKLOAD_NAMES[cfg])
