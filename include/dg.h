@@ -41,6 +41,10 @@
  *     one at least twice its size and is never freed, so a HIP graph that
  *     captured calls keeps valid addresses; replay such a graph on the stream
  *     it was captured on (calls on one stream share that stream's workspace).
+ *     Two graphs that captured calls on the same stream share its workspace
+ *     too, so they must not be replayed concurrently (on other streams) when
+ *     their shapes use split-K (few rows, long K) or a K-contiguous rewrite:
+ *     that races on the partial sums and arrival counters and is unsupported.
  *     A call that compiles or allocates cannot run under stream capture: make
  *     the first call of each shape on each stream eagerly, then capture.
  *   - Work queued on different streams must not share output buffers.
@@ -266,6 +270,20 @@ dg_status dg_m_grouped_fp4_fp4_gemm_nt_masked(const void *A, const int32_t *sfa,
                                               const int32_t *sfb, const int32_t *masked_m,
                                               const float *C, void *D, int M_max, int N, int K,
                                               int num_groups, void *stream);
+
+/*
+ * Health of the current device's kernels.  The producer/consumer kernel
+ * variant (one wave streams the A tiles into an LDS ring, the others wait on
+ * per-slot LDS flags; chosen for few rows, e.g. M <= 128) bounds every such
+ * wait (about 30 ms) so that a fault in its hand-off can never hang the
+ * device.  A wait that runs out adds one to a device-wide counter, and the D of
+ * that call is then not to be trusted.  dg_get_wait_giveups() copies the
+ * counter to *count and dg_reset_wait_giveups() clears it; both synchronise
+ * with the device (not for use inside stream capture).  The counter is 0
+ * unless something went wrong.
+ */
+dg_status dg_get_wait_giveups(unsigned int *count);
+dg_status dg_reset_wait_giveups(void);
 
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library. */
 const char *dg_last_error(void);

@@ -3,6 +3,7 @@ contiguous and M-grouped masked forms (FP32 or UE8M0 scales, FP8 x FP4 and FP4 x
 the NN/TN/TT storage layouts, the K-grouped TN form and an unscaled BF16 GEMM,
 as a C-ABI library (libdg.so) with a thin Python binding.  See include/dg.h
 for the contract."""
+from .dg import get_wait_giveups, reset_wait_giveups  # noqa: F401
 from .dg import (DGError, describe_config, dg_fp8_gemm_nt, dg_m_grouped_fp8_gemm_nt_contiguous,  # noqa: F401
                  dg_m_grouped_fp8_gemm_nt_masked, fp8_gemm_nt, get_mk_alignment_for_contiguous_layout,
                  get_num_cus, init, m_grouped_fp8_gemm_nt_contiguous, m_grouped_fp8_gemm_nt_masked,

@@ -1,9 +1,10 @@
 """Build libdg.so in-tree.
 
-The host library (C++, HIP runtime + hipRTC; no device code) is compiled
-with the host C++ compiler against the ROCm headers; the
-device kernel source is embedded into it as text and compiled for gfx950 by
-hipRTC at run time.  ``precompile()`` runs that hipRTC step ahead of time
+The host library (C++, HIP runtime + hipRTC) is compiled with the host C++
+compiler against the ROCm headers, plus one HIP source (csrc/device.hip: the
+library's status words and its measurement probes) compiled for gfx950 by
+hipcc; the GEMM kernel source is embedded into the library as text and
+compiled for gfx950 by hipRTC at run time, once per shape.  ``precompile()`` runs that hipRTC step ahead of time
 (no GPU needed) so that the code objects of the standard workloads sit in the
 in-tree cache and the device source is known to compile for gfx950.
 """
@@ -22,6 +23,11 @@ LIB = os.path.join(PKG, "libdg.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HOST_SOURCES = ["api.cpp", "jit.cpp", "heuristics.cpp"]
+DEVICE_SOURCES = ["device.hip"]
+BUILD_DIR = os.path.join(PKG, "_build")
+# every HIP source is compiled for gfx950 with packed FP32 instructions off
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 DELIM = "DGSRC"
 
 
@@ -39,11 +45,21 @@ def write_kernel_include() -> None:
 
 def build_library(verbose: bool = False) -> str:
     write_kernel_include()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [os.path.join(ROCM, "bin", "hipcc"), *HIP_FLAGS, "-c",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
     cxx = os.environ.get("CXX", "g++")
     cmd = [cxx, "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROCM, "include"),
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in HOST_SOURCES],
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], *objs,
            "-L", os.path.join(ROCM, "lib"), "-lhiprtc", "-lamdhip64",
            "-Wl,-rpath," + os.path.join(ROCM, "lib"),
            "-o", LIB + ".tmp"]

@@ -35,6 +35,7 @@ struct LaunchParams {
     int M;
     int num_tiles;
     int kt;
+    unsigned int* status;
 };
 
 struct Workspace {
@@ -67,6 +68,7 @@ using PlanKey = std::tuple<int, int, int, int, int, int, int, int, std::string>;
 
 struct DeviceState {
     int num_cus = 0;
+    unsigned int* status = nullptr;   // the device's status words (device.hip)
     std::map<hipStream_t, Workspace> ws;
     std::map<PlanKey, Plan> plans;
 };
@@ -89,6 +91,10 @@ dg_status device_state(DeviceState** out, int* dev_out) {
         e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
         st.num_cus = n;
+    }
+    if (!st.status) {
+        dg_status s = status_words(&st.status);
+        if (s != DG_OK) return s;
     }
     *out = &st;
     *dev_out = dev;
@@ -260,6 +266,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         lp.M = p.rows;
         lp.num_tiles = (int)seg.items;
         lp.kt = p.kt;
+        lp.status = st->status;
         if (cfg.splitk > 1) {
             const int64_t mn = seg.items / cfg.splitk;
             Workspace* w = nullptr;
@@ -273,7 +280,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
             std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), seg.grid,
                          cfg.threads(), (long long)seg.items, cfg.lds_bytes());
         void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
-                        &lp.num_tiles, &lp.kt};
+                        &lp.num_tiles, &lp.kt, &lp.status};
         hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
         if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     }
@@ -409,6 +416,28 @@ dg_status dg_init(void) {
     if (s != DG_OK) return s;
     Workspace* w = nullptr;
     return ensure_workspace(*st, nullptr, 0, 0, &w);
+}
+
+dg_status dg_get_wait_giveups(unsigned int* count) {
+    if (!count) return set_error(DG_ERR_INVALID_ARG, "count must be non-NULL");
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* st = nullptr;
+    int dev = 0;
+    dg_status s = device_state(&st, &dev);
+    if (s != DG_OK) return s;
+    hipError_t e = hipMemcpy(count, st->status, sizeof(unsigned int), hipMemcpyDeviceToHost);
+    return e == hipSuccess ? DG_OK : hip_fail(e, "hipMemcpy(status words)");
+}
+
+dg_status dg_reset_wait_giveups(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState* st = nullptr;
+    int dev = 0;
+    dg_status s = device_state(&st, &dev);
+    if (s != DG_OK) return s;
+    const unsigned int zero = 0;
+    hipError_t e = hipMemcpy(st->status, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    return e == hipSuccess ? DG_OK : hip_fail(e, "hipMemcpy(status words)");
 }
 
 // Scale format encoded in `kind` by the DG_SCALE_* flags

@@ -93,6 +93,10 @@ dg_status get_function(const KernelConfig& c, void** function /* hipFunction_t *
 inline int k_grouped_pitch(int k) { return (k + 1023) / 1024 * 1024; }
 std::string cache_dir();
 
+// Device address of the library's status words on the current device
+// (device.hip); [0] counts bounded waits in the kernels that gave up.
+dg_status status_words(unsigned int** out);
+
 // Errors (api.cpp).
 dg_status set_error(dg_status s, const std::string& msg);
 bool env_flag(const char* name);

@@ -160,6 +160,7 @@ struct Params {
     int M;                 // rows of A (dense, contiguous) or M_max (masked)
     int num_tiles;         // total work items for this launch
     int kt;                // K-grouped: K rows of the operands (the groups' segments are cut there)
+    u32* status;           // library status words: [0] counts bounded waits that gave up
 };
 
 // Promotion scale of one MFMA result: one FP32 per (row, 128-row block of B),
@@ -387,13 +388,17 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
     // ---- split-K: publish the partial, the last arrival sums all in split order
     if constexpr (SPLITK > 1) {
         float* ws = p.ws + ((u64)tl.mn * SPLITK) * (BM * BN);
-        // Partials go out as agent-scope (write-through) stores and come back as
-        // agent-scope loads, so no cache maintenance is needed: an agent-scope
-        // release fence here (a write-back of the whole L2) measured 7-10 us per
-        // work item, longer than the K loop itself.  Once this wave's stores are
-        // acknowledged (vmcnt 0) they are visible at agent scope; the barrier
-        // orders every wave's stores before the arrival count.
-        // (sc1 = agent scope on the 16-byte buffer stores and loads below)
+        // The splits of a tile run on any of the 8 XCDs, each with its own L2, so
+        // a partial must be visible across L2s without a cache write-back (an
+        // agent-scope release fence writes back the whole L2: 7-10 us per work
+        // item, longer than the K loop).  The stores carry the agent-scope cache
+        // policy (sc1), which writes them through this XCD's L2 to the
+        // device-coherent side (Infinity Fabric, MALL, HBM); the last arrival
+        // reads them back with agent-scope loads, which do not take a line from
+        // its own L2.  This wave waits for its stores' acknowledgement (vmcnt 0)
+        // before the barrier, and the barrier comes before the agent-scope
+        // arrival atomic, so when the count shows every split arrived, every
+        // partial is at the coherence point.
         constexpr int CPOL_AGENT = 16;
         const __amdgpu_buffer_rsrc_t rs_ws =
             __builtin_amdgcn_make_buffer_rsrc(ws, 0, SPLITK * BM * BN * 4, 0x00020000);
@@ -584,8 +589,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THR
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles, int kt) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
+                      int num_tiles, int kt, u32* __restrict__ status) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt, status};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -1210,8 +1215,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THR
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles, int kt) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
+                      int num_tiles, int kt, u32* __restrict__ status) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt, status};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -1493,7 +1498,10 @@ constexpr int LAG = (SLOTS - 1) < (63 / PU) ? (SLOTS - 1) : (63 / PU);
 static_assert(SLOTS >= 2 && LAG >= 1, "ring too small");
 constexpr int V3_THREADS = NTHREADS + 64;
 constexpr int V3_MAX_DECL = V3_THREADS < 512 ? 512 : V3_THREADS;
-constexpr int SPIN_LIMIT = 1 << 20;               // about 30 ms of s_sleep 1 before giving up
+#ifndef DG_SPIN_LIMIT
+#define DG_SPIN_LIMIT (1 << 20)
+#endif
+constexpr int SPIN_LIMIT = DG_SPIN_LIMIT;         // about 30 ms of s_sleep 1 before giving up
 constexpr int A_BANK = 32768;
 constexpr int NBANK = (LDS_BYTES + A_BANK - 1) / A_BANK;
 #ifndef DG_FA_AHEAD
@@ -1502,13 +1510,22 @@ constexpr int NBANK = (LDS_BYTES + A_BANK - 1) / A_BANK;
 constexpr int FA_AHEAD = DG_FA_AHEAD < TM ? DG_FA_AHEAD : TM;
 
 // Bounded wait until *flag >= target (an LDS word written by another wave).
-__device__ __forceinline__ void wait_flag(u32* flag, u32 target) {
+// A wait that runs out is counted in the library's status word (one vector
+// atomic from the wave's first lane), so the host can tell that this call's D
+// is not to be trusted; the wave then goes on, so the grid always drains.
+__device__ __forceinline__ void wait_flag(u32* flag, u32 target, u32* status) {
+    bool landed = false;
     for (int i = 0; i < SPIN_LIMIT; ++i) {
         const u32 v = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (v >= target) break;
+        if (v >= target) {
+            landed = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (!landed && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::: "memory");   // later LDS reads stay after the wait
 }
 
@@ -1516,8 +1533,8 @@ extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, V3_MAX_
 dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
                       const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
                       const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
-                      int num_tiles, int kt) {
-    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt};
+                      int num_tiles, int kt, u32* __restrict__ status) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt, status};
     // Every argument in one round trip of scalar loads: otherwise the loop bound
     // is fetched first and the pointers only after it arrives (~0.5 us each).
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
@@ -1599,7 +1616,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             static_for<NKB>([&]<int KB>() __attribute__((always_inline)) {
                 constexpr int slot = KB % SLOTS;
                 // the slot's previous block (KB - SLOTS) has been read by every consumer
-                if constexpr (KB >= SLOTS) wait_flag(&freed[slot], (u32)(NWAVES * (KB / SLOTS)));
+                if constexpr (KB >= SLOTS) wait_flag(&freed[slot], (u32)(NWAVES * (KB / SLOTS)), p.status);
                 const u32 ka = __builtin_amdgcn_readfirstlane((u32)(tl.kb0 + KB) * KBLK);
 #pragma unroll
                 for (int i = 0; i < NA_INS; ++i) dma16(rs_a, voff_a[i], ka, st + A_OFF + slot * SLOT_A + i * 1024);
@@ -1684,7 +1701,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 tie(breg[IT][b][1]);
             }
             constexpr int slot = IT % SLOTS;
-            wait_flag(&ready[slot], (u32)(IT + 1));
+            wait_flag(&ready[slot], (u32)(IT + 1), p.status);
             if constexpr (IT + DEPTH < NKB) issue_b(tl.kb0 + IT + DEPTH, breg[IT + DEPTH]);
 
             constexpr int a_off = A_OFF + slot * SLOT_A;

@@ -84,6 +84,10 @@ def _load():
     lib.dg_precompile.restype = i32
     lib.dg_describe_config.argtypes = [i32] * 7 + [ctypes.c_char_p, i32]
     lib.dg_describe_config.restype = i32
+    lib.dg_get_wait_giveups.argtypes = [ctypes.POINTER(ctypes.c_uint)]
+    lib.dg_get_wait_giveups.restype = i32
+    lib.dg_reset_wait_giveups.argtypes = []
+    lib.dg_reset_wait_giveups.restype = i32
     return lib
 
 
@@ -248,6 +252,17 @@ def init() -> None:
 def precompile(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,
                num_cus: int = 0) -> None:
     _check(lib.dg_precompile(kind, rows, N, K, num_groups, int(has_c), num_cus))
+
+
+def get_wait_giveups() -> int:
+    """Bounded kernel waits on the current device that ran out (0 unless something went wrong)."""
+    c = ctypes.c_uint(0)
+    _check(lib.dg_get_wait_giveups(ctypes.byref(c)))
+    return int(c.value)
+
+
+def reset_wait_giveups() -> None:
+    _check(lib.dg_reset_wait_giveups())
 
 
 def describe_config(kind: int, rows: int, N: int, K: int, num_groups: int = 1, has_c: bool = False,

@@ -1,6 +1,7 @@
-"""The C ABI on the CPU: the library loads, exports every symbol include/dg.h
-declares, and rejects bad arguments before any HIP call."""
+"""The C ABI on the CPU: the library loads, exports every symbol that the
+headers under include/ declare, and rejects bad arguments before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 
@@ -15,8 +16,8 @@ HEADER = os.path.join(ROOT, "include", "dg.h")
 FAKE = 0x100000   # a 16-byte aligned address that is never dereferenced
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
 
@@ -25,8 +26,27 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert "dg_fp8_gemm_nt" in names and "dg_m_grouped_fp8_gemm_nt_masked" in names
     lib = ctypes.CDLL(dg.LIB_PATH)
-    for n in names:
-        assert hasattr(lib, n), f"{n} declared in dg.h but not exported"
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        for n in declared_functions(h):
+            assert hasattr(lib, n), f"{n} declared in {os.path.basename(h)} but not exported"
+
+
+def test_probe_arguments_rejected_before_launch():
+    """Probe entry points validate on the host (no GPU is touched for these)."""
+    lib = dg.lib
+    v = ctypes.c_void_p
+    lib.dg_probe_null.argtypes = [ctypes.c_int, v]
+    lib.dg_probe_spin.argtypes = [ctypes.c_int, v]
+    lib.dg_probe_stream_read.argtypes = [v, ctypes.c_size_t, v, ctypes.c_int, v]
+    lib.dg_probe_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, v, v]
+    assert lib.dg_probe_null(0, None) == -1
+    assert lib.dg_probe_spin(0, None) == -1
+    assert lib.dg_probe_spin(2000000, None) == -1
+    assert lib.dg_probe_stream_read(None, 1024, v(FAKE), 4, None) == -1
+    assert lib.dg_probe_stream_read(v(FAKE), 1000, v(FAKE), 4, None) == -3
+    assert lib.dg_probe_stream_read(v(FAKE + 4), 1024, v(FAKE), 4, None) == -3
+    assert lib.dg_probe_mfma_fp8(4, 0, v(FAKE), None) == -1
+    assert lib.dg_probe_mfma_fp8(4, 10, None, None) == -1
 
 
 def test_alignment_query():
