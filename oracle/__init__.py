@@ -66,6 +66,10 @@ def _declare(lib):
     lib.oracle_ue8m0_unpack_mn_major.argtypes = [p, c.c_int64, c.c_int, c.c_int64, p]
     lib.oracle_ue8m0_unpack_k_major.restype = None
     lib.oracle_ue8m0_unpack_k_major.argtypes = [p, c.c_int64, c.c_int, p]
+    lib.oracle_ue8m0_pairs_unpack_lhs.restype = None
+    lib.oracle_ue8m0_pairs_unpack_lhs.argtypes = [p, c.c_int64, c.c_int, c.c_int64, p]
+    lib.oracle_ue8m0_pairs_unpack_rhs.restype = None
+    lib.oracle_ue8m0_pairs_unpack_rhs.argtypes = [p, c.c_int64, c.c_int, c.c_int64, p]
     lib.oracle_e2m1_value.restype = c.c_double
     lib.oracle_e2m1_value.argtypes = [c.c_uint8]
     lib.oracle_fp8_fp4_gemm.restype = c.c_int
@@ -182,6 +186,33 @@ class Oracle:
         Kb = np.shape(A)[-1] // KBLOCK
         return self.m_grouped_masked(A, self.unpack_sfa_ue8m0(sfa, Kb), B, self.unpack_sfb_ue8m0(sfb, Kb),
                                      masked_m, C, rows, threads)
+
+    # ---------------------------------------------------------- UE8M0 pairs (int16, MN-major)
+    def unpack_sfa_ue8m0_pairs(self, pairs, Kb: int) -> np.ndarray:
+        """[..., ceil(Kb/2), M] int16 -> [..., Kb, M] fp32 (MN-major LHS scales)."""
+        pk = _c(pairs, np.int16)
+        *lead, P, M = pk.shape
+        assert P == (Kb + 1) // 2
+        n = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, Kb, M), dtype=np.float32)
+        self.lib.oracle_ue8m0_pairs_unpack_lhs(_ptr(pk), n, Kb, M, _ptr(out))
+        return out
+
+    def unpack_sfb_ue8m0_pairs(self, pairs, Kb: int) -> np.ndarray:
+        """[..., ceil(Kb/2), Nb] int16 (MN-major) -> [..., Nb, Kb] fp32 (the FP32 sfb layout)."""
+        pk = _c(pairs, np.int16)
+        *lead, P, Nb = pk.shape
+        assert P == (Kb + 1) // 2
+        n = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, Nb, Kb), dtype=np.float32)
+        self.lib.oracle_ue8m0_pairs_unpack_rhs(_ptr(pk), n, Kb, Nb, _ptr(out))
+        return out
+
+    def fp8_gemm_nt_ue8m0_pairs(self, A, sfa, B, sfb, C=None, rows=None, threads=0):
+        """Dense form with UE8M0 pairs: sfa int16 [ceil(Kb/2), M], sfb int16 [ceil(Kb/2), Nb]."""
+        Kb = np.shape(A)[-1] // KBLOCK
+        return self.fp8_gemm_nt(A, self.unpack_sfa_ue8m0_pairs(sfa, Kb), B, self.unpack_sfb_ue8m0_pairs(sfb, Kb), C,
+                                rows, threads)
 
     # ---------------------------------------------------------- FP8 x FP4
     def e2m1_value(self, nibble: int) -> float:

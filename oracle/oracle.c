@@ -127,6 +127,47 @@ void oracle_ue8m0_unpack_k_major(const int32_t *packed, int64_t n_rows, int Kb, 
 }
 
 /* ------------------------------------------------------------------ */
+/* UE8M0 scale pairs in 16-bit words (DeepGEMM-Ascend news article,    */
+/* "Cómo funciona": on Ascend every pair of UE8M0 scale factors along  */
+/* K is packed into one int16, and the values are stored MN-major).    */
+/* Readings: byte h (bits 8h..8h+7) of pair word p holds the scale of  */
+/* K block 2p + h (the earlier K block in the low byte, as in the      */
+/* four-to-a-word packing); a trailing high byte past the last K block */
+/* is ignored; MN-major for both operands: the LHS words are           */
+/* [ceil(Kb/2)][M] and the RHS words [ceil(Kb/2)][Nb], the index of    */
+/* the row (LHS) or of the 128-row block of B (RHS) running fastest.   */
+/* The block sizes stay 1x128 (LHS) and 128x128 (RHS).                 */
+/* ------------------------------------------------------------------ */
+static uint8_t ue8m0_pair_half(int16_t word, int h)
+{
+    return (uint8_t)(((uint16_t)word >> (h ? 8 : 0)) & 0xFFu);
+}
+
+/* LHS: pairs [n_mats][ceil(Kb/2)][M] -> out [n_mats][Kb][M] FP32 (the FP32 sfa layout). */
+void oracle_ue8m0_pairs_unpack_lhs(const int16_t *pairs, int64_t n_mats, int Kb, int64_t M, float *out)
+{
+    const int P = (Kb + 1) / 2;
+    for (int64_t g = 0; g < n_mats; ++g)
+        for (int kb = 0; kb < Kb; ++kb)
+            for (int64_t m = 0; m < M; ++m) {
+                int16_t w = pairs[(g * P + kb / 2) * M + m];
+                out[(g * Kb + kb) * M + m] = (float)oracle_ue8m0_value(ue8m0_pair_half(w, kb % 2));
+            }
+}
+
+/* RHS: pairs [n_mats][ceil(Kb/2)][Nb] -> out [n_mats][Nb][Kb] FP32 (the FP32 sfb layout). */
+void oracle_ue8m0_pairs_unpack_rhs(const int16_t *pairs, int64_t n_mats, int Kb, int64_t Nb, float *out)
+{
+    const int P = (Kb + 1) / 2;
+    for (int64_t g = 0; g < n_mats; ++g)
+        for (int64_t nb = 0; nb < Nb; ++nb)
+            for (int kb = 0; kb < Kb; ++kb) {
+                int16_t pw = pairs[(g * P + kb / 2) * Nb + nb];
+                out[(g * Nb + nb) * Kb + kb] = (float)oracle_ue8m0_value(ue8m0_pair_half(pw, kb & 1));
+            }
+}
+
+/* ------------------------------------------------------------------ */
 /* FP4 E2M1 (OCP MX FP4; the pages' FP8 x FP4 GEMM takes FP4 weights:  */
 /* DeepGEMM-Ascend hub page, precision table; README news 2026.04.16). */
 /* Bits: sign = bit 3, exponent = bits 2..1 (bias 1), mantissa bit 0.  */

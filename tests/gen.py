@@ -63,6 +63,35 @@ def pack_ue8m0(e: torch.Tensor) -> torch.Tensor:
         torch.where(w >= 2**31, w - 2**32, w).to(torch.int32)
 
 
+def pack_ue8m0_pairs(e: torch.Tensor) -> torch.Tensor:
+    """[..., Kb, cols] biased exponents (MN-major) -> [..., ceil(Kb/2), cols] int16:
+    byte h of pair word p is K block 2p + h; a missing last block is padded with 127."""
+    *lead, Kb, cols = e.shape
+    P = (Kb + 1) // 2
+    pad = torch.full((*lead, 2 * P - Kb, cols), 127, dtype=torch.int64)
+    b = torch.cat([e.to(torch.int64), pad], dim=-2).reshape(*lead, P, 2, cols)
+    w = b[..., 0, :] | (b[..., 1, :] << 8)
+    return torch.where(w >= 2**15, w - 2**16, w).to(torch.int16)
+
+
+def unpack_ue8m0_exponents(words: torch.Tensor, Kb: int) -> torch.Tensor:
+    """[..., ceil(Kb/4)] int32 words -> [..., Kb] biased exponents (byte j = K block 4w + j)."""
+    w = words.to(torch.int64) & 0xFFFFFFFF
+    b = torch.stack([(w >> (8 * j)) & 0xFF for j in range(4)], dim=-1)
+    return b.reshape(*words.shape[:-1], -1)[..., :Kb]
+
+
+def to_ue8m0_pairs(p: "Problem") -> "Problem":
+    """The same problem with its four-to-a-word UE8M0 scales repacked as int16 pairs
+    along K, both stored MN-major: sfa [.., ceil(Kb/2), M], sfb [.., ceil(Kb/2), Nb]."""
+    assert p.ue8m0 and not p.fp4, "a packed-UE8M0 FP8 problem"
+    Kb = p.K // KBLOCK
+    ea = unpack_ue8m0_exponents(p.sfa.transpose(-1, -2), Kb).transpose(-1, -2)   # [.., Kb, M]
+    eb = unpack_ue8m0_exponents(p.sfb, Kb).transpose(-1, -2)                      # [.., Kb, Nb]
+    return dataclasses.replace(p, sfa=pack_ue8m0_pairs(ea).contiguous(), sfb=pack_ue8m0_pairs(eb).contiguous(),
+                               ue8m0=False, ue8m0_pairs=True)
+
+
 def quantize_1x128(x: torch.Tensor, ue8m0: bool = False):
     """x [..., M, K] fp32 -> (codes u8 [..., M, K], sfa [..., K/128, M] fp32, or
     [..., ceil(K/512), M] int32 packed UE8M0)."""
@@ -146,6 +175,7 @@ class Problem:
     fp4: bool = False               # B holds E2M1 pairs [.., N, K/2], sfb [.., N, K/128] words (1x32 blocks)
     bf16: bool = False              # A and B are torch.bfloat16, no scales (sfa, sfb None)
     fp4a: bool = False              # A also E2M1 pairs [.., M, K/2] with sfa [.., M, K/128] words (FP4 x FP4)
+    ue8m0_pairs: bool = False       # sfa/sfb are UE8M0 pairs in int16, MN-major ([.., ceil(Kb/2), M|Nb])
 
     @property
     def M(self):
@@ -360,7 +390,9 @@ def workload_seed(cfg) -> int:
     return 1000 + (1 if cfg == "1c" else int(cfg))
 
 
-def make_workload(cfg, ue8m0=False, fp4=False, fp4x4=False) -> Problem:
+def make_workload(cfg, ue8m0=False, fp4=False, fp4x4=False, ue8m0_pairs=False) -> Problem:
+    if ue8m0_pairs:
+        return to_ue8m0_pairs(make_workload(cfg, ue8m0=True))
     c = WORKLOADS[cfg]
     seed = workload_seed(cfg)
     kw = dict(ue8m0=ue8m0, fp4=fp4, fp4x4=fp4x4)

@@ -332,6 +332,66 @@ def test_ue8m0_all_ones_closed_form(oracle):
     assert np.array_equal(d, want)
 
 
+# ------------------------------------------------------------------ UE8M0 pairs in int16 (MN-major)
+def _hex16(rows):
+    return np.array([[int(h, 16) for h in r] for r in rows], dtype=np.uint16).view(np.int16)
+
+
+def test_ue8m0_pairs_worked_example(oracle):
+    """A hand-written example of the pair packing (tests/golden/ue8m0_pairs_layout.json):
+    byte h of word p = K block 2p + h, MN-major for both operands, trailing byte ignored."""
+    ex = json.load(open(os.path.join(GOLDEN, "ue8m0_pairs_layout.json")))
+    Kb = ex["Kb"]
+    sfa = oracle.unpack_sfa_ue8m0_pairs(_hex16(ex["lhs_pairs_hex"]), Kb)        # [Kb][M]
+    assert np.array_equal(sfa, np.ldexp(1.0, np.array(ex["lhs_scales_log2"])).astype(np.float32))
+    sfb = oracle.unpack_sfb_ue8m0_pairs(_hex16(ex["rhs_pairs_hex"]), Kb)        # [Nb][Kb]
+    assert np.array_equal(sfb, np.ldexp(1.0, np.array(ex["rhs_scales_log2"])).astype(np.float32))
+
+
+def test_ue8m0_pairs_equal_quads(oracle):
+    """The same exponents packed two to an int16 (MN-major) and four to an int32 unpack to
+    the same FP32 scales, and the GEMMs agree bit for bit (odd Kb, grouped lead dims)."""
+    g = torch.Generator().manual_seed(12)
+    Kb, M, Nb = 7, 5, 3
+    ea = torch.randint(100, 150, (2, Kb, M), generator=g)
+    eb = torch.randint(100, 150, (2, Nb, Kb), generator=g)
+    quad_a = gen.pack_ue8m0(ea.transpose(-1, -2)).transpose(-1, -2).contiguous()   # [2][W][M]
+    quad_b = gen.pack_ue8m0(eb)                                                     # [2][Nb][W]
+    pair_a = gen.pack_ue8m0_pairs(ea)                                               # [2][P][M]
+    pair_b = gen.pack_ue8m0_pairs(eb.transpose(-1, -2))                             # [2][P][Nb]
+    assert tuple(pair_a.shape) == (2, 4, M) and tuple(pair_b.shape) == (2, 4, Nb)
+    assert np.array_equal(oracle.unpack_sfa_ue8m0_pairs(pair_a.numpy(), Kb),
+                          oracle.unpack_sfa_ue8m0(quad_a.numpy(), Kb))
+    assert np.array_equal(oracle.unpack_sfb_ue8m0_pairs(pair_b.numpy(), Kb),
+                          oracle.unpack_sfb_ue8m0(quad_b.numpy(), Kb))
+    p = gen.make_dense(9, 300, 7 * 128, seed=13, with_c=True, ue8m0=True)
+    q = gen.to_ue8m0_pairs(p)
+    d = gen.to_numpy(p)
+    want = oracle.fp8_gemm_nt_ue8m0(d["A"], d["sfa"], d["B"], d["sfb"], d["C"])
+    got = oracle.fp8_gemm_nt_ue8m0_pairs(d["A"], q.sfa.numpy(), d["B"], q.sfb.numpy(), d["C"])
+    assert np.array_equal(got, want)
+
+
+def test_ue8m0_pairs_all_ones_closed_form(oracle):
+    """All-ones codes with pair-packed scales: D = 128 * sum_kb 2^(ea-127) 2^(eb-127) + C, exactly."""
+    g = torch.Generator().manual_seed(14)
+    M, N, K = 6, 260, 640
+    Kb, Nb = K // 128, (N + 127) // 128
+    ea = torch.randint(118, 134, (Kb, M), generator=g)
+    eb = torch.randint(121, 132, (Kb, Nb), generator=g)            # MN-major: [Kb][Nb]
+    A = torch.full((M, K), gen.E4M3_ONE, dtype=torch.uint8)
+    B = torch.full((N, K), gen.E4M3_ONE, dtype=torch.uint8)
+    C = torch.randn(M, N, generator=g)
+    d = oracle.fp8_gemm_nt_ue8m0_pairs(A.numpy(), gen.pack_ue8m0_pairs(ea).numpy(), B.numpy(),
+                                       gen.pack_ue8m0_pairs(eb).numpy(), C.numpy())
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            want[m, n] = 128.0 * sum(2.0 ** (int(ea[kb, m]) - 127) * 2.0 ** (int(eb[kb, n // 128]) - 127)
+                                     for kb in range(Kb)) + float(C[m, n])
+    assert np.array_equal(d, want)
+
+
 def test_ue8m0_generator_scales(oracle):
     """The UE8M0 quantiser picks the least power of two >= amax/448 and keeps codes in range."""
     p = gen.make_dense(33, 260, 768, seed=41, ue8m0=True)

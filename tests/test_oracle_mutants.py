@@ -69,6 +69,13 @@ MUTANTS = [
     ("fp4x4_last_block_dropped", "for (int j = 0; j < 4; ++j) {\n                double blk = 0.0;",
      "for (int j = 0; j < 3; ++j) {\n                double blk = 0.0;"),
     ("bf16_c_ignored", "out[n] = acc + (p->C ? (double)p->C[r * (int64_t)p->N + n] : 0.0);", "out[n] = acc;"),
+    ("ue8m0_pairs_bytes_swapped", "return (uint8_t)(((uint16_t)word >> (h ? 8 : 0)) & 0xFFu);",
+     "return (uint8_t)(((uint16_t)word >> (h ? 0 : 8)) & 0xFFu);"),
+    ("ue8m0_pairs_lhs_k_major", "int16_t w = pairs[(g * P + kb / 2) * M + m];",
+     "int16_t w = pairs[(g * M + m) * P + kb / 2];"),
+    ("ue8m0_pairs_rhs_k_major", "int16_t pw = pairs[(g * P + kb / 2) * Nb + nb];",
+     "int16_t pw = pairs[(g * Nb + nb) * P + kb / 2];"),
+    ("ue8m0_pairs_rhs_low_byte_only", "ue8m0_pair_half(pw, kb & 1)", "ue8m0_pair_half(pw, 0)"),
     ("bf16_masked_group0", "        const uint16_t *b = p->B + g * (int64_t)p->N * p->K;",
      "        const uint16_t *b = p->B;"),
 ]
@@ -90,6 +97,8 @@ def _pin_calls(o):
               pins.test_masked_rows_and_groups, pins.test_masked_negative_and_subset,
               pins.test_ue8m0_points_from_format, pins.test_ue8m0_packing_byte_order_and_layouts,
               pins.test_ue8m0_all_ones_closed_form, pins.test_e2m1_points_from_format,
+              pins.test_ue8m0_pairs_worked_example, pins.test_ue8m0_pairs_equal_quads,
+              pins.test_ue8m0_pairs_all_ones_closed_form,
               pins.test_fp8_fp4_nibble_order_and_block_scales, pins.test_fp8_fp4_grouped_equal_dense,
               pins.test_k_grouped_equals_dense_nt_on_transposed_operands,
               pins.test_k_grouped_operand_swap_transposes, pins.test_k_grouped_empty_group_and_closed_form):
