@@ -161,7 +161,7 @@ void oracle_ue8m0_pairs_unpack_rhs(const int16_t *pairs, int64_t n_mats, int Kb,
     const int P = (Kb + 1) / 2;
     for (int64_t g = 0; g < n_mats; ++g)
         for (int64_t nb = 0; nb < Nb; ++nb)
-            for (int kb = 0; kb < Kb; ++kb) {
+            for (int kb = 0; Kb > kb; ++kb) {
                 int16_t pw = pairs[(g * P + kb / 2) * Nb + nb];
                 out[(g * Nb + nb) * Kb + kb] = (float)oracle_ue8m0_value(ue8m0_pair_half(pw, kb & 1));
             }
