@@ -168,6 +168,32 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *A, const int32_t *sf
                                                 int num_groups, void *stream);
 
 /*
+ * The same three forms with UE8M0 scale factors packed in pairs along K into
+ * 16-bit words, stored MN-major (DeepGEMM-Ascend news article, the paragraph
+ * on the scale-factor format: on Ascend each pair of UE8M0 factors along K is
+ * packed into one int16, values in MN-major order).  Readings: byte h (bits
+ * 8h..8h+7) of pair word p holds the scale of K block 2p + h; a trailing byte
+ * past the last K block is ignored; both operands are MN-major.  With
+ * P = ceil(K/256):
+ *   sfa int16 [P][M] (masked: [G][P][M_max]): row m fastest, like the FP32 sfa;
+ *   sfb int16 [P][Nb] (grouped: [G][P][Nb]): the 128-row block index of B fastest.
+ * The scale arrays must be 2-byte aligned.  Block sizes (1x128, 128x128),
+ * A, B, C, D, groups, masks, ownership and errors as for the entry points
+ * above; the matrix core applies the scales (no promotion step), and
+ * D = C + sum_kb 2^(ea-127) 2^(eb-127) P_kb, rounded once to BF16.
+ */
+dg_status dg_fp8_gemm_nt_ue8m0_i16(const void *A, const int16_t *sfa, const void *B, const int16_t *sfb,
+                                   const float *C, void *D, int M, int N, int K, void *stream);
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16(const void *A, const int16_t *sfa, const void *B,
+                                                        const int16_t *sfb, const int32_t *m_indices,
+                                                        const float *C, void *D, int M, int N, int K,
+                                                        int num_groups, void *stream);
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16(const void *A, const int16_t *sfa, const void *B,
+                                                    const int16_t *sfb, const int32_t *masked_m,
+                                                    const float *C, void *D, int M_max, int N, int K,
+                                                    int num_groups, void *stream);
+
+/*
  * FP8 x FP4: the same three forms with FP4 weights (DeepGEMM-Ascend hub page,
  * precision table "FP8 x FP4"; DeepGEMM README, news of 2026.04.16: an
  * FP8 x FP4 GEMM with FP4 weights and UE8M0 scale factors).
@@ -315,13 +341,15 @@ dg_status dg_init(void);
 #define DG_SCALE_FP8_FP4 8
 #define DG_BF16 16           /* BF16 x BF16 without scales (K in elements) */
 #define DG_SCALE_FP4_FP4 32  /* FP4 x FP4 */
+#define DG_SCALE_UE8M0_I16 64   /* UE8M0 pairs in 16-bit words, MN-major */
 
 /*
  * Compile (or load from the cache) the kernel(s) that a later call with these
  * arguments would use, without launching anything.  kind: 0 dense,
  * 1 contiguous, 2 masked, 3 K-grouped (K = the K rows; the FP32 scale form
- * only) (| DG_SCALE_UE8M0 for packed UE8M0 scales,
- * | DG_SCALE_FP8_FP4 for FP8 x FP4); has_c:
+ * only) (| DG_SCALE_UE8M0 for packed UE8M0 scales, | DG_SCALE_UE8M0_I16 for
+ * UE8M0 pairs in 16-bit words, | DG_SCALE_FP8_FP4 for FP8 x FP4, | DG_BF16,
+ * | DG_SCALE_FP4_FP4); has_c:
  * 0/1; rows = M (dense/contiguous) or M_max.
  * Needs no GPU: the code object is built for gfx950 and stored in the cache
  * directory (DG_CACHE_DIR, else <library dir>/jit_cache).

@@ -4,6 +4,8 @@ the NN/TN/TT storage layouts, the K-grouped TN form and an unscaled BF16 GEMM,
 as a C-ABI library (libdg.so) with a thin Python binding.  See include/dg.h
 for the contract."""
 from .dg import get_wait_giveups, reset_wait_giveups  # noqa: F401
+from .dg import (SCALE_UE8M0_I16, dg_fp8_gemm_nt_ue8m0_i16, dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16,  # noqa: F401
+                 dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16)
 from .dg import (DGError, describe_config, dg_fp8_gemm_nt, dg_m_grouped_fp8_gemm_nt_contiguous,  # noqa: F401
                  dg_m_grouped_fp8_gemm_nt_masked, fp8_gemm_nt, get_mk_alignment_for_contiguous_layout,
                  get_num_cus, init, m_grouped_fp8_gemm_nt_contiguous, m_grouped_fp8_gemm_nt_masked,

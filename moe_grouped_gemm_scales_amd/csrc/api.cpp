@@ -156,14 +156,16 @@ dg_status ensure_kmajor(DeviceState& st, hipStream_t stream, size_t need, uint8_
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 dg_status check_common(const void* A, const void* sfa, const void* B, const void* sfb, const float* C,
-                       const void* D, int rows, int N, int K) {
+                       const void* D, int rows, int N, int K, size_t sf_align = 4) {
     if (!A || !sfa || !B || !sfb || !D) return set_error(DG_ERR_INVALID_ARG, "A, sfa, B, sfb and D must be non-NULL");
     if (rows < 0 || N <= 0 || K <= 0)
         return set_error(DG_ERR_INVALID_ARG, "sizes must be positive (M may be 0)");
     if (K % 128 != 0) return set_error(DG_ERR_UNSUPPORTED, "K must be a multiple of 128 (the scale block)");
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
         return set_error(DG_ERR_ALIGNMENT, "A, B, C and D must be 16-byte aligned");
-    if (!aligned(sfa, 4) || !aligned(sfb, 4)) return set_error(DG_ERR_ALIGNMENT, "scales must be 4-byte aligned");
+    if (!aligned(sfa, sf_align) || !aligned(sfb, sf_align))
+        return set_error(DG_ERR_ALIGNMENT, sf_align == 4 ? "scales must be 4-byte aligned"
+                                                         : "16-bit scale words must be 2-byte aligned");
     // per-tile buffer offsets are 32-bit: one scale plane of A and one 256-row slab must fit
     if ((uint64_t)(K / 128) * (uint64_t)rows * 4u >= (1ull << 32) || (uint64_t)K * 256u >= (1ull << 32))
         return set_error(DG_ERR_UNSUPPORTED, "sizes exceed 32-bit buffer offsets");
@@ -310,7 +312,7 @@ namespace {
 // FP4 with E2M1 B; the scale pointers are only passed through to the kernel).
 dg_status dense(const void* A, const void* sfa, const void* B, const void* sfb, const float* C, void* D, int M,
                 int N, int K, int sf, void* stream, int a_k_outer = 0, int b_k_outer = 0) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K, sf == 5 ? 2 : 4);
     if (s != DG_OK) return s;
     if (M == 0) return DG_OK;
     Problem p{kDense, M, N, K, 1, C ? 1 : 0, sf};
@@ -322,7 +324,7 @@ dg_status dense(const void* A, const void* sfa, const void* B, const void* sfb, 
 dg_status contiguous(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* m_indices,
                      const float* C, void* D, int M, int N, int K, int num_groups, int sf, void* stream,
                      int b_k_outer = 0) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K, sf == 5 ? 2 : 4);
     if (s != DG_OK) return s;
     if (!m_indices) return set_error(DG_ERR_INVALID_ARG, "m_indices must be non-NULL");
     if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
@@ -337,7 +339,7 @@ dg_status contiguous(const void* A, const void* sfa, const void* B, const void* 
 
 dg_status masked(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* masked_m,
                  const float* C, void* D, int M_max, int N, int K, int num_groups, int sf, void* stream) {
-    dg_status s = check_common(A, sfa, B, sfb, C, D, M_max, N, K);
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M_max, N, K, sf == 5 ? 2 : 4);
     if (s != DG_OK) return s;
     if (!masked_m) return set_error(DG_ERR_INVALID_ARG, "masked_m must be non-NULL");
     if (num_groups <= 0) return set_error(DG_ERR_INVALID_ARG, "num_groups must be positive");
@@ -442,9 +444,9 @@ dg_status dg_reset_wait_giveups(void) {
 
 // Scale format encoded in `kind` by the DG_SCALE_* flags
 int scale_format(int* kind) {
-    const int sf = (*kind & DG_SCALE_FP4_FP4) ? 4 : (*kind & DG_BF16) ? 3 : (*kind & DG_SCALE_FP8_FP4) ? 2
-                 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
-    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4 | DG_BF16 | DG_SCALE_FP4_FP4);
+    const int sf = (*kind & DG_SCALE_UE8M0_I16) ? 5 : (*kind & DG_SCALE_FP4_FP4) ? 4 : (*kind & DG_BF16) ? 3
+                 : (*kind & DG_SCALE_FP8_FP4) ? 2 : (*kind & DG_SCALE_UE8M0) ? 1 : 0;
+    *kind &= ~(DG_SCALE_UE8M0 | DG_SCALE_FP8_FP4 | DG_BF16 | DG_SCALE_FP4_FP4 | DG_SCALE_UE8M0_I16);
     return sf;
 }
 
@@ -522,6 +524,23 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const int32_t* sf
                                                 const int32_t* sfb, const int32_t* masked_m, const float* C,
                                                 void* D, int M_max, int N, int K, int num_groups, void* stream) {
     return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 1, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0_i16(const void* A, const int16_t* sfa, const void* B, const int16_t* sfb,
+                                   const float* C, void* D, int M, int N, int K, void* stream) {
+    return dense(A, sfa, B, sfb, C, D, M, N, K, 5, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16(const void* A, const int16_t* sfa, const void* B,
+                                                        const int16_t* sfb, const int32_t* m_indices, const float* C,
+                                                        void* D, int M, int N, int K, int num_groups, void* stream) {
+    return contiguous(A, sfa, B, sfb, m_indices, C, D, M, N, K, num_groups, 5, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16(const void* A, const int16_t* sfa, const void* B,
+                                                    const int16_t* sfb, const int32_t* masked_m, const float* C,
+                                                    void* D, int M_max, int N, int K, int num_groups, void* stream) {
+    return masked(A, sfa, B, sfb, masked_m, C, D, M_max, N, K, num_groups, 5, stream);
 }
 
 dg_status dg_fp8_fp4_gemm_nt(const void* A, const int32_t* sfa, const void* B, const int32_t* sfb, const float* C,

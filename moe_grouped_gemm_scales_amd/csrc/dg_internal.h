@@ -31,7 +31,8 @@ struct KernelConfig {
     int n = 0, k = 0, g = 1;
     int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0),
                                // 3 BF16 x BF16 without scales (k is then the row length in bytes),
-                               // 4 FP4 x FP4 (E2M1 A and B, 1x32 UE8M0 per row)
+                               // 4 FP4 x FP4 (E2M1 A and B, 1x32 UE8M0 per row),
+                               // 5 UE8M0 pairs in 16-bit words, MN-major (A and B)
     int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
                                // launch two column ranges with different tile widths
 
@@ -68,7 +69,7 @@ struct Problem {
     int rows;      // M (dense, contiguous) or M_max (masked)
     int n, k, g;
     int has_c;
-    int sf = 0;    // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4
+    int sf = 0;    // scale format: as KernelConfig::sf
     int kt = 0;    // K-grouped: K rows of the operands (n, k above: N and the padded pitch)
     int a_k_outer = 0, b_k_outer = 0;   // A stored [K][rows] (T), B stored [(G)][K][N] (N)
 };

@@ -150,7 +150,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.bm % (8 / c.kstep) || c.bn % (8 / c.kstep) || c.stages < 2) return false;
     if (dma_per_wave(c) * (c.stages - 1) > 63) return false;   // vmcnt field
     // more than 32 sub-tiles per wave: only 4-wave groups without promotion (accumulators in AGPRs)
-    const bool agpr_acc = (c.sf == 1 || c.sf == 3) && c.wm * c.wn == 4;
+    const bool agpr_acc = (c.sf == 1 || c.sf == 3 || c.sf == 5) && c.wm * c.wn == 4;
     if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > (agpr_acc ? 64 : 32)) return false;
     if ((p.k / 128) % (c.splitk * c.kstep)) return false;
     return true;

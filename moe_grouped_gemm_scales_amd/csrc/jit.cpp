@@ -189,6 +189,7 @@ std::string KernelConfig::key() const {
     if (sf == 2) s << "_f8f4";
     if (sf == 3) s << "_bf16";
     if (sf == 4) s << "_f4f4";
+    if (sf == 5) s << "_e8m0x2";
     if (ne > 0) s << "_cols" << nb << "-" << ne;
     return s.str();
 }

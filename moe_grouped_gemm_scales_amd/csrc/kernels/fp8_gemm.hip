@@ -82,6 +82,11 @@ typedef u16 v4u16 __attribute__((ext_vector_type(4)));
 // 4 = FP4 x FP4 (DeepGEMM-Ascend hub page, precision table): A as well as B
 // in E2M1, [rows][K/2], each row with one UE8M0 scale per 1x32 block, sfa
 // [rows][K/128] words (masked [G][M_max][K/128]) laid out like sfb of 2.
+// 5 = UE8M0 scale pairs (DeepGEMM-Ascend news article, scale-factor format:
+// every pair of UE8M0 scales along K in one int16, stored MN-major): byte h
+// of pair word p is K block 2p + h; sfa int16 [ceil(K/256)][rows] (masked
+// [G][.][M_max]), sfb int16 [ceil(K/256)][ceil(N/128)] (grouped [G][.][.]).
+// Otherwise as 1: the MFMA applies the scales.
 #ifndef DG_SF
 #define DG_SF 0
 #endif
@@ -113,12 +118,14 @@ constexpr int NBLKS = (N + KBLK - 1) / KBLK;
 constexpr int N_BEGIN = DG_NB, N_END = DG_NE;  // columns [N_BEGIN, N_END) of D; N is the row pitch
 static_assert(0 <= N_BEGIN && N_BEGIN < N_END && N_END <= N && N_BEGIN % 16 == 0, "column range");
 constexpr int NUM_NT = (N_END - N_BEGIN + BN - 1) / BN;     // n tiles
-constexpr bool SF_E8 = DG_SF == 1 || DG_SF == 2 || DG_SF == 4;
+constexpr bool SF_E8 = DG_SF == 1 || DG_SF == 2 || DG_SF == 4 || DG_SF == 5;
+constexpr bool PAIRS = DG_SF == 5;            // UE8M0 pairs in 16-bit words, MN-major (A and B)
 constexpr bool FP4B = DG_SF == 2 || DG_SF == 4;   // B in E2M1 with per-row 1x32 UE8M0 scales
 constexpr bool FP4A = DG_SF == 4;             // A in E2M1 with per-row 1x32 UE8M0 scales too
 constexpr bool BF16 = DG_SF == 3;             // BF16 operands, no scales
-constexpr int KW = (KBLKS + 3) / 4;           // packed UE8M0 words per row of scales
+constexpr int KW = PAIRS ? (KBLKS + 1) / 2 : (KBLKS + 3) / 4;   // packed UE8M0 words per row of scales
 constexpr int SF_KB = SF_E8 ? KW : KBLKS;     // scale entries (floats or words) along K
+constexpr int SF_BYTES = PAIRS ? 2 : 4;       // bytes of one scale entry (float, 32-bit or 16-bit word)
 constexpr int KB_B = FP4B ? K / 2 : K;        // bytes of one row of B
 constexpr int KB_A = FP4A ? K / 2 : K;        // ... of A
 // a wave's n range [n0 + wn*WAVE_N, +WAVE_N) never crosses a 128 boundary when
@@ -144,7 +151,7 @@ static_assert(STAGES >= 2, "at least double buffering");
 // Exception: with no promotion step (UE8M0 scales applied by the MFMA, or BF16)
 // a 4-wave workgroup with more than 32 sub-tiles per wave keeps its accumulators
 // in AGPRs, which the MFMAs read and write directly; it declares its own size.
-constexpr bool ACC_IN_AGPR = (DG_SF == 1 || DG_SF == 3) && NTHREADS == 256 && TM * TN > 32;
+constexpr bool ACC_IN_AGPR = (DG_SF == 1 || DG_SF == 3 || DG_SF == 5) && NTHREADS == 256 && TM * TN > 32;
 constexpr int MAX_THREADS_DECL = (NTHREADS < 512 && !ACC_IN_AGPR) ? 512 : NTHREADS;
 
 struct Params {
@@ -198,6 +205,16 @@ __device__ __forceinline__ void dma16(v4i rsrc, u32 voff, u32 soff, u32 lds) {
 __device__ __forceinline__ void dma4(v4i rsrc, u32 voff, u32 soff, u32 lds) {
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+// Two bytes per lane, zero-extended into the lane's 4-byte LDS word (lds + 4*l).
+__device__ __forceinline__ void dma2(v4i rsrc, u32 voff, u32 soff, u32 lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_ushort %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+// The scale DMA of a stage: 32-bit entries, or 16-bit UE8M0 pairs
+__device__ __forceinline__ void dma_sf(v4i rsrc, u32 voff, u32 soff, u32 lds) {
+    if constexpr (PAIRS) dma2(rsrc, voff, soff, lds);
+    else dma4(rsrc, voff, soff, lds);
 }
 template <int CNT>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -637,7 +654,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         int a_rows_total;        // rows of this A (for sfa stride)
         if constexpr (kKind == 2) {
             a_base = p.A + ((u64)tl.g * p.M + tl.m0) * KB_A;
-            sfa_base = p.sfa + (u64)tl.g * (FP4A ? KBLKS : SF_KB) * p.M;
+            sfa_base = (const float*)((const u8*)p.sfa +
+                                      (u64)tl.g * (FP4A ? KBLKS : SF_KB) * p.M * (FP4A ? 4u : (u32)SF_BYTES));
         } else {
             a_base = p.A + (u64)tl.m0 * KB_A;
             sfa_base = p.sfa;
@@ -647,10 +665,11 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         const u8* b_base = p.B + ((u64)(KG ? 0 : tl.g) * N + tl.n0) * KB_B;
         const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * KB_A);
         const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
-        const v4i rs_s = make_rsrc(sfa_base, (u32)(FP4A ? KBLKS : SF_KB) * a_rows_total * 4u);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)(FP4A ? KBLKS : SF_KB) * a_rows_total * (FP4A ? 4u : (u32)SF_BYTES));
         const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
                          : KG ? make_rsrc(p.sfb, (u32)(p.kt / KBLK) * N * 4u)
-                              : make_rsrc(p.sfb + (u64)tl.g * NBLKS * SF_KB, (u32)NBLKS * SF_KB * 4u);
+                              : make_rsrc((const u8*)p.sfb + (u64)tl.g * NBLKS * SF_KB * SF_BYTES,
+                                          (u32)NBLKS * SF_KB * (u32)SF_BYTES);
         const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
 
         // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
@@ -685,7 +704,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
             const int mm = m < a_rows_total ? m : a_rows_total - 1;
             // FP4 A: word [m][kb] (row-major); otherwise sfa [kb][m] (MN-major)
-            voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * 4u + (u32)h * a_rows_total * 4u;
+            voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * SF_BYTES + (u32)h * a_rows_total * SF_BYTES;
         }
         u32 voff_t[IT > 0 ? IT : 1];
 #pragma unroll
@@ -699,14 +718,17 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 voff_t[j] = (u32)min(tl.n0 + 64 * h + lane, N - 1) * 4u;
             } else {
                 const int nb = min(nb_t0 + lane, NBLKS - 1);
-                voff_t[j] = (u32)nb * SF_KB * 4u + (u32)h * 4u;
+                // UE8M0 pairs: MN-major [K/256][NBLKS]; otherwise K-contiguous [NBLKS][SF_KB]
+                voff_t[j] = PAIRS ? (u32)nb * 2u : (u32)nb * SF_KB * 4u + (u32)h * 4u;
             }
         }
 
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
         // (kb: first K block of the stage)
         // index along K of the scales of K block kb (a word holds four UE8M0 scales)
-        auto sf_row = [](int kb) { return SF_E8 ? kb >> 2 : kb; };
+        auto sf_row = [](int kb) { return PAIRS ? kb >> 1 : SF_E8 ? kb >> 2 : kb; };
+        // scalar offset of K block kb's B scales: a row of the MN-major pairs, or a K-contiguous entry
+        auto sfb_soff = [](int kb) { return PAIRS ? (u32)(kb >> 1) * NBLKS * 2u : (u32)(SF_E8 ? kb >> 2 : kb) * 4u; };
         // live = false: a placeholder load whose buffer size is zero, so it moves
         // no data (every lane is out of range) but keeps the vmcnt count fixed.
         auto issue_one = [&](int j, int kb, int stage, bool live = true) {
@@ -733,14 +755,15 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                           __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
-                dma4(lim(rs_s), voff_s[j - IA - IB],
-                     __builtin_amdgcn_readfirstlane(FP4A ? (u32)kb * 4u : (u32)sf_row(kb) * a_rows_total * 4u),
-                     st + S_OFF + i * 256);
+                dma_sf(lim(rs_s), voff_s[j - IA - IB],
+                       __builtin_amdgcn_readfirstlane(FP4A ? (u32)kb * 4u
+                                                           : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES),
+                       st + S_OFF + i * 256);
             } else {
                 const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
-                dma4(lim(rs_t), voff_t[j - IA - IB - IS],
-                     __builtin_amdgcn_readfirstlane((u32)(FP4B ? kb : KG ? kb * N : sf_row(kb)) * 4u),
-                     st + T_OFF + h * 256);
+                dma_sf(lim(rs_t), voff_t[j - IA - IB - IS],
+                       __builtin_amdgcn_readfirstlane(FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb)),
+                       st + T_OFF + h * 256);
             }
         };
         auto issue_stage = [&](int kb, int stage, bool live = true) {
@@ -763,16 +786,17 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                       __builtin_amdgcn_readfirstlane((u32)kb_b * KBLK), sb_base + i * 1024);
             } else if (j < IB + IT) {
                 const int h = min(wave + (j - IB) * NWAVES, NT_INS - 1);
-                dma4(lim(rs_t, live_b), voff_t[j - IB], __builtin_amdgcn_readfirstlane((u32)sf_row(kb_b) * 4u),
-                     sb_base + BN * ROWB_B + h * 256);
+                dma_sf(lim(rs_t, live_b), voff_t[j - IB], __builtin_amdgcn_readfirstlane(sfb_soff(kb_b)),
+                       sb_base + BN * ROWB_B + h * 256);
             } else if (j < IB + IT + IA) {
                 const int i = min(wave + (j - IB - IT) * NWAVES, NA_INS - 1);
                 dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                       __builtin_amdgcn_readfirstlane((u32)kb_a * KBLK), sa_base + i * 1024);
             } else {
                 const int i = min(wave + (j - IB - IT - IA) * NWAVES, NS_INS - 1);
-                dma4(lim(rs_s, live_a), voff_s[j - IB - IT - IA],
-                     __builtin_amdgcn_readfirstlane((u32)sf_row(kb_a) * a_rows_total * 4u), sa_base + BM * ROWB_A + i * 256);
+                dma_sf(lim(rs_s, live_a), voff_s[j - IB - IT - IA],
+                       __builtin_amdgcn_readfirstlane((u32)sf_row(kb_a) * a_rows_total * (u32)SF_BYTES),
+                       sa_base + BM * ROWB_A + i * 256);
             }
         };
 
@@ -940,7 +964,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
                 int ea[TM], eb[TN];
                 if constexpr (SF_E8) {
-                    const u32 sh = 8u * (u32)((tl.kb0 + it) & 3);
+                    const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
 #pragma unroll
                     for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> (FP4A ? sh_q : sh));
 #pragma unroll
@@ -1093,7 +1117,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
                 int ea[TM], eb[TN];
                 if constexpr (SF_E8) {
-                    const u32 sh = 8u * (u32)((tl.kb0 + it) & 3);
+                    const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
 #pragma unroll
                     for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
 #pragma unroll

@@ -84,6 +84,12 @@ def _load():
     lib.dg_precompile.restype = i32
     lib.dg_describe_config.argtypes = [i32] * 7 + [ctypes.c_char_p, i32]
     lib.dg_describe_config.restype = i32
+    lib.dg_fp8_gemm_nt_ue8m0_i16.argtypes = lib.dg_fp8_gemm_nt.argtypes
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16.argtypes = lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+    lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+    for f in (lib.dg_fp8_gemm_nt_ue8m0_i16, lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16,
+              lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16):
+        f.restype = i32
     lib.dg_get_wait_giveups.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     lib.dg_get_wait_giveups.restype = i32
     lib.dg_reset_wait_giveups.argtypes = []
@@ -294,6 +300,78 @@ def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(A, sfa, B, sfb, masked_m, C, D, stream
     if sfa.dtype != torch.int32:
         raise TypeError("dg_m_grouped_fp8_gemm_nt_masked_ue8m0 takes packed UE8M0 int32 scales")
     return dg_m_grouped_fp8_gemm_nt_masked(A, sfa, B, sfb, masked_m, C, D, stream)
+
+
+# ---------------------------------------------------------------- UE8M0 pairs in int16 (MN-major)
+SCALE_UE8M0_I16 = 64   # DG_SCALE_UE8M0_I16: OR into `kind` of precompile / describe_config
+
+
+def _i16(t: torch.Tensor, name: str, shape):
+    if t.dtype != torch.int16:
+        raise TypeError(f"{name} must be int16 (UE8M0 pairs), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _dev(t, name)
+
+
+def dg_fp8_gemm_nt_ue8m0_i16(A, sfa, B, sfb, C, D, stream=None):
+    """D = C + A @ B.T with UE8M0 scale pairs: sfa int16 [ceil(K/256), M], sfb int16 [ceil(K/256), ceil(N/128)]."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B must share K")
+    P = _cdiv(_cdiv(K, 128), 2)
+    _i16(sfa, "sfa", (P, M))
+    _i16(sfb, "sfb", (P, _cdiv(N, 128)))
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_fp8_gemm_nt_ue8m0_i16(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K,
+                                        _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16(A, sfa, B, sfb, m_indices, C, D, stream=None):
+    """Contiguous M-grouped with UE8M0 pairs: sfa int16 [ceil(K/256), M], sfb int16 [G, ceil(K/256), ceil(N/128)]."""
+    _fp8(A, "A"); _fp8(B, "B")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    if B.shape[2] != K:
+        raise ValueError("A and B must share K")
+    P = _cdiv(_cdiv(K, 128), 2)
+    _i16(sfa, "sfa", (P, M))
+    _i16(sfb, "sfb", (G, P, _cdiv(N, 128)))
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError("m_indices must be int32 [M]")
+    _dev(m_indices, "m_indices")
+    if C is not None:
+        _f32(C, "C", (M, N))
+    _out(D, (M, N))
+    _check(lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(m_indices),
+                                                             _ptr(C), _ptr(D), M, N, K, G, _stream(stream)))
+    return D
+
+
+def dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16(A, sfa, B, sfb, masked_m, C, D, stream=None):
+    """Masked M-grouped with UE8M0 pairs: sfa int16 [G, ceil(K/256), M_max], sfb int16 [G, ceil(K/256), ceil(N/128)]."""
+    _fp8(A, "A"); _fp8(B, "B")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != G or B.shape[2] != K:
+        raise ValueError("B must be [G, N, K]")
+    P = _cdiv(_cdiv(K, 128), 2)
+    _i16(sfa, "sfa", (G, P, M_max))
+    _i16(sfb, "sfb", (G, P, _cdiv(N, 128)))
+    if masked_m.dtype != torch.int32 or tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be int32 [G]")
+    _dev(masked_m, "masked_m")
+    if C is not None:
+        _f32(C, "C", (G, M_max, N))
+    _out(D, (G, M_max, N))
+    _check(lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(masked_m),
+                                                         _ptr(C), _ptr(D), M_max, N, K, G, _stream(stream)))
+    return D
 
 
 # names without the C prefix, as on the pages

@@ -29,7 +29,16 @@ def run(p: gen.Problem, sentinel_seed: int = 12345, dev=None, D=None):
         D = sent.to("cuda")
     else:
         D.copy_(sent.to("cuda"))
-    if p.bf16:
+    if p.ue8m0_pairs:
+        if p.kind == "dense":
+            dg.dg_fp8_gemm_nt_ue8m0_i16(dev["A"], dev["sfa"], dev["B"], dev["sfb"], dev["C"], D)
+        elif p.kind == "contiguous":
+            dg.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16(dev["A"], dev["sfa"], dev["B"], dev["sfb"],
+                                                             dev["m_indices"], dev["C"], D)
+        else:
+            dg.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16(dev["A"], dev["sfa"], dev["B"], dev["sfb"],
+                                                         dev["masked_m"], dev["C"], D)
+    elif p.bf16:
         if p.kind == "dense":
             dg.dg_bf16_gemm_nt(dev["A"], dev["B"], dev["C"], D)
         elif p.kind == "contiguous":
@@ -85,6 +94,10 @@ def oracle_rows(oracle, p: gen.Problem, rows=None, threads=0):
         Kb = p.K // 128
         d["sfa"] = oracle.unpack_sfa_ue8m0(d["sfa"], Kb)
         d["sfb"] = oracle.unpack_sfb_ue8m0(d["sfb"], Kb)
+    if p.ue8m0_pairs:  # UE8M0 pairs in int16, MN-major: the same, from the pair packing
+        Kb = p.K // 128
+        d["sfa"] = oracle.unpack_sfa_ue8m0_pairs(d["sfa"], Kb)
+        d["sfb"] = oracle.unpack_sfb_ue8m0_pairs(d["sfb"], Kb)
     if p.kind == "dense":
         ref = oracle.fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], rows=rows, threads=threads)
         return ref, np.ones(ref.shape[0], dtype=bool)
