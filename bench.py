@@ -363,6 +363,31 @@ def host_overhead(p):
                 python_binding_us=round(binding, 3), shape=f"{p.M}x{p.N}x{p.K}")
 
 
+def library_reference(steps: int = 20):
+    """Context for the large dense shape: torch._scaled_mm (hipBLASLt on ROCm) on
+    4096 x 7168 x 16384 E4M3 operands with ONE scale per tensor, i.e. without the
+    fine-grained block scales and their promotion; not the same operation."""
+    import torch
+    M, N, K = 4096, 7168, 16384
+    g = torch.Generator(device="cpu").manual_seed(7)
+    a = (torch.randn(M, K, generator=g) * 0.5).to(torch.float8_e4m3fn).to("cuda")
+    b = (torch.randn(N, K, generator=g) * 0.5).to(torch.float8_e4m3fn).to("cuda")
+    one = torch.ones((), dtype=torch.float32, device="cuda")
+    f = lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        f()
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / steps
+    return dict(library="torch._scaled_mm (hipBLASLt), per-tensor scales", shape=f"{M}x{N}x{K}",
+                kernel_us=round(us, 3), tflops=round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1))
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -471,6 +496,8 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the probe measurements (streaming read, MFMA)")
     ap.add_argument("--no-host", action="store_true", help="skip the host-overhead measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="only time torch._scaled_mm (hipBLASLt, per-tensor scales) on 4096 x 7168 x 16384")
     ap.add_argument("--out", default=None, help="also write all lines as JSON here")
     args = ap.parse_args()
 
@@ -484,6 +511,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_kernel_bytes_read": 256 << 20, "copy_kernel_bytes_written": 256 << 20,
                           "launches": 3}))
+        return
+
+    if args.library_reference:
+        print(json.dumps(library_reference(args.steps)), flush=True)
         return
 
     if args.gpus != 1:
