@@ -83,6 +83,27 @@ dg_status dg_fp8_gemm_nt(const void *A, const float *sfa, const void *B, const f
                          const float *C, void *D, int M, int N, int K, void *stream);
 
 /*
+ * The dense call for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, layouts and errors as dg_fp8_gemm_nt, except:
+ *   - It allocates nothing: no hipMalloc or hipFree, no compile, no module
+ *     load.  The kernels for the sizes must already be loaded on the device:
+ *     call dg_fp8_gemm_nt once with the same M, N, K and C presence first
+ *     (otherwise DG_ERR_UNSUPPORTED).
+ *   - Split-K partial sums and arrival counters (shapes with few rows and a
+ *     long K) live in a static device array of the library, 32 MiB of partial
+ *     sums plus 64 KiB of counters per device, held until the process ends,
+ *     instead of a per-stream workspace.  A shape whose split-K needs more is
+ *     rejected with DG_ERR_UNSUPPORTED.  Each call first zeroes the counters
+ *     it uses (a small kernel on `stream`).
+ *   - Every call on a device shares that array, which keeps the last call's
+ *     contents: calls that overlap in time on one GPU (on other streams, or
+ *     graph replays running concurrently) race and give wrong results.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const void *A, const float *sfa, const void *B, const float *sfb,
+                                 const float *C, void *D, int M, int N, int K, void *stream);
+
+/*
  * M-grouped, contiguous layout (MoE prefill / training forward).
  * DeepGEMM README, "Grouped GEMM (contiguous layout)": only M is grouped, N
  * and K are shared; the experts' tokens are concatenated along M and every

@@ -69,6 +69,7 @@ using PlanKey = std::tuple<int, int, int, int, int, int, int, int, std::string>;
 struct DeviceState {
     int num_cus = 0;
     unsigned int* status = nullptr;   // the device's status words (device.hip)
+    void* scratch = nullptr;          // the device's copy of the no-alloc entry point's scratch (device.hip)
     std::map<hipStream_t, Workspace> ws;
     std::map<PlanKey, Plan> plans;
 };
@@ -94,6 +95,12 @@ dg_status device_state(DeviceState** out, int* dev_out) {
     }
     if (!st.status) {
         dg_status s = status_words(&st.status);
+        if (s != DG_OK) return s;
+    }
+    if (!st.scratch) {
+        // set-up, once per device, with the device current: the device address
+        // of the static scratch array (the host-side symbol is not it)
+        dg_status s = scratch_address(&st.scratch);
         if (s != DG_OK) return s;
     }
     *out = &st;
@@ -172,8 +179,11 @@ dg_status check_common(const void* A, const void* sfa, const void* B, const void
     return DG_OK;
 }
 
+// noalloc: the plan must already be loaded on the device (no compile, no module
+// load), split-K partials and counters go to the library's static scratch array
+// instead of the stream's workspace, and nothing is allocated.
 dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B, const void* sfb,
-                 const int32_t* grp, const float* C, void* D, void* stream_ptr) {
+                 const int32_t* grp, const float* C, void* D, void* stream_ptr, bool noalloc = false) {
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState* st = nullptr;
@@ -185,6 +195,53 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
     PlanKey key{p.kind, p.rows, p.n, p.k, p.g, p.has_c, p.sf, cus,
                 std::string(forced ? forced : "") + "|" + jit_extra_option()};
     auto it = st->plans.find(key);
+    if (noalloc) {
+        if (it == st->plans.end())
+            return set_error(DG_ERR_UNSUPPORTED,
+                             "dg_fp8_gemm_nt_noalloc: the kernels for these sizes are not loaded on this device; "
+                             "call dg_fp8_gemm_nt once with the same M, N, K and C presence first");
+        size_t partial_bytes = 0, counter_bytes = 0;
+        for (const Segment& seg : it->second.segs) {
+            if (seg.cfg.splitk <= 1 || seg.items <= 0) continue;
+            partial_bytes = std::max(partial_bytes, (size_t)seg.items * seg.cfg.bm * seg.cfg.bn * sizeof(float));
+            counter_bytes = std::max(counter_bytes, (size_t)(seg.items / seg.cfg.splitk) * sizeof(uint32_t));
+        }
+        if (partial_bytes > kScratchPartialBytes || counter_bytes > kScratchCounterBytes)
+            return set_error(DG_ERR_UNSUPPORTED,
+                             "dg_fp8_gemm_nt_noalloc: this shape's split-K needs " + std::to_string(partial_bytes) +
+                                 " bytes of partial sums and " + std::to_string(counter_bytes) +
+                                 " of counters, more than the scratch holds (" +
+                                 std::to_string(kScratchPartialBytes) + " and " +
+                                 std::to_string(kScratchCounterBytes) + ")");
+        float* partials = static_cast<float*>(st->scratch);
+        uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(st->scratch) +
+                                                         kScratchPartialBytes);
+        if (counter_bytes > 0) {
+            // the array keeps the last call's contents: its arrival counters start at zero here
+            s = clear_words(counters, (int)(counter_bytes / sizeof(uint32_t)), stream);
+            if (s != DG_OK) return s;
+        }
+        for (const Segment& seg : it->second.segs) {
+            const KernelConfig& cfg = seg.cfg;
+            if (seg.items <= 0) continue;
+            LaunchParams lp{};
+            lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
+            lp.M = p.rows;
+            lp.num_tiles = (int)seg.items;
+            lp.kt = p.kt;
+            lp.status = st->status;
+            if (cfg.splitk > 1) {
+                lp.ws = partials;
+                lp.counters = counters;
+            }
+            void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
+                            &lp.num_tiles, &lp.kt, &lp.status};
+            hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args,
+                                                 nullptr);
+            if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+        }
+        return DG_OK;
+    }
     if (it == st->plans.end()) {
         Plan plan;
         for (const KernelConfig& c : select_plan(p, cus)) {
@@ -495,6 +552,15 @@ dg_status dg_describe_config(int kind, int rows, int N, int K, int num_groups, i
 dg_status dg_fp8_gemm_nt(const void* A, const float* sfa, const void* B, const float* sfb, const float* C, void* D,
                          int M, int N, int K, void* stream) {
     return dense(A, sfa, B, sfb, C, D, M, N, K, 0, stream);
+}
+
+dg_status dg_fp8_gemm_nt_noalloc(const void* A, const float* sfa, const void* B, const float* sfb, const float* C,
+                                 void* D, int M, int N, int K, void* stream) {
+    dg_status s = check_common(A, sfa, B, sfb, C, D, M, N, K);
+    if (s != DG_OK) return s;
+    if (M == 0) return DG_OK;
+    Problem p{kDense, M, N, K, 1, C ? 1 : 0, 0};
+    return launch(p, A, sfa, B, sfb, nullptr, C, D, stream, true);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const float* sfa, const void* B, const float* sfb,

@@ -22,6 +22,14 @@ namespace dg {
 // that gave up before their flag was set.  Each device holds its own copy.
 __device__ unsigned int g_status[4];
 
+// Scratch of dg_fp8_gemm_nt_noalloc, the entry point for callers that cannot
+// allocate: split-K partial sums (kScratchPartialBytes), then the arrival
+// counters (kScratchCounterBytes).  Each device holds its own copy until the
+// process ends; every call on a device shares it.  Host code must use the
+// address hipGetSymbolAddress gives for it (scratch_address below), never the
+// array's name.
+static __device__ __align__(256) unsigned char scratch[kScratchPartialBytes + kScratchCounterBytes];
+
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -29,6 +37,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void dg_probe_null_kernel() {}
+
+__global__ void __launch_bounds__(256) dg_clear_words_kernel(unsigned int* __restrict__ p, int n) {
+    for (int i = (int)(blockIdx.x * 256u + threadIdx.x); i < n; i += (int)(gridDim.x * 256u)) p[i] = 0u;
+}
 
 // Every lane reads 16 bytes per step, four steps in flight, grid-stride over
 // the buffer; the XOR of everything read is stored only if it equals a value it
@@ -87,6 +99,23 @@ dg_status status_words(unsigned int** out) {
         return set_error(DG_ERR_HIP, std::string("hipGetSymbolAddress(status words): ") + hipGetErrorString(e));
     *out = static_cast<unsigned int*>(p);
     return DG_OK;
+}
+
+dg_status scratch_address(void** out) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return set_error(DG_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    *out = ptr;
+    return DG_OK;
+}
+
+dg_status clear_words(uint32_t* p, int n, void* stream) {
+    if (n <= 0) return DG_OK;
+    const int grid = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    hipLaunchKernelGGL(dg_clear_words_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p, n);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : set_error(DG_ERR_HIP, std::string("clear_words: ") + hipGetErrorString(e));
 }
 
 }  // namespace dg

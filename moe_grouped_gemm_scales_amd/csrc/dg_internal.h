@@ -98,6 +98,16 @@ std::string cache_dir();
 // (device.hip); [0] counts bounded waits in the kernels that gave up.
 dg_status status_words(unsigned int** out);
 
+// Scratch of dg_fp8_gemm_nt_noalloc (device.hip): a static device array of
+// split-K partial sums followed by arrival counters, one copy per device.
+constexpr size_t kScratchPartialBytes = size_t(32) << 20;
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;
+// its device address on the current device (hipGetSymbolAddress)
+dg_status scratch_address(void** out);
+// zero n words at p on the stream with a small kernel (no memset node, so the
+// call can be captured in a graph)
+dg_status clear_words(uint32_t* p, int n, void* stream);
+
 // Errors (api.cpp).
 dg_status set_error(dg_status s, const std::string& msg);
 bool env_flag(const char* name);

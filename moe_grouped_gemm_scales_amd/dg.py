@@ -90,6 +90,8 @@ def _load():
     for f in (lib.dg_fp8_gemm_nt_ue8m0_i16, lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_i16,
               lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_i16):
         f.restype = i32
+    lib.dg_fp8_gemm_nt_noalloc.argtypes = lib.dg_fp8_gemm_nt.argtypes
+    lib.dg_fp8_gemm_nt_noalloc.restype = i32
     lib.dg_get_wait_giveups.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     lib.dg_get_wait_giveups.restype = i32
     lib.dg_reset_wait_giveups.argtypes = []
