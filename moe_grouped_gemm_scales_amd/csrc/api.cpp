@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <tuple>
@@ -76,7 +77,57 @@ struct DeviceState {
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
-int g_num_cus_limit = 0;   // 0: use the device's count
+std::atomic<int> g_num_cus_limit{0};   // 0: use the device's count
+
+// The calling thread's previous call, kept so that a repeated call (same sizes,
+// format, device, stream, CU limit and configuration environment) launches
+// without the lock, the plan lookup or any allocation.  Plans live in std::map
+// nodes that are never erased, and workspaces a call outgrows are retired, not
+// freed, so the pointers stay valid.
+struct WarmCall {
+    int kind = -1, rows = 0, n = 0, k = 0, g = 0, has_c = 0, sf = 0, dev = -1, limit = 0;
+    uint64_t env = 0;
+    hipStream_t stream = nullptr;
+    const Plan* plan = nullptr;
+    float* partials = nullptr;       // split-K workspace of the plan's launches on this stream
+    uint32_t* counters = nullptr;
+    unsigned int* status = nullptr;
+};
+thread_local WarmCall t_warm;
+
+dg_status hip_fail(hipError_t e, const char* what);
+
+uint64_t fnv1a_str(const char* s, uint64_t h) {
+    if (!s) return h ^ 0x9e37u;
+    for (; *s; ++s) h = (h ^ (unsigned char)*s) * 1099511628211ull;
+    return h;
+}
+
+// Launches of one plan, in order (they share the split-K workspace: each leaves
+// its arrival counters at zero).
+dg_status launch_segments(const Plan& plan, const Problem& p, const void* A, const void* sfa, const void* B,
+                          const void* sfb, const int32_t* grp, const float* C, void* D, hipStream_t stream,
+                          float* partials, uint32_t* counters, unsigned int* status) {
+    for (const Segment& seg : plan.segs) {
+        const KernelConfig& cfg = seg.cfg;
+        if (seg.items <= 0) continue;
+        LaunchParams lp{};
+        lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
+        lp.M = p.rows;
+        lp.num_tiles = (int)seg.items;
+        lp.kt = p.kt;
+        lp.status = status;
+        if (cfg.splitk > 1) {
+            lp.ws = partials;
+            lp.counters = counters;
+        }
+        void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
+                        &lp.num_tiles, &lp.kt, &lp.status};
+        hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
+        if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+    }
+    return DG_OK;
+}
 
 dg_status hip_fail(hipError_t e, const char* what) {
     return set_error(DG_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -109,7 +160,8 @@ dg_status device_state(DeviceState** out, int* dev_out) {
 }
 
 int effective_cus(const DeviceState& st) {
-    if (g_num_cus_limit > 0 && g_num_cus_limit < st.num_cus) return g_num_cus_limit;
+    const int limit = g_num_cus_limit.load();
+    if (limit > 0 && limit < st.num_cus) return limit;
     return st.num_cus;
 }
 
@@ -185,6 +237,18 @@ dg_status check_common(const void* A, const void* sfa, const void* B, const void
 dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B, const void* sfb,
                  const int32_t* grp, const float* C, void* D, void* stream_ptr, bool noalloc = false) {
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const bool rewrite = p.kind == kKGrouped || p.a_k_outer || p.b_k_outer;
+    // ---- warm call: the previous call of this thread had the same key
+    int dev_now = 0;
+    if (hipGetDevice(&dev_now) != hipSuccess) dev_now = -1;
+    const uint64_t env = fnv1a_str(std::getenv("DG_JIT_EXTRA_OPTION"),
+                                   fnv1a_str(std::getenv("DG_FORCE_CONFIG"), 14695981039346656037ull));
+    const int limit = g_num_cus_limit.load(std::memory_order_relaxed);
+    WarmCall& w = t_warm;
+    if (!noalloc && !rewrite && w.plan && w.kind == p.kind && w.rows == p.rows && w.n == p.n && w.k == p.k &&
+        w.g == p.g && w.has_c == p.has_c && w.sf == p.sf && w.dev == dev_now && w.stream == stream &&
+        w.env == env && w.limit == limit)
+        return launch_segments(*w.plan, p, A, sfa, B, sfb, grp, C, D, stream, w.partials, w.counters, w.status);
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState* st = nullptr;
     int dev = 0;
@@ -262,7 +326,6 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         }
         it = st->plans.emplace(key, plan).first;
     }
-    const bool rewrite = p.kind == kKGrouped || p.a_k_outer || p.b_k_outer;
     if (rewrite && !it->second.transpose) {
         void* fptr = nullptr;
         s = get_function(it->second.segs.front().cfg, &fptr, "dg_transpose_k_major");
@@ -315,33 +378,34 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         A = at;
         B = bt;
     }
-    // Launches of one call run in stream order, so they can share the split-K
-    // workspace (each leaves its arrival counters at zero).
+    // the split-K workspace the plan's launches need on this stream
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    size_t need_p = 0, need_c = 0;
     for (const Segment& seg : it->second.segs) {
-        const KernelConfig& cfg = seg.cfg;
-        if (seg.items <= 0) continue;
-        LaunchParams lp{};
-        lp.A = A; lp.sfa = sfa; lp.B = B; lp.sfb = sfb; lp.C = C; lp.D = D; lp.grp = grp;
-        lp.M = p.rows;
-        lp.num_tiles = (int)seg.items;
-        lp.kt = p.kt;
-        lp.status = st->status;
-        if (cfg.splitk > 1) {
-            const int64_t mn = seg.items / cfg.splitk;
-            Workspace* w = nullptr;
-            s = ensure_workspace(*st, stream, (size_t)seg.items * cfg.bm * cfg.bn * sizeof(float),
-                                 (size_t)mn * sizeof(uint32_t), &w);
-            if (s != DG_OK) return s;
-            lp.ws = w->partials;
-            lp.counters = w->counters;
-        }
-        if (env_flag("DG_PRINT_CONFIGS"))
-            std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", cfg.key().c_str(), seg.grid,
-                         cfg.threads(), (long long)seg.items, cfg.lds_bytes());
-        void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
-                        &lp.num_tiles, &lp.kt, &lp.status};
-        hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
-        if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+        if (seg.cfg.splitk <= 1 || seg.items <= 0) continue;
+        need_p = std::max(need_p, (size_t)seg.items * seg.cfg.bm * seg.cfg.bn * sizeof(float));
+        need_c = std::max(need_c, (size_t)(seg.items / seg.cfg.splitk) * sizeof(uint32_t));
+    }
+    if (need_p > 0) {
+        Workspace* ws = nullptr;
+        s = ensure_workspace(*st, stream, need_p, need_c, &ws);
+        if (s != DG_OK) return s;
+        partials = ws->partials;
+        counters = ws->counters;
+    }
+    const bool print = env_flag("DG_PRINT_CONFIGS");
+    if (print)
+        for (const Segment& seg : it->second.segs)
+            std::fprintf(stderr, "[dg] launch %s grid=%d block=%d items=%lld lds=%d\n", seg.cfg.key().c_str(),
+                         seg.grid, seg.cfg.threads(), (long long)seg.items, seg.cfg.lds_bytes());
+    s = launch_segments(it->second, p, A, sfa, B, sfb, grp, C, D, stream, partials, counters, st->status);
+    if (s != DG_OK) return s;
+    if (!rewrite && !print) {
+        WarmCall& r = t_warm;
+        r.kind = p.kind; r.rows = p.rows; r.n = p.n; r.k = p.k; r.g = p.g; r.has_c = p.has_c; r.sf = p.sf;
+        r.dev = dev; r.limit = limit; r.env = env; r.stream = stream; r.plan = &it->second;
+        r.partials = partials; r.counters = counters; r.status = st->status;
     }
     return DG_OK;
 }
@@ -463,7 +527,8 @@ int dg_get_num_cus(void) {
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState* st = nullptr;
     int dev = 0;
-    if (device_state(&st, &dev) != DG_OK) return g_num_cus_limit > 0 ? g_num_cus_limit : 0;
+    const int limit = g_num_cus_limit.load();
+    if (device_state(&st, &dev) != DG_OK) return limit > 0 ? limit : 0;
     return effective_cus(*st);
 }
 
