@@ -70,7 +70,8 @@ typedef enum {
     DG_ERR_INVALID_ARG = -1,   /* NULL pointer, non-positive size, bad group count */
     DG_ERR_UNSUPPORTED = -2,   /* K not a multiple of 128, sizes beyond 32-bit offsets */
     DG_ERR_ALIGNMENT = -3,     /* pointer not 16-byte aligned, contiguous M not aligned */
-    DG_ERR_JIT = -4,           /* hipRTC compile or code-object load failed */
+    DG_ERR_JIT = -4,           /* hipRTC compile or code-object load failed, or a forced tile of a
+                                  variant that loads B into registers spilled registers */
     DG_ERR_HIP = -5            /* a HIP runtime call failed (no device, launch error) */
 } dg_status;
 

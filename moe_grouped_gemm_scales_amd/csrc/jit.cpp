@@ -214,9 +214,46 @@ std::string jit_extra_option() {
     return v ? std::string(v) : std::string();
 }
 
+// Largest value of a code-object metadata field (a msgpack string key followed
+// by an unsigned integer) over the kernels of the object; 0 if absent.
+uint64_t metadata_max(const std::vector<char>& code, const std::string& key) {
+    uint64_t best = 0;
+    const std::string k = key;
+    for (size_t pos = 0; (pos = std::string(code.data(), code.size()).find(k, pos)) != std::string::npos; pos += k.size()) {
+        size_t i = pos + k.size();
+        if (i >= code.size()) break;
+        const unsigned char t = (unsigned char)code[i];
+        uint64_t v = 0;
+        if (t <= 0x7f) v = t;                                       // positive fixint
+        else if (t >= 0xcc && t <= 0xcf) {                          // uint 8/16/32/64, big-endian
+            const int n = 1 << (t - 0xcc);
+            if (i + n >= code.size()) break;
+            for (int b = 1; b <= n; ++b) v = (v << 8) | (unsigned char)code[i + b];
+        }
+        best = std::max(best, v);
+    }
+    return best;
+}
+
+// The variants that load B straight into VGPRs (1, 2, 3, 5) keep loads in flight
+// into registers the compiler believes written at issue; a spill there could
+// hand such a register to another value while the load is still landing.  Their
+// code objects must therefore use no scratch at all.
+dg_status check_register_loads(const KernelConfig& c, const std::vector<char>& code) {
+    if (c.variant == 0 || c.variant == 4) return DG_OK;
+    const uint64_t scratch = metadata_max(code, ".private_segment_fixed_size");
+    const uint64_t spills = metadata_max(code, ".vgpr_spill_count");
+    if (scratch || spills)
+        return set_error(DG_ERR_JIT, c.key() + ": this kernel variant must not spill registers (" +
+                                         std::to_string(spills) + " VGPRs spilled, " + std::to_string(scratch) +
+                                         " bytes of scratch); pick a smaller tile");
+    return DG_OK;
+}
+
 dg_status compile_code(const KernelConfig& c, std::vector<char>* code) {
     std::lock_guard<std::mutex> lock(g_mu);
-    return compile_locked(c, code);
+    dg_status s = compile_locked(c, code);
+    return s != DG_OK ? s : check_register_loads(c, *code);
 }
 
 dg_status get_function(const KernelConfig& c, void** function, const char* name) {
@@ -232,6 +269,8 @@ dg_status get_function(const KernelConfig& c, void** function, const char* name)
     }
     std::vector<char> code;
     dg_status s = compile_locked(c, &code);
+    if (s != DG_OK) return s;
+    s = check_register_loads(c, code);
     if (s != DG_OK) return s;
     auto t0 = std::chrono::steady_clock::now();
     hipModule_t mod;
