@@ -26,7 +26,9 @@ struct KernelConfig {
     int variant = 0;           // 0: A and B through LDS; 1: B straight into VGPRs, A through an LDS
                                // ring; 2: B straight into VGPRs, A of the K range resident in LDS;
                                // 3: as 1, with an extra producer wave for A and no K-loop barrier;
-                               // 4: as 0, with A requested one K block further ahead than B
+                               // 4: as 0, with A requested one K block further ahead than B;
+                               // 5: B straight into VGPRs (each wave its own columns), A through a
+                               //    ring of `stages` LDS slots (large tiles)
     int has_c = 0;
     int n = 0, k = 0, g = 1;
     int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0),
@@ -54,6 +56,7 @@ struct KernelConfig {
             return (stages + 1) * (bm * 128 + sa) + stages * (bn * 128 + sb);
         }
         if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
+        if (variant == 5) return stages * (bm * 128 + bm * 4 + 256);   // A ring: tile, A scales, B scales
         if (variant == 3) {   // as many ring slots as fit (at most 16), see the kernel
             const int slot = bm * 128 + (bm + 63) / 64 * 256;
             const int slots = std::min(16, (160 * 1024 - 1024 - 768) / slot);

@@ -126,10 +126,20 @@ bool valid(const KernelConfig& c, const Problem& p) {
         return false;
     if (c.sf && ((c.variant != 0 && c.variant != 4) || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
     if (p.kind == kKGrouped && (c.sf || c.variant != 0 || c.kstep != 1)) return false;   // K-grouped: the same
-    if (c.variant < 0 || c.variant > 4) return false;
+    if (c.variant < 0 || c.variant > 5) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
     if (c.bn > 256) return false;
+    if (c.variant == 5) {
+        // B in VGPRs (each wave its own columns), A through a ring of `stages` slots;
+        // FP32 scales, one K block a slot, no split-K, the M forms
+        const int nw = c.wm * c.wn;
+        if (c.sf || c.kstep != 1 || c.splitk != 1 || c.wm != 1 || p.kind == kKGrouped) return false;
+        if (c.bm % 64 || (c.bm / 8) % nw || c.bm / 64 + 1 > nw || c.stages < 3) return false;
+        if (128 % (c.bn / nw) || tm % 4 || tm * tn > 32 || tn < 1) return false;
+        if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
+        return (c.bm / 8 / nw + 1 + 2 * tn) * 2 <= 63;           // vmcnt field (two K blocks of B ahead)
+    }
     if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
     if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
     if (c.variant != 0 && c.variant != 4) {

@@ -585,7 +585,21 @@ constexpr int IA = (NA_INS + NWAVES - 1) / NWAVES;
 constexpr int IB = (NB_INS + NWAVES - 1) / NWAVES;
 constexpr int IS = (NS_INS + NWAVES - 1) / NWAVES;
 constexpr int IT = (NT_INS + NWAVES - 1) / NWAVES;
-constexpr int INS_PER_WAVE = IA + IB + IS + IT;
+// One scale instruction per wave: scale instruction i goes to wave i (the A
+// scales first, then the B scales) and the waves past them repeat the last B
+// one, so a stage costs the CU NWAVES scale instructions instead of
+// NWAVES * (IS + IT) (8 instead of 16 for a 256 x 256 tile).  The wave's choice
+// is made with scalar selects, so the MFMA sequence it is spread over has no
+// branch, and every wave still issues the same count.
+#ifndef DG_SCALE_DIET
+#define DG_SCALE_DIET 1
+#endif
+// Wave priority (0-3) while a wave issues one n sub-tile's MFMAs; 0 leaves it alone.
+#ifndef DG_SETPRIO
+#define DG_SETPRIO 0
+#endif
+constexpr bool DIET = DG_SCALE_DIET != 0 && !AAHEAD && NS_INS + NT_INS > 0 && NS_INS + NT_INS <= NWAVES;
+constexpr int INS_PER_WAVE = DIET ? IA + IB + 1 : IA + IB + IS + IT;
 static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
 // MFMA steps (n sub-tiles of a stage's first K block) the refill is spread over;
 // 0: all at once.  It must be issued before the last sub-tile, where the wait
@@ -709,7 +723,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
         u32 voff_t[IT > 0 ? IT : 1];
 #pragma unroll
         for (int j = 0; j < IT; ++j) {
-            const int h = min(wave + j * NWAVES, NT_INS - 1);
+            // without repeats, wave NS_INS + h issues B-scale instruction h
+            const int h = DIET ? min(max(wave - NS_INS, 0), NT_INS - 1) : min(wave + j * NWAVES, NT_INS - 1);
             if constexpr (FP4B) {
                 // word [n0 + 64 h + lane][kb]; rows past the tile read as zero
                 voff_t[j] = (u32)(64 * h + lane) * KBLKS * 4u;
@@ -723,6 +738,16 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
             }
         }
 
+        // one scale instruction per wave: an A-scale one (waves 0 .. NS_INS-1) or a B-scale one
+        const bool is_a_sc = wave < NS_INS;
+        const u32 voff_sc = is_a_sc ? voff_s[0] : voff_t[0];
+        const u32 lds_sc = __builtin_amdgcn_readfirstlane(
+            is_a_sc ? (u32)(S_OFF + wave * 256) : (u32)(T_OFF + min(max(wave - NS_INS, 0), NT_INS - 1) * 256));
+        v4i rs_sc = is_a_sc ? rs_s : rs_t;
+        rs_sc.x = __builtin_amdgcn_readfirstlane(rs_sc.x);
+        rs_sc.y = __builtin_amdgcn_readfirstlane(rs_sc.y);
+        rs_sc.z = __builtin_amdgcn_readfirstlane(rs_sc.z);
+        rs_sc.w = __builtin_amdgcn_readfirstlane(rs_sc.w);
         // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
         // (kb: first K block of the stage)
         // index along K of the scales of K block kb (a word holds four UE8M0 scales)
@@ -753,6 +778,13 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 else
                     dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
                           __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+            } else if (DIET) {
+                // this wave's scale instruction: resource, lane offset and LDS place chosen
+                // once per tile (rs_sc, voff_sc, lds_sc); only the K block's offset varies
+                const u32 soff = is_a_sc ? (FP4A ? (u32)kb * 4u : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES)
+                                         : (FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb));
+                dma_sf(lim(rs_sc), voff_sc, __builtin_amdgcn_readfirstlane(soff),
+                       __builtin_amdgcn_readfirstlane(st + lds_sc));
             } else if (j < IA + IB + IS) {
                 const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
                 dma_sf(lim(rs_s), voff_s[j - IA - IB],
@@ -1024,6 +1056,8 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                     v4f prev[TM];
 #pragma unroll
                     for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+                    // optional: the wave asks for issue priority while it has MFMAs to issue
+                    if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(DG_SETPRIO);
 #pragma unroll
                     for (int a = 0; a < TM; ++a) {
                         if constexpr (SF_E8) {
@@ -1048,6 +1082,7 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                         if (last) fa[a] = read_fa(kan + a_frag, kan + a_frag_hi, a * 16 * ROWB_A);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                    if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(0);
                     if (!last) {
                         fb = fb_next;
                     } else {
@@ -1775,6 +1810,261 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
                 for (int b = 0; b < TN; ++b) asm volatile("" : "+v"(acc[a][b]));
         });
         acc[TM - 1][TN - 1] += p_carry * s_carry;
+
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+    }
+}
+#elif DG_VARIANT == 5
+// ============================================================ variant 5: B in VGPRs, A through a deep ring (large tiles)
+// For the large, MFMA-bound shapes.  With both operands staged through LDS a
+// 256 x 256 tile leaves room for two stages only, so each K block's loads are
+// requested about one K block ahead, less than the fabric latency under load.
+// Here every wave owns WAVE_N = BN / NWAVES columns (no two waves share a row of
+// B) and loads its B fragments straight into VGPRs, DEPTH K blocks ahead of
+// their use; only A (shared by all waves) and the scales pass through LDS, in
+// a ring of STAGES slots, so A is requested STAGES - 1 K blocks ahead.  Per K
+// block each wave issues the same vector-memory instructions: its share of
+// the A DMA, one scale DMA (the A scales of 64 rows, or the B scales), and
+// its B loads; waiting for its own B loads of a block therefore also waits for
+// its A share of that block (issued earlier), and one barrier per K block makes
+// the A slot visible to all and frees the slot the previous block used.
+static_assert(WM == 1, "variant 5 spreads its waves along n only");
+static_assert(!SF_E8 && !KG && !BF16, "variant 5: FP32 scales");
+static_assert(KSTEP == 1 && SPLITK == 1, "variant 5: one K block a slot, no split-K");
+#ifndef DG_BDEPTH
+#define DG_BDEPTH 2
+#endif
+constexpr int DEPTH = DG_BDEPTH;                  // K blocks of B in flight ahead of the one multiplied
+constexpr int NSETS = DEPTH + 1;                  // B register sets; the K loop is unrolled by this
+constexpr int SLOTS = STAGES;                     // A ring slots
+static_assert(DEPTH >= 1 && SLOTS - 1 >= DEPTH, "A is requested at least as far ahead as B");
+constexpr int NA_INS = BM / 8;                    // 1 KB DMA instructions for one K block of A
+constexpr int NS_INS = BM / 64;                   // 256 B DMA instructions for its A scales
+static_assert(BM % 64 == 0 && NA_INS % NWAVES == 0, "whole A DMA instructions per wave");
+static_assert(NS_INS + 1 <= NWAVES, "one scale DMA per wave and K block");
+constexpr int IA = NA_INS / NWAVES;
+constexpr int UB = 2 * TN;                        // B loads per lane per K block
+constexpr int UNIT = IA + 1 + UB;                 // vector-memory instructions per wave per K block
+static_assert(UNIT * DEPTH <= 63, "vmcnt range");
+static_assert(BN <= 256 && (KBLK % WAVE_N) == 0, "a wave's columns lie in one 128-row block of B");
+// LDS slot: [A: BM rows x 128 B][A scales: BM floats][B scales: 64 floats].  The
+// A scales are stored so that lane (l16, *) finds those of its rows l16 + 16 a,
+// a = 0 .. TM-1, in TM consecutive floats: float i of the slot's scale area
+// holds row (i % TM) * 16 + i / TM.
+constexpr int S_OFF = BM * 128;
+constexpr int T_OFF = S_OFF + BM * 4;
+constexpr int SLOT_BYTES = T_OFF + 256;
+constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS exceeds 160 KB");
+static_assert(TM % 4 == 0, "A scales are read four at a time");
+#ifndef DG_FA_AHEAD
+#define DG_FA_AHEAD 1
+#endif
+constexpr int FA_AHEAD = DG_FA_AHEAD < TM ? DG_FA_AHEAD : TM;   // A fragments read ahead of use
+
+extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(1, MAX_THREADS_DECL)))
+dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, const u8* __restrict__ B,
+                      const float* __restrict__ sfb, const float* __restrict__ C, u16* __restrict__ D,
+                      const int* __restrict__ grp, float* __restrict__ ws, u32* __restrict__ counters, int M,
+                      int num_tiles, int kt, u32* __restrict__ status) {
+    const Params p{A, sfa, B, sfb, C, D, grp, ws, counters, M, num_tiles, kt, status};
+    asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(M), "s"(num_tiles),
+                 "s"(gridDim.x));
+    __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int q = lane >> 4;
+    const u32 smem_base = lds_addr(smem);
+    // A fragments: the swizzled chunk pair {q, q ^ 4} of row l16 (+16 a), as in variant 0
+    const int sw = l16 & 7;
+    const u32 chunk_lo = (u32)((q ^ sw) << 4);
+    const u32 chunk_hi = (u32)(((q ^ 4) ^ sw) << 4);
+    const int wave_n = wave * WAVE_N;             // first column of this wave inside the tile
+
+#pragma unroll 1
+    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
+        const Tile tl = decode_tile(p, t);
+        if (tl.skip) continue;
+
+        const u8* a_base;
+        const float* sfa_base;
+        if constexpr (kKind == 2) {
+            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * K;
+            sfa_base = p.sfa + (u64)tl.g * KBLKS * p.M;
+        } else {
+            a_base = p.A + (u64)tl.m0 * K;
+            sfa_base = p.sfa;
+        }
+        const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
+        const int nb_t0 = tl.n0 / KBLK;
+        // A rows past the tile's valid rows lie past the buffer: they load as zeros
+        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * K);
+        const v4i rs_s = make_rsrc(sfa_base, (u32)KBLKS * p.M * 4u);
+        const v4i rs_t = make_rsrc(p.sfb + (u64)tl.g * NBLKS * KBLKS, (u32)NBLKS * KBLKS * 4u);
+        const v4i rs_b = make_rsrc(p.B + ((u64)tl.g * N + tl.n0) * K, (u32)n_rows * K);
+        // this wave's share of the A DMA: instruction i = wave + j * NWAVES writes tile rows
+        // 8 i .. 8 i + 7; lane l: row 8 i + l / 8, physical chunk l % 8 holding logical
+        // chunk (l % 8) ^ (row & 7) (8 i is a multiple of 8, so the lane part is fixed)
+        const u32 voff_a = (u32)(lane >> 3) * K + (u32)(((lane & 7) ^ ((lane >> 3) & 7)) << 4);
+        // the wave's scale DMA: waves 0 .. NS_INS-1 the A scales of 64 rows each (in the
+        // slot order above), the others the B scales of the tile's 128-row blocks
+        u32 voff_sc;
+        if (wave < NS_INS) {
+            const int i = wave * 64 + lane;
+            const int m = tl.m0 + (i % TM) * 16 + i / TM;
+            voff_sc = (u32)(m < p.M ? m : p.M - 1) * 4u;
+        } else {
+            voff_sc = (u32)min(nb_t0 + lane, NBLKS - 1) * KBLKS * 4u;
+        }
+        // B: sub-tile b, row l16 (clamped to the valid rows), logical chunks q and q + 4
+        u32 bvoff[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int r = wave_n + b * 16 + l16;
+            bvoff[b] = (u32)(r < n_rows ? r : n_rows - 1) * K + q * 16;
+        }
+        // K blocks of this tile, opaque to the compiler: with a short constant count it
+        // would unroll the K loop and run out of registers
+        int nst = tl.kb1 - tl.kb0;
+        asm volatile("" : "+s"(nst));
+        // K block `it` of the tile (blocks past the end reload the last one: the loads
+        // keep every wave's instruction count fixed, and land in a free slot / set)
+        auto kb_of = [&](int it) { return tl.kb0 + (it < nst ? it : nst - 1); };
+        auto issue_a = [&](int it) __attribute__((always_inline)) {
+            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + (u32)(it % SLOTS) * SLOT_BYTES);
+            const int kb = kb_of(it);
+            // the instruction's row offset goes into the scalar offset, so the lane offset
+            // is one register for all of them (no per-instruction copies kept live)
+#pragma unroll
+            for (int j = 0; j < IA; ++j) {
+                const int i = wave + j * NWAVES;
+                dma16(rs_a, voff_a, __builtin_amdgcn_readfirstlane((u32)kb * KBLK + (u32)(i * 8) * (u32)K),
+                      st + i * 1024);
+            }
+            if (wave < NS_INS)
+                dma4(rs_s, voff_sc, __builtin_amdgcn_readfirstlane((u32)kb * p.M * 4u), st + S_OFF + wave * 256);
+            else
+                dma4(rs_t, voff_sc, __builtin_amdgcn_readfirstlane((u32)kb * 4u), st + T_OFF);
+        };
+        auto issue_b = [&](int it, v4i (&dst)[TN][2]) __attribute__((always_inline)) {
+            const u32 ka = __builtin_amdgcn_readfirstlane((u32)kb_of(it) * KBLK);
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                dst[b][0] = load16<0>(rs_b, bvoff[b], ka);
+                dst[b][1] = load16<64>(rs_b, bvoff[b], ka);
+            }
+        };
+        lds_u8* const lds = (lds_u8*)smem_base;
+        // the wave's B scale: its columns' 128-row block, relative to the tile's first
+        int nblk = (tl.n0 + wave_n) / KBLK;
+        nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+        const int sb_off = T_OFF + (nblk - nb_t0) * 4;
+        const int sa_off = S_OFF + l16 * TM * 4;
+        const u32 a_frag = (u32)l16 * 128u;
+
+        v4f acc[TM][TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        // the last product of a K block and its scale, promoted under the next block's first MFMA
+        v4f p_carry = {0.f, 0.f, 0.f, 0.f};
+        float s_carry = 0.f;
+        v4i breg[NSETS][TN][2];
+
+        // earlier tile's stores and LDS reads are finished before the ring is refilled
+        wait_vmcnt<0>();
+        __syncthreads();
+        // A of K blocks 0 .. SLOTS-2, then B of K blocks 0 .. DEPTH-1
+#pragma unroll
+        for (int i = 0; i < SLOTS - 1; ++i) issue_a(i);
+        static_for<DEPTH>([&]<int J>() __attribute__((always_inline)) { issue_b(J, breg[J]); });
+
+        // One K block.  WAIT: this wave's loads issued after B of block `it` (the first
+        // DEPTH-1 blocks follow the prologue's order, the rest the loop's).
+        auto kblock = [&]<int SET, int WAIT>(int it) __attribute__((always_inline)) {
+            wait_vmcnt<WAIT>();
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                tie(breg[SET][b][0]);
+                tie(breg[SET][b][1]);
+            }
+            // every wave's A share of block `it` has landed, and every wave is done with
+            // the slot of block it-1, which is refilled now with block it+SLOTS-1
+            __syncthreads();
+            issue_a(it + SLOTS - 1);
+            issue_b(it + DEPTH, breg[(SET + DEPTH) % NSETS]);
+
+            lds_u8* const slot = lds + (u32)(it % SLOTS) * SLOT_BYTES;
+            const float sb = lds_read_f32(slot, sb_off);
+            // A scales of four sub-tiles at a time, the next four read one group ahead
+            auto read_s4 = [&](int a4) __attribute__((always_inline)) {
+                return *(__attribute__((address_space(3))) const v4f*)(slot + sa_off + a4 * 16);
+            };
+            v4f s4 = read_s4(0), s4_next = s4;
+            lds_u8* const a_lo = slot + a_frag + chunk_lo;
+            lds_u8* const a_hi = slot + a_frag + chunk_hi;
+            v8i fb[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const v4i x = breg[SET][b][0], y = breg[SET][b][1];
+                fb[b] = v8i{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            }
+            // A fragments read FA_AHEAD sub-tiles ahead; each MFMA runs while the FMAs
+            // promote the previous sub-tile's product
+            v8i fa[TM];
+#pragma unroll
+            for (int a = 0; a < FA_AHEAD; ++a) fa[a] = lds_read_frag(a_lo, a_hi, a * 16 * 128);
+            v4f prev = p_carry;
+            float sprev = s_carry;
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                if (a + FA_AHEAD < TM) fa[a + FA_AHEAD] = lds_read_frag(a_lo, a_hi, (a + FA_AHEAD) * 16 * 128);
+                if (a % 4 == 0 && a + 4 < TM) s4_next = read_s4(a / 4 + 1);
+                const float sab = s4[a % 4] * sb;
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                    // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[b], fa[a], zero, 0, 0, 0, 0, 0, 0);
+                    if (a == 0 && b == 0) acc[TM - 1][TN - 1] += prev * sprev;
+                    else if (b == 0) acc[a - 1][TN - 1] += prev * sprev;
+                    else acc[a][b - 1] += prev * sprev;
+                    prev = pr;
+                    sprev = sab;
+                }
+                if (a % 4 == 3) s4 = s4_next;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            p_carry = prev;
+            s_carry = sprev;
+        };
+        // blocks 0 .. DEPTH-2: after B of block j come the prologue's B of blocks
+        // j+1 .. DEPTH-1 and the loop's first j iterations
+        static_for<DEPTH - 1>([&]<int J>() __attribute__((always_inline)) {
+            if (J < nst) kblock.template operator()<J % NSETS, (DEPTH - 1 - J) * UB + J * UNIT>(J);
+        });
+        // the rest, unrolled by NSETS so every B register set has a fixed name
+#pragma unroll 1
+        for (int it0 = DEPTH - 1; it0 < nst; it0 += NSETS) {
+            static_for<NSETS>([&]<int U>() __attribute__((always_inline)) {
+                if (it0 + U < nst) kblock.template operator()<(DEPTH - 1 + U) % NSETS, (DEPTH - 1) * UNIT>(it0 + U);
+            });
+        }
+        acc[TM - 1][TN - 1] += p_carry * s_carry;
+        // the loads past the tile's last block land before their registers are released
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s2 = 0; s2 < NSETS; ++s2)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                tie(breg[s2][b][0]);
+                tie(breg[s2][b][1]);
+            }
 
         finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
     }

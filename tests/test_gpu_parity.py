@@ -216,9 +216,9 @@ FORCED = [
     "32,128,1,4,2,4,2",
     # variant 1: B straight into VGPRs (fields 7-8: kstep 1, variant 1)
     "128,128,1,8,9,1,1,1",
-    "128,128,1,4,4,1,1,1",
+    "128,128,1,4,3,1,1,1",
     "64,96,1,2,4,2,1,1",
-    "256,64,1,4,3,1,1,1",
+    "256,64,1,4,2,1,1,1",
     "32,64,1,1,3,4,1,1",
     "16,48,1,1,2,8,1,1",
     # variant 2: B straight into VGPRs, A of the K range resident in LDS
@@ -326,12 +326,53 @@ def test_bdirect_grouped(oracle, monkeypatch, forced):
     _compare(pc, D, sent, ref, comp, what=f"contiguous {forced}")
 
 
+# ------------------------------------------------------------------ variant 5: B in VGPRs, A through a deep ring
+V5_FORCED = ["192,256,1,8,4,1,1,5", "128,256,1,8,6,1,1,5", "64,128,1,4,3,1,1,5", "128,128,1,4,4,1,1,5"]
+
+
+@pytest.mark.parametrize("forced", V5_FORCED)
+def test_b_in_registers_large_tile(oracle, monkeypatch, forced):
+    """Variant 5 on ragged dense problems (K of 1, 2, 3 and 9 blocks: the prologue's and the
+    tail's loads past the last block), and on masked and contiguous problems."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    for M, N, K in ((300, 520, 1152), (77, 333, 128), (257, 260, 256), (130, 515, 384)):
+        p = gen.make_dense(M, N, K, seed=61 + M + K, with_c=(K != 256))
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"dense {M}x{N}x{K} {forced}")
+    pm = gen.make_masked(3, 200, 333, 640, seed=62, with_c=True, masked_m=[200, 0, 77])
+    D, sent = run(pm)
+    ref, comp = oracle_rows(oracle, pm)
+    _compare(pm, D, sent, ref, comp, what=f"masked {forced}")
+    if int(forced.split(",")[0]) <= 128:
+        pc = gen.make_contiguous([128, 0, 256, 100], 200, 384, seed=63, with_c=True, pad_rows=128)
+        D, sent = run(pc)
+        ref, comp = oracle_rows(oracle, pc)
+        _compare(pc, D, sent, ref, comp, what=f"contiguous {forced}")
+
+
+def test_b_in_registers_integer_data_bitwise(oracle, monkeypatch):
+    """Variant 5 with integer data and power-of-two scales: D equals the oracle's BF16 bitwise
+    (maps the B-register lanes and the permuted A-scale layout)."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", "192,256,1,8,4,1,1,5")
+    g = torch.Generator().manual_seed(97)
+    M, N, K = 200, 520, 1280
+    A = gen.integer_codes((M, K), g, max_abs=8)
+    B = gen.integer_codes((N, K), g, max_abs=8)
+    sfa = gen.pow2_scales((K // 128, M), g, -2, 2)
+    sfb = gen.pow2_scales(((N + 127) // 128, K // 128), g, -2, 2)
+    p = gen.Problem("dense", A, sfa, B, sfb)
+    D, _ = run(p)
+    ref, _ = oracle_rows(oracle, p)
+    assert np.array_equal(check.bf16_bits(D), oracle.bf16_rne(ref).reshape(M, N))
+
+
 # ------------------------------------------------------------------ two launches over column ranges
 # (fields 9-10 of a launch: first and end column; launches separated by ';')
 SEGMENTS = [   # (launches, kinds they are valid for)
     ("128,128,4,2,2,1,1,0,0,256;64,96,2,2,3,1,1,0,256,520", "dense masked contiguous"),
     ("256,256,4,2,2,1,1,0,0,256;256,192,4,2,2,1,1,0,256,520", "dense masked"),
-    ("64,64,1,4,3,2,1,2,0,128;64,96,1,2,4,1,1,1,128,520", "dense"),
+    ("64,64,1,4,3,2,1,2,0,128;64,96,1,2,3,1,1,1,128,520", "dense"),
     ("128,96,1,6,3,1,1,3,0,96;64,112,1,1,2,1,1,0,96,520", "dense masked contiguous"),
     ("64,64,1,4,3,4,1,3,0,192;64,64,1,4,3,2,1,3,192,520", "dense"),
 ]
