@@ -29,6 +29,9 @@ struct KernelConfig {
                                // 4: as 0, with A requested one K block further ahead than B;
                                // 5: B straight into VGPRs (each wave its own columns), A through a
                                //    ring of `stages` LDS slots (large tiles)
+                               // 6: as 0, each slot refilled in two parts: A, the scales and the
+                               //    first half of B after a barrier in the middle of the K block,
+                               //    the second half of B after the block
     int has_c = 0;
     int n = 0, k = 0, g = 1;
     int sf = 0;                // scale format: 0 FP32, 1 packed UE8M0, 2 FP8 x FP4 (E2M1 B, 1x32 UE8M0),

@@ -124,9 +124,14 @@ bool valid(const KernelConfig& c, const Problem& p) {
     // slots), for FP8 operands with FP32 or UE8M0 scales and the M forms
     if (c.variant == 4 && (c.kstep != 1 || c.stages != 2 || c.sf == 2 || c.sf == 4 || p.kind == kKGrouped))
         return false;
-    if (c.sf && ((c.variant != 0 && c.variant != 4) || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
+    // variant 6: variant 0 with the split refill (FP8 operands, FP32 or UE8M0 scales,
+    // one K block a stage, an even number of n sub-tiles per wave, the M forms)
+    if (c.variant == 6 && (c.kstep != 1 || c.sf == 2 || c.sf == 3 || c.sf == 4 || p.kind == kKGrouped ||
+                           (c.bn / c.wn / 16) % 2 || c.bn / c.wn / 16 < 4))
+        return false;
+    if (c.sf && ((c.variant != 0 && c.variant != 4 && c.variant != 6) || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
     if (p.kind == kKGrouped && (c.sf || c.variant != 0 || c.kstep != 1)) return false;   // K-grouped: the same
-    if (c.variant < 0 || c.variant > 5) return false;
+    if (c.variant < 0 || c.variant > 6) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
     if (c.bn > 256) return false;
@@ -141,8 +146,11 @@ bool valid(const KernelConfig& c, const Problem& p) {
         return (c.bm / 8 / nw + 1 + 2 * tn) * 2 <= 63;           // vmcnt field (two K blocks of B ahead)
     }
     if (p.kind == kContiguous && 128 % c.bm != 0 && c.bm % 128 != 0) return false;
-    if (p.kind == kContiguous && c.bm > 128) return false;   // one expert per row block
-    if (c.variant != 0 && c.variant != 4) {
+    // one expert per row block; 256-row blocks (both operands through LDS) make one
+    // pass per expert of their two 128-row blocks
+    if (p.kind == kContiguous && c.bm > 128 && !(c.bm == 256 && (c.variant == 0 || c.variant == 4 || c.variant == 6)))
+        return false;
+    if (c.variant != 0 && c.variant != 4 && c.variant != 6) {
         // waves along n only, one K block at a time, the whole K range of a
         // work item unrolled, B registers of stages - 1 blocks in flight
         if (c.wm != 1 || c.kstep != 1 || c.stages < 2) return false;
@@ -159,6 +167,7 @@ bool valid(const KernelConfig& c, const Problem& p) {
     if (c.kstep != 1 && c.kstep != 2) return false;
     if (c.bm % (8 / c.kstep) || c.bn % (8 / c.kstep) || c.stages < 2) return false;
     if (dma_per_wave(c) * (c.stages - 1) > 63) return false;   // vmcnt field
+    if (c.variant == 6 && (dma_per_wave(c) + 1) * (c.stages - 1) > 63) return false;   // split groups round up
     // more than 32 sub-tiles per wave: only 4-wave groups without promotion (accumulators in AGPRs)
     const bool agpr_acc = (c.sf == 1 || c.sf == 3 || c.sf == 5) && c.wm * c.wn == 4;
     if (tm < 1 || tn < 1 || tm > 8 || tn > 8 || tm * tn > (agpr_acc ? 64 : 32)) return false;
@@ -184,8 +193,11 @@ const Tuned kTuned[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 1, 4, 4, 7, 1, 2, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3, 0, 0},
     {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0, 0, 0},
-    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 0, 0, 0},
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    // the large shapes: 256 x 256 with the split refill (variant 6), 475 us against
+    // 490-505 us for the one-part refill; contiguous: 995-1002 us against 1037-1040 us
+    // for the one-part refill and 1045-1088 us for 128 x 256 with three slots
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
     // K-grouped weight gradient of the contiguous workload (K: the row pitch of the
     // K-contiguous operands, 4 x 8192 tokens): 192 x 256 with two stages measured 2-4 %

@@ -64,8 +64,9 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     def("DG_N", c.n);
     def("DG_K", c.k);
     def("DG_G", c.g);
-    def("DG_VARIANT", c.variant == 4 ? 0 : c.variant);
+    def("DG_VARIANT", c.variant == 4 || c.variant == 6 ? 0 : c.variant);
     if (c.variant == 4) def("DG_AAHEAD", 1);
+    if (c.variant == 6) def("DG_SPLIT", 1);
     def("DG_SF", c.sf);
     if (c.ne > 0) {
         def("DG_NB", c.nb);
@@ -240,7 +241,7 @@ uint64_t metadata_max(const std::vector<char>& code, const std::string& key) {
 // hand such a register to another value while the load is still landing.  Their
 // code objects must therefore use no scratch at all.
 dg_status check_register_loads(const KernelConfig& c, const std::vector<char>& code) {
-    if (c.variant == 0 || c.variant == 4) return DG_OK;
+    if (c.variant == 0 || c.variant == 4 || c.variant == 6) return DG_OK;
     const uint64_t scratch = metadata_max(code, ".private_segment_fixed_size");
     const uint64_t spills = metadata_max(code, ".vgpr_spill_count");
     if (scratch || spills)

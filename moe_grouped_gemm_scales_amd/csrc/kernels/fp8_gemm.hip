@@ -264,12 +264,14 @@ struct Tile {
     int kb0, kb1;    // K-block range
     int split;       // split index
     int mn;          // output tile index (for split-K bookkeeping)
+    int g2;          // contiguous, 256-row blocks: the expert of rows 128.. when it differs, else -1
     bool skip;
 };
 
 __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
     Tile tl;
     tl.skip = false;
+    tl.g2 = -1;
     tl.split = 0;
     tl.kb0 = 0;
     tl.kb1 = KBLKS;
@@ -376,6 +378,14 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
             int g = p.grp[tl.m0];
             tl.g = g;
             tl.skip = (g < 0 || g >= G);
+            // every 128-row block of the layout names one expert (its first row's):
+            // a 256-row block covers two, which may differ
+            if constexpr (BM > 128) {
+                if (tl.m0 + 128 < p.M) {
+                    const int g2 = p.grp[tl.m0 + 128];
+                    if (g2 >= 0 && g2 < G && g2 != g) tl.g2 = g2;
+                }
+            }
         } else {
             tl.g = 0;
         }
@@ -609,6 +619,42 @@ static_assert(INS_PER_WAVE * (STAGES - 1) <= 63, "vmcnt range");
 #endif
 constexpr int SPREAD = DG_SPREAD < TN - 1 ? DG_SPREAD : TN - 1;
 
+// Split refill (DG_SPLIT): a slot is handed back in two parts.  Its A tile, its
+// scales and the B rows of the first half of every wave's n sub-tiles are read
+// by the middle of the K block (A and the scales at its start, those B rows by
+// sub-tile TN/2 - 1), so after a barrier there they are refilled with the K
+// block STAGES ahead (the "mid" group); the B rows of the second half follow
+// after the barrier at the end of the block (the "end" group).  Every load then
+// has about half a K block more time to land, and the CU keeps more bytes in
+// flight.  Each wait is for one group, with the (STAGES - 1) later mid and end
+// groups still pending.
+#ifndef DG_SPLIT
+#define DG_SPLIT 0
+#endif
+constexpr bool SPLIT = DG_SPLIT != 0;
+constexpr int HALF_TN = TN / 2;
+constexpr int NB_HALF = NB_INS / 2;                      // B DMA instructions of one half
+constexpr int IBH = (NB_HALF + NWAVES - 1) / NWAVES;    // ... per wave
+constexpr int NSC_PER_WAVE = INS_PER_WAVE - IA - IB;    // scale DMA instructions per wave
+constexpr int G_MID = IA + IBH + NSC_PER_WAVE;
+constexpr int G_END = IBH;
+constexpr int SPLIT_PENDING = (STAGES - 1) * (G_MID + G_END);
+static_assert(!SPLIT || (KSTEP == 1 && !AAHEAD && TN % 2 == 0 && TN >= 4 && !FP4A && !FP4B && !KG && !BF16),
+              "split refill: FP8 operands, one K block a slot, an even number of n sub-tiles");
+// B instruction i covers 8 rows inside one 16-row n sub-tile of one wave column
+// (2 TN instructions per column): the first TN of a column are the first half
+static_assert(!SPLIT || (RPI == 8 && NB_INS == WN * 2 * TN), "split refill: 8 B rows per instruction");
+static_assert(!SPLIT || SPLIT_PENDING <= 63, "vmcnt range");
+// The mid group is spread over the sub-tiles from the mid barrier on, the end
+// group over the first ones of the next block; each must be issued in full
+// before the next wait, which counts it.
+constexpr int MID_STEPS = TN - HALF_TN;                  // steps HALF_TN - 1 .. TN - 2
+constexpr int END_STEPS = HALF_TN - 1;                   // steps 0 .. HALF_TN - 2
+
+// contiguous form with 256-row blocks: up to two passes over a tile, one per expert
+constexpr int PIECES = (kKind == 1 && BM > 128) ? 2 : 1;
+static_assert(kKind != 1 || BM <= 128 || BM == 256, "contiguous row blocks: at most 128 rows, or 256");
+
 // Wait until at most PENDING whole stages of this wave's DMA remain in flight.
 template <int PENDING>
 __device__ __forceinline__ void wait_stages() { wait_vmcnt<PENDING * INS_PER_WAVE>(); }
@@ -659,555 +705,619 @@ dg_fp8_gemm_nt_kernel(const u8* __restrict__ A, const float* __restrict__ sfa, c
 
 #pragma unroll 1
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
-        const Tile tl = decode_tile(p, t);
-        if (tl.skip) continue;
-
-        // ---- per-tile buffer resources (bases advanced to the tile's rows)
-        const u8* a_base;
-        const float* sfa_base;
-        int a_rows_total;        // rows of this A (for sfa stride)
-        if constexpr (kKind == 2) {
-            a_base = p.A + ((u64)tl.g * p.M + tl.m0) * KB_A;
-            sfa_base = (const float*)((const u8*)p.sfa +
-                                      (u64)tl.g * (FP4A ? KBLKS : SF_KB) * p.M * (FP4A ? 4u : (u32)SF_BYTES));
-        } else {
-            a_base = p.A + (u64)tl.m0 * KB_A;
-            sfa_base = p.sfa;
-        }
-        a_rows_total = p.M;
-        const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
-        const u8* b_base = p.B + ((u64)(KG ? 0 : tl.g) * N + tl.n0) * KB_B;
-        const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * KB_A);
-        const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
-        const v4i rs_s = make_rsrc(sfa_base, (u32)(FP4A ? KBLKS : SF_KB) * a_rows_total * (FP4A ? 4u : (u32)SF_BYTES));
-        const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
-                         : KG ? make_rsrc(p.sfb, (u32)(p.kt / KBLK) * N * 4u)
-                              : make_rsrc((const u8*)p.sfb + (u64)tl.g * NBLKS * SF_KB * SF_BYTES,
-                                          (u32)NBLKS * SF_KB * (u32)SF_BYTES);
-        const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
-
-        // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
-        // writes LDS bytes [16 l, 16 l + 16) of its 1 KB: tile row RPI*i + l / (ROWB/16),
-        // K block h of the stage, physical chunk p = l % 8, which holds logical
-        // chunk p ^ (row & 7).  The lane part is kept in one register (two when
-        // RPI = 4, where the swizzle also depends on the parity of i) and the
-        // instruction's row offset i*RPI*K is added at issue.  Rows past the tile
-        // (ragged M or N) give offsets past the buffer's size: the load returns
-        // zeros without touching memory, and those rows are never stored.
-        auto lane_voff = [&](int i) {
-            const int r = i * RPI + lane / (ROWB / 16);
-            const int h = (lane % (ROWB / 16)) / 8;
-            const int c = (lane & 7) ^ (r & 7);
-            return (u32)(lane / (ROWB / 16)) * K + h * 128 + c * 16;
-        };
-        constexpr int NPAR = (RPI % 8) == 0 ? 1 : 8 / RPI;   // distinct (i*RPI) & 7 values
-        static_assert(NPAR == 1 || NPAR == 2, "rows per instruction");
-        u32 voff_rows[NPAR];
-#pragma unroll
-        for (int par = 0; par < NPAR; ++par) voff_rows[par] = lane_voff(par);
-        // FP4 B: lane l writes row l / 4 of the instruction's 16, physical chunk
-        // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
-        // swizzle term does not depend on the instruction (16 rows each)
-        const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-        const u32 voff_b4a = (u32)(lane >> 2) * KB_A + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);   // FP4 A
-        u32 voff_s[IS > 0 ? IS : 1];   // A scales: clamped rows (the offset includes the K block's row of sfa)
-#pragma unroll
-        for (int j = 0; j < IS; ++j) {
-            const int i = min(wave + j * NWAVES, NS_INS - 1);
-            const int h = i / NS_PER_KB;
-            const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
-            const int mm = m < a_rows_total ? m : a_rows_total - 1;
-            // FP4 A: word [m][kb] (row-major); otherwise sfa [kb][m] (MN-major)
-            voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * SF_BYTES + (u32)h * a_rows_total * SF_BYTES;
-        }
-        u32 voff_t[IT > 0 ? IT : 1];
-#pragma unroll
-        for (int j = 0; j < IT; ++j) {
-            // without repeats, wave NS_INS + h issues B-scale instruction h
-            const int h = DIET ? min(max(wave - NS_INS, 0), NT_INS - 1) : min(wave + j * NWAVES, NT_INS - 1);
-            if constexpr (FP4B) {
-                // word [n0 + 64 h + lane][kb]; rows past the tile read as zero
-                voff_t[j] = (u32)(64 * h + lane) * KBLKS * 4u;
-            } else if constexpr (KG) {
-                // sfb[kb][n0 + 64 h + lane], columns past N clamped (never stored)
-                voff_t[j] = (u32)min(tl.n0 + 64 * h + lane, N - 1) * 4u;
-            } else {
-                const int nb = min(nb_t0 + lane, NBLKS - 1);
-                // UE8M0 pairs: MN-major [K/256][NBLKS]; otherwise K-contiguous [NBLKS][SF_KB]
-                voff_t[j] = PAIRS ? (u32)nb * 2u : (u32)nb * SF_KB * 4u + (u32)h * 4u;
-            }
-        }
-
-        // one scale instruction per wave: an A-scale one (waves 0 .. NS_INS-1) or a B-scale one
-        const bool is_a_sc = wave < NS_INS;
-        const u32 voff_sc = is_a_sc ? voff_s[0] : voff_t[0];
-        const u32 lds_sc = __builtin_amdgcn_readfirstlane(
-            is_a_sc ? (u32)(S_OFF + wave * 256) : (u32)(T_OFF + min(max(wave - NS_INS, 0), NT_INS - 1) * 256));
-        v4i rs_sc = is_a_sc ? rs_s : rs_t;
-        rs_sc.x = __builtin_amdgcn_readfirstlane(rs_sc.x);
-        rs_sc.y = __builtin_amdgcn_readfirstlane(rs_sc.y);
-        rs_sc.z = __builtin_amdgcn_readfirstlane(rs_sc.z);
-        rs_sc.w = __builtin_amdgcn_readfirstlane(rs_sc.w);
-        // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
-        // (kb: first K block of the stage)
-        // index along K of the scales of K block kb (a word holds four UE8M0 scales)
-        auto sf_row = [](int kb) { return PAIRS ? kb >> 1 : SF_E8 ? kb >> 2 : kb; };
-        // scalar offset of K block kb's B scales: a row of the MN-major pairs, or a K-contiguous entry
-        auto sfb_soff = [](int kb) { return PAIRS ? (u32)(kb >> 1) * NBLKS * 2u : (u32)(SF_E8 ? kb >> 2 : kb) * 4u; };
-        // live = false: a placeholder load whose buffer size is zero, so it moves
-        // no data (every lane is out of range) but keeps the vmcnt count fixed.
-        auto issue_one = [&](int j, int kb, int stage, bool live = true) {
-            const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
-            auto lim = [&](v4i r) {
-                r.z = live ? r.z : 0;
-                return r;
-            };
-            if (j < IA) {
-                const int i = min(wave + j * NWAVES, NA_INS - 1);
-                if constexpr (FP4A)
-                    dma16(lim(rs_a), voff_b4a + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_A) * (u32)KB_A),
-                          __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + A_OFF + i * 1024);
-                else
-                    dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
-                          __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
-            } else if (j < IA + IB) {
-                const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
-                if constexpr (FP4B)
-                    dma16(lim(rs_b), voff_b4 + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_B) * (u32)KB_B),
-                          __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + B_OFF + i * 1024);
-                else
-                    dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
-                          __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
-            } else if (DIET) {
-                // this wave's scale instruction: resource, lane offset and LDS place chosen
-                // once per tile (rs_sc, voff_sc, lds_sc); only the K block's offset varies
-                const u32 soff = is_a_sc ? (FP4A ? (u32)kb * 4u : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES)
-                                         : (FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb));
-                dma_sf(lim(rs_sc), voff_sc, __builtin_amdgcn_readfirstlane(soff),
-                       __builtin_amdgcn_readfirstlane(st + lds_sc));
-            } else if (j < IA + IB + IS) {
-                const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
-                dma_sf(lim(rs_s), voff_s[j - IA - IB],
-                       __builtin_amdgcn_readfirstlane(FP4A ? (u32)kb * 4u
-                                                           : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES),
-                       st + S_OFF + i * 256);
-            } else {
-                const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
-                dma_sf(lim(rs_t), voff_t[j - IA - IB - IS],
-                       __builtin_amdgcn_readfirstlane(FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb)),
-                       st + T_OFF + h * 256);
-            }
-        };
-        auto issue_stage = [&](int kb, int stage, bool live = true) {
-#pragma unroll
-            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage, live);
-        };
-        // A ahead: instruction j of one iteration's issue, in the order B, sfb (K block
-        // kb_b into B slot sl_b), then A, sfa (K block kb_a into A slot sl_a), so that
-        // waiting until only the last IA + IS are in flight lands everything but A's.
-        auto issue_one_aa = [&](int j, int kb_a, int sl_a, bool live_a, int kb_b, int sl_b, bool live_b) {
-            auto lim = [&](v4i r, bool live) {
-                r.z = live ? r.z : 0;
-                return r;
-            };
-            const u32 sa_base = __builtin_amdgcn_readfirstlane(smem_base + sl_a * A_SLOT);
-            const u32 sb_base = __builtin_amdgcn_readfirstlane(smem_base + B_RING + sl_b * B_SLOT);
-            if (j < IB) {
-                const int i = min(wave + j * NWAVES, NB_INS - 1);
-                dma16(lim(rs_b, live_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
-                      __builtin_amdgcn_readfirstlane((u32)kb_b * KBLK), sb_base + i * 1024);
-            } else if (j < IB + IT) {
-                const int h = min(wave + (j - IB) * NWAVES, NT_INS - 1);
-                dma_sf(lim(rs_t, live_b), voff_t[j - IB], __builtin_amdgcn_readfirstlane(sfb_soff(kb_b)),
-                       sb_base + BN * ROWB_B + h * 256);
-            } else if (j < IB + IT + IA) {
-                const int i = min(wave + (j - IB - IT) * NWAVES, NA_INS - 1);
-                dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
-                      __builtin_amdgcn_readfirstlane((u32)kb_a * KBLK), sa_base + i * 1024);
-            } else {
-                const int i = min(wave + (j - IB - IT - IA) * NWAVES, NS_INS - 1);
-                dma_sf(lim(rs_s, live_a), voff_s[j - IB - IT - IA],
-                       __builtin_amdgcn_readfirstlane((u32)sf_row(kb_a) * a_rows_total * (u32)SF_BYTES),
-                       sa_base + BM * ROWB_A + i * 256);
-            }
-        };
-
-        // ---- accumulators
-        v4f acc[TM][TN];
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-        // MFMA results of the last n sub-tile of the previous K block and their
-        // scales: promoted while the next K block's first MFMAs run.
-        v4f p_carry[TM];
-        sc_t s_carry[TM];
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            p_carry[a] = v4f{0.f, 0.f, 0.f, 0.f};
-            s_carry[a] = 0.f;
-        }
-
-        // earlier tile's stores and LDS reads are finished before the ring is refilled
-        wait_vmcnt<0>();
-        __syncthreads();
-
-        const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
-        if constexpr (AAHEAD) {
-            // B and A of K block 0, then A of K block 1 (placeholders past the tile)
-#pragma unroll
-            for (int j = 0; j < INS_PER_WAVE; ++j) issue_one_aa(j, tl.kb0, 0, nst > 0, tl.kb0, 0, nst > 0);
-#pragma unroll
-            for (int j = IB + IT; j < INS_PER_WAVE; ++j)
-                issue_one_aa(j, tl.kb0 + min(1, nst - 1), 1, nst > 1, tl.kb0, 0, false);
-        } else {
-#pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s)
-                if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
-        }
-
-        // row offsets of this lane's fragments inside a stage
-        const int a_row0 = wm * WAVE_M + l16;   // + a*16
-        const int wave_n0 = tl.n0 + wn * WAVE_N;
-        // LDS byte offset of each n sub-tile's sfb inside a K block's sfb slice
-        int sb_off[TN];
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            int nblk = (wave_n0 + b * 16) / KBLK;
-            nblk = nblk < NBLKS ? nblk : NBLKS - 1;
-            sb_off[b] = __builtin_amdgcn_readfirstlane((nblk - nb_t0) * 4);
-        }
-
-        if constexpr (KSTEP == 1) {
-            // One K block per stage: the barrier sits in the last n sub-tile, where
-            // the next K block's fragments are fetched while its MFMAs run.
-            // LDS bases of one K block (stage slot, K block h inside the stage)
-            const u32 b_frag = b_frag_off + b_chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
-            const u32 a_frag = a_frag_off + a_chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
-            // B fragment of the sub-tile at byte offset off of a K block (lo/hi:
-            // the block's base plus this lane's chunk offsets)
-            auto read_fb = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
-                if constexpr (FP4B) return lds_read_frag4(lo, off);
-                else return lds_read_frag(lo, hi, off);
-            };
-            auto read_fa = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
-                if constexpr (FP4A) return lds_read_frag4(lo, off);
-                else return lds_read_frag(lo, hi, off);
-            };
-            // FP4 B scales: this lane's row of each n sub-tile, one word per K block
-            const int sb4_off = (wn * WAVE_N + l16) * 4;
-            const u32 sh_q = 8u * (u32)q;    // lane group q takes byte q (its 32-wide K block)
-            // LDS bases of the A tile, the B tile, the A scales and the B scales of a
-            // slot (one K block per stage here; with A ahead A and B have rings of their own)
-            auto a_tile = [&](int slot) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(
-                    smem_base + (AAHEAD ? slot * A_SLOT : slot * STAGE_BYTES + A_OFF));
-            };
-            auto b_tile = [&](int slot) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(
-                    smem_base + (AAHEAD ? B_RING + slot * B_SLOT : slot * STAGE_BYTES + B_OFF));
-            };
-            auto a_scales = [&](int slot) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(
-                    smem_base + (AAHEAD ? slot * A_SLOT + BM * ROWB_A : slot * STAGE_BYTES + S_OFF));
-            };
-            auto b_scales = [&](int slot) __attribute__((always_inline)) {
-                return (lds_u8*)__builtin_amdgcn_readfirstlane(
-                    smem_base + (AAHEAD ? B_RING + slot * B_SLOT + BN * ROWB_B : slot * STAGE_BYTES + T_OFF));
-            };
-            // Registers of the K block being multiplied: its A fragments, its first
-            // (then current) B fragment and the scales.  They are read from LDS one K
-            // block ahead, during the last n sub-tile of the previous one.
-            v8i fa[TM];
-            v8i fb;
-            float sa[TM];
-            sc_t sb[TN];
-            // K-grouped B scales: the lane's four columns of each n sub-tile
-            const int sbk_off = (wn * WAVE_N + 4 * q) * 4;
-            auto read_scales = [&](int slot_a, int slot_b) __attribute__((always_inline)) {
-                if constexpr (BF16) return;       // no scales
-                lds_u8* const sb_p = b_scales(slot_b);
-                if constexpr (FP4B) {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
-                } else if constexpr (KG) {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b)
-                        sb[b] = *(__attribute__((address_space(3))) const sc_t*)(sb_p + sbk_off + b * 64);
-                } else if constexpr (SB_UNIFORM) {
-                    sb[0] = lds_read_f32(sb_p, sb_off[0]);
-                } else {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
-                }
-                lds_u8* const sa_p = a_scales(slot_a) + a_row0 * 4;
-#pragma unroll
-                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, a * 64);
-            };
-
-            // stage 0 in LDS (this wave's DMA, then everyone's), then its registers
-            if constexpr (AAHEAD) wait_vmcnt<IA + IS>();     // all but A of K block 1
-            else if (STAGES - 1 <= nst) wait_stages<STAGES - 2>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-            {
-                lds_u8* const ka0 = a_tile(0);
-                lds_u8* const kb0 = b_tile(0);
-                read_scales(0, 0);
-#pragma unroll
-                for (int a = 0; a < TM; ++a) fa[a] = read_fa(ka0 + a_frag, ka0 + a_frag_hi, a * 16 * ROWB_A);
-                fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, 0);
-            }
-
+        const Tile tl0 = decode_tile(p, t);
+        // A contiguous row block of 256 rows holds two 128-row blocks of the
+        // layout; when their experts differ the tile is computed once for each
+        // (the epilogue stores a row only for its own expert).
 #pragma unroll 1
-            for (int it = 0; it < nst; ++it) {
-                const int stage = it % STAGES;
-                // The slot of stage it-1 is free: every wave read all of it into
-                // registers before the barrier in the previous iteration.  Its refill
-                // (the stage STAGES-1 ahead) is spread over the first MFMA steps.  In
-                // the last STAGES-1 iterations the refill is a placeholder that moves
-                // no data, so the loop has no branch and the number of stages in
-                // flight is always the same.
-                const bool live = it + STAGES - 1 < nst;
-                const int kb_fill = tl.kb0 + min(it + STAGES - 1, nst - 1) * KSTEP;
-                const int slot_fill = (it + STAGES - 1) % STAGES;
-                // A ahead: A of K block it+2 into its A slot, B of it+1 into its B slot
-                const int a_fill_slot = (it + 2) % A_SLOTS;
-                const int a_fill_kb = tl.kb0 + min(it + 2, nst - 1);
-                const bool a_live = it + 2 < nst;
-                // the K block after the last one of this stage: first of the next stage
-                const int stage_next = (it + 1) % STAGES;
-                const int a_slot = AAHEAD ? it % A_SLOTS : stage;
-                const int a_slot_next = AAHEAD ? (it + 1) % A_SLOTS : stage_next;
-#pragma unroll
-                for (int h = 0; h < KSTEP; ++h) {
-                lds_u8* const kbp = b_tile(stage);
-                lds_u8* const b_lo = kbp + b_frag;
-                lds_u8* const b_hi = kbp + b_frag_hi;
-                lds_u8* const kan = a_tile(a_slot_next);
-                lds_u8* const kbn = b_tile(stage_next);
-                (void)a_slot;
+        for (int piece = 0; piece < PIECES; ++piece) {
+            Tile tl = tl0;
+            if (piece == 1) {
+                if (tl0.g2 < 0) break;
+                tl.g = tl0.g2;
+                tl.skip = false;
+            }
+            if (tl.skip) continue;
 
-                float sab[TM];           // sa * sb for the uniform case
-                if constexpr (SB_UNIFORM && !SF_E8) {
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * first(sb[0]);
+            // ---- per-tile buffer resources (bases advanced to the tile's rows)
+            const u8* a_base;
+            const float* sfa_base;
+            int a_rows_total;        // rows of this A (for sfa stride)
+            if constexpr (kKind == 2) {
+                a_base = p.A + ((u64)tl.g * p.M + tl.m0) * KB_A;
+                sfa_base = (const float*)((const u8*)p.sfa +
+                                          (u64)tl.g * (FP4A ? KBLKS : SF_KB) * p.M * (FP4A ? 4u : (u32)SF_BYTES));
+            } else {
+                a_base = p.A + (u64)tl.m0 * KB_A;
+                sfa_base = p.sfa;
+            }
+            a_rows_total = p.M;
+            const int n_rows = N_END - tl.n0 < BN ? N_END - tl.n0 : BN;
+            const u8* b_base = p.B + ((u64)(KG ? 0 : tl.g) * N + tl.n0) * KB_B;
+            const v4i rs_a = make_rsrc(a_base, (u32)tl.rows * KB_A);
+            const v4i rs_b = make_rsrc(b_base, (u32)n_rows * KB_B);
+            const v4i rs_s = make_rsrc(sfa_base, (u32)(FP4A ? KBLKS : SF_KB) * a_rows_total * (FP4A ? 4u : (u32)SF_BYTES));
+            const v4i rs_t = FP4B ? make_rsrc(p.sfb + ((u64)tl.g * N + tl.n0) * KBLKS, (u32)n_rows * KBLKS * 4u)
+                             : KG ? make_rsrc(p.sfb, (u32)(p.kt / KBLK) * N * 4u)
+                                  : make_rsrc((const u8*)p.sfb + (u64)tl.g * NBLKS * SF_KB * SF_BYTES,
+                                              (u32)NBLKS * SF_KB * (u32)SF_BYTES);
+            const int nb_t0 = tl.n0 / KBLK;                  // first 128-row block of B in this tile
+
+            // ---- per-lane DMA offsets (fixed over K).  Lane l of an instruction
+            // writes LDS bytes [16 l, 16 l + 16) of its 1 KB: tile row RPI*i + l / (ROWB/16),
+            // K block h of the stage, physical chunk p = l % 8, which holds logical
+            // chunk p ^ (row & 7).  The lane part is kept in one register (two when
+            // RPI = 4, where the swizzle also depends on the parity of i) and the
+            // instruction's row offset i*RPI*K is added at issue.  Rows past the tile
+            // (ragged M or N) give offsets past the buffer's size: the load returns
+            // zeros without touching memory, and those rows are never stored.
+            auto lane_voff = [&](int i) {
+                const int r = i * RPI + lane / (ROWB / 16);
+                const int h = (lane % (ROWB / 16)) / 8;
+                const int c = (lane & 7) ^ (r & 7);
+                return (u32)(lane / (ROWB / 16)) * K + h * 128 + c * 16;
+            };
+            constexpr int NPAR = (RPI % 8) == 0 ? 1 : 8 / RPI;   // distinct (i*RPI) & 7 values
+            static_assert(NPAR == 1 || NPAR == 2, "rows per instruction");
+            u32 voff_rows[NPAR];
+    #pragma unroll
+            for (int par = 0; par < NPAR; ++par) voff_rows[par] = lane_voff(par);
+            // FP4 B: lane l writes row l / 4 of the instruction's 16, physical chunk
+            // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
+            // swizzle term does not depend on the instruction (16 rows each)
+            const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+            const u32 voff_b4a = (u32)(lane >> 2) * KB_A + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);   // FP4 A
+            u32 voff_s[IS > 0 ? IS : 1];   // A scales: clamped rows (the offset includes the K block's row of sfa)
+    #pragma unroll
+            for (int j = 0; j < IS; ++j) {
+                const int i = min(wave + j * NWAVES, NS_INS - 1);
+                const int h = i / NS_PER_KB;
+                const int m = tl.m0 + (i % NS_PER_KB) * 64 + lane;
+                const int mm = m < a_rows_total ? m : a_rows_total - 1;
+                // FP4 A: word [m][kb] (row-major); otherwise sfa [kb][m] (MN-major)
+                voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * SF_BYTES + (u32)h * a_rows_total * SF_BYTES;
+            }
+            u32 voff_t[IT > 0 ? IT : 1];
+    #pragma unroll
+            for (int j = 0; j < IT; ++j) {
+                // without repeats, wave NS_INS + h issues B-scale instruction h
+                const int h = DIET ? min(max(wave - NS_INS, 0), NT_INS - 1) : min(wave + j * NWAVES, NT_INS - 1);
+                if constexpr (FP4B) {
+                    // word [n0 + 64 h + lane][kb]; rows past the tile read as zero
+                    voff_t[j] = (u32)(64 * h + lane) * KBLKS * 4u;
+                } else if constexpr (KG) {
+                    // sfb[kb][n0 + 64 h + lane], columns past N clamped (never stored)
+                    voff_t[j] = (u32)min(tl.n0 + 64 * h + lane, N - 1) * 4u;
+                } else {
+                    const int nb = min(nb_t0 + lane, NBLKS - 1);
+                    // UE8M0 pairs: MN-major [K/256][NBLKS]; otherwise K-contiguous [NBLKS][SF_KB]
+                    voff_t[j] = PAIRS ? (u32)nb * 2u : (u32)nb * SF_KB * 4u + (u32)h * 4u;
                 }
-                // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
-                int ea[TM], eb[TN];
-                if constexpr (SF_E8) {
-                    const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> (FP4A ? sh_q : sh));
-#pragma unroll
-                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
-                        eb[b] = (int)(__builtin_bit_cast(u32, first(sb[b])) >> (FP4B ? sh_q : sh));
+            }
+
+            // one scale instruction per wave: an A-scale one (waves 0 .. NS_INS-1) or a B-scale one
+            const bool is_a_sc = wave < NS_INS;
+            const u32 voff_sc = is_a_sc ? voff_s[0] : voff_t[0];
+            const u32 lds_sc = __builtin_amdgcn_readfirstlane(
+                is_a_sc ? (u32)(S_OFF + wave * 256) : (u32)(T_OFF + min(max(wave - NS_INS, 0), NT_INS - 1) * 256));
+            v4i rs_sc = is_a_sc ? rs_s : rs_t;
+            rs_sc.x = __builtin_amdgcn_readfirstlane(rs_sc.x);
+            rs_sc.y = __builtin_amdgcn_readfirstlane(rs_sc.y);
+            rs_sc.z = __builtin_amdgcn_readfirstlane(rs_sc.z);
+            rs_sc.w = __builtin_amdgcn_readfirstlane(rs_sc.w);
+            // DMA instruction j (0 <= j < INS_PER_WAVE) of one stage for this wave
+            // (kb: first K block of the stage)
+            // index along K of the scales of K block kb (a word holds four UE8M0 scales)
+            auto sf_row = [](int kb) { return PAIRS ? kb >> 1 : SF_E8 ? kb >> 2 : kb; };
+            // scalar offset of K block kb's B scales: a row of the MN-major pairs, or a K-contiguous entry
+            auto sfb_soff = [](int kb) { return PAIRS ? (u32)(kb >> 1) * NBLKS * 2u : (u32)(SF_E8 ? kb >> 2 : kb) * 4u; };
+            // live = false: a placeholder load whose buffer size is zero, so it moves
+            // no data (every lane is out of range) but keeps the vmcnt count fixed.
+            auto issue_one = [&](int j, int kb, int stage, bool live = true) {
+                const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+                auto lim = [&](v4i r) {
+                    r.z = live ? r.z : 0;
+                    return r;
+                };
+                if (j < IA) {
+                    const int i = min(wave + j * NWAVES, NA_INS - 1);
+                    if constexpr (FP4A)
+                        dma16(lim(rs_a), voff_b4a + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_A) * (u32)KB_A),
+                              __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + A_OFF + i * 1024);
+                    else
+                        dma16(lim(rs_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
+                              __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + A_OFF + i * 1024);
+                } else if (j < IA + IB) {
+                    const int i = min(wave + (j - IA) * NWAVES, NB_INS - 1);
+                    if constexpr (FP4B)
+                        dma16(lim(rs_b), voff_b4 + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI_B) * (u32)KB_B),
+                              __builtin_amdgcn_readfirstlane((u32)kb * (KBLK / 2)), st + B_OFF + i * 1024);
+                    else
+                        dma16(lim(rs_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
+                              __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+                } else if (DIET) {
+                    // this wave's scale instruction: resource, lane offset and LDS place chosen
+                    // once per tile (rs_sc, voff_sc, lds_sc); only the K block's offset varies
+                    const u32 soff = is_a_sc ? (FP4A ? (u32)kb * 4u : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES)
+                                             : (FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb));
+                    dma_sf(lim(rs_sc), voff_sc, __builtin_amdgcn_readfirstlane(soff),
+                           __builtin_amdgcn_readfirstlane(st + lds_sc));
+                } else if (j < IA + IB + IS) {
+                    const int i = min(wave + (j - IA - IB) * NWAVES, NS_INS - 1);
+                    dma_sf(lim(rs_s), voff_s[j - IA - IB],
+                           __builtin_amdgcn_readfirstlane(FP4A ? (u32)kb * 4u
+                                                               : (u32)sf_row(kb) * a_rows_total * (u32)SF_BYTES),
+                           st + S_OFF + i * 256);
+                } else {
+                    const int h = min(wave + (j - IA - IB - IS) * NWAVES, NT_INS - 1);
+                    dma_sf(lim(rs_t), voff_t[j - IA - IB - IS],
+                           __builtin_amdgcn_readfirstlane(FP4B ? (u32)kb * 4u : KG ? (u32)kb * N * 4u : sfb_soff(kb)),
+                           st + T_OFF + h * 256);
+                }
+            };
+            auto issue_stage = [&](int kb, int stage, bool live = true) {
+    #pragma unroll
+                for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage, live);
+            };
+            // split refill: B instruction of half `hi` with index bi inside that half
+            auto issue_b_half = [&](int bi, bool hi, int kb, int stage, bool live) {
+                const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+                v4i r = rs_b;
+                r.z = live ? r.z : 0;
+                const int i = (bi / TN) * (2 * TN) + (hi ? TN : 0) + bi % TN;
+                dma16(r, voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
+                      __builtin_amdgcn_readfirstlane((u32)kb * KBLK), st + B_OFF + i * 1024);
+            };
+            // instruction j of the mid group (A, first-half B rows, scales) and of the end group
+            auto issue_mid = [&](int j, int kb, int stage, bool live) {
+                if (j < IA) issue_one(j, kb, stage, live);
+                else if (j < IA + IBH) issue_b_half(min(wave + (j - IA) * NWAVES, NB_HALF - 1), false, kb, stage, live);
+                else issue_one(j - IBH + IB, kb, stage, live);
+            };
+            auto issue_end = [&](int j, int kb, int stage, bool live) {
+                issue_b_half(min(wave + j * NWAVES, NB_HALF - 1), true, kb, stage, live);
+            };
+            // A ahead: instruction j of one iteration's issue, in the order B, sfb (K block
+            // kb_b into B slot sl_b), then A, sfa (K block kb_a into A slot sl_a), so that
+            // waiting until only the last IA + IS are in flight lands everything but A's.
+            auto issue_one_aa = [&](int j, int kb_a, int sl_a, bool live_a, int kb_b, int sl_b, bool live_b) {
+                auto lim = [&](v4i r, bool live) {
+                    r.z = live ? r.z : 0;
+                    return r;
+                };
+                const u32 sa_base = __builtin_amdgcn_readfirstlane(smem_base + sl_a * A_SLOT);
+                const u32 sb_base = __builtin_amdgcn_readfirstlane(smem_base + B_RING + sl_b * B_SLOT);
+                if (j < IB) {
+                    const int i = min(wave + j * NWAVES, NB_INS - 1);
+                    dma16(lim(rs_b, live_b), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
+                          __builtin_amdgcn_readfirstlane((u32)kb_b * KBLK), sb_base + i * 1024);
+                } else if (j < IB + IT) {
+                    const int h = min(wave + (j - IB) * NWAVES, NT_INS - 1);
+                    dma_sf(lim(rs_t, live_b), voff_t[j - IB], __builtin_amdgcn_readfirstlane(sfb_soff(kb_b)),
+                           sb_base + BN * ROWB_B + h * 256);
+                } else if (j < IB + IT + IA) {
+                    const int i = min(wave + (j - IB - IT) * NWAVES, NA_INS - 1);
+                    dma16(lim(rs_a, live_a), voff_rows[i % NPAR] + (u32)__builtin_amdgcn_readfirstlane((u32)(i * RPI) * (u32)K),
+                          __builtin_amdgcn_readfirstlane((u32)kb_a * KBLK), sa_base + i * 1024);
+                } else {
+                    const int i = min(wave + (j - IB - IT - IA) * NWAVES, NS_INS - 1);
+                    dma_sf(lim(rs_s, live_a), voff_s[j - IB - IT - IA],
+                           __builtin_amdgcn_readfirstlane((u32)sf_row(kb_a) * a_rows_total * (u32)SF_BYTES),
+                           sa_base + BM * ROWB_A + i * 256);
+                }
+            };
+
+            // ---- accumulators
+            v4f acc[TM][TN];
+    #pragma unroll
+            for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+            // MFMA results of the last n sub-tile of the previous K block and their
+            // scales: promoted while the next K block's first MFMAs run.
+            v4f p_carry[TM];
+            sc_t s_carry[TM];
+    #pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                p_carry[a] = v4f{0.f, 0.f, 0.f, 0.f};
+                s_carry[a] = 0.f;
+            }
+
+            // earlier tile's stores and LDS reads are finished before the ring is refilled
+            wait_vmcnt<0>();
+            __syncthreads();
+
+            const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
+            if constexpr (AAHEAD) {
+                // B and A of K block 0, then A of K block 1 (placeholders past the tile)
+    #pragma unroll
+                for (int j = 0; j < INS_PER_WAVE; ++j) issue_one_aa(j, tl.kb0, 0, nst > 0, tl.kb0, 0, nst > 0);
+    #pragma unroll
+                for (int j = IB + IT; j < INS_PER_WAVE; ++j)
+                    issue_one_aa(j, tl.kb0 + min(1, nst - 1), 1, nst > 1, tl.kb0, 0, false);
+            } else if constexpr (SPLIT) {
+                // K blocks 0 .. STAGES-1 without the end group of the last (issued in the
+                // first steps of block 0); placeholders past the tile keep the counts fixed
+    #pragma unroll
+                for (int s = 0; s < STAGES; ++s) {
+    #pragma unroll
+                    for (int j = 0; j < G_MID; ++j) issue_mid(j, tl.kb0 + min(s, nst - 1), s, s < nst);
+                    if (s + 1 < STAGES) {
+    #pragma unroll
+                        for (int j = 0; j < G_END; ++j) issue_end(j, tl.kb0 + min(s, nst - 1), s, s < nst);
+                    }
+                }
+            } else {
+    #pragma unroll
+                for (int s = 0; s < STAGES - 1; ++s)
+                    if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
+            }
+
+            // row offsets of this lane's fragments inside a stage
+            const int a_row0 = wm * WAVE_M + l16;   // + a*16
+            const int wave_n0 = tl.n0 + wn * WAVE_N;
+            // LDS byte offset of each n sub-tile's sfb inside a K block's sfb slice
+            int sb_off[TN];
+    #pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                int nblk = (wave_n0 + b * 16) / KBLK;
+                nblk = nblk < NBLKS ? nblk : NBLKS - 1;
+                sb_off[b] = __builtin_amdgcn_readfirstlane((nblk - nb_t0) * 4);
+            }
+
+            if constexpr (KSTEP == 1) {
+                // One K block per stage: the barrier sits in the last n sub-tile, where
+                // the next K block's fragments are fetched while its MFMAs run.
+                // LDS bases of one K block (stage slot, K block h inside the stage)
+                const u32 b_frag = b_frag_off + b_chunk_lo, b_frag_hi = b_frag_off + chunk_hi;
+                const u32 a_frag = a_frag_off + a_chunk_lo, a_frag_hi = a_frag_off + chunk_hi;
+                // B fragment of the sub-tile at byte offset off of a K block (lo/hi:
+                // the block's base plus this lane's chunk offsets)
+                auto read_fb = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
+                    if constexpr (FP4B) return lds_read_frag4(lo, off);
+                    else return lds_read_frag(lo, hi, off);
+                };
+                auto read_fa = [&](lds_u8* lo, lds_u8* hi, int off) __attribute__((always_inline)) {
+                    if constexpr (FP4A) return lds_read_frag4(lo, off);
+                    else return lds_read_frag(lo, hi, off);
+                };
+                // FP4 B scales: this lane's row of each n sub-tile, one word per K block
+                const int sb4_off = (wn * WAVE_N + l16) * 4;
+                const u32 sh_q = 8u * (u32)q;    // lane group q takes byte q (its 32-wide K block)
+                // LDS bases of the A tile, the B tile, the A scales and the B scales of a
+                // slot (one K block per stage here; with A ahead A and B have rings of their own)
+                auto a_tile = [&](int slot) __attribute__((always_inline)) {
+                    return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                        smem_base + (AAHEAD ? slot * A_SLOT : slot * STAGE_BYTES + A_OFF));
+                };
+                auto b_tile = [&](int slot) __attribute__((always_inline)) {
+                    return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                        smem_base + (AAHEAD ? B_RING + slot * B_SLOT : slot * STAGE_BYTES + B_OFF));
+                };
+                auto a_scales = [&](int slot) __attribute__((always_inline)) {
+                    return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                        smem_base + (AAHEAD ? slot * A_SLOT + BM * ROWB_A : slot * STAGE_BYTES + S_OFF));
+                };
+                auto b_scales = [&](int slot) __attribute__((always_inline)) {
+                    return (lds_u8*)__builtin_amdgcn_readfirstlane(
+                        smem_base + (AAHEAD ? B_RING + slot * B_SLOT + BN * ROWB_B : slot * STAGE_BYTES + T_OFF));
+                };
+                // Registers of the K block being multiplied: its A fragments, its first
+                // (then current) B fragment and the scales.  They are read from LDS one K
+                // block ahead, during the last n sub-tile of the previous one.
+                v8i fa[TM];
+                v8i fb;
+                float sa[TM];
+                sc_t sb[TN];
+                // K-grouped B scales: the lane's four columns of each n sub-tile
+                const int sbk_off = (wn * WAVE_N + 4 * q) * 4;
+                auto read_scales = [&](int slot_a, int slot_b) __attribute__((always_inline)) {
+                    if constexpr (BF16) return;       // no scales
+                    lds_u8* const sb_p = b_scales(slot_b);
+                    if constexpr (FP4B) {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
+                    } else if constexpr (KG) {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            sb[b] = *(__attribute__((address_space(3))) const sc_t*)(sb_p + sbk_off + b * 64);
+                    } else if constexpr (SB_UNIFORM) {
+                        sb[0] = lds_read_f32(sb_p, sb_off[0]);
+                    } else {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
+                    }
+                    lds_u8* const sa_p = a_scales(slot_a) + a_row0 * 4;
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, a * 64);
+                };
+
+                // stage 0 in LDS (this wave's DMA, then everyone's), then its registers
+                if constexpr (AAHEAD) wait_vmcnt<IA + IS>();     // all but A of K block 1
+                else if constexpr (SPLIT) wait_vmcnt<SPLIT_PENDING>();   // the mid group of block 0
+                else if (STAGES - 1 <= nst) wait_stages<STAGES - 2>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                {
+                    lds_u8* const ka0 = a_tile(0);
+                    lds_u8* const kb0 = b_tile(0);
+                    read_scales(0, 0);
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a) fa[a] = read_fa(ka0 + a_frag, ka0 + a_frag_hi, a * 16 * ROWB_A);
+                    fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, 0);
                 }
 
-                // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
-                // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
-                // last sub-tile of the previous K block).
-                v4f pr[TM];
-#pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    if (h == 0) {
-                        if constexpr (AAHEAD) {
-                            const int nspread = SPREAD == 0 ? 1 : SPREAD;
-                            if (b < nspread) {
-#pragma unroll
-                                for (int j = b * INS_PER_WAVE / nspread; j < (b + 1) * INS_PER_WAVE / nspread; ++j)
-                                    issue_one_aa(j, a_fill_kb, a_fill_slot, a_live, kb_fill, slot_fill, live);
+    #pragma unroll 1
+                for (int it = 0; it < nst; ++it) {
+                    const int stage = it % STAGES;
+                    // The slot of stage it-1 is free: every wave read all of it into
+                    // registers before the barrier in the previous iteration.  Its refill
+                    // (the stage STAGES-1 ahead) is spread over the first MFMA steps.  In
+                    // the last STAGES-1 iterations the refill is a placeholder that moves
+                    // no data, so the loop has no branch and the number of stages in
+                    // flight is always the same.
+                    const bool live = it + STAGES - 1 < nst;
+                    const int kb_fill = tl.kb0 + min(it + STAGES - 1, nst - 1) * KSTEP;
+                    const int slot_fill = (it + STAGES - 1) % STAGES;
+                    // A ahead: A of K block it+2 into its A slot, B of it+1 into its B slot
+                    const int a_fill_slot = (it + 2) % A_SLOTS;
+                    const int a_fill_kb = tl.kb0 + min(it + 2, nst - 1);
+                    const bool a_live = it + 2 < nst;
+                    // the K block after the last one of this stage: first of the next stage
+                    const int stage_next = (it + 1) % STAGES;
+                    const int a_slot = AAHEAD ? it % A_SLOTS : stage;
+                    const int a_slot_next = AAHEAD ? (it + 1) % A_SLOTS : stage_next;
+    #pragma unroll
+                    for (int h = 0; h < KSTEP; ++h) {
+                    lds_u8* const kbp = b_tile(stage);
+                    lds_u8* const b_lo = kbp + b_frag;
+                    lds_u8* const b_hi = kbp + b_frag_hi;
+                    lds_u8* const kan = a_tile(a_slot_next);
+                    lds_u8* const kbn = b_tile(stage_next);
+                    (void)a_slot;
+
+                    float sab[TM];           // sa * sb for the uniform case
+                    if constexpr (SB_UNIFORM && !SF_E8) {
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) sab[a] = sa[a] * first(sb[0]);
+                    }
+                    // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
+                    int ea[TM], eb[TN];
+                    if constexpr (SF_E8) {
+                        const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> (FP4A ? sh_q : sh));
+    #pragma unroll
+                        for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
+                            eb[b] = (int)(__builtin_bit_cast(u32, first(sb[b])) >> (FP4B ? sh_q : sh));
+                    }
+
+                    // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
+                    // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
+                    // last sub-tile of the previous K block).
+                    v4f pr[TM];
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b) {
+                        if constexpr (SPLIT) {
+                            // end group of block it + STAGES - 1 (into the slot block it - 1 used),
+                            // then, after the mid barrier, the mid group of block it + STAGES
+                            // (into this block's slot)
+                            if (b < END_STEPS) {
+                                const int f = it + STAGES - 1;
+    #pragma unroll
+                                for (int j = b * G_END / END_STEPS; j < (b + 1) * G_END / END_STEPS; ++j)
+                                    issue_end(j, tl.kb0 + min(f, nst - 1), f % STAGES, f < nst);
                             }
-                        } else if constexpr (SPREAD == 0) {
-                            if (b == 0) issue_stage(kb_fill, slot_fill, live);
-                        } else if (b < SPREAD) {
-#pragma unroll
-                            for (int j = b * INS_PER_WAVE / SPREAD; j < (b + 1) * INS_PER_WAVE / SPREAD; ++j)
-                                issue_one(j, kb_fill, slot_fill, live);
+                            if (b + 1 == HALF_TN) {
+                                wait_vmcnt<SPLIT_PENDING>();      // end group of this block landed
+                                __syncthreads();
+                            }
+                            if (b + 1 >= HALF_TN && b + 1 < TN) {
+                                const int f = it + STAGES, sb = b + 1 - HALF_TN;
+    #pragma unroll
+                                for (int j = sb * G_MID / MID_STEPS; j < (sb + 1) * G_MID / MID_STEPS; ++j)
+                                    issue_mid(j, tl.kb0 + min(f, nst - 1), stage, f < nst);
+                            }
+                        } else if (h == 0) {
+                            if constexpr (AAHEAD) {
+                                const int nspread = SPREAD == 0 ? 1 : SPREAD;
+                                if (b < nspread) {
+    #pragma unroll
+                                    for (int j = b * INS_PER_WAVE / nspread; j < (b + 1) * INS_PER_WAVE / nspread; ++j)
+                                        issue_one_aa(j, a_fill_kb, a_fill_slot, a_live, kb_fill, slot_fill, live);
+                                }
+                            } else if constexpr (SPREAD == 0) {
+                                if (b == 0) issue_stage(kb_fill, slot_fill, live);
+                            } else if (b < SPREAD) {
+    #pragma unroll
+                                for (int j = b * INS_PER_WAVE / SPREAD; j < (b + 1) * INS_PER_WAVE / SPREAD; ++j)
+                                    issue_one(j, kb_fill, slot_fill, live);
+                            }
                         }
-                    }
-                    const bool last = b + 1 == TN;
-                    v8i fb_next;
-                    if (!last) fb_next = read_fb(b_lo, b_hi, (b + 1) * 16 * ROWB_B);
-                    // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
-                    // b itself (carried), taken before the next K block's replace them
-                    sc_t sc_prev[TM], s_last[TM];
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) {
-                        if constexpr (SF_E8 || BF16) sc_prev[a] = s_last[a] = 0.f;
-                        else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
-                        else {
-                            sc_prev[a] = sa[a] * sb[b > 0 ? b - 1 : 0];
-                            if (b == 0) sc_prev[a] = 0.f;
-                            s_last[a] = sa[a] * sb[b];
+                        const bool last = b + 1 == TN;
+                        v8i fb_next;
+                        if (!last) fb_next = read_fb(b_lo, b_hi, (b + 1) * 16 * ROWB_B);
+                        // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
+                        // b itself (carried), taken before the next K block's replace them
+                        sc_t sc_prev[TM], s_last[TM];
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) {
+                            if constexpr (SF_E8 || BF16) sc_prev[a] = s_last[a] = 0.f;
+                            else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
+                            else {
+                                sc_prev[a] = sa[a] * sb[b > 0 ? b - 1 : 0];
+                                if (b == 0) sc_prev[a] = 0.f;
+                                s_last[a] = sa[a] * sb[b];
+                            }
                         }
-                    }
-                    if (last) {
-                        if (h + 1 == KSTEP) {
-                            // next stage landed (own DMA; the later stages pending), then
-                            // everyone's; all reads of this stage are in registers.  A ahead:
-                            // everything but A of K block it+2 (issued last) has landed
-                            if constexpr (AAHEAD) wait_vmcnt<IA + IS>();
-                            else wait_stages<STAGES - 2>();
-                            __syncthreads();
+                        if (last) {
+                            if (h + 1 == KSTEP) {
+                                // next stage landed (own DMA; the later stages pending), then
+                                // everyone's; all reads of this stage are in registers.  A ahead:
+                                // everything but A of K block it+2 (issued last) has landed
+                                if constexpr (AAHEAD) wait_vmcnt<IA + IS>();
+                                else if constexpr (SPLIT) wait_vmcnt<SPLIT_PENDING>();   // next block's mid group
+                                else wait_stages<STAGES - 2>();
+                                __syncthreads();
+                            }
+                            read_scales(a_slot_next, stage_next);
                         }
-                        read_scales(a_slot_next, stage_next);
-                    }
-                    v4f prev[TM];
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) prev[a] = pr[a];
-                    // optional: the wave asks for issue priority while it has MFMAs to issue
-                    if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(DG_SETPRIO);
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) {
-                        if constexpr (SF_E8) {
-                            // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
-                            // scales (its srcA is B, scaled by eb; its srcB is A, by ea).
-                            // operand formats: 0 = E4M3, 4 = E2M1 (srcA: B, srcB: A)
-                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                fb, fa[a], acc[a][b], FP4B ? 4 : 0, FP4A ? 4 : 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
-                        } else if constexpr (BF16) {
-                            // 64 BF16 elements: K chunks q (elements 8q..8q+7) then q+4 (32+8q..)
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_lo(fb), bf_lo(fa[a]), acc[a][b], 0, 0, 0);
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_hi(fb), bf_hi(fa[a]), acc[a][b], 0, 0, 0);
+                        v4f prev[TM];
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+                        // optional: the wave asks for issue priority while it has MFMAs to issue
+                        if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(DG_SETPRIO);
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) {
+                            if constexpr (SF_E8) {
+                                // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
+                                // scales (its srcA is B, scaled by eb; its srcB is A, by ea).
+                                // operand formats: 0 = E4M3, 4 = E2M1 (srcA: B, srcB: A)
+                                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fb, fa[a], acc[a][b], FP4B ? 4 : 0, FP4A ? 4 : 0, 0, eb[SB_UNIFORM ? 0 : b], 0, ea[a]);
+                            } else if constexpr (BF16) {
+                                // 64 BF16 elements: K chunks q (elements 8q..8q+7) then q+4 (32+8q..)
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_lo(fb), bf_lo(fa[a]), acc[a][b], 0, 0, 0);
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_hi(fb), bf_hi(fa[a]), acc[a][b], 0, 0, 0);
+                            } else {
+                                const v4f zero = {0.f, 0.f, 0.f, 0.f};
+                                // P[n][m] over this 128-wide K block: exact products, FP32 sums
+                                pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
+                                if (b == 0) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                                else acc[a][b - 1] += prev[a] * sc_prev[a];
+                            }
+                            // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
+                            // (after the tile's last block these reads are unused)
+                            if (last) fa[a] = read_fa(kan + a_frag, kan + a_frag_hi, a * 16 * ROWB_A);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(0);
+                        if (!last) {
+                            fb = fb_next;
                         } else {
+                            fb = read_fb(kbn + b_frag, kbn + b_frag_hi, 0);
+    #pragma unroll
+                            for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
+                        }
+                    }
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a) p_carry[a] = pr[a];
+                    }   // K blocks of the stage
+                }
+                wait_vmcnt<0>();         // no DMA (placeholders included) outlives the tile
+            } else {
+                // Two K blocks per stage (short K loops): barrier at the top of each
+                // stage, fragments read at the start of each K block.
+    #pragma unroll 1
+                for (int it = 0; it < nst; ++it) {
+                    const int stage = it % STAGES;
+                    // stage `it` has landed (for this wave) once at most the later stages are pending
+                    if (it + STAGES - 1 <= nst) wait_stages<STAGES - 2>();
+                    else wait_vmcnt<0>();
+                    __syncthreads();
+                    // Refill the slot every wave finished reading last iteration.  With two
+                    // slots the refill is needed by the next iteration, so it goes out
+                    // at once; with three or more it is spread over this iteration's
+                    // MFMA steps, so no wave stalls on a burst of vector-memory issue.
+                    const bool refill = it + STAGES - 1 < nst;
+                    const int kb_fill = tl.kb0 + (it + STAGES - 1) * KSTEP, slot_fill = (it + STAGES - 1) % STAGES;
+                    if constexpr (STAGES == 2) {
+                        if (refill) issue_stage(kb_fill, slot_fill);
+                    }
+
+                    const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
+    #pragma unroll
+                    for (int h = 0; h < KSTEP; ++h) {
+                    const int kb = tl.kb0 + it * KSTEP + h;
+                    // scale of B from the stage (same address in every lane: a broadcast read)
+                    lds_u8* const sb_p = (lds_u8*)(st + T_OFF + h * 256);
+                    float sb[TN];
+                    if constexpr (SB_UNIFORM) {
+                        sb[0] = lds_read_f32(sb_p, sb_off[0]);
+                    } else {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
+                    }
+                    lds_u8* const stp = (lds_u8*)(st + h * 128);
+                    lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
+                    lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
+                    lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
+                    lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
+                    lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
+
+                    float sa[TM];
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
+                    v8i fa[TM];
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
+                    v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
+
+                    float sab[TM];           // sa * sb for the uniform case
+                    if constexpr (SB_UNIFORM && !SF_E8) {
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
+                    }
+                    // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
+                    int ea[TM], eb[TN];
+                    if constexpr (SF_E8) {
+                        const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
+    #pragma unroll
+                        for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
+                    }
+
+                    // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
+                    // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
+                    // last sub-tile of the previous K block).
+                    v4f pr[TM];
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b) {
+                        if constexpr (STAGES > 2) {
+                            if (refill && h == 0) {
+    #pragma unroll
+                                for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
+                                    issue_one(j, kb_fill, slot_fill);
+                            }
+                        }
+                        v8i fb_next;
+                        if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
+                        v4f prev[TM];
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) prev[a] = pr[a];
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a) {
                             const v4f zero = {0.f, 0.f, 0.f, 0.f};
                             // P[n][m] over this 128-wide K block: exact products, FP32 sums
                             pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
-                            if (b == 0) acc[a][TN - 1] += p_carry[a] * s_carry[a];
-                            else acc[a][b - 1] += prev[a] * sc_prev[a];
+                            if (b == 0) {
+                                acc[a][TN - 1] += p_carry[a] * s_carry[a];
+                            } else {
+                                float sc;
+                                if constexpr (SB_UNIFORM) sc = sab[a];
+                                else sc = sa[a] * sb[b - 1];
+                                acc[a][b - 1] += prev[a] * sc;
+                            }
                         }
-                        // the last sub-tile's MFMA has taken fa[a]: fetch the next K block's
-                        // (after the tile's last block these reads are unused)
-                        if (last) fa[a] = read_fa(kan + a_frag, kan + a_frag_hi, a * 16 * ROWB_A);
-                        __builtin_amdgcn_sched_barrier(0);
+                        if (b + 1 < TN) fb = fb_next;
                     }
-                    if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(0);
-                    if (!last) {
-                        fb = fb_next;
-                    } else {
-                        fb = read_fb(kbn + b_frag, kbn + b_frag_hi, 0);
-#pragma unroll
-                        for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
-                    }
-                }
-#pragma unroll
-                for (int a = 0; a < TM; ++a) p_carry[a] = pr[a];
-                }   // K blocks of the stage
-            }
-            wait_vmcnt<0>();         // no DMA (placeholders included) outlives the tile
-        } else {
-            // Two K blocks per stage (short K loops): barrier at the top of each
-            // stage, fragments read at the start of each K block.
-#pragma unroll 1
-            for (int it = 0; it < nst; ++it) {
-                const int stage = it % STAGES;
-                // stage `it` has landed (for this wave) once at most the later stages are pending
-                if (it + STAGES - 1 <= nst) wait_stages<STAGES - 2>();
-                else wait_vmcnt<0>();
-                __syncthreads();
-                // Refill the slot every wave finished reading last iteration.  With two
-                // slots the refill is needed by the next iteration, so it goes out
-                // at once; with three or more it is spread over this iteration's
-                // MFMA steps, so no wave stalls on a burst of vector-memory issue.
-                const bool refill = it + STAGES - 1 < nst;
-                const int kb_fill = tl.kb0 + (it + STAGES - 1) * KSTEP, slot_fill = (it + STAGES - 1) % STAGES;
-                if constexpr (STAGES == 2) {
-                    if (refill) issue_stage(kb_fill, slot_fill);
-                }
-
-                const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
-#pragma unroll
-                for (int h = 0; h < KSTEP; ++h) {
-                const int kb = tl.kb0 + it * KSTEP + h;
-                // scale of B from the stage (same address in every lane: a broadcast read)
-                lds_u8* const sb_p = (lds_u8*)(st + T_OFF + h * 256);
-                float sb[TN];
-                if constexpr (SB_UNIFORM) {
-                    sb[0] = lds_read_f32(sb_p, sb_off[0]);
-                } else {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
-                }
-                lds_u8* const stp = (lds_u8*)(st + h * 128);
-                lds_u8* const sa_p = (lds_u8*)(st + h * S_BYTES) + a_row0 * 4;
-                lds_u8* const a_lo = stp + a_frag_off + chunk_lo;
-                lds_u8* const a_hi = stp + a_frag_off + chunk_hi;
-                lds_u8* const b_lo = stp + b_frag_off + chunk_lo;
-                lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
-
-                float sa[TM];
-#pragma unroll
-                for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
-                v8i fa[TM];
-#pragma unroll
-                for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
-                v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
-
-                float sab[TM];           // sa * sb for the uniform case
-                if constexpr (SB_UNIFORM && !SF_E8) {
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
-                }
-                // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
-                int ea[TM], eb[TN];
-                if constexpr (SF_E8) {
-                    const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
-#pragma unroll
-                    for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
-                }
-
-                // Software pipeline over the n sub-tiles: the MFMAs of sub-tile b
-                // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
-                // last sub-tile of the previous K block).
-                v4f pr[TM];
-#pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    if constexpr (STAGES > 2) {
-                        if (refill && h == 0) {
-#pragma unroll
-                            for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
-                                issue_one(j, kb_fill, slot_fill);
-                        }
-                    }
-                    v8i fb_next;
-                    if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
-                    v4f prev[TM];
-#pragma unroll
-                    for (int a = 0; a < TM; ++a) prev[a] = pr[a];
-#pragma unroll
+    #pragma unroll
                     for (int a = 0; a < TM; ++a) {
-                        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-                        // P[n][m] over this 128-wide K block: exact products, FP32 sums
-                        pr[a] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[a], zero, 0, 0, 0, 0, 0, 0);
-                        if (b == 0) {
-                            acc[a][TN - 1] += p_carry[a] * s_carry[a];
-                        } else {
-                            float sc;
-                            if constexpr (SB_UNIFORM) sc = sab[a];
-                            else sc = sa[a] * sb[b - 1];
-                            acc[a][b - 1] += prev[a] * sc;
-                        }
+                        p_carry[a] = pr[a];
+                        if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
+                        else s_carry[a] = sa[a] * sb[TN - 1];
                     }
-                    if (b + 1 < TN) fb = fb_next;
+                    }   // K blocks of the stage
                 }
-#pragma unroll
-                for (int a = 0; a < TM; ++a) {
-                    p_carry[a] = pr[a];
-                    if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
-                    else s_carry[a] = sa[a] * sb[TN - 1];
-                }
-                }   // K blocks of the stage
             }
-        }
-        if constexpr (!SF_E8 && !BF16) {
-#pragma unroll
-            for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
-        }
+            if constexpr (!SF_E8 && !BF16) {
+    #pragma unroll
+                for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
+            }
 
-        finish_tile<TM, TN>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag);
+            finish_tile<TM, TN>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag);
+        }   // pieces
     }
 }
 

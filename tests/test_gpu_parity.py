@@ -130,6 +130,26 @@ def test_workload_masked(oracle):
     _compare(p, D, sent, ref, comp, rows=rows, what=gen.WORKLOAD_NAMES[4])
 
 
+# ------------------------------------------------------------------ contiguous, 256-row blocks
+@pytest.mark.parametrize("forced", ["256,256,4,2,2,1,1,0", "256,256,4,2,2,1,1,6", "256,128,4,2,3,1,1,6",
+                                    "256,224,4,2,2,1,1,4"])
+@pytest.mark.parametrize("group_rows,N,K,pad", [
+    ([128, 384, 0, 256, 100], 300, 512, 128),    # blocks of 256 rows that hold two experts
+    ([256, 256, 512], 520, 384, 0),              # every block one expert
+    ([100, 1, 129], 96, 256, 128),               # padding and an odd tail (M = 512)
+])
+def test_contiguous_256_row_blocks(oracle, monkeypatch, forced, group_rows, N, K, pad):
+    """Row blocks of 256 rows in the contiguous form: a block whose two 128-row halves
+    name different experts is computed once for each, so every row gets its own
+    expert's result; padding rows stay untouched."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    for e8 in (False, True):
+        p = gen.make_contiguous(group_rows, N, K, seed=sum(group_rows) + N + K, with_c=True, pad_rows=pad, ue8m0=e8)
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"contiguous {group_rows} {forced} ue8m0={e8}")
+
+
 # ------------------------------------------------------------------ contiguous, edge cases
 @pytest.mark.parametrize("group_rows,N,K,pad,with_c", [
     ([128, 0, 256, 100], 200, 256, 128, True),
@@ -160,7 +180,8 @@ def test_contiguous_groups_independent(oracle):
         (-D1.float())[idx == 1], D2.float()[idx == 1])
 
 
-@pytest.mark.parametrize("forced", [None, "128,128,4,2,2,1,1,0", "64,96,2,2,4,1,1,0", "32,64,1,2,3,1,1,0"])
+@pytest.mark.parametrize("forced", [None, "128,128,4,2,2,1,1,0", "64,96,2,2,4,1,1,0", "32,64,1,2,3,1,1,0",
+                                    "256,256,4,2,2,1,1,0", "256,128,4,2,3,1,1,6"])
 def test_contiguous_mixed_blocks_never_use_another_experts_weights(oracle, monkeypatch, forced):
     """Aligned blocks that break the layout (rows naming another expert inside a
     block, a block that starts with a padding row): whatever the tile size, every
@@ -226,6 +247,11 @@ FORCED = [
     "64,192,1,4,4,2,1,2",
     "128,64,1,4,4,1,1,2",
     "32,48,1,1,3,4,1,2",
+    # variant 6: both operands through LDS, each slot refilled in two parts
+    "256,256,4,2,2,1,1,6",
+    "128,128,2,2,3,1,1,6",
+    "64,128,1,2,4,2,1,6",
+    "128,256,4,2,3,1,1,6",
     # variant 3: B straight into VGPRs, a producer wave streams A through LDS
     "128,96,1,6,3,1,1,3",
     "64,64,1,4,3,1,1,3",
@@ -299,6 +325,47 @@ def test_a_ahead_variant(oracle, monkeypatch, forced):
             D, sent = run(pc)
             ref, comp = oracle_rows(oracle, pc)
             _compare(pc, D, sent, ref, comp, what=f"contiguous {forced} ue8m0={e8}")
+
+
+@pytest.mark.parametrize("forced", ["256,256,4,2,2,1,1,6", "128,256,4,2,3,1,1,6", "128,128,2,2,3,1,1,6",
+                                    "64,128,1,2,4,2,1,6", "128,128,4,2,2,1,1,6"])
+def test_split_refill_variant(oracle, monkeypatch, forced):
+    """Variant 6 (each LDS slot refilled in two parts, after a barrier in the middle of the
+    K block and after its end) on ragged dense (split-K included), masked and contiguous
+    problems, FP32, UE8M0 and UE8M0-pair scales."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+    for e8 in (False, True):
+        p = gen.make_dense(300, 520, 1024, seed=141, with_c=True, ue8m0=e8)
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"dense {forced} ue8m0={e8}")
+        if e8:
+            pp = gen.to_ue8m0_pairs(p)
+            D, sent = run(pp)
+            _compare(pp, D, sent, ref, comp, what=f"dense {forced} ue8m0 pairs")
+        if forced.split(",")[5] != "1":
+            continue                      # split-K is dense only
+        pm = gen.make_masked(3, 200, 333, 512, seed=142, with_c=True, masked_m=[200, 0, 77], ue8m0=e8)
+        D, sent = run(pm)
+        ref, comp = oracle_rows(oracle, pm)
+        _compare(pm, D, sent, ref, comp, what=f"masked {forced} ue8m0={e8}")
+        if int(forced.split(",")[0]) <= 128:
+            pc = gen.make_contiguous([128, 0, 256, 100], 200, 384, seed=143, with_c=True, pad_rows=128, ue8m0=e8)
+            D, sent = run(pc)
+            ref, comp = oracle_rows(oracle, pc)
+            _compare(pc, D, sent, ref, comp, what=f"contiguous {forced} ue8m0={e8}")
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_split_refill_short_k(oracle, monkeypatch, K):
+    """Variant 6 with one to five K blocks per tile and two or three slots: the prologue's
+    later groups and the loop's refills are placeholders there."""
+    for forced in ("256,256,4,2,2,1,1,6", "128,128,2,2,3,1,1,6"):
+        monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+        p = gen.make_dense(260, 300, K, seed=150 + K, with_c=True)
+        D, sent = run(p)
+        ref, comp = oracle_rows(oracle, p)
+        _compare(p, D, sent, ref, comp, what=f"{forced} K={K}")
 
 
 @pytest.mark.parametrize("K", [128, 256, 384])
