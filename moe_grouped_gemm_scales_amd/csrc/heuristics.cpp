@@ -205,14 +205,15 @@ const Tuned kTuned[] = {
     {kKGrouped, 4096, 7168, 32768, 4, 0, 192, 256, 4, 2, 2, 1, 1, 0, 0, 0},
 };
 
-// Packed UE8M0 scales (variant 0 only; no promotion in the K loop).  The large
-// shape uses variant 4 (A one K block further ahead, 256 x 224: 469 us against
-// 484 us for 256 x 256 with one ring, same box)
+// Packed UE8M0 scales (one K block a stage; no promotion in the K loop).  The
+// large shapes use 256 x 256 with the split refill (variant 6): 432-435 us against
+// 454-462 us for 256 x 224 with A a block further ahead (variant 4); contiguous
+// 872-891 us against 980-1000 us for 128 x 256 with three slots (one box)
 const Tuned kTunedE8[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
-    {kDense, 4096, 7168, 16384, 1, 0, 256, 224, 4, 2, 2, 1, 1, 4, 0, 0},
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
@@ -224,19 +225,19 @@ const Tuned kTunedF4[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 3, 1, 1, 0, 0, 0},
-    // FP4 B leaves room for a fourth stage: 128 x 224 with four measured 6 % under
-    // 128 x 256 with three on the contiguous workload (1112 vs 1183 us, one box)
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 224, 4, 2, 4, 1, 1, 0, 0, 0},
+    // contiguous: 256-row blocks with three stages, 849-854 us against 1100-1111 us
+    // for 128 x 224 with four (one box)
+    {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 3, 1, 1, 0, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
-// FP4 x FP4: the FP8 x FP4 choices, except that the contiguous workload keeps
-// 128 x 256 with three stages (1079 us against 1097-1108 us for 128 x 224 with four)
+// FP4 x FP4: the FP8 x FP4 choices (contiguous: 724-728 us against 917-924 us for
+// 128 x 256 with three stages)
 const Tuned kTunedF4F4[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 3, 1, 1, 0, 0, 0},
-    {kContiguous, -1, 4096, 7168, 4, 0, 128, 256, 4, 2, 3, 1, 1, 0, 0, 0},
+    {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 3, 1, 1, 0, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
 };
 
