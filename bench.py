@@ -324,6 +324,31 @@ def measured_peaks():
         b.record(stream)
         torch.cuda.synchronize()
         out["null_kernel_us"] = round(a.elapsed_time(b) * 1e3 / 200, 3)
+        # the floor of the small dense shape (64 x 2112 x 7168): one launch that does
+        # nothing but read its 15.9 MB of operands once, from 32 rotating copies (512 MB,
+        # twice the Infinity Cache) so that each launch reads from HBM; launches
+        # back-to-back in one graph, as the GEMM is timed
+        small = 15_886_048                                   # bytes of A, B, the scales and D
+        bufs = [torch.empty(small, dtype=torch.uint8, device="cuda").fill_(5) for _ in range(32)]
+        best = None
+        for grid in (512, 1024, 2048):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in bufs:
+                    _ok(plib, plib.dg_probe_stream_read(ctypes.c_void_p(t.data_ptr()), small,
+                                                        ctypes.c_void_p(sink.data_ptr()), grid, sp))
+            g.replay()
+            torch.cuda.synchronize()
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / len(bufs)
+                best = us if best is None else min(best, us)
+        out["read_15.9MB_us"] = round(best, 3)
+        del bufs
     return out
 
 
@@ -359,8 +384,12 @@ def host_overhead(p):
     c_abi = per_call(lambda: lib.dg_fp8_gemm_nt(*args))
     trivial = per_call(lambda: lib.dg_get_mk_alignment_for_contiguous_layout())
     binding = per_call(lambda: dg.dg_fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D))
+    # the HIP runtime's own cost of one kernel launch: an empty kernel through the same ctypes path
+    plib = _probe_lib()
+    launch = per_call(lambda: plib.dg_probe_null(1, args[-1]))
     return dict(c_abi_us=round(c_abi - trivial, 3), ctypes_floor_us=round(trivial, 3),
-                python_binding_us=round(binding, 3), shape=f"{p.M}x{p.N}x{p.K}")
+                hip_launch_us=round(launch - trivial, 3), python_binding_us=round(binding, 3),
+                shape=f"{p.M}x{p.N}x{p.K}")
 
 
 def library_reference(steps: int = 20):

@@ -3,6 +3,7 @@
 // layouts are specified in include/dg.h.
 #include <algorithm>
 #include <climits>
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -38,6 +39,10 @@ struct LaunchParams {
     int kt;
     unsigned int* status;
 };
+// The GEMM kernel takes these fields as its one by-value argument (KernArgs in
+// the kernel source, same layout): one launch argument instead of thirteen.
+static_assert(sizeof(LaunchParams) == 96 && offsetof(LaunchParams, M) == 72 && offsetof(LaunchParams, status) == 88,
+              "the kernel reads this layout");
 
 struct Workspace {
     float* partials = nullptr;
@@ -121,8 +126,7 @@ dg_status launch_segments(const Plan& plan, const Problem& p, const void* A, con
             lp.ws = partials;
             lp.counters = counters;
         }
-        void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
-                        &lp.num_tiles, &lp.kt, &lp.status};
+        void* args[] = {&lp};
         hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args, nullptr);
         if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
     }
@@ -298,8 +302,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
                 lp.ws = partials;
                 lp.counters = counters;
             }
-            void* args[] = {&lp.A, &lp.sfa, &lp.B, &lp.sfb, &lp.C, &lp.D, &lp.grp, &lp.ws, &lp.counters, &lp.M,
-                            &lp.num_tiles, &lp.kt, &lp.status};
+            void* args[] = {&lp};
             hipError_t e = hipModuleLaunchKernel(seg.fn, seg.grid, 1, 1, cfg.threads(), 1, 1, 0, stream, args,
                                                  nullptr);
             if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");

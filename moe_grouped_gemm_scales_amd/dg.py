@@ -111,9 +111,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# torch's current device and the raw handle of its current stream, without
+# building Python device and stream objects (a few microseconds per call)
+_cur_device = torch._C._cuda_getDevice
+_cur_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(_cur_raw_stream(_cur_device()))
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -124,11 +130,12 @@ def _fp8(t: torch.Tensor, name: str):
 
 
 def _dev(t: torch.Tensor, name: str):
-    if not t.is_cuda:
+    d = t.get_device()                  # -1 for host tensors
+    if d < 0:
         raise ValueError(f"{name} must be a device tensor")
-    if t.device.index != torch.cuda.current_device():
+    if d != _cur_device():
         # the library launches on the current device; another device's memory is not its operand
-        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{_cur_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 

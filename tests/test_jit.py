@@ -147,3 +147,33 @@ def test_register_load_variant_that_spills_is_refused(tmp_path):
     assert " -4 " in r.stdout and "must not spill registers" in r.stdout, r.stdout
     r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path, {"DG_FORCE_CONFIG": "128,128,1,4,3,1,1,1"})
     assert r.returncode == 0 and " 0 " in r.stdout, r.stdout + r.stderr[-2000:]
+
+
+@pytest.mark.skipif(not os.path.exists(READELF), reason="LLVM tools not installed")
+def test_kernel_takes_one_by_value_argument_of_the_host_layout(tmp_path):
+    """The GEMM kernel's only explicit argument is the 96-byte struct the host fills
+    (api.cpp's LaunchParams: nine pointers, three ints, the status pointer); its code
+    object metadata must say so, for every variant a table selects."""
+    plans = [(0, 64, 2112, 7168, 1, 0), (0, 128, 24576, 1536, 1, 0), (0, 4096, 7168, 16384, 1, 0),
+             (2, 256, 7168, 2048, 4, 0), (1, 32768, 4096, 7168, 4, 0)]
+    r = _run(PRECOMPILE.format(plans=repr(plans)), tmp_path)
+    assert r.returncode == 0, r.stderr[-2000:]
+    objs = glob.glob(str(tmp_path / "*.hsaco"))
+    assert len(objs) >= len(plans)
+    for path in objs:
+        out = subprocess.run([READELF, "--notes", path], capture_output=True, text=True).stdout
+        lines = out.split(".name:           dg_fp8_gemm_nt_kernel")[0].splitlines()
+        start = max(i for i, line in enumerate(lines) if line.strip() == ".args:")
+        items, cur = [], None
+        for line in lines[start + 1:]:
+            if line.startswith("      - "):
+                cur = {}
+                items.append(cur)
+                line = line.replace("- ", "  ", 1)
+            elif not line.startswith("        "):
+                break                                   # the next key of the kernel's entry
+            k, _, v = line.strip().partition(":")
+            cur[k] = v.strip()
+        explicit = [it for it in items if not it[".value_kind"].startswith("hidden_")]
+        assert explicit == [{".offset": "0", ".size": "96", ".value_kind": "by_value"}], (os.path.basename(path),
+                                                                                          explicit)
