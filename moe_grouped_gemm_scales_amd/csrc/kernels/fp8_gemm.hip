@@ -291,6 +291,23 @@ struct Tile {
     bool skip;
 };
 
+// Workgroups go to the 8 XCDs (each with its own L2) round-robin by index.
+// Within every round of the persistent grid (the last one possibly partial,
+// with R < grid work items), give XCD x a contiguous range of the logical
+// order, so that the items it runs at the same time are neighbours there and
+// share their A and B blocks in its L2.  WG b of the round runs on XCD b % 8
+// as the (b / 8)-th of the ceil((R - x) / 8) WGs there; the ranges of the
+// XCDs partition [0, R).
+__device__ __forceinline__ int xcd_spread(int t, int num_items) {
+    const int grid = gridDim.x;
+    if (grid % 8 != 0) return t;
+    const int r0 = t - t % grid;                          // first item of this round
+    const int R = num_items - r0 < grid ? num_items - r0 : grid;
+    const int b = t - r0;                                 // < R
+    const int x = b % 8;
+    return r0 + x * (R / 8) + (x < R % 8 ? x : R % 8) + b / 8;
+}
+
 __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
     Tile tl;
     tl.skip = false;
@@ -333,15 +350,7 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         // undefined, never an access out of bounds)
         const int num_mt = (p.M + BM - 1) / BM;
         const int per_g = num_mt * NUM_NT;
-        // the XCD-aware spread of each full round of the grid, as for dense below
-        const int grid = gridDim.x;
-        if (grid % 8 == 0) {
-            const int r0 = t - t % grid;
-            if (r0 + grid <= p.num_tiles) {
-                const int b = t - r0;
-                t = r0 + (b % 8) * (grid / 8) + b / 8;
-            }
-        }
+        t = xcd_spread(t, p.num_tiles);
         const int g = t / per_g;
         const int local = t % per_g;
         int off = 0;
@@ -367,18 +376,7 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         tl.mn = 0;
     } else {
         const int num_mt = (p.M + BM - 1) / BM;
-        // Workgroups go to the 8 XCDs (each with its own L2) round-robin by
-        // index.  Within every full round of the persistent grid, give XCD x
-        // the contiguous logical range [x, x + 1) * grid / 8, so tiles that are
-        // neighbours in the order below (and share A or B) share an L2.
-        const int grid = gridDim.x;
-        if (grid % 8 == 0) {
-            const int r0 = t - t % grid;                  // first tile of this round
-            if (r0 + grid <= p.num_tiles) {
-                const int b = t - r0;
-                t = r0 + (b % 8) * (grid / 8) + b / 8;
-            }
-        }
+        t = xcd_spread(t, p.num_tiles);
         int mn = t / SPLITK;
         tl.split = t % SPLITK;
         tl.mn = mn;
