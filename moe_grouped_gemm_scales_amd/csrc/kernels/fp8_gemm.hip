@@ -789,7 +789,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             constexpr int NPAR = (RPI % 8) == 0 ? 1 : 8 / RPI;   // distinct (i*RPI) & 7 values
             static_assert(NPAR == 1 || NPAR == 2, "rows per instruction");
             u32 voff_rows[NPAR];
-    #pragma unroll
+#pragma unroll
             for (int par = 0; par < NPAR; ++par) voff_rows[par] = lane_voff(par);
             // FP4 B: lane l writes row l / 4 of the instruction's 16, physical chunk
             // l & 3, which holds logical chunk (l & 3) ^ ((row >> 2) & 3); the row's
@@ -797,7 +797,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             const u32 voff_b4 = (u32)(lane >> 2) * KB_B + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
             const u32 voff_b4a = (u32)(lane >> 2) * KB_A + (u32)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);   // FP4 A
             u32 voff_s[IS > 0 ? IS : 1];   // A scales: clamped rows (the offset includes the K block's row of sfa)
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < IS; ++j) {
                 const int i = min(wave + j * NWAVES, NS_INS - 1);
                 const int h = i / NS_PER_KB;
@@ -807,7 +807,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 voff_s[j] = FP4A ? (u32)mm * KBLKS * 4u : (u32)mm * SF_BYTES + (u32)h * a_rows_total * SF_BYTES;
             }
             u32 voff_t[IT > 0 ? IT : 1];
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < IT; ++j) {
                 // without repeats, wave NS_INS + h issues B-scale instruction h
                 const int h = DIET ? min(max(wave - NS_INS, 0), NT_INS - 1) : min(wave + j * NWAVES, NT_INS - 1);
@@ -885,7 +885,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 }
             };
             auto issue_stage = [&](int kb, int stage, bool live = true) {
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < INS_PER_WAVE; ++j) issue_one(j, kb, stage, live);
             };
             // split refill: B instruction of half `hi` with index bi inside that half
@@ -938,15 +938,15 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
 
             // ---- accumulators
             v4f acc[TM][TN];
-    #pragma unroll
+#pragma unroll
             for (int a = 0; a < TM; ++a)
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
             // MFMA results of the last n sub-tile of the previous K block and their
             // scales: promoted while the next K block's first MFMAs run.
             v4f p_carry[TM];
             sc_t s_carry[TM];
-    #pragma unroll
+#pragma unroll
             for (int a = 0; a < TM; ++a) {
                 p_carry[a] = v4f{0.f, 0.f, 0.f, 0.f};
                 s_carry[a] = 0.f;
@@ -959,25 +959,25 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
             if constexpr (AAHEAD) {
                 // B and A of K block 0, then A of K block 1 (placeholders past the tile)
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < INS_PER_WAVE; ++j) issue_one_aa(j, tl.kb0, 0, nst > 0, tl.kb0, 0, nst > 0);
-    #pragma unroll
+#pragma unroll
                 for (int j = IB + IT; j < INS_PER_WAVE; ++j)
                     issue_one_aa(j, tl.kb0 + min(1, nst - 1), 1, nst > 1, tl.kb0, 0, false);
             } else if constexpr (SPLIT) {
                 // K blocks 0 .. STAGES-1 without the end group of the last (issued in the
                 // first steps of block 0); placeholders past the tile keep the counts fixed
-    #pragma unroll
+#pragma unroll
                 for (int s = 0; s < STAGES; ++s) {
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < G_MID; ++j) issue_mid(j, tl.kb0 + min(s, nst - 1), s, s < nst);
                     if (s + 1 < STAGES) {
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < G_END; ++j) issue_end(j, tl.kb0 + min(s, nst - 1), s, s < nst);
                     }
                 }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int s = 0; s < STAGES - 1; ++s)
                     if (s < nst) issue_stage(tl.kb0 + s * KSTEP, s);
             }
@@ -987,7 +987,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             const int wave_n0 = tl.n0 + wn * WAVE_N;
             // LDS byte offset of each n sub-tile's sfb inside a K block's sfb slice
             int sb_off[TN];
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < TN; ++b) {
                 int nblk = (wave_n0 + b * 16) / KBLK;
                 nblk = nblk < NBLKS ? nblk : NBLKS - 1;
@@ -1044,20 +1044,20 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     if constexpr (BF16) return;       // no scales
                     lds_u8* const sb_p = b_scales(slot_b);
                     if constexpr (FP4B) {
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb4_off + b * 64);
                     } else if constexpr (KG) {
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < TN; ++b)
                             sb[b] = *(__attribute__((address_space(3))) const sc_t*)(sb_p + sbk_off + b * 64);
                     } else if constexpr (SB_UNIFORM) {
                         sb[0] = lds_read_f32(sb_p, sb_off[0]);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
                     }
                     lds_u8* const sa_p = a_scales(slot_a) + a_row0 * 4;
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, a * 64);
                 };
 
@@ -1071,12 +1071,12 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     lds_u8* const ka0 = a_tile(0);
                     lds_u8* const kb0 = b_tile(0);
                     read_scales(0, 0);
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) fa[a] = read_fa(ka0 + a_frag, ka0 + a_frag_hi, a * 16 * ROWB_A);
                     fb = read_fb(kb0 + b_frag, kb0 + b_frag_hi, 0);
                 }
 
-    #pragma unroll 1
+#pragma unroll 1
                 for (int it = 0; it < nst; ++it) {
                     const int stage = it % STAGES;
                     // The slot of stage it-1 is free: every wave read all of it into
@@ -1096,7 +1096,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     const int stage_next = (it + 1) % STAGES;
                     const int a_slot = AAHEAD ? it % A_SLOTS : stage;
                     const int a_slot_next = AAHEAD ? (it + 1) % A_SLOTS : stage_next;
-    #pragma unroll
+#pragma unroll
                     for (int h = 0; h < KSTEP; ++h) {
                     lds_u8* const kbp = b_tile(stage);
                     lds_u8* const b_lo = kbp + b_frag;
@@ -1107,16 +1107,16 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
 
                     float sab[TM];           // sa * sb for the uniform case
                     if constexpr (SB_UNIFORM && !SF_E8) {
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) sab[a] = sa[a] * first(sb[0]);
                     }
                     // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
                     int ea[TM], eb[TN];
                     if constexpr (SF_E8) {
                         const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> (FP4A ? sh_q : sh));
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b)
                             eb[b] = (int)(__builtin_bit_cast(u32, first(sb[b])) >> (FP4B ? sh_q : sh));
                     }
@@ -1125,7 +1125,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
                     // last sub-tile of the previous K block).
                     v4f pr[TM];
-    #pragma unroll
+#pragma unroll
                     for (int b = 0; b < TN; ++b) {
                         if constexpr (SPLIT) {
                             // end group of block it + STAGES - 1 (into the slot block it - 1 used),
@@ -1133,7 +1133,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                             // (into this block's slot)
                             if (b < END_STEPS) {
                                 const int f = it + STAGES - 1;
-    #pragma unroll
+#pragma unroll
                                 for (int j = b * G_END / END_STEPS; j < (b + 1) * G_END / END_STEPS; ++j)
                                     issue_end(j, tl.kb0 + min(f, nst - 1), f % STAGES, f < nst);
                             }
@@ -1143,7 +1143,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                             }
                             if (b + 1 >= HALF_TN && b + 1 < TN) {
                                 const int f = it + STAGES, sb = b + 1 - HALF_TN;
-    #pragma unroll
+#pragma unroll
                                 for (int j = sb * G_MID / MID_STEPS; j < (sb + 1) * G_MID / MID_STEPS; ++j)
                                     issue_mid(j, tl.kb0 + min(f, nst - 1), stage, f < nst);
                             }
@@ -1151,14 +1151,14 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                             if constexpr (AAHEAD) {
                                 const int nspread = SPREAD == 0 ? 1 : SPREAD;
                                 if (b < nspread) {
-    #pragma unroll
+#pragma unroll
                                     for (int j = b * INS_PER_WAVE / nspread; j < (b + 1) * INS_PER_WAVE / nspread; ++j)
                                         issue_one_aa(j, a_fill_kb, a_fill_slot, a_live, kb_fill, slot_fill, live);
                                 }
                             } else if constexpr (SPREAD == 0) {
                                 if (b == 0) issue_stage(kb_fill, slot_fill, live);
                             } else if (b < SPREAD) {
-    #pragma unroll
+#pragma unroll
                                 for (int j = b * INS_PER_WAVE / SPREAD; j < (b + 1) * INS_PER_WAVE / SPREAD; ++j)
                                     issue_one(j, kb_fill, slot_fill, live);
                             }
@@ -1169,7 +1169,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                         // scales of sub-tile b-1 (promoted now) and, in the last sub-tile, of
                         // b itself (carried), taken before the next K block's replace them
                         sc_t sc_prev[TM], s_last[TM];
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) {
                             if constexpr (SF_E8 || BF16) sc_prev[a] = s_last[a] = 0.f;
                             else if constexpr (SB_UNIFORM) sc_prev[a] = s_last[a] = sab[a];
@@ -1192,11 +1192,11 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                             read_scales(a_slot_next, stage_next);
                         }
                         v4f prev[TM];
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) prev[a] = pr[a];
                         // optional: the wave asks for issue priority while it has MFMAs to issue
                         if constexpr (DG_SETPRIO != 0) __builtin_amdgcn_s_setprio(DG_SETPRIO);
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) {
                             if constexpr (SF_E8) {
                                 // acc += 2^(eb-127) 2^(ea-127) P: the MFMA applies both block
@@ -1225,11 +1225,11 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                             fb = fb_next;
                         } else {
                             fb = read_fb(kbn + b_frag, kbn + b_frag_hi, 0);
-    #pragma unroll
+#pragma unroll
                             for (int a = 0; a < TM; ++a) s_carry[a] = s_last[a];
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) p_carry[a] = pr[a];
                     }   // K blocks of the stage
                 }
@@ -1237,7 +1237,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             } else {
                 // Two K blocks per stage (short K loops): barrier at the top of each
                 // stage, fragments read at the start of each K block.
-    #pragma unroll 1
+#pragma unroll 1
                 for (int it = 0; it < nst; ++it) {
                     const int stage = it % STAGES;
                     // stage `it` has landed (for this wave) once at most the later stages are pending
@@ -1255,7 +1255,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     }
 
                     const u32 st = __builtin_amdgcn_readfirstlane(smem_base + stage * STAGE_BYTES);
-    #pragma unroll
+#pragma unroll
                     for (int h = 0; h < KSTEP; ++h) {
                     const int kb = tl.kb0 + it * KSTEP + h;
                     // scale of B from the stage (same address in every lane: a broadcast read)
@@ -1264,7 +1264,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     if constexpr (SB_UNIFORM) {
                         sb[0] = lds_read_f32(sb_p, sb_off[0]);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < TN; ++b) sb[b] = lds_read_f32(sb_p, sb_off[b]);
                     }
                     lds_u8* const stp = (lds_u8*)(st + h * 128);
@@ -1275,25 +1275,25 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     lds_u8* const b_hi = stp + b_frag_off + chunk_hi;
 
                     float sa[TM];
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) sa[a] = lds_read_f32(sa_p, S_OFF + a * 64);
                     v8i fa[TM];
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) fa[a] = lds_read_frag(a_lo, a_hi, A_OFF + a * 16 * ROWB);
                     v8i fb = lds_read_frag(b_lo, b_hi, B_OFF);
 
                     float sab[TM];           // sa * sb for the uniform case
                     if constexpr (SB_UNIFORM && !SF_E8) {
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) sab[a] = sa[a] * sb[0];
                     }
                     // UE8M0: this K block's scale bytes, shifted to bits 0-7 of each word
                     int ea[TM], eb[TN];
                     if constexpr (SF_E8) {
                         const u32 sh = 8u * (u32)((tl.kb0 + it) & (PAIRS ? 1 : 3));
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) ea[a] = (int)(__builtin_bit_cast(u32, sa[a]) >> sh);
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < (SB_UNIFORM ? 1 : TN); ++b) eb[b] = (int)(__builtin_bit_cast(u32, sb[b]) >> sh);
                     }
 
@@ -1301,11 +1301,11 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                     // run while the FMAs promote sub-tile b-1 (for b = 0: the carried
                     // last sub-tile of the previous K block).
                     v4f pr[TM];
-    #pragma unroll
+#pragma unroll
                     for (int b = 0; b < TN; ++b) {
                         if constexpr (STAGES > 2) {
                             if (refill && h == 0) {
-    #pragma unroll
+#pragma unroll
                                 for (int j = b * INS_PER_WAVE / TN; j < (b + 1) * INS_PER_WAVE / TN; ++j)
                                     issue_one(j, kb_fill, slot_fill);
                             }
@@ -1313,9 +1313,9 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                         v8i fb_next;
                         if (b + 1 < TN) fb_next = lds_read_frag(b_lo, b_hi, B_OFF + (b + 1) * 16 * ROWB);
                         v4f prev[TM];
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) prev[a] = pr[a];
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < TM; ++a) {
                             const v4f zero = {0.f, 0.f, 0.f, 0.f};
                             // P[n][m] over this 128-wide K block: exact products, FP32 sums
@@ -1331,7 +1331,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                         }
                         if (b + 1 < TN) fb = fb_next;
                     }
-    #pragma unroll
+#pragma unroll
                     for (int a = 0; a < TM; ++a) {
                         p_carry[a] = pr[a];
                         if constexpr (SB_UNIFORM) s_carry[a] = sab[a];
@@ -1341,7 +1341,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 }
             }
             if constexpr (!SF_E8 && !BF16) {
-    #pragma unroll
+#pragma unroll
                 for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
             }
 
