@@ -124,7 +124,7 @@ def _probe_lib():
     lib.dg_probe_spin.argtypes = [i32, vp]
     lib.dg_probe_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     lib.dg_probe_mfma_fp8.argtypes = [i32, i32, vp, vp]
-    for f in (lib.dg_probe_null, lib.dg_probe_spin, lib.dg_probe_stream_read, lib.dg_probe_mfma_fp8):
+    for f in (lib.dg_probe_null, lib.dg_probe_spin, lib.dg_probe_stream_read, lib.dg_probe_mfma_fp8, lib.dg_probe_call_floor):
         f.restype = i32
     return lib
 
@@ -354,8 +354,9 @@ def measured_peaks():
 
 def host_overhead(p):
     """Host cost of one call on a warm shape, without synchronising: the raw C ABI
-    through ctypes (less the cost of a ctypes call to a trivial C function) and
-    the Python binding."""
+    through ctypes (less the cost of a ctypes call with the same arguments to a C
+    function that does nothing), the HIP runtime's own cost of launching an empty
+    kernel (less a ctypes call without arguments) and the Python binding."""
     import torch
 
     import moe_grouped_gemm_scales_amd as dg
@@ -382,13 +383,15 @@ def host_overhead(p):
         return best * 1e6
 
     c_abi = per_call(lambda: lib.dg_fp8_gemm_nt(*args))
-    trivial = per_call(lambda: lib.dg_get_mk_alignment_for_contiguous_layout())
+    # a call with the same arguments that does nothing: ctypes' cost of passing them
+    trivial = per_call(lambda: lib.dg_probe_call_floor(*args))
     binding = per_call(lambda: dg.dg_fp8_gemm_nt(d["A"], d["sfa"], d["B"], d["sfb"], d["C"], D))
     # the HIP runtime's own cost of one kernel launch: an empty kernel through the same ctypes path
     plib = _probe_lib()
     launch = per_call(lambda: plib.dg_probe_null(1, args[-1]))
+    bare = per_call(lambda: lib.dg_get_mk_alignment_for_contiguous_layout())
     return dict(c_abi_us=round(c_abi - trivial, 3), ctypes_floor_us=round(trivial, 3),
-                hip_launch_us=round(launch - trivial, 3), python_binding_us=round(binding, 3),
+                hip_launch_us=round(launch - bare, 3), python_binding_us=round(binding, 3),
                 shape=f"{p.M}x{p.N}x{p.K}")
 
 

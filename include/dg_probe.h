@@ -50,6 +50,15 @@ dg_status dg_probe_stream_read(const void *src, size_t bytes, unsigned int *sink
  */
 dg_status dg_probe_mfma_fp8(int grid, int iters, float *sink, void *stream);
 
+/*
+ * Does nothing and returns DG_OK.  It takes the arguments of dg_fp8_gemm_nt,
+ * so that timing calls of both through the same foreign-function layer (for
+ * instance Python's ctypes) and subtracting gives the library's own host cost
+ * of a call, without the cost of passing its arguments.
+ */
+dg_status dg_probe_call_floor(const void *A, const void *sfa, const void *B, const void *sfb, const float *C,
+                              void *D, int M, int N, int K, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

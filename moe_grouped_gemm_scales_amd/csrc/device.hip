@@ -162,4 +162,9 @@ dg_status dg_probe_mfma_fp8(int grid, int iters, float* sink, void* stream) {
                            : set_error(DG_ERR_HIP, std::string("dg_probe_mfma_fp8: ") + hipGetErrorString(e));
 }
 
+dg_status dg_probe_call_floor(const void*, const void*, const void*, const void*, const float*, void*, int, int, int,
+                              void*) {
+    return DG_OK;
+}
+
 }  // extern "C"
