@@ -124,13 +124,13 @@ bool valid(const KernelConfig& c, const Problem& p) {
     // slots), for FP8 operands with FP32 or UE8M0 scales and the M forms
     if (c.variant == 4 && (c.kstep != 1 || c.stages != 2 || c.sf == 2 || c.sf == 4 || p.kind == kKGrouped))
         return false;
-    // variant 6: variant 0 with the split refill (FP8 operands, FP32 or UE8M0 scales,
-    // one K block a stage, an even number of n sub-tiles per wave, the M forms)
-    if (c.variant == 6 && (c.kstep != 1 || c.sf == 2 || c.sf == 3 || c.sf == 4 || p.kind == kKGrouped ||
+    // variant 6: variant 0 with the split refill (FP8 operands with FP32 or UE8M0 scales,
+    // or BF16; one K block a stage, an even number of n sub-tiles per wave)
+    if (c.variant == 6 && (c.kstep != 1 || c.sf == 2 || c.sf == 4 ||
                            (c.bn / c.wn / 16) % 2 || c.bn / c.wn / 16 < 4))
         return false;
     if (c.sf && ((c.variant != 0 && c.variant != 4 && c.variant != 6) || c.kstep != 1)) return false;   // UE8M0, FP4: variant 0, one K block a stage
-    if (p.kind == kKGrouped && (c.sf || c.variant != 0 || c.kstep != 1)) return false;   // K-grouped: the same
+    if (p.kind == kKGrouped && (c.sf || (c.variant != 0 && c.variant != 6) || c.kstep != 1)) return false;   // K-grouped: the same
     if (c.variant < 0 || c.variant > 6) return false;
     int tm = c.bm / c.wm / 16, tn = c.bn / c.wn / 16;
     if (c.lds_bytes() > kLdsBytes) return false;
@@ -201,8 +201,9 @@ const Tuned kTuned[] = {
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
     // K-grouped weight gradient of the contiguous workload (K: the row pitch of the
     // K-contiguous operands, 4 x 8192 tokens): 192 x 256 with two stages measured 2-4 %
-    // under 128 x 256 with three (22 row tiles, the last one a third full)
-    {kKGrouped, 4096, 7168, 32768, 4, 0, 192, 256, 4, 2, 2, 1, 1, 0, 0, 0},
+    // under 128 x 256 with three (22 row tiles, the last one a third full); with the split
+    // refill 1274-1280 us against 1310-1344 us
+    {kKGrouped, 4096, 7168, 32768, 4, 0, 192, 256, 4, 2, 2, 1, 1, 6, 0, 0},
 };
 
 // Packed UE8M0 scales (one K block a stage; no promotion in the K loop).  The
@@ -243,9 +244,10 @@ const Tuned kTunedF4F4[] = {
 
 // BF16 x BF16 (k here is the row length in bytes, 2 x K).  A 128-byte K block is
 // 64 elements, half the MFMA time of an FP8 one, so the loads' lead matters more:
-// variant 4 (A one K block further ahead) 794 us against 865 us for variant 0
+// variant 4 (A one K block further ahead) 794 us against 865 us for variant 0; the split
+// refill with 256 x 256 812-816 us against 819-839 us for variant 4 with 256 x 224
 const Tuned kTunedBF16[] = {
-    {kDense, 4096, 7168, 32768, 1, 0, 256, 224, 4, 2, 2, 1, 1, 4, 0, 0},
+    {kDense, 4096, 7168, 32768, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
 };
 
 std::vector<KernelConfig> tuned(const Problem& p, int num_cus, const KernelConfig& base) {

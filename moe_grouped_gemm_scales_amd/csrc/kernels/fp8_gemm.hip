@@ -660,8 +660,8 @@ constexpr int NSC_PER_WAVE = INS_PER_WAVE - IA - IB;    // scale DMA instruction
 constexpr int G_MID = IA + IBH + NSC_PER_WAVE;
 constexpr int G_END = IBH;
 constexpr int SPLIT_PENDING = (STAGES - 1) * (G_MID + G_END);
-static_assert(!SPLIT || (KSTEP == 1 && !AAHEAD && TN % 2 == 0 && TN >= 4 && !FP4A && !FP4B && !KG && !BF16),
-              "split refill: FP8 operands, one K block a slot, an even number of n sub-tiles");
+static_assert(!SPLIT || (KSTEP == 1 && !AAHEAD && TN % 2 == 0 && TN >= 4 && !FP4A && !FP4B),
+              "split refill: FP8 or BF16 operands, one K block a slot, an even number of n sub-tiles");
 // B instruction i covers 8 rows inside one 16-row n sub-tile of one wave column
 // (2 TN instructions per column): the first TN of a column are the first half
 static_assert(!SPLIT || (RPI == 8 && NB_INS == WN * 2 * TN), "split refill: 8 B rows per instruction");

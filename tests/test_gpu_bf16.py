@@ -62,7 +62,8 @@ def test_bf16_grouped(oracle):
 
 @pytest.mark.parametrize("forced", ["128,128,4,2,2,1,1,0", "256,256,4,2,2,1,1,0", "64,96,2,2,4,2,1,0",
                                     "32,64,1,2,3,4,1,0", "256,224,2,2,2,1,1,0",    # AGPR accumulators
-                                    "256,256,4,2,2,1,1,4"])                        # A ahead
+                                    "256,256,4,2,2,1,1,4",                         # A ahead
+                                    "256,256,4,2,2,1,1,6", "128,128,2,2,3,1,1,6"])  # split refill
 def test_bf16_forced_tile_configs(oracle, monkeypatch, forced):
     monkeypatch.setenv("DG_FORCE_CONFIG", forced)
     p = gen.make_bf16("dense", seed=15, M=300, N=520, K=1024, with_c=True)

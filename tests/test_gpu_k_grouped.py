@@ -76,7 +76,8 @@ def test_k_grouped_integer_data_bitwise(oracle):
 
 
 @pytest.mark.parametrize("forced", ["128,128,4,2,2,1,1,0", "64,96,2,2,4,1,1,0", "256,256,4,2,2,1,1,0",
-                                    "32,64,1,2,3,1,1,0", "192,256,4,2,2,1,1,0", "128,256,4,2,3,1,1,0"])
+                                    "32,64,1,2,3,1,1,0", "192,256,4,2,2,1,1,0", "128,256,4,2,3,1,1,0",
+                                    "192,256,4,2,2,1,1,6", "128,256,4,2,2,1,1,6"])     # split refill
 def test_k_grouped_forced_tile_configs(oracle, monkeypatch, forced):
     monkeypatch.setenv("DG_FORCE_CONFIG", forced)
     p = gen.make_k_grouped([256, 0, 640], 300, 520, seed=19, with_c=True)
