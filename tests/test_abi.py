@@ -147,6 +147,6 @@ def test_layout_and_bf16_validation():
 
 def test_describe_config_for_new_forms():
     assert pkg.describe_config(0 | pkg.SCALE_FP8_FP4, 128, 24576, 1536, num_cus=256).endswith("_f8f4")
-    assert pkg.describe_config(pkg.KIND_K_GROUPED, 4096, 7168, 32768, 4, num_cus=256).startswith("k3_")
+    assert pkg.describe_config(pkg.KIND_K_GROUPED, 4096, 7168, 32768, 4, num_cus=256).startswith("k3")
     key = pkg.describe_config(pkg.KIND_BF16, 4096, 7168, 16384, num_cus=256)
     assert key.endswith("_bf16") and "_K32768_" in key       # BF16 rows counted in bytes
