@@ -53,10 +53,15 @@ struct KernelConfig {
         if (kind == kKGrouped) return (bm + bn) * 128 + (bm + 63) / 64 * 256 + (bn + 63) / 64 * 256;
         return (bm + bn) * 128 * kstep + kstep * ((bm + 63) / 64) * 256 + kstep * 256;
     }
+    // variants 0, 4 and 6 of the contiguous form: 256 bytes per wave for the experts of its rows
+    int row_group_bytes() const {
+        const bool v046 = variant == 0 || variant == 4 || variant == 6;
+        return v046 && kind == kContiguous && bm / wm <= 64 ? 256 * wm * wn : 0;
+    }
     int lds_bytes() const {
         if (variant == 4) {   // three A slots (tile + sfa), two B slots (tile + sfb); BF16: no scales
             const int sa = sf == 3 ? 0 : (bm + 63) / 64 * 256, sb = sf == 3 ? 0 : 256;
-            return (stages + 1) * (bm * 128 + sa) + stages * (bn * 128 + sb);
+            return (stages + 1) * (bm * 128 + sa) + stages * (bn * 128 + sb) + row_group_bytes();
         }
         if (variant == 2) return k / 128 / splitk * (bm * 128 + (bm + 63) / 64 * 256) + 3 * 256;
         if (variant == 5) return stages * (bm * 128 + bm * 4 + 256);   // A ring: tile, A scales, B scales
@@ -65,7 +70,7 @@ struct KernelConfig {
             const int slots = std::min(16, (160 * 1024 - 1024 - 768) / slot);
             return 768 + slots * slot;
         }
-        return stages * stage_bytes();
+        return stages * stage_bytes() + row_group_bytes();
     }
     std::string key() const;
 };

@@ -246,10 +246,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ u16 f32_to_bf16(float f) {
-    u32 u = __builtin_bit_cast(u32, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);   // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                          // nearest-even
-    return (u16)(u >> 16);
+    const u32 u = __builtin_bit_cast(u32, f);
+    const u32 rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;    // nearest-even
+    const u32 qnan = (u >> 16) | 0x40u;                              // NaN: quiet, sign and payload top kept
+    return (u16)((u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded);  // a select, not a branch
 }
 
 __device__ __forceinline__ u32 lds_addr(const void* p) {
@@ -308,7 +308,36 @@ __device__ __forceinline__ int xcd_spread(int t, int num_items) {
     return r0 + x * (R / 8) + (x < R % 8 ? x : R % 8) + b / 8;
 }
 
-__device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
+// Dense and contiguous forms: output tile (mt, nt) and K split of work item t.
+// Grouped order: walk 8 m-tiles per column sweep so that concurrently resident
+// workgroups share A and B tiles in L2.
+__device__ __forceinline__ void tile_position(const Params& p, int t, int& mn, int& split, int& mt, int& nt) {
+    const int num_mt = (p.M + BM - 1) / BM;
+    t = xcd_spread(t, p.num_tiles);
+    mn = t / SPLITK;
+    split = t % SPLITK;
+    constexpr int GROUP_M = 8;
+    const int width = GROUP_M * NUM_NT;
+    const int first_m = mn / width * GROUP_M;
+    const int gsize = num_mt - first_m < GROUP_M ? num_mt - first_m : GROUP_M;
+    mt = first_m + (mn % width) % gsize;
+    nt = (mn % width) / gsize;
+}
+
+// Contiguous form: the experts of the first and (256-row blocks) second 128 rows
+// of work item t's row block, read ahead of the tile's decode.
+__device__ __forceinline__ void tile_experts(const Params& p, int t, int& g, int& g2) {
+    int mn, split, mt, nt;
+    tile_position(p, t, mn, split, mt, nt);
+    const int m0 = mt * BM;
+    g = p.grp[m0];
+    g2 = (BM > 128 && m0 + 128 < p.M) ? p.grp[m0 + 128] : -1;
+}
+
+// PRE: the contiguous form's experts come from tile_experts() (g_pre, g2_pre)
+// instead of being read here.
+template <bool PRE = false>
+__device__ __forceinline__ Tile decode_tile(const Params& p, int t, int g_pre = 0, int g2_pre = -1) {
     Tile tl;
     tl.skip = false;
     tl.g2 = -1;
@@ -375,20 +404,9 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         tl.kb1 = kb1 > kb0 ? kb1 : kb0;
         tl.mn = 0;
     } else {
-        const int num_mt = (p.M + BM - 1) / BM;
-        t = xcd_spread(t, p.num_tiles);
-        int mn = t / SPLITK;
-        tl.split = t % SPLITK;
+        int mn, mt, nt;
+        tile_position(p, t, mn, tl.split, mt, nt);
         tl.mn = mn;
-        // Grouped order: walk 8 m-tiles per column sweep so that concurrently
-        // resident workgroups share A and B tiles in L2.
-        constexpr int GROUP_M = 8;
-        int width = GROUP_M * NUM_NT;
-        int grp_id = mn / width;
-        int first_m = grp_id * GROUP_M;
-        int gsize = num_mt - first_m < GROUP_M ? num_mt - first_m : GROUP_M;
-        int mt = first_m + (mn % width) % gsize;
-        int nt = (mn % width) / gsize;
         tl.m0 = mt * BM;
         tl.n0 = N_BEGIN + nt * BN;
         tl.rows = p.M - tl.m0 < BM ? p.M - tl.m0 : BM;
@@ -396,14 +414,14 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
         tl.kb0 = tl.split * (KBLKS / SPLITK);
         tl.kb1 = tl.kb0 + KBLKS / SPLITK;
         if constexpr (kKind == 1) {
-            int g = p.grp[tl.m0];
+            const int g = PRE ? g_pre : p.grp[tl.m0];
             tl.g = g;
             tl.skip = (g < 0 || g >= G);
             // every 128-row block of the layout names one expert (its first row's):
             // a 256-row block covers two, which may differ
             if constexpr (BM > 128) {
                 if (tl.m0 + 128 < p.M) {
-                    const int g2 = p.grp[tl.m0 + 128];
+                    const int g2 = PRE ? g2_pre : p.grp[tl.m0 + 128];
                     if (g2 >= 0 && g2 < G && g2 != g) tl.g2 = g2;
                 }
             }
@@ -420,9 +438,11 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t) {
 // holds TM_ x TN_ blocks of 16 x 16: lane (l16, q) owns row row0 + 16 a and
 // the four columns col0 + 16 b + [0, 4) of each (row0, col0 relative to the
 // tile).  Returns after storing, or early when another split finishes the tile.
-template <int TM_, int TN_>
+// GRP_LDS (contiguous form): the expert of the lane's row row0 + 16 a is the
+// int at LDS address grp_lds + 64 a, instead of being read from global memory.
+template <int TM_, int TN_, bool GRP_LDS = false>
 __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f (&acc)[TM_][TN_], int row0,
-                                            int col0, int tid, int* s_flag) {
+                                            int col0, int tid, int* s_flag, u32 grp_lds = 0) {
     // An MFMA reads the operands of every lane of its wave, whatever EXEC
     // holds.  Pin every accumulator here, while the whole wave is active:
     // otherwise, when the K loop is short enough to be laid out straight, the
@@ -505,6 +525,12 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
     }
 
     // ---- epilogue: (+C), BF16 nearest-even, store rows that may be written
+    // The lane's row and column bases pass through an empty asm here, so the
+    // store addresses are computed now: otherwise the compiler computes all of
+    // them before the K loop, and with no register left across the loop it
+    // spills them, so every store first waits for a scratch reload (and with it
+    // for every store issued before it).
+    asm volatile("" : "+v"(row0), "+v"(col0));
     u64 row_base;      // element offset of row 0 of this tile in C/D
     if constexpr (kKind == 2 || kKind == 3) row_base = ((u64)tl.g * p.M + tl.m0) * N;
     else row_base = (u64)tl.m0 * N;
@@ -512,7 +538,11 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
     for (int a = 0; a < TM_; ++a) {
         const int r = row0 + a * 16;            // row inside the tile
         bool row_ok = r < tl.row_limit;
-        if constexpr (kKind == 1) row_ok = row_ok && (p.grp[tl.m0 + r] == tl.g);
+        if constexpr (kKind == 1) {
+            const int gr = GRP_LDS ? *(__attribute__((address_space(3))) const int*)(grp_lds + a * 64)
+                                   : p.grp[tl.m0 + r];
+            row_ok = row_ok && gr == tl.g;
+        }
         if (!row_ok) continue;
 #pragma unroll
         for (int b = 0; b < TN_; ++b) {
@@ -604,7 +634,14 @@ constexpr int A_SLOT = BM * ROWB_A + S_BYTES;                 // A ahead: one A 
 constexpr int B_SLOT = BN * ROWB_B + NT_INS * 256;            // A ahead: one B slot
 constexpr int A_SLOTS = STAGES + 1;
 constexpr int B_RING = A_SLOTS * A_SLOT;
-constexpr int LDS_BYTES = AAHEAD ? B_RING + STAGES * B_SLOT : STAGES * STAGE_BYTES;
+constexpr int RING_BYTES = AAHEAD ? B_RING + STAGES * B_SLOT : STAGES * STAGE_BYTES;
+// Contiguous form: the expert of each of the wave's rows (WAVE_M <= 64 of them),
+// brought into LDS by one DMA of the wave at the start of the tile, so the
+// epilogue does not wait on global reads of the group index while every CU
+// stores its tile.
+constexpr bool ROW_GRP_LDS = kKind == 1 && WAVE_M <= 64;
+constexpr int GRP_OFF = RING_BYTES;
+constexpr int LDS_BYTES = RING_BYTES + (ROW_GRP_LDS ? NWAVES * 256 : 0);
 static_assert(BM % RPI_A == 0 && BN % RPI_B == 0, "tiles are loaded RPI rows per instruction");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
 
@@ -732,9 +769,18 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
     const u32 b_chunk_lo = FP4B ? (u32)((q ^ ((l16 >> 2) & 3)) << 4) : chunk_lo;
     const u32 a_chunk_lo = FP4A ? (u32)((q ^ ((l16 >> 2) & 3)) << 4) : chunk_lo;
 
+    // contiguous form: the experts of the next work item's row block, read one
+    // work item ahead so that the decode does not wait for them
+    int g_next = 0, g2_next = -1;
+    if constexpr (kKind == 1) {
+        if ((int)blockIdx.x < p.num_tiles) tile_experts(p, blockIdx.x, g_next, g2_next);
+    }
 #pragma unroll 1
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
-        const Tile tl0 = decode_tile(p, t);
+        const Tile tl0 = decode_tile<kKind == 1>(p, t, g_next, g2_next);
+        if constexpr (kKind == 1) {
+            if (t + (int)gridDim.x < p.num_tiles) tile_experts(p, t + gridDim.x, g_next, g2_next);
+        }
         // A contiguous row block of 256 rows holds two 128-row blocks of the
         // layout; when their experts differ the tile is computed once for each
         // (the epilogue stores a row only for its own expert).
@@ -952,9 +998,18 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 s_carry[a] = 0.f;
             }
 
-            // earlier tile's stores and LDS reads are finished before the ring is refilled
-            wait_vmcnt<0>();
+            // Every wave has finished reading the ring (the earlier tile's last K
+            // block) before any refills it.  The earlier tile's stores may still be
+            // in flight: the loads below overlap them, and each wait of the ring
+            // counts only the loads issued after the group it waits for, which
+            // complete in order, so a store still pending only delays a wait.
             __syncthreads();
+            // the experts of this wave's rows (contiguous form), for the epilogue;
+            // rows past M read as 0 and are never stored
+            if constexpr (ROW_GRP_LDS) {
+                dma4(make_rsrc(p.grp, (u32)p.M * 4u), (u32)(tl.m0 + wm * WAVE_M + lane) * 4u, 0u,
+                     __builtin_amdgcn_readfirstlane(smem_base + GRP_OFF + wave * 256));
+            }
 
             const int nst = (tl.kb1 - tl.kb0) / KSTEP;       // stages of this tile
             if constexpr (AAHEAD) {
@@ -1345,7 +1400,9 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 for (int a = 0; a < TM; ++a) acc[a][TN - 1] += p_carry[a] * s_carry[a];
             }
 
-            finish_tile<TM, TN>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag);
+            // (the row experts' DMA has landed: no DMA of this wave outlives the K loop)
+            finish_tile<TM, TN, ROW_GRP_LDS>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag,
+                                             smem_base + GRP_OFF + wave * 256 + l16 * 4);
         }   // pieces
     }
 }
