@@ -139,10 +139,10 @@ def test_register_load_variant_that_spills_is_refused(tmp_path):
     """The kernels that load B straight into registers issue those loads in inline
     assembly, so the compiler must not spill a register such a load may still be
     writing: a forced tile whose code object spills comes back as DG_ERR_JIT instead
-    of running.  (128 x 128 with four waves and four stages spills; three stages
+    of running.  (128 x 128 with four waves and six stages spills; three stages
     do not.)"""
     plan = [(0, 300, 520, 1024, 1, 1)]
-    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path, {"DG_FORCE_CONFIG": "128,128,1,4,4,1,1,1"})
+    r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path, {"DG_FORCE_CONFIG": "128,128,1,4,6,1,1,1"})
     assert r.returncode == 0, r.stderr[-2000:]
     assert " -4 " in r.stdout and "must not spill registers" in r.stdout, r.stdout
     r = _run(PRECOMPILE.format(plans=repr(plan)), tmp_path, {"DG_FORCE_CONFIG": "128,128,1,4,3,1,1,1"})
