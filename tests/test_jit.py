@@ -71,10 +71,9 @@ def _k_loop_scratch_ops(path):
 
 @pytest.mark.skipif(not (os.path.exists(READELF) and os.path.exists(OBJDUMP)), reason="LLVM tools not installed")
 def test_selected_kernels_keep_their_k_loop_out_of_scratch(tmp_path):
-    """No kernel a measured table selects touches scratch memory in its K loop.  (Some
-    256 x 256 kernels and the K-grouped 192 x 256 one spill a few VGPRs of per-tile set-up
-    and epilogue values, stored and reloaded outside the loop; every other selected kernel
-    has no spill at all.)"""
+    """No kernel a measured table selects touches scratch memory, in its K loop or
+    anywhere else.  (A spilled epilogue store address costs a scratch reload, and with
+    it a wait for every store issued before, per store.)"""
     r = _run(PRECOMPILE.format(plans=repr(PLANS)), tmp_path)
     assert r.returncode == 0, r.stderr[-2000:]
     assert all(line.split(")")[1].split()[0] == "0" for line in r.stdout.strip().splitlines()), r.stdout
@@ -88,8 +87,7 @@ def test_selected_kernels_keep_their_k_loop_out_of_scratch(tmp_path):
         assert not _k_loop_scratch_ops(path), f"{name}: scratch access in the K loop"
         if max(v.get("vgpr_spill_count", [0])) or max(v.get("private_segment_fixed_size", [0])):
             spilling.append(name.rsplit("-", 1)[0])
-    # only the largest tiles (192 or 256 rows by 256 columns, eight waves) spill at all
-    assert all("_m256n256_" in n or "_m192n256_" in n for n in spilling), spilling
+    assert not spilling, spilling
 
 
 def test_compile_error_is_dg_err_jit(tmp_path):
