@@ -252,6 +252,9 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
     return (u16)((u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded);  // a select, not a branch
 }
 
+// two BF16 values (x in the low half) in one word
+__device__ __forceinline__ u32 bf16_pair(float x, float y) { return (u32)f32_to_bf16(x) | ((u32)f32_to_bf16(y) << 16); }
+
 __device__ __forceinline__ u32 lds_addr(const void* p) {
     return (u32)(u64)(const __attribute__((address_space(3))) void*)p;
 }
@@ -438,6 +441,11 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t, int g_pre = 
 // holds TM_ x TN_ blocks of 16 x 16: lane (l16, q) owns row row0 + 16 a and
 // the four columns col0 + 16 b + [0, 4) of each (row0, col0 relative to the
 // tile).  Returns after storing, or early when another split finishes the tile.
+// Paired 16-byte stores (see the epilogue) need an even number of n sub-tiles
+// and 8-column alignment of every row, tile and column range.
+template <int TN_>
+constexpr bool PAIRED_STORES = TN_ % 2 == 0 && N % 8 == 0 && N_BEGIN % 8 == 0 && N_END % 8 == 0 && BN % 8 == 0;
+
 // GRP_LDS (contiguous form): the expert of the lane's row row0 + 16 a is the
 // int at LDS address grp_lds + 64 a, instead of being read from global memory.
 template <int TM_, int TN_, bool GRP_LDS = false>
@@ -544,6 +552,35 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
             row_ok = row_ok && gr == tl.g;
         }
         if (!row_ok) continue;
+        if constexpr (PAIRED_STORES<TN_>) {
+            // Sub-tiles b, b + 1 in pairs: lanes q and q ^ 1 (16 apart, same row,
+            // same row_ok) swap four values, so that each lane holds 8 consecutive
+            // columns and the four lanes of a row cover 64 contiguous bytes: even q
+            // keeps its b values and takes its partner's (4 columns on), odd q keeps
+            // its b + 1 values and takes its partner's (4 columns before).
+            const bool odd = ((col0 >> 2) & 1) != 0;
+#pragma unroll
+            for (int b = 0; b < TN_; b += 2) {
+                const int n = tl.n0 + col0 + b * 16;      // this lane's columns of sub-tile b
+                const u64 off = row_base + (u64)r * N + n;
+                v4f v0 = acc[a][b], v1 = acc[a][b + 1];
+                if constexpr (HAS_C) {
+                    if (n < N_END) v0 += *(const v4f*)(p.C + off);
+                    if (n + 16 < N_END) v1 += *(const v4f*)(p.C + off + 16);
+                }
+                const u32 lo0 = bf16_pair(v0.x, v0.y), hi0 = bf16_pair(v0.z, v0.w);
+                const u32 lo1 = bf16_pair(v1.x, v1.y), hi1 = bf16_pair(v1.z, v1.w);
+                // ds_swizzle, bit mode: lane ^ 16 inside each half of the wave
+                const u32 r_lo = (u32)__builtin_amdgcn_ds_swizzle((int)(odd ? lo0 : lo1), 0x401F);
+                const u32 r_hi = (u32)__builtin_amdgcn_ds_swizzle((int)(odd ? hi0 : hi1), 0x401F);
+                const int n_out = odd ? n + 12 : n;         // odd: columns 16 (b + 1) + 4 (q - 1) ..
+                if (n_out >= N_END) continue;
+                const v4i o = odd ? v4i{(int)r_lo, (int)r_hi, (int)lo1, (int)hi1}
+                                  : v4i{(int)lo0, (int)hi0, (int)r_lo, (int)r_hi};
+                *(v4i*)(p.D + row_base + (u64)r * N + n_out) = o;
+            }
+            continue;
+        }
 #pragma unroll
         for (int b = 0; b < TN_; ++b) {
             const int n = tl.n0 + col0 + b * 16;
