@@ -1649,8 +1649,10 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
         float s_carry = 0.f;
         v4i breg[NKB][TN][2];
 
-        // earlier tile's stores and LDS reads are finished before LDS is refilled
-        wait_vmcnt<0>();
+        // Every wave has finished reading LDS (the earlier tile's) before it is
+        // refilled.  The earlier tile's stores may still be in flight: the waits
+        // below count only loads issued after the ones they wait for, which
+        // complete in order, so a pending store only delays a wait.
         __syncthreads();
 
         if constexpr (ARES) {
@@ -1996,8 +1998,8 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
         float s_carry = 0.f;
         v4i breg[NKB][TN][2];
 
-        // earlier tile's stores are finished before this wave's load accounting starts
-        wait_vmcnt<0>();
+        // (no load of the earlier tile is in flight, only its stores, which the
+        // waits below may wait for but never count as loads that landed)
         static_for<PRE_UNITS>([&]<int J>() __attribute__((always_inline)) { issue_b(tl.kb0 + J, breg[J]); });
 
         static_for<NKB>([&]<int IT>() __attribute__((always_inline)) {
@@ -2233,8 +2235,8 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
         float s_carry = 0.f;
         v4i breg[NSETS][TN][2];
 
-        // earlier tile's stores and LDS reads are finished before the ring is refilled
-        wait_vmcnt<0>();
+        // every wave has finished reading the ring before it is refilled (the
+        // earlier tile's stores may still be in flight; see variant 1)
         __syncthreads();
         // A of K blocks 0 .. SLOTS-2, then B of K blocks 0 .. DEPTH-1
 #pragma unroll
