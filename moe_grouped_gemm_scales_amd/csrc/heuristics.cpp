@@ -193,9 +193,9 @@ const Tuned kTuned[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 1, 4, 4, 7, 1, 2, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 1, 6, 3, 1, 1, 3, 0, 0},
     {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 2, 1, 2, 0, 0, 0},
-    // the large shapes: 256 x 256 with the split refill (variant 6), 475 us against
-    // 490-505 us for the one-part refill; contiguous: 995-1002 us against 1037-1040 us
-    // for the one-part refill and 1045-1088 us for 128 x 256 with three slots
+    // the large shapes: 256 x 256 with the split refill (variant 6): 426-434 us against
+    // 449 us for the one-part refill and 447-465 us for 256 x 224 (512 tiles, two full
+    // rounds); contiguous: 808 us against 862 us for the one-part refill (one box)
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
@@ -207,9 +207,9 @@ const Tuned kTuned[] = {
 };
 
 // Packed UE8M0 scales (one K block a stage; no promotion in the K loop).  The
-// large shapes use 256 x 256 with the split refill (variant 6): 432-435 us against
-// 454-462 us for 256 x 224 with A a block further ahead (variant 4); contiguous
-// 872-891 us against 980-1000 us for 128 x 256 with three slots (one box)
+// large shapes use 256 x 256 with the split refill (variant 6): 399-404 us against
+// 411 us for four waves of 128 x 128 with accumulators in AGPRs; contiguous 739-746 us
+// against 790 us for the four-wave tile and 845 us for it without the split (one box)
 const Tuned kTunedE8[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
