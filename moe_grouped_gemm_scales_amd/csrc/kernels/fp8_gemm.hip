@@ -252,6 +252,14 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
     return (u16)((u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded);  // a select, not a branch
 }
 
+// The lane's index within its wave, computed where it is called (an asm the
+// compiler neither hoists nor merges with an earlier copy).
+__device__ __forceinline__ int lane_id_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // two BF16 values (x in the low half) in one word
 __device__ __forceinline__ u32 bf16_pair(float x, float y) { return (u32)f32_to_bf16(x) | ((u32)f32_to_bf16(y) << 16); }
 
@@ -1438,8 +1446,12 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             }
 
             // (the row experts' DMA has landed: no DMA of this wave outlives the K loop)
-            finish_tile<TM, TN, ROW_GRP_LDS>(p, tl, acc, a_row0, wn * WAVE_N + 4 * q, tid, &s_flag,
-                                             smem_base + GRP_OFF + wave * 256 + l16 * 4);
+            // The lane's row and column bases and its thread index are taken afresh from
+            // the lane id here, so that no per-lane value has to live across the K loop
+            // for the epilogue.
+            const int ln = lane_id_now();
+            finish_tile<TM, TN, ROW_GRP_LDS>(p, tl, acc, wm * WAVE_M + (ln & 15), wn * WAVE_N + 4 * (ln >> 4),
+                                             wave * 64 + ln, &s_flag, smem_base + GRP_OFF + wave * 256 + (ln & 15) * 4);
         }   // pieces
     }
 }
