@@ -90,6 +90,33 @@ def test_selected_kernels_keep_their_k_loop_out_of_scratch(tmp_path):
     assert not spilling, spilling
 
 
+def _epilogue_stores(path):
+    """Global store instructions of the GEMM kernel, by width, in the AMD disassembly."""
+    out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", path], capture_output=True, text=True).stdout
+    body = out.split("<dg_fp8_gemm_nt_kernel>:", 1)[1].split("\n\n", 1)[0]
+    return {w: body.count(f"global_store_{w} ") for w in ("dwordx4", "dwordx2", "short", "dword")}
+
+
+@pytest.mark.skipif(not (os.path.exists(READELF) and os.path.exists(OBJDUMP)), reason="LLVM tools not installed")
+def test_wide_tile_epilogues_store_sixteen_bytes(tmp_path):
+    """The selected 256-column tiles of eight waves (an even number of n sub-tiles per
+    wave) store D in 16-byte pieces only: lanes 16 apart swap values so that a lane holds 8
+    consecutive columns.  (With 8-byte stores the contiguous workload wrote D to the fabric
+    twice.)"""
+    plans = [pl for pl in PLANS if pl[2] in (4096, 7168)]
+    r = _run(PRECOMPILE.format(plans=repr(plans)), tmp_path)
+    assert r.returncode == 0, r.stderr[-2000:]
+    checked = 0
+    for path in glob.glob(str(tmp_path / "*.hsaco")):
+        name = os.path.basename(path)
+        if "n256_w4x2" not in name:
+            continue
+        st = _epilogue_stores(path)
+        assert st["dwordx4"] >= 8 and st["dwordx2"] == 0 and st["short"] == 0, (name, st)
+        checked += 1
+    assert checked >= 5, checked
+
+
 def test_compile_error_is_dg_err_jit(tmp_path):
     r = _run(PRECOMPILE.format(plans=repr([(0, 64, 64, 128, 1, 0)])), tmp_path,
              {"DG_JIT_EXTRA_OPTION": "-DDG_BM=not_a_number"})
