@@ -93,7 +93,7 @@ dg_status dg_fp8_gemm_nt(const void *A, const float *sfa, const void *B, const f
  *     (otherwise DG_ERR_UNSUPPORTED).
  *   - Split-K partial sums and arrival counters (shapes with few rows and a
  *     long K) live in a static device array of the library, 32 MiB of partial
- *     sums plus 64 KiB of counters per device, held until the process ends,
+ *     sums plus 256 KiB of counters per device, held until the process ends,
  *     instead of a per-stream workspace.  A shape whose split-K needs more is
  *     rejected with DG_ERR_UNSUPPORTED.  Each call first zeroes the counters
  *     it uses (a small kernel on `stream`).

@@ -272,7 +272,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
         for (const Segment& seg : it->second.segs) {
             if (seg.cfg.splitk <= 1 || seg.items <= 0) continue;
             partial_bytes = std::max(partial_bytes, (size_t)seg.items * seg.cfg.bm * seg.cfg.bn * sizeof(float));
-            counter_bytes = std::max(counter_bytes, (size_t)(seg.items / seg.cfg.splitk) * sizeof(uint32_t));
+            counter_bytes = std::max(counter_bytes, split_k_counter_bytes(seg.cfg, seg.items));
         }
         if (partial_bytes > kScratchPartialBytes || counter_bytes > kScratchCounterBytes)
             return set_error(DG_ERR_UNSUPPORTED,
@@ -388,7 +388,7 @@ dg_status launch(const Problem& p, const void* A, const void* sfa, const void* B
     for (const Segment& seg : it->second.segs) {
         if (seg.cfg.splitk <= 1 || seg.items <= 0) continue;
         need_p = std::max(need_p, (size_t)seg.items * seg.cfg.bm * seg.cfg.bn * sizeof(float));
-        need_c = std::max(need_c, (size_t)(seg.items / seg.cfg.splitk) * sizeof(uint32_t));
+        need_c = std::max(need_c, split_k_counter_bytes(seg.cfg, seg.items));
     }
     if (need_p > 0) {
         Workspace* ws = nullptr;

@@ -105,6 +105,9 @@ constexpr int kKind = DG_KIND;
 constexpr int BM = DG_BM, BN = DG_BN, WM = DG_WM, WN = DG_WN;
 constexpr int NWAVES = WM * WN;
 constexpr int NTHREADS = 64 * NWAVES;
+// split-K arrival counters: one per output tile and wave, each in a 128-byte
+// line of its own (the host sizes the counter buffer with the same stride)
+constexpr int CTR_STRIDE = 32;
 constexpr int WAVE_M = BM / WM, WAVE_N = BN / WN;
 constexpr int TM = WAVE_M / 16, TN = WAVE_N / 16;
 constexpr int STAGES = DG_STAGES;
@@ -445,10 +448,11 @@ __device__ __forceinline__ Tile decode_tile(const Params& p, int t, int g_pre = 
 
 
 // ------------------------------------------------------------ end of a work item
-// Split-K bookkeeping and the epilogue, shared by both kernel variants.  acc
+// Split-K bookkeeping and the epilogue, shared by every kernel variant.  acc
 // holds TM_ x TN_ blocks of 16 x 16: lane (l16, q) owns row row0 + 16 a and
 // the four columns col0 + 16 b + [0, 4) of each (row0, col0 relative to the
-// tile).  Returns after storing, or early when another split finishes the tile.
+// tile).  Returns after storing, or early when another split finishes this
+// wave's slice of the tile.
 // Paired 16-byte stores (see the epilogue) need an even number of n sub-tiles
 // and 8-column alignment of every row, tile and column range.
 template <int TN_>
@@ -458,7 +462,7 @@ constexpr bool PAIRED_STORES = TN_ % 2 == 0 && N % 8 == 0 && N_BEGIN % 8 == 0 &&
 // int at LDS address grp_lds + 64 a, instead of being read from global memory.
 template <int TM_, int TN_, bool GRP_LDS = false>
 __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f (&acc)[TM_][TN_], int row0,
-                                            int col0, int tid, int* s_flag, u32 grp_lds = 0) {
+                                            int col0, int tid, u32 grp_lds = 0) {
     // An MFMA reads the operands of every lane of its wave, whatever EXEC
     // holds.  Pin every accumulator here, while the whole wave is active:
     // otherwise, when the K loop is short enough to be laid out straight, the
@@ -479,13 +483,18 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
         // policy (sc1), which writes them through this XCD's L2 to the
         // device-coherent side (Infinity Fabric, MALL, HBM); the last arrival
         // reads them back with agent-scope loads, which do not take a line from
-        // its own L2.  This wave waits for its stores' acknowledgement (vmcnt 0)
-        // before the barrier, and the barrier comes before the agent-scope
-        // arrival atomic, so when the count shows every split arrived, every
-        // partial is at the coherence point.
+        // its own L2.  Each wave hands off its own slice of the tile: its lanes
+        // write, and the lanes of that wave in the last split read, the same
+        // words of every split's partial, and the wave's arrival has a counter of
+        // its own, alone in a 128-byte line (atomics on one line are serialised
+        // where they are performed: with four counters to a line the hand-off
+        // took 0.9 us longer).  The wave waits for its stores' acknowledgement (vmcnt 0)
+        // before its agent-scope arrival atomic, so when that count shows every
+        // split arrived, every split's slice is at the coherence point.  No
+        // workgroup barrier: a wave that is not last returns at once.
         constexpr int CPOL_AGENT = 16;
-        const __amdgpu_buffer_rsrc_t rs_ws =
-            __builtin_amdgcn_make_buffer_rsrc(ws, 0, SPLITK * BM * BN * 4, 0x00020000);
+        constexpr u32 WS_BYTES = SPLITK * BM * BN * 4;
+        const __amdgpu_buffer_rsrc_t rs_ws = __builtin_amdgcn_make_buffer_rsrc(ws, 0, WS_BYTES, 0x00020000);
 #pragma unroll
         for (int a = 0; a < TM_; ++a)
 #pragma unroll
@@ -494,20 +503,27 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
                     __builtin_bit_cast(v4i, acc[a][b]), rs_ws,
                     (tl.split * BM * BN + ((a * TN_ + b) * NTHREADS + tid) * 4) * 4, 0, CPOL_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) {
-            u32 old = __hip_atomic_fetch_add(&p.counters[tl.mn], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *s_flag = (old == (u32)(SPLITK - 1));
-            if (old == (u32)(SPLITK - 1))
-                __hip_atomic_store(&p.counters[tl.mn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        u32* const ctr = p.counters + ((u64)tl.mn * NWAVES + (tid >> 6)) * CTR_STRIDE;
+        u32 old = 0;
+        if ((tid & 63) == 0) {
+            old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == (u32)(SPLITK - 1)) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
-        if (!*s_flag) return;
+        if (__builtin_amdgcn_readfirstlane(old) != (u32)(SPLITK - 1)) return;
         asm volatile("" ::: "memory");
-        // Every partial, this split's own included (it reads back exactly what it
-        // wrote), is loaded unconditionally, CH splits at a time so that their
-        // loads are in flight together without running out of registers; they
-        // are summed in split order, the same order on every run.
+        // Every partial is summed in split order, the same order on every run,
+        // CH splits' loads in flight together without running out of registers.
+        // With few sub-tiles this split's own partial is kept in registers (the
+        // same bits it stored) and its load is given an offset past the buffer,
+        // which returns zeros without a memory access.
+        constexpr bool OWN = TM_ * TN_ <= 8;
+        v4f own[OWN ? TM_ : 1][OWN ? TN_ : 1];
+        if constexpr (OWN) {
+#pragma unroll
+            for (int a = 0; a < TM_; ++a)
+#pragma unroll
+                for (int b = 0; b < TN_; ++b) own[a][b] = acc[a][b];
+        }
         constexpr int CH0 = 28 / (TM_ * TN_);
         constexpr int CH = CH0 < 1 ? 1 : (CH0 > SPLITK ? SPLITK : CH0);
         int wofs = 0;
@@ -516,23 +532,32 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Tile& tl, v4f
             v4f part[CH][TM_][TN_];
 #pragma unroll
             for (int c = 0; c < CH; ++c)
-                if (s0 + c < SPLITK)
+                if (s0 + c < SPLITK) {
+                    const bool mine = OWN && s0 + c == tl.split;
 #pragma unroll
                     for (int a = 0; a < TM_; ++a)
 #pragma unroll
                         for (int b = 0; b < TN_; ++b)
                             part[c][a][b] = __builtin_bit_cast(
                                 v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rs_ws, (wofs + (s0 + c) * BM * BN + ((a * TN_ + b) * NTHREADS + tid) * 4) * 4,
+                                         rs_ws,
+                                         mine ? WS_BYTES
+                                              : (wofs + (s0 + c) * BM * BN + ((a * TN_ + b) * NTHREADS + tid) * 4) * 4,
                                          0, CPOL_AGENT));
+                }
 #pragma unroll
             for (int c = 0; c < CH; ++c)
-                if (s0 + c < SPLITK)
+                if (s0 + c < SPLITK) {
+                    const bool mine = OWN && s0 + c == tl.split;
 #pragma unroll
                     for (int a = 0; a < TM_; ++a)
 #pragma unroll
-                        for (int b = 0; b < TN_; ++b)
-                            acc[a][b] = (s0 + c == 0) ? part[c][a][b] : acc[a][b] + part[c][a][b];
+                        for (int b = 0; b < TN_; ++b) {
+                            v4f v = part[c][a][b];
+                            if constexpr (OWN) v = mine ? own[a][b] : v;
+                            acc[a][b] = (s0 + c == 0) ? v : acc[a][b] + v;
+                        }
+                }
             // the next chunk's loads depend on this opaque zero, taken after this
             // chunk's sums, so the compiler cannot hoist them all (and spill them)
             // ahead of those sums
@@ -784,7 +809,6 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
                  "s"(num_tiles), "s"(gridDim.x));
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1451,7 +1475,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
             // for the epilogue.
             const int ln = lane_id_now();
             finish_tile<TM, TN, ROW_GRP_LDS>(p, tl, acc, wm * WAVE_M + (ln & 15), wn * WAVE_N + 4 * (ln >> 4),
-                                             wave * 64 + ln, &s_flag, smem_base + GRP_OFF + wave * 256 + (ln & 15) * 4);
+                                             wave * 64 + ln, smem_base + GRP_OFF + wave * 256 + (ln & 15) * 4);
         }   // pieces
     }
 }
@@ -1534,7 +1558,6 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(ws), "s"(counters), "s"(M),
                  "s"(num_tiles), "s"(gridDim.x));
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1768,7 +1791,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
         });
         acc[TM - 1][TN - 1] += p_carry * s_carry;
 
-        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid);
     }
 }
 #elif DG_VARIANT == 3
@@ -1864,7 +1887,6 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
     __shared__ u32 ready[SLOTS];     // K block index + 1 held by the slot, once landed
     __shared__ u32 freed[SLOTS];     // consumer waves done with the slot's current block
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1957,12 +1979,6 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 wait_vmcnt<(NKB - 1 - kb) * PU>();
                 publish(kb);
             });
-            // the two workgroup barriers of the split-K hand-off in finish_tile
-            // (the producer holds no partial sums)
-            if constexpr (SPLITK > 1) {
-                __syncthreads();
-                __syncthreads();
-            }
             continue;
         }
 
@@ -2074,7 +2090,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
         });
         acc[TM - 1][TN - 1] += p_carry * s_carry;
 
-        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid);
     }
 }
 #elif DG_VARIANT == 5
@@ -2142,7 +2158,6 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
     asm volatile("" :: "s"(A), "s"(sfa), "s"(B), "s"(sfb), "s"(C), "s"(D), "s"(grp), "s"(M), "s"(num_tiles),
                  "s"(gridDim.x));
     __shared__ __attribute__((aligned(1024))) u8 smem[LDS_BYTES];
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -2337,7 +2352,7 @@ dg_fp8_gemm_nt_kernel(const KernArgs ka) {
                 tie(breg[s2][b][1]);
             }
 
-        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid, &s_flag);
+        finish_tile<TM, TN>(p, tl, acc, l16, wave_n + 4 * q, tid);
     }
 }
 #endif
