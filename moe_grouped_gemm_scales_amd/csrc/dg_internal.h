@@ -109,8 +109,6 @@ std::string cache_dir();
 // (device.hip); [0] counts bounded waits in the kernels that gave up.
 dg_status status_words(unsigned int** out);
 
-// Scratch of dg_fp8_gemm_nt_noalloc (device.hip): a static device array of
-// split-K partial sums followed by arrival counters, one copy per device.
 // Split-K arrival counters of a launch of `items` work items: one per output
 // tile and computing wave (each wave hands off its own slice of the tile), each
 // alone in a 128-byte line (the kernel's CTR_STRIDE of 32 words).
@@ -119,6 +117,8 @@ inline size_t split_k_counter_bytes(const KernelConfig& c, int items) {
     return (size_t)(items / c.splitk) * (size_t)(c.wm * c.wn) * kCounterStrideBytes;
 }
 
+// Scratch of dg_fp8_gemm_nt_noalloc (device.hip): a static device array of
+// split-K partial sums followed by arrival counters, one copy per device.
 constexpr size_t kScratchPartialBytes = size_t(32) << 20;
 constexpr size_t kScratchCounterBytes = size_t(256) << 10;
 // its device address on the current device (hipGetSymbolAddress)

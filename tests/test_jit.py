@@ -202,3 +202,16 @@ def test_kernel_takes_one_by_value_argument_of_the_host_layout(tmp_path):
         explicit = [it for it in items if not it[".value_kind"].startswith("hidden_")]
         assert explicit == [{".offset": "0", ".size": "96", ".value_kind": "by_value"}], (os.path.basename(path),
                                                                                           explicit)
+
+
+def test_split_k_counter_stride_agrees_between_kernel_and_host():
+    """The kernel indexes a wave's arrival counter CTR_STRIDE words apart and the
+    host sizes the counter buffer kCounterStrideBytes per counter: the two are
+    compiled separately (hipRTC and the host compiler), so they are compared here."""
+    import re
+    kern = open(os.path.join(ROOT, "moe_grouped_gemm_scales_amd", "csrc", "kernels", "fp8_gemm.hip")).read()
+    host = open(os.path.join(ROOT, "moe_grouped_gemm_scales_amd", "csrc", "dg_internal.h")).read()
+    words = int(re.search(r"constexpr int CTR_STRIDE = (\d+);", kern).group(1))
+    stride = int(re.search(r"constexpr size_t kCounterStrideBytes = (\d+);", host).group(1))
+    assert words * 4 == stride
+    assert stride >= 128, "one counter per 128-byte line: atomics on a shared line are serialised"
