@@ -17,7 +17,11 @@ MI355X peak (8 TB/s HBM, 5.0 PFLOP/s dense FP8), and also of the peaks this
 part reaches with the library's probes (a streaming read, back-to-back MFMAs).
 
 Timing.  The K timed steps are captured in one HIP graph and replayed between
-one event pair on the launching stream (the average launch duration); besides,
+one event pair on the launching stream (the average launch duration).  Before
+that the W warm-up calls run and the graph is replayed once untimed; where one
+replay takes a millisecond or more, further untimed replays follow until the
+GPU has run at least 60 ms back to back, since the part raises its clock over
+some tens of milliseconds of sustained load.  Besides,
 every shape is timed launch by launch (at least 50 launches for the short
 shapes, 10 for the long ones), each behind a spin kernel that keeps the GPU
 busy while the host enqueues the launch, for the median and the minimum.
@@ -45,6 +49,7 @@ PEAK_FP8_TFLOPS = 5000.0    # also the peak used for FP8 x FP4: each MFMA there 
 PEAK_BF16_TFLOPS = 2500.0   # dense BF16 MFMA peak (the unscaled BF16 GEMM)
 PEAK_FP4_TFLOPS = 10100.0   # dense FP4 MFMA peak (FP4 x FP4)
 RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
+WARM_S = 0.06               # seconds of back-to-back untimed work before a timed region
 # The pages' H800 numbers for the same shapes (DeepGEMM launch article,
 # section 3 dense table): other hardware, context only.
 PAGES_TFLOPS = {0: 206.0, 1: 535.0, 2: 1358.0}
@@ -228,8 +233,23 @@ def bench_workload(p, steps: int, warmup: int, samples: int, graph: bool, mode: 
             with torch.cuda.graph(g, stream=stream):
                 for i in range(steps):
                     call(i)
+            t_up = time.perf_counter()
             g.replay()
             torch.cuda.synchronize()
+            t_up = time.perf_counter() - t_up
+        # The part raises its clock over some tens of milliseconds of sustained
+        # load: after an idle pause, 20 steps of 4096 x 7168 x 16384 timed 472,
+        # 435, 404 and 401 us per step after 0, 1, 3 and 10 untimed replays.  So
+        # where one replay takes a millisecond or more, the untimed replays go on
+        # until the GPU has run WARM_S back to back.  A short timed region keeps
+        # the single replay: after 60-90 ms of back-to-back short kernels, 20
+        # steps of 64 x 2112 x 7168 (0.2 ms) now and then landed in a clock
+        # transition (10.5 us per step became 13-18 us).  Either way the timed
+        # region below is exactly the K steps.
+        if graph and t_up >= 1e-3:
+            for _ in range(max(0, math.ceil(WARM_S / t_up) - 1)):
+                g.replay()
+        torch.cuda.synchronize()
         # Timed region: the K calls back to back on this stream, one HIP event pair
         # (recorded on this stream) around all of them.
         torch.cuda.synchronize()
