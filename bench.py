@@ -246,9 +246,9 @@ def bench_workload(p, steps: int, warmup: int, samples: int, graph: bool, mode: 
         # steps of 64 x 2112 x 7168 (0.2 ms) now and then landed in a clock
         # transition (10.5 us per step became 13-18 us).  Either way the timed
         # region below is exactly the K steps.
-        if graph and t_up >= 1e-3:
-            for _ in range(max(0, math.ceil(WARM_S / t_up) - 1)):
-                g.replay()
+        n_warm = max(0, math.ceil(WARM_S / t_up) - 1) if graph and t_up >= 1e-3 else 0
+        for _ in range(n_warm):
+            g.replay()
         torch.cuda.synchronize()
         # Timed region: the K calls back to back on this stream, one HIP event pair
         # (recorded on this stream) around all of them.
@@ -288,7 +288,7 @@ def bench_workload(p, steps: int, warmup: int, samples: int, graph: bool, mode: 
                 kernel_ms=kernel_ms, ms_per_step=wall * 1e3 / steps, wall_s=wall, tflops=tflops, gbs=gbs,
                 bound=bound, frac=frac, jit_s=t_jit, step_tflops=flops / (wall / steps) / 1e12,
                 median_us=statistics.median(per_launch), min_us=min(per_launch), samples=samples,
-                spin_us=spin_us)
+                spin_us=spin_us, untimed_replays=(1 + n_warm) if graph else 0)
 
 
 def measured_peaks():
@@ -644,6 +644,7 @@ def main():
         "kernel_median_us": round(r["median_us"], 3),
         "kernel_min_us": round(r["min_us"], 3),
         "kernel_samples": r["samples"],
+        "untimed_replays": r["untimed_replays"],
         "kernel_tflops": round(r["tflops"], 3),
         "hbm_gbs": round(r["gbs"], 1),
         "roofline": roof,
