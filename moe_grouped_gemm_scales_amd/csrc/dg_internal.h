@@ -40,6 +40,8 @@ struct KernelConfig {
                                // 5 UE8M0 pairs in 16-bit words, MN-major (A and B)
     int nb = 0, ne = 0;        // columns [nb, ne) of D (ne = 0: all N); one call may
                                // launch two column ranges with different tile widths
+    int bstream = 0;           // each B block is read by at most two row blocks of the launch
+                               // (dense or masked, few rows): B loads carry the non-temporal hint
 
     int n_begin() const { return nb; }
     int n_end() const { return ne > 0 ? ne : n; }

@@ -68,6 +68,7 @@ std::vector<std::string> compile_options(const KernelConfig& c) {
     if (c.variant == 4) def("DG_AAHEAD", 1);
     if (c.variant == 6) def("DG_SPLIT", 1);
     def("DG_SF", c.sf);
+    if (c.bstream) def("DG_BSTREAM", 1);
     if (c.ne > 0) {
         def("DG_NB", c.nb);
         def("DG_NE", c.ne);
@@ -186,6 +187,7 @@ std::string KernelConfig::key() const {
     s << "k" << kind << (variant ? "v" + std::to_string(variant) : std::string()) << "_m" << bm << "n" << bn << "_w" << wm << "x" << wn << "_s" << stages << "x" << kstep
       << "_sk" << splitk
       << "_c" << has_c << "_N" << n << "_K" << k << "_G" << g;
+    if (bstream) s << "_bs";
     if (sf == 1) s << "_e8m0";
     if (sf == 2) s << "_f8f4";
     if (sf == 3) s << "_bf16";
