@@ -483,9 +483,9 @@ def cpu_baseline(p, budget_s: float = 20.0):
                 sample=desc, cpu_model=cpu_model())
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel source and the same plan."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -494,7 +494,7 @@ def traffic_for(workload: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -610,7 +610,7 @@ def main():
                 peak=r["peak"] if r["bound"] == "mfma" else PEAK_HBM_GBS,
                 unit="TFLOP/s" if r["bound"] == "mfma" else "GB/s",
                 frac=round(r["frac"], 4),
-                traffic=traffic_for(name))
+                traffic=traffic_for(name, r["kernel"]))
     if peaks and r["peak"] == PEAK_FP8_TFLOPS:
         meas = peaks["mfma_fp8_tflops"] if r["bound"] == "mfma" else peaks["hbm_read_gbs"]
         roof["measured_peak"] = meas

@@ -198,7 +198,10 @@ const Tuned kTuned[] = {
     // rounds); contiguous: 808 us against 862 us for the one-part refill (one box)
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
-    {kMasked, 256, 7168, 2048, 4, 0, 128, 112, 1, 7, 3, 1, 1, 3, 0, 0},
+    // the masked decode shape, B streamed: 128 x 128 on variant 0 with three stages
+    // 17.47-17.58 us against 17.97-18.10 us for the producer variant with 128 x 112
+    // (one box; before B was streamed the producer variant led, 20.6 against 20.4-21.7)
+    {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},
     // K-grouped weight gradient of the contiguous workload (K: the row pitch of the
     // K-contiguous operands, 4 x 8192 tokens): 192 x 256 with two stages measured 2-4 %
     // under 128 x 256 with three (22 row tiles, the last one a third full); with the split

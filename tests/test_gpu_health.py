@@ -38,11 +38,15 @@ def _giveups() -> int:
 
 
 # ------------------------------------------------------------------ bounded waits
-def test_variant3_waits_never_give_up(oracle):
+def test_variant3_waits_never_give_up(oracle, monkeypatch):
     import moe_grouped_gemm_scales_amd as dg
     dg.reset_wait_giveups()
     assert _giveups() == 0
-    for cfg in (1, 4):                       # the two workloads whose plans use the producer wave
+    # the dense 128-row workload's plan uses the producer wave; the masked decode
+    # workload runs it with the producer variant forced
+    for cfg, forced in ((1, None), (4, "128,112,1,7,3,1,1,3")):
+        if forced:
+            monkeypatch.setenv("DG_FORCE_CONFIG", forced)
         p = gen.make_workload(cfg)
         kind = 0 if p.kind == "dense" else 2
         rows = p.A.shape[1] if p.kind == "masked" else p.M
