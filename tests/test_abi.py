@@ -150,3 +150,20 @@ def test_describe_config_for_new_forms():
     assert pkg.describe_config(pkg.KIND_K_GROUPED, 4096, 7168, 32768, 4, num_cus=256).startswith("k3")
     key = pkg.describe_config(pkg.KIND_BF16, 4096, 7168, 16384, num_cus=256)
     assert key.endswith("_bf16") and "_K32768_" in key       # BF16 rows counted in bytes
+
+
+def test_b_is_streamed_only_where_two_row_blocks_at_most_read_it():
+    """Plans whose B blocks at most two row blocks of the launch read (dense or
+    masked with few rows) carry `_bs`; the large and contiguous plans, whose row
+    blocks share B blocks through L2, do not."""
+    streamed = [pkg.describe_config(0, 64, 2112, 7168, num_cus=256),
+                pkg.describe_config(0, 128, 24576, 1536, num_cus=256),
+                pkg.describe_config(0, 128, 24576, 1536, has_c=True, num_cus=256),
+                pkg.describe_config(2, 256, 7168, 2048, 4, num_cus=256),
+                pkg.describe_config(0 | pkg.SCALE_UE8M0, 128, 24576, 1536, num_cus=256)]
+    shared = [pkg.describe_config(0, 4096, 7168, 16384, num_cus=256),
+              pkg.describe_config(1, 32768, 4096, 7168, 4, num_cus=256),
+              pkg.describe_config(pkg.KIND_K_GROUPED, 4096, 7168, 32768, 4, num_cus=256),
+              pkg.describe_config(0, 1024, 4096, 1024, num_cus=256)]
+    assert all("_bs" in k for k in streamed), streamed
+    assert not any("_bs" in k for k in shared), shared
