@@ -216,6 +216,8 @@ const Tuned kTuned[] = {
 const Tuned kTunedE8[] = {
     {kDense, 64, 2112, 7168, 1, 0, 64, 64, 2, 2, 4, 7, 1, 0, 0, 0},
     {kDense, 128, 24576, 1536, 1, 0, 128, 96, 4, 2, 3, 1, 1, 0, 0, 0},
+    // with C: 15.8 us against 16.7-16.8 us for the model's 128 x 128 with 2 x 4 waves (one box)
+    {kDense, 128, 24576, 1536, 1, 1, 128, 96, 4, 2, 4, 1, 1, 0, 0, 0},
     {kDense, 4096, 7168, 16384, 1, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kContiguous, -1, 4096, 7168, 4, 0, 256, 256, 4, 2, 2, 1, 1, 6, 0, 0},
     {kMasked, 256, 7168, 2048, 4, 0, 128, 128, 4, 2, 3, 1, 1, 0, 0, 0},

@@ -516,7 +516,7 @@ def test_ue8m0_forced_tile_configs(oracle, monkeypatch, forced):
     _compare(p, D, sent, ref, comp, what=f"ue8m0 forced {forced}")
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, "1c", 2, 3, 4])
 def test_ue8m0_workloads(oracle, cfg):
     p = gen.make_workload(cfg, ue8m0=True)
     D, sent = run(p)
